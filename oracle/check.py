@@ -1,0 +1,77 @@
+"""Pass criteria of the parity tests — test infrastructure only.
+
+* Quantized activation and weight bytes and their float32 scales are unique
+  under the oracle's readings, so they must match bit for bit.
+* The bfloat16 outputs depend on the order of the float32 accumulation on
+  the GPU, so they are compared with the oracle's float64 value elementwise,
+  with a relative tolerance of 1e-2 against the oracle's own magnitude.
+  Reading of "relative to the output magnitude": the reference magnitude of
+  an element is ``max(|y64[m, n]|, 2^-8 * rms(y64[m, :]))``; the floor stops a
+  legitimate float32 cancellation near zero from failing, and is far below
+  anything that an error in the method (a dropped term, a wrong scale) would
+  produce.  A row whose oracle output is all zero must be exactly +-0.
+  NaN or infinity in the GPU output is always a failure.
+"""
+
+import numpy as np
+
+from .bf16 import bf16_bits_to_f32, f64_to_bf16_bits
+
+REL_TOL = 1e-2
+RMS_FLOOR = 2.0 ** -8
+
+
+def check_bytes(got: np.ndarray, want: np.ndarray, what: str = "bytes"):
+    """Raise AssertionError with the first mismatches unless equal bit for bit."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    if got.shape != want.shape:
+        raise AssertionError(f"{what}: shape {got.shape} != {want.shape}")
+    if got.dtype.itemsize != want.dtype.itemsize:
+        raise AssertionError(f"{what}: itemsize differs")
+    g = got.view(np.dtype(f"u{got.dtype.itemsize}"))
+    w = want.view(np.dtype(f"u{want.dtype.itemsize}"))
+    bad = np.argwhere(g != w)
+    if bad.size:
+        first = [tuple(int(i) for i in b) for b in bad[:8]]
+        detail = ", ".join(f"{i}: got {g[i]:#x} want {w[i]:#x}" for i in first)
+        raise AssertionError(f"{what}: {len(bad)} mismatches; first {detail}")
+
+
+def close_report(y_bf16_bits: np.ndarray, y64: np.ndarray) -> dict:
+    """Elementwise comparison data (no assertion)."""
+    y = bf16_bits_to_f32(y_bf16_bits).astype(np.float64)
+    y64 = np.asarray(y64, dtype=np.float64)
+    if y.shape != y64.shape:
+        raise AssertionError(f"output shape {y.shape} != {y64.shape}")
+    rms = np.sqrt(np.mean(y64 * y64, axis=-1, keepdims=True)) if y64.size \
+        else np.zeros(y64.shape[:-1] + (1,))
+    ref = np.maximum(np.abs(y64), RMS_FLOOR * rms)
+    err = np.abs(y - y64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(ref > 0, err / np.where(ref > 0, ref, 1.0),
+                       np.where(err > 0, np.inf, 0.0))
+    finite = np.isfinite(y)
+    exact_bf16 = f64_to_bf16_bits(y64) == np.asarray(y_bf16_bits, np.uint16)
+    return {
+        "max_rel": float(np.max(rel)) if rel.size else 0.0,
+        "worst_index": tuple(int(i) for i in np.unravel_index(
+            np.argmax(rel), rel.shape)) if rel.size else (),
+        "n_bad": int(np.sum((rel > REL_TOL) | ~finite)),
+        "all_finite": bool(np.all(finite)),
+        "frac_bf16_equal": float(np.mean(exact_bf16)) if rel.size else 1.0,
+        "rel": rel,
+    }
+
+
+def check_close(y_bf16_bits: np.ndarray, y64: np.ndarray, what="output"):
+    """Raise unless every element is within the elementwise tolerance."""
+    r = close_report(y_bf16_bits, y64)
+    if r["n_bad"]:
+        idx = r["worst_index"]
+        y = bf16_bits_to_f32(np.asarray(y_bf16_bits, np.uint16))
+        raise AssertionError(
+            f"{what}: {r['n_bad']} elements out of tolerance; worst at {idx}: "
+            f"got {float(y[idx])!r} want {float(np.asarray(y64)[idx])!r} "
+            f"rel {r['max_rel']:.3g}")
+    return r
