@@ -1,0 +1,16 @@
+"""FP8_DYNAMIC W8A8 Linear for AMD Instinct MI355X (gfx950).
+
+Per-token dynamic E4M3 activations x channel-wise static E4M3 weights, float32
+accumulation, token-scale x channel-scale epilogue to bfloat16, as in the
+FP8-Dynamic recipe of the MOSS-VL quantization README.  The work happens in
+hand-written HIP kernels behind the C ABI of ``include/fp8w8a8.h``; this
+package is its Python binding (argument marshalling only).
+"""
+
+from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
+                      load_library, quant_linear, quantize_act_per_token,
+                      quantize_weight_channelwise, workspace_bytes)
+
+__all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
+           "load_library", "quant_linear", "quantize_act_per_token",
+           "quantize_weight_channelwise", "workspace_bytes"]

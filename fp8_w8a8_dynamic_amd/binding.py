@@ -1,0 +1,223 @@
+"""Thin ctypes binding of ``libfp8w8a8.so`` (the C ABI in include/fp8w8a8.h).
+
+The functions here only marshal torch tensors into pointers, sizes and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  If the library is missing or fails to load, every call raises:
+there is no fallback path.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG_DIR, "libfp8w8a8.so")
+
+_c_i64 = ctypes.c_int64
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+#: exported symbol -> (restype, argtypes), mirroring include/fp8w8a8.h
+SIGNATURES = {
+    "fp8w8a8_quantize_weight_channelwise":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fp8w8a8_quantize_act_per_token":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fp8w8a8_fp8_linear":
+        (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                        _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_quant_linear":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                        _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, ctypes.c_int]),
+    "fp8w8a8_workspace_init": (ctypes.c_int, [_c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp8w8a8_last_hip_error": (ctypes.c_int, []),
+}
+
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN",
+          4: "ERR_ALIAS", 5: "ERR_WORKSPACE", 6: "ERR_DEVICE", 7: "ERR_HIP"}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class Fp8W8A8Error(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, what: str):
+        lib = load_library()
+        msg = lib.fp8w8a8_status_string(status).decode()
+        if status in (6, 7):
+            msg += f" (hipError {lib.fp8w8a8_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIBRARY_PATH):
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with "
+                "`python -m fp8_w8a8_dynamic_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise Fp8W8A8Error(status, what)
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _as_codes(t: torch.Tensor) -> torch.Tensor:
+    """Accept E4M3 tensors as float8_e4m3fn or as raw uint8 bytes."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"expected float8_e4m3fn or uint8 codes, got {t.dtype}")
+    return t
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+class _Workspaces:
+    """One zero-initialised workspace per (device, stream), grown on demand.
+
+    The library's split-K counters sit in the first 64 KiB and are left at
+    zero by every call, so a workspace is reusable by consecutive calls on its
+    stream.  A grown workspace is zeroed by the library's own fill kernel.
+    """
+
+    def __init__(self):
+        self._bufs = {}
+        self._lock = threading.Lock()
+
+    def get(self, device: torch.device, nbytes: int) -> torch.Tensor:
+        if nbytes == 0:
+            return None
+        stream = torch.cuda.current_stream(device)
+        key = (device.index, stream.cuda_stream)
+        with self._lock:
+            buf = self._bufs.get(key)
+            if buf is None or buf.numel() < nbytes:
+                size = max(nbytes, 1 << 20)
+                size = (size + 255) // 256 * 256
+                buf = torch.empty(size, dtype=torch.uint8, device=device)
+                _check(load_library().fp8w8a8_workspace_init(
+                    buf.data_ptr(), size, stream.cuda_stream),
+                    "fp8w8a8_workspace_init")
+                self._bufs[key] = buf
+            return buf
+
+
+_workspaces = _Workspaces()
+
+
+def workspace_bytes(m: int, n: int, k: int, fused: bool) -> int:
+    return int(load_library().fp8w8a8_workspace_bytes(m, n, k, int(fused)))
+
+
+def quantize_weight_channelwise(w: torch.Tensor):
+    """bf16 W[N, K] -> (qW float8_e4m3fn [N, K], w_scale float32 [N])."""
+    lib = load_library()
+    if w.dtype != torch.bfloat16:
+        raise TypeError("w must be bfloat16")
+    n, k, ld = _rows(w, "w")
+    qw = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    sw = torch.empty((n,), dtype=torch.float32, device=w.device)
+    if n == 0:
+        return qw.view(torch.float8_e4m3fn), sw
+    _check(lib.fp8w8a8_quantize_weight_channelwise(
+        w.data_ptr(), n, k, ld, qw.data_ptr(), sw.data_ptr(),
+        _stream_ptr(w.device)), "quantize_weight_channelwise")
+    return qw.view(torch.float8_e4m3fn), sw
+
+
+def quantize_act_per_token(x: torch.Tensor):
+    """bf16 X[M, K] -> (qX float8_e4m3fn [M, K], x_scale float32 [M])."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    m, k, ld = _rows(x, "x")
+    qx = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((m,), dtype=torch.float32, device=x.device)
+    if m == 0:
+        return qx.view(torch.float8_e4m3fn), sx
+    _check(lib.fp8w8a8_quantize_act_per_token(
+        x.data_ptr(), m, k, ld, qx.data_ptr(), sx.data_ptr(),
+        _stream_ptr(x.device)), "quantize_act_per_token")
+    return qx.view(torch.float8_e4m3fn), sx
+
+
+def _out(m, n, device, out):
+    if out is None:
+        return torch.empty((m, n), dtype=torch.bfloat16, device=device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be bfloat16 [M, N] with contiguous rows")
+    return out
+
+
+def fp8_linear(qx, x_scale, qw, w_scale, out=None):
+    """Y[M, N] = bf16((qX @ qW^T) * x_scale[:, None] * w_scale[None, :])."""
+    lib = load_library()
+    qx, qw = _as_codes(qx), _as_codes(qw)
+    m, k, ldq = _rows(qx, "qx")
+    n, k2, ldw = _rows(qw, "qw")
+    if k2 != k or ldq != k or ldw != k:
+        raise ValueError("qx [M, K] and qw [N, K] must be contiguous with one K")
+    y = _out(m, n, qx.device, out)
+    if m == 0 or n == 0:
+        return y
+    need = workspace_bytes(m, n, k, False)
+    ws = _workspaces.get(qx.device, need)
+    _check(lib.fp8w8a8_fp8_linear(
+        qx.data_ptr(), x_scale.data_ptr(), qw.data_ptr(), w_scale.data_ptr(),
+        m, n, k, y.data_ptr(), y.stride(0),
+        ws.data_ptr() if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream_ptr(qx.device)),
+        "fp8_linear")
+    return y
+
+
+def quant_linear(x, qw, w_scale, out=None):
+    """Fused FP8_DYNAMIC forward: bf16 X[M, K] -> bf16 Y[M, N]."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    qw = _as_codes(qw)
+    m, k, ldx = _rows(x, "x")
+    n, k2, ldw = _rows(qw, "qw")
+    if k2 != k or ldw != k:
+        raise ValueError("qw must be contiguous [N, K] with the K of x")
+    y = _out(m, n, x.device, out)
+    if m == 0 or n == 0:
+        return y
+    need = workspace_bytes(m, n, k, True)
+    ws = _workspaces.get(x.device, need)
+    _check(lib.fp8w8a8_quant_linear(
+        x.data_ptr(), ldx, qw.data_ptr(), w_scale.data_ptr(), m, n, k,
+        y.data_ptr(), y.stride(0), ws.data_ptr() if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream_ptr(x.device)),
+        "quant_linear")
+    return y

@@ -1,0 +1,300 @@
+// C ABI of the FP8_DYNAMIC W8A8 Linear: argument validation, the gfx950
+// device check and the choice between the decode (M <= 16) and prefill
+// kernels.  Nothing here allocates, frees or synchronizes device memory.
+#include "../../include/fp8w8a8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+using fp8w8a8::kGemvMaxM;
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int fail_hip(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return FP8W8A8_ERR_HIP;
+}
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip_error = static_cast<int>(e);
+    return FP8W8A8_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int st = g_device_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return FP8W8A8_OK;
+    if (st == 2) return FP8W8A8_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return FP8W8A8_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices)
+    g_device_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FP8W8A8_OK : FP8W8A8_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t rows, int64_t cols, int64_t ld,
+           size_t elem) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0 || cols <= 0) return Range{lo, lo};
+  const size_t bytes = (static_cast<size_t>(rows - 1) * ld + cols) * elem;
+  return Range{lo, lo + bytes};
+}
+
+bool overlap(Range a, Range b) {
+  return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
+}
+
+// Sizes are kept below 2^31 per dimension so that kernels can index rows
+// with 32-bit integers; element offsets use 64-bit arithmetic.
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+int check_quant_args(const uint16_t* src, int64_t rows, int64_t k, int64_t ld,
+                     const uint8_t* q, const float* scale) {
+  if (!src || !q || !scale) return FP8W8A8_ERR_NULL;
+  if (rows < 0 || rows > kMaxDim || k < 1 || k > kMaxDim || k % 8 != 0 ||
+      ld < k || ld % 8 != 0)
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(q) ||
+      (reinterpret_cast<uintptr_t>(scale) & 3u) != 0)
+    return FP8W8A8_ERR_ALIGN;
+  const Range in = span(src, rows, k, ld, 2);
+  const Range rq = span(q, rows, k, k, 1);
+  const Range rs = span(scale, rows, 1, 1, 4);
+  if (overlap(in, rq) || overlap(in, rs) || overlap(rq, rs))
+    return FP8W8A8_ERR_ALIAS;
+  return FP8W8A8_OK;
+}
+
+int check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t ldy) {
+  if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || n % 16 != 0 ||
+      k < 128 || k > kMaxDim || k % 128 != 0 || ldy < n || ldy % 8 != 0)
+    return FP8W8A8_ERR_SHAPE;
+  return FP8W8A8_OK;
+}
+
+enum class Path { kGemv, kGemm };
+
+// Decode-sized inputs stream the weights through the split-K MFMA GEMV;
+// everything else takes the tiled MFMA GEMM.  FP8W8A8_FORCE_PATH=gemm|gemv
+// overrides the choice (the GEMV only where m <= 16) so that the two kernels
+// can be cross-checked on identical inputs.
+Path choose_path(int64_t m) {
+  const char* force = std::getenv("FP8W8A8_FORCE_PATH");
+  if (force && std::strcmp(force, "gemm") == 0) return Path::kGemm;
+  if (force && std::strcmp(force, "gemv") == 0 && m <= kGemvMaxM)
+    return Path::kGemv;
+  return m <= kGemvMaxM ? Path::kGemv : Path::kGemm;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout, the same for every call:
+//   [0, kCounterBytes)            split-K arrival counters (zero between calls)
+//   [kCounterBytes, +partials)    float32 split-K partial tiles
+//   [.., +qx)                     quantized activations [m, k] (fused calls
+//   [.., +sx)                     that quantize in a separate kernel), scales
+struct Layout {
+  size_t partials = 0, qx = 0, sx = 0, total = 0;
+  size_t partial_bytes = 0;
+  bool any = false;
+};
+
+Layout layout_for(int64_t m, int64_t n, int64_t k, bool fused, Path path) {
+  Layout L;
+  if (m == 0 || n == 0) return L;
+  const bool gemv = path == Path::kGemv;
+  const bool fused_in_kernel = gemv && fused && fp8w8a8::gemv_fused_fits(m, n, k);
+  const bool separate_quant = fused && !fused_in_kernel;
+  L.partial_bytes =
+      gemv ? fp8w8a8::gemv_partial_bytes(m, n, k, fused_in_kernel) : 0;
+  if (L.partial_bytes == 0 && !separate_quant) return L;
+  L.any = true;
+  L.partials = fp8w8a8::kCounterBytes;
+  L.qx = L.partials + round_up(L.partial_bytes, 256);
+  L.sx = L.qx + (separate_quant ? round_up(static_cast<size_t>(m) * k, 256) : 0);
+  L.total = L.sx + (separate_quant ? round_up(static_cast<size_t>(m) * 4, 256) : 0);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8w8a8_status_string(int status) {
+  switch (status) {
+    case FP8W8A8_OK: return "FP8W8A8_OK";
+    case FP8W8A8_ERR_NULL: return "FP8W8A8_ERR_NULL: a required pointer is NULL";
+    case FP8W8A8_ERR_SHAPE: return "FP8W8A8_ERR_SHAPE: a size or stride is out of range";
+    case FP8W8A8_ERR_ALIGN: return "FP8W8A8_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case FP8W8A8_ERR_ALIAS: return "FP8W8A8_ERR_ALIAS: an output overlaps another buffer";
+    case FP8W8A8_ERR_WORKSPACE: return "FP8W8A8_ERR_WORKSPACE: workspace missing or too small";
+    case FP8W8A8_ERR_DEVICE: return "FP8W8A8_ERR_DEVICE: no HIP device or not gfx950";
+    case FP8W8A8_ERR_HIP: return "FP8W8A8_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "FP8W8A8: unknown status";
+  }
+}
+
+int fp8w8a8_last_hip_error(void) { return g_last_hip_error; }
+
+int fp8w8a8_quantize_weight_channelwise(const uint16_t* w, int64_t n,
+                                        int64_t k, int64_t ldw, uint8_t* qw,
+                                        float* w_scale, void* stream) {
+  int st = check_quant_args(w, n, k, ldw, qw, w_scale);
+  if (st != FP8W8A8_OK) return st;
+  if (n == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_quant_rows(w, n, k, ldw, qw, w_scale,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
+                                   int64_t ldx, uint8_t* qx, float* x_scale,
+                                   void* stream) {
+  int st = check_quant_args(x, m, k, ldx, qx, x_scale);
+  if (st != FP8W8A8_OK) return st;
+  if (m == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_quant_rows(x, m, k, ldx, qx, x_scale,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
+  if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
+  return layout_for(m, n, k, fused != 0, choose_path(m)).total;
+}
+
+int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
+                       const uint8_t* qw, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!qx || !x_scale || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
+  int st = check_linear_shape(m, n, k, ldy);
+  if (st != FP8W8A8_OK) return st;
+  if (!aligned16(qx) || !aligned16(x_scale) || !aligned16(qw) ||
+      !aligned16(w_scale) || !aligned16(y) ||
+      (workspace && !aligned16(workspace)))
+    return FP8W8A8_ERR_ALIGN;
+  const Range ry = span(y, m, n, ldy, 2);
+  if (overlap(ry, span(qx, m, k, k, 1)) || overlap(ry, span(x_scale, m, 1, 1, 4)) ||
+      overlap(ry, span(qw, n, k, k, 1)) || overlap(ry, span(w_scale, n, 1, 1, 4)))
+    return FP8W8A8_ERR_ALIAS;
+  const Path path = choose_path(m);
+  const Layout L = layout_for(m, n, k, false, path);
+  const size_t need = L.total;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
+    const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(rw, ry) || overlap(rw, span(qx, m, k, k, 1)) ||
+        overlap(rw, span(qw, n, k, k, 1)) ||
+        overlap(rw, span(x_scale, m, 1, 1, 4)) ||
+        overlap(rw, span(w_scale, n, 1, 1, 4)))
+      return FP8W8A8_ERR_ALIAS;
+  }
+  if (m == 0 || n == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (path == Path::kGemv)
+    e = fp8w8a8::launch_gemv(nullptr, 0, qx, x_scale, qw, w_scale, m, n, k, y,
+                             ldy, reinterpret_cast<unsigned*>(ws),
+                             reinterpret_cast<float*>(ws + L.partials), s);
+  else
+    e = fp8w8a8::launch_gemm(qx, x_scale, qw, w_scale, m, n, k, y, ldy, s);
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
+                         const float* w_scale, int64_t m, int64_t n, int64_t k,
+                         uint16_t* y, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!x || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
+  int st = check_linear_shape(m, n, k, ldy);
+  if (st != FP8W8A8_OK) return st;
+  if (ldx < k || ldx % 8 != 0) return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) ||
+      !aligned16(y) || (workspace && !aligned16(workspace)))
+    return FP8W8A8_ERR_ALIGN;
+  const Range ry = span(y, m, n, ldy, 2);
+  const Range rx = span(x, m, k, ldx, 2);
+  if (overlap(ry, rx) || overlap(ry, span(qw, n, k, k, 1)) ||
+      overlap(ry, span(w_scale, n, 1, 1, 4)))
+    return FP8W8A8_ERR_ALIAS;
+  const Path path = choose_path(m);
+  const Layout L = layout_for(m, n, k, true, path);
+  const size_t need = L.total;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
+    const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(rw, ry) || overlap(rw, rx) || overlap(rw, span(qw, n, k, k, 1)) ||
+        overlap(rw, span(w_scale, n, 1, 1, 4)))
+      return FP8W8A8_ERR_ALIAS;
+  }
+  if (m == 0 || n == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+  float* partials = L.any ? reinterpret_cast<float*>(ws + L.partials) : nullptr;
+  hipError_t e;
+  if (path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k)) {
+    e = fp8w8a8::launch_gemv(x, ldx, nullptr, nullptr, qw, w_scale, m, n, k,
+                             y, ldy, counters, partials, s);
+  } else {
+    // Quantize into the workspace, then run the matching linear kernel.
+    uint8_t* qx = ws + L.qx;
+    float* sx = reinterpret_cast<float*>(ws + L.sx);
+    e = fp8w8a8::launch_quant_rows(x, m, k, ldx, qx, sx, s);
+    if (e == hipSuccess) {
+      if (path == Path::kGemv)
+        e = fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y,
+                                 ldy, counters, partials, s);
+      else
+        e = fp8w8a8::launch_gemm(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
+    }
+  }
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return FP8W8A8_ERR_NULL;
+  if (bytes % 16 != 0) return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(workspace)) return FP8W8A8_ERR_ALIGN;
+  if (bytes == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_zero_fill(workspace, bytes,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+}  // extern "C"

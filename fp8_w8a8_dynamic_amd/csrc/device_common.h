@@ -1,0 +1,111 @@
+// Device helpers shared by the FP8_DYNAMIC kernels (gfx950 only).
+//
+// E4M3 here is the OCP float8_e4m3fn format the MOSS-VL quantization README
+// names for the FP8-Dynamic recipe: 4 exponent bits (bias 7), 3 mantissa
+// bits, no infinities, largest finite magnitude 448.  gfx950 converts to and
+// multiplies this exact format in hardware (v_cvt_pk_fp8_f32, the f8f6f4
+// MFMA family with format selector 0), so no byte translation is needed
+// anywhere on the path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8w8a8 {
+
+constexpr float kE4M3Max = 448.0f;
+
+// bfloat16 is the upper half of a float32: widening is a shift / mask.
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// Magnitudes of two packed bf16 as 16-bit integers.  For non-negative
+// floats the bit patterns order exactly like the values, so the row amax can
+// be taken on integers (one packed max per two elements) and widened once.
+__device__ __forceinline__ uint32_t bf16x2_abs_bits(uint32_t w) {
+  return w & 0x7fff7fffu;
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  uint32_t lo = max(a & 0xffffu, b & 0xffffu);
+  uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+__device__ __forceinline__ float amax_bits_to_float(uint32_t packed) {
+  uint32_t m = max(packed & 0xffffu, packed >> 16);
+  return __uint_as_float(m << 16);
+}
+
+// Row scale: scale = amax / 448 with one IEEE float32 division (the default
+// lowering of '/' for float on gfx950 is correctly rounded; the library is
+// never built with fast-math).
+__device__ __forceinline__ float row_scale(float amax) {
+  return amax / kE4M3Max;
+}
+
+// fl32(v / scale); a zero scale means an all-zero row: keep v (a signed zero).
+__device__ __forceinline__ float quotient(float v, float scale) {
+  return v / scale;
+}
+
+// Four float32 quotients -> four E4M3 codes packed little-endian in a dword
+// (code of `a` in the lowest byte).  The clamp to +-448 makes the hardware
+// conversion's round-to-nearest-even saturate instead of overflowing.
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c,
+                                            float d) {
+  a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+  d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Quantize 8 bf16 (one 16-byte vector) with a row scale -> 8 codes.
+__device__ __forceinline__ uint2 quantize8(uint4 v, float scale) {
+  uint2 out;
+  if (scale == 0.0f) {
+    // amax == 0: every element is +-0; the codes are the sign bits.
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t r[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t a = w[2 * i], b = w[2 * i + 1];
+      r[i] = ((a >> 15) & 1u) << 7 | ((a >> 31) & 1u) << 15 |
+             ((b >> 15) & 1u) << 23 | ((b >> 31) & 1u) << 31;
+    }
+    out.x = r[0];
+    out.y = r[1];
+    return out;
+  }
+  out.x = encode4(quotient(bf16_lo(v.x), scale), quotient(bf16_hi(v.x), scale),
+                  quotient(bf16_lo(v.y), scale), quotient(bf16_hi(v.y), scale));
+  out.y = encode4(quotient(bf16_lo(v.z), scale), quotient(bf16_hi(v.z), scale),
+                  quotient(bf16_lo(v.w), scale), quotient(bf16_hi(v.w), scale));
+  return out;
+}
+
+// Max over the 64 lanes of a wave (result valid in every lane).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
+// float32 -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+}  // namespace fp8w8a8

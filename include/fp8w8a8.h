@@ -1,0 +1,157 @@
+/*
+ * fp8w8a8.h — C ABI of the FP8_DYNAMIC W8A8 Linear for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the library computes (MOSS-VL quantization README, "FP8-Dynamic"
+ * recipe; MOSS-VL-Realtime-FP8 article, section on why the 252 Linears use
+ * FP8 E4M3):
+ *   - weights are stored as float8_e4m3fn (OCP E4M3: 4 exponent bits,
+ *     3 mantissa bits, bias 7, largest finite value 448) with one static
+ *     float32 scale per output channel, computed once, offline;
+ *   - the Linear's bf16 input is quantized at run time to E4M3 with one
+ *     dynamic float32 scale per token (row);
+ *   - the Linear multiplies the two FP8 operands, accumulates in float32 and
+ *     writes bfloat16: y[m,n] = bf16( sum_k dec(qx[m,k]) * dec(qw[n,k])
+ *                                     * x_scale[m] * w_scale[n] ), no bias.
+ * Quantization of one row r (token or output channel), where the pages give
+ * no formula (readings, stated once here):
+ *     amax  = max_k |v[r,k]|
+ *     scale = amax / 448            (IEEE float32 division)
+ *     code  = e4m3(v[r,k] / scale)  (IEEE float32 division, then round to
+ *                                    nearest, ties to even, saturate to
+ *                                    +-448, sign kept; amax == 0 gives
+ *                                    scale 0 and codes +-0)
+ *
+ * Conventions for every entry point:
+ *   - tensor pointers are DEVICE pointers on the current HIP device;
+ *   - all matrices are row-major; ld* are row strides in ELEMENTS;
+ *   - bfloat16 values are passed as their uint16_t bit patterns, E4M3 codes
+ *     as uint8_t bytes; scales are float32;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     kernels are enqueued on it and the call returns without waiting;
+ *   - the caller owns every buffer; the library never allocates, frees or
+ *     synchronizes device memory, and keeps only a cache of device facts;
+ *   - arguments are validated before anything is enqueued; on a non-zero
+ *     status nothing was enqueued and no output was touched, except
+ *     FP8W8A8_ERR_HIP from a failed launch (outputs then unspecified);
+ *   - M == 0 or N == 0 is a valid empty call that enqueues nothing;
+ *   - inputs must be finite; NaN/Inf inputs give unspecified (but
+ *     memory-safe) results;
+ *   - outputs must not overlap inputs or each other (FP8W8A8_ERR_ALIAS);
+ *   - faults inside a kernel surface at the caller's next synchronization.
+ *
+ * The library runs only on gfx950; any other current device gives
+ * FP8W8A8_ERR_DEVICE.
+ */
+#ifndef FP8W8A8_H
+#define FP8W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8w8a8_status {
+  FP8W8A8_OK = 0,
+  FP8W8A8_ERR_NULL = 1,      /* a required pointer is NULL                  */
+  FP8W8A8_ERR_SHAPE = 2,     /* a size or stride breaks the rules below     */
+  FP8W8A8_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned            */
+  FP8W8A8_ERR_ALIAS = 4,     /* an output overlaps an input or an output    */
+  FP8W8A8_ERR_WORKSPACE = 5, /* workspace missing or smaller than required  */
+  FP8W8A8_ERR_DEVICE = 6,    /* no HIP device, or the device is not gfx950  */
+  FP8W8A8_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed  */
+} fp8w8a8_status;
+
+/*
+ * Channel-wise static weight quantization (the offline, one-shot step of the
+ * FP8-Dynamic recipe; README "FP8-Dynamic": weights float8_e4m3fn,
+ * channel-wise static).
+ *   w        bf16 [n, k], row stride ldw >= k, ldw % 8 == 0 (input)
+ *   qw       E4M3 [n, k], contiguous (row stride k)            (output)
+ *   w_scale  float32 [n], one scale per output channel         (output)
+ * Rules: n >= 0, k >= 1, k % 8 == 0; w, qw 16-byte aligned; w_scale 4-byte
+ * aligned.  The result is bit-identical to the per-row definition above.
+ */
+int fp8w8a8_quantize_weight_channelwise(const uint16_t* w, int64_t n,
+                                        int64_t k, int64_t ldw, uint8_t* qw,
+                                        float* w_scale, void* stream);
+
+/*
+ * Per-token dynamic activation quantization (README "FP8-Dynamic": the input
+ * activations of the quantized kernels are FP8, per token, dynamic).
+ *   x        bf16 [m, k], row stride ldx >= k, ldx % 8 == 0   (input)
+ *   qx       E4M3 [m, k], contiguous                           (output)
+ *   x_scale  float32 [m]                                       (output)
+ * Rules: m >= 0, k >= 1, k % 8 == 0; x, qx 16-byte aligned.
+ */
+int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
+                                   int64_t ldx, uint8_t* qx, float* x_scale,
+                                   void* stream);
+
+/*
+ * The W8A8 Linear on already-quantized operands ("the quantized kernels" of
+ * README "FP8-Dynamic"):
+ *   y[m,n] = bf16_rne( (sum_k dec(qx[m,k]) * dec(qw[n,k])) * x_scale[m]
+ *                      * w_scale[n] )
+ * with float32 accumulation (summation order unspecified).
+ *   qx, x_scale  from fp8w8a8_quantize_act_per_token, [m, k] and [m]
+ *   qw, w_scale  from fp8w8a8_quantize_weight_channelwise, [n, k] and [n]
+ *   y            bf16 [m, n], row stride ldy >= n, ldy % 8 == 0 (output)
+ *   workspace    device scratch of at least
+ *                fp8w8a8_workspace_bytes(m, n, k, 0) bytes; see below
+ * Rules: m, n >= 0; n % 16 == 0; k >= 128, k % 128 == 0; all pointers
+ * 16-byte aligned.
+ */
+int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
+                       const uint8_t* qw, const float* w_scale, int64_t m,
+                       int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused FP8_DYNAMIC forward, bf16 in -> bf16 out: per-token quantization of
+ * x (exactly as fp8w8a8_quantize_act_per_token) followed by
+ * fp8w8a8_fp8_linear.  This is what a quantized Linear's forward is to its
+ * caller.
+ *   x        bf16 [m, k], row stride ldx >= k, ldx % 8 == 0   (input)
+ *   qw, w_scale, y, ldy as for fp8w8a8_fp8_linear
+ *   workspace    at least fp8w8a8_workspace_bytes(m, n, k, 1) bytes
+ * Rules as for fp8w8a8_fp8_linear.
+ */
+int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
+                         const float* w_scale, int64_t m, int64_t n, int64_t k,
+                         uint16_t* y, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace size in bytes for fp8w8a8_fp8_linear (fused == 0) or
+ * fp8w8a8_quant_linear (fused != 0) at the given sizes; 0 for invalid sizes.
+ * The workspace holds split-K partial sums with their arrival counters and,
+ * for the fused call, the quantized activations.  Contract: the workspace
+ * must be all zero before its first use (fp8w8a8_workspace_init does this);
+ * every call that returns FP8W8A8_OK leaves the counters zero again, so one
+ * workspace can be reused by consecutive calls on ONE stream.  Calls that
+ * may run concurrently need distinct workspaces.
+ */
+size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused);
+
+/*
+ * Zero-fill a workspace with a kernel on `stream` (no hipMemsetAsync, so it
+ * can sit inside a captured graph).  bytes % 16 == 0, workspace 16-byte
+ * aligned.
+ */
+int fp8w8a8_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8w8a8_status_string(int status);
+
+/* The hipError_t behind the calling thread's last FP8W8A8_ERR_HIP or
+ * FP8W8A8_ERR_DEVICE (0 if none). */
+int fp8w8a8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W8A8_H */

@@ -1,0 +1,124 @@
+"""The C ABI: the library loads, exports every declared symbol, and rejects
+bad arguments on the host before touching a device (CPU only: no call here
+reaches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_w8a8_dynamic_amd import SIGNATURES, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w8a8.h")
+
+OK, ENULL, ESHAPE, EALIGN, EALIAS, EWS, EDEV, EHIP = range(8)
+A = 1 << 20          # fake, 16-byte aligned "device" addresses (never used)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8w8a8_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(SIGNATURES) == names
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert lib.fp8w8a8_status_string(code).decode().startswith("FP8W8A8_")
+    assert b"unknown" in lib.fp8w8a8_status_string(99)
+
+
+def _q(lib, fn, src, rows, k, ld, q, s):
+    return getattr(lib, fn)(src, rows, k, ld, q, s, None)
+
+
+@pytest.mark.parametrize("fn", ["fp8w8a8_quantize_act_per_token",
+                                "fp8w8a8_quantize_weight_channelwise"])
+def test_quant_validation(lib, fn):
+    src, q, s = A, 64 * A, 128 * A
+    assert _q(lib, fn, None, 4, 64, 64, q, s) == ENULL
+    assert _q(lib, fn, src, 4, 64, 64, None, s) == ENULL
+    assert _q(lib, fn, src, 4, 64, 64, q, None) == ENULL
+    assert _q(lib, fn, src, -1, 64, 64, q, s) == ESHAPE
+    assert _q(lib, fn, src, 4, 0, 64, q, s) == ESHAPE
+    assert _q(lib, fn, src, 4, 60, 64, q, s) == ESHAPE       # k % 8
+    assert _q(lib, fn, src, 4, 64, 32, q, s) == ESHAPE       # ld < k
+    assert _q(lib, fn, src, 4, 64, 68, q, s) == ESHAPE       # ld % 8
+    assert _q(lib, fn, src + 8, 4, 64, 64, q, s) == EALIGN
+    assert _q(lib, fn, src, 4, 64, 64, q + 4, s) == EALIGN
+    assert _q(lib, fn, src, 4, 64, 64, q, s + 2) == EALIGN
+    assert _q(lib, fn, src, 4, 64, 64, src + 64, s) == EALIAS  # q inside x
+    assert _q(lib, fn, src, 4, 64, 64, q, q + 16) == EALIAS    # s inside q
+    # empty is a valid no-op and needs no device
+    assert _q(lib, fn, src, 0, 64, 64, q, s) == OK
+
+
+def _lin(lib, qx=A, sx=2 * A, qw=4 * A, sw=8 * A, m=32, n=64, k=256,
+         y=16 * A, ldy=64, ws=None, wsb=0):
+    return lib.fp8w8a8_fp8_linear(qx, sx, qw, sw, m, n, k, y, ldy, ws, wsb, None)
+
+
+def test_linear_validation(lib):
+    assert _lin(lib, qx=None) == ENULL
+    assert _lin(lib, y=None) == ENULL
+    assert _lin(lib, n=24) == ESHAPE            # n % 16
+    assert _lin(lib, k=192) == ESHAPE           # k % 128
+    assert _lin(lib, k=0) == ESHAPE
+    assert _lin(lib, m=-1) == ESHAPE
+    assert _lin(lib, ldy=32) == ESHAPE          # ldy < n
+    assert _lin(lib, ldy=68) == ESHAPE          # ldy % 8
+    assert _lin(lib, qw=4 * A + 8) == EALIGN
+    assert _lin(lib, y=A + 64) == EALIAS        # y overlaps qx
+    assert _lin(lib, m=0) == OK
+    assert _lin(lib, n=0) == OK
+    # decode-sized m needs split-K workspace for a small n
+    need = lib.fp8w8a8_workspace_bytes(1, 64, 4096, 0)
+    assert need > 0
+    assert _lin(lib, m=1, k=4096, ws=None) == EWS
+    assert _lin(lib, m=1, k=4096, ws=32 * A, wsb=need - 16) == EWS
+    assert _lin(lib, m=1, k=4096, ws=A, wsb=need) == EALIAS
+
+
+def test_quant_linear_validation(lib):
+    f = lib.fp8w8a8_quant_linear
+    args = dict(x=A, ldx=256, qw=4 * A, sw=8 * A, m=64, n=64, k=256, y=16 * A,
+                ldy=64, ws=32 * A, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["ldx"], a["qw"], a["sw"], a["m"], a["n"], a["k"],
+                 a["y"], a["ldy"], a["ws"], a["wsb"], None)
+
+    assert call(x=None) == ENULL
+    assert call(ldx=128) == ESHAPE
+    assert call(ldx=260) == ESHAPE
+    assert call(sw=8 * A + 4) == EALIGN
+    assert call(y=A + 32) == EALIAS
+    assert call(ws=None, wsb=0) == EWS
+    assert call(ws=A, wsb=1 << 30) == EALIAS
+    assert call(m=0) == OK
+
+
+def test_workspace_sizes(lib):
+    assert lib.fp8w8a8_workspace_bytes(4096, 4096, 4096, 0) == 0   # GEMM: none
+    fused = lib.fp8w8a8_workspace_bytes(4096, 4096, 4096, 1)
+    assert fused >= 4096 * 4096 + 4 * 4096                       # qx + sx
+    assert lib.fp8w8a8_workspace_bytes(1, 4096, 4096, 1) >= 64 * 1024
+    assert lib.fp8w8a8_workspace_bytes(1, 24, 4096, 0) == 0      # invalid n
+    assert lib.fp8w8a8_workspace_init(None, 16, None) == ENULL
+    assert lib.fp8w8a8_workspace_init(A, 8, None) == ESHAPE
+    assert lib.fp8w8a8_workspace_init(A + 8, 16, None) == EALIGN
+    assert lib.fp8w8a8_workspace_init(A, 0, None) == OK

@@ -1,0 +1,165 @@
+"""GPU parity of the W8A8 Linear (decode GEMV and prefill GEMM paths)
+against the oracle: bf16 outputs within the elementwise tolerance of
+oracle.check (1e-2 relative to the oracle's magnitude), quantized bytes
+bit-exact.  Calls go through the C ABI via the Python binding."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_dynamic_amd as fq
+import oracle
+from oracle import check_bytes, check_close
+from tests.gpu_util import host_bits, to_dev_bf16, to_dev_f32, to_dev_u8
+from workloads import LAYER_SHAPES, bf16_from_f64, c1_inputs, c2_inputs, c3_inputs
+from workloads.generators import c5_rows, c5_x, weight_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E          # no NaN codes
+    return c
+
+
+def _rand_operands(m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    qx, qw = _rand_codes(rng, (m, k)), _rand_codes(rng, (n, k))
+    sx = (2.0 ** rng.uniform(-12, -4, m)).astype(np.float32)
+    sw = (2.0 ** rng.uniform(-12, -4, n)).astype(np.float32)
+    return qx, sx, qw, sw
+
+
+def _run_linear(qx, sx, qw, sw):
+    y = fq.fp8_linear(to_dev_u8(qx), to_dev_f32(sx), to_dev_u8(qw), to_dev_f32(sw))
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+SHAPES = [(1, 16, 128), (4, 48, 384), (8, 272, 1024), (16, 1040, 512),
+          (17, 16, 128), (100, 272, 384), (300, 1040, 256), (513, 528, 640),
+          (256, 256, 4096), (64, 4096, 256), (2, 4096, 4096), (1, 1024, 12288)]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_fp8_linear_random_codes(m, n, k):
+    qx, sx, qw, sw = _rand_operands(m, n, k, m * 1000 + n + k)
+    y = _run_linear(qx, sx, qw, sw)
+    check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"linear {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8, 16])
+@pytest.mark.parametrize("path", ["gemm", "gemv"])
+def test_forced_path_cross_check(m, path, monkeypatch):
+    """GEMV and GEMM on identical decode-sized inputs, both vs the oracle."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", path)
+    qx, sx, qw, sw = _rand_operands(m, 1024, 4096, 77 + m)
+    y = _run_linear(qx, sx, qw, sw)
+    check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"{path} m={m}")
+
+
+def _quant_weights_gpu(w_bits):
+    qw, sw = fq.quantize_weight_channelwise(to_dev_bf16(w_bits))
+    return qw, sw
+
+
+def test_c1_q_proj_end_to_end():
+    x, w = c1_inputs()
+    qw, sw = _quant_weights_gpu(w)
+    y = fq.quant_linear(to_dev_bf16(x), qw, sw)
+    torch.cuda.synchronize()
+    rqw, rsw = oracle.quant_weight_ref(w)
+    check_bytes(host_bits(qw), rqw, "c1 qw")
+    check_bytes(host_bits(sw).view(np.uint32), rsw.view(np.uint32), "c1 sw")
+    y64, _, _ = oracle.quant_linear_ref(x, rqw, rsw)
+    check_close(host_bits(y), y64, "c1 y")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+@pytest.mark.parametrize("linear", range(7))
+def test_c2_decode_layer(m, linear):
+    x, w = c2_inputs(m, linear)
+    qw, sw = _quant_weights_gpu(w)
+    y = fq.quant_linear(to_dev_bf16(x), qw, sw)
+    torch.cuda.synchronize()
+    y64, _, _ = oracle.quant_linear_ref(x, host_bits(qw), host_bits(sw))
+    check_close(host_bits(y), y64, f"c2 {LAYER_SHAPES[linear][0]} m={m}")
+
+
+@pytest.mark.parametrize("linear", range(7))
+def test_c3_prefill_sampled_rows(linear):
+    """Full 4096-token GEMM; the oracle checks 96 sampled rows (all columns)."""
+    x, w = c3_inputs(linear, m=4096)
+    qw, sw = _quant_weights_gpu(w)
+    xd = to_dev_bf16(x)
+    y = fq.quant_linear(xd, qw, sw)
+    qx, sx = fq.quantize_act_per_token(xd)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(linear).choice(4096, 96, replace=False)
+    rq, rs = oracle.quant_act_ref(x[rows])
+    check_bytes(host_bits(qx)[rows], rq, "c3 qx")
+    y64 = oracle.linear_ref(rq, rs, host_bits(qw), host_bits(sw))
+    check_close(host_bits(y)[rows], y64, f"c3 {LAYER_SHAPES[linear][0]}")
+
+
+@pytest.mark.parametrize("linear", [1, 4, 6])
+def test_c5_long_prefill_sampled_rows(linear):
+    m = 16384
+    _, n, k = LAYER_SHAPES[linear]
+    x = c5_x(m, k, linear)
+    w = weight_bf16(5, 0, linear, n, k)
+    qw, sw = _quant_weights_gpu(w)
+    y = host_bits(fq.quant_linear(to_dev_bf16(x), qw, sw))
+    torch.cuda.synchronize()
+    zero, big, heavy = c5_rows(m)
+    rows = np.unique(np.concatenate(
+        [zero, big, heavy, np.random.default_rng(linear).choice(m, 48, replace=False)]))
+    y64, _, _ = oracle.quant_linear_ref(x[rows], host_bits(qw), host_bits(sw))
+    check_close(y[rows], y64, f"c5 {LAYER_SHAPES[linear][0]}")
+    assert np.all((y[zero] & 0x7FFF) == 0)
+
+
+def test_workspace_reuse_across_shapes():
+    """Split-K counters must be back at zero after every call."""
+    shapes = [(1, 1024, 4096), (300, 1040, 512), (4, 4096, 12288),
+              (1, 1024, 4096), (16, 48, 384), (1, 1024, 4096)]
+    for i, (m, n, k) in enumerate(shapes):
+        qx, sx, qw, sw = _rand_operands(m, n, k, 500 + i)
+        y = _run_linear(qx, sx, qw, sw)
+        check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"reuse {i}")
+
+
+def test_strided_output_and_input():
+    rng = np.random.default_rng(12)
+    m, n, k = 24, 64, 256
+    xfull = bf16_from_f64(rng.standard_normal((m, k + 64)))
+    w = bf16_from_f64(rng.standard_normal((n, k)) * 0.02)
+    qw, sw = _quant_weights_gpu(w)
+    xd = to_dev_bf16(xfull)[:, :k]
+    out = torch.zeros((m, n + 40), dtype=torch.bfloat16, device="cuda")
+    view = out[:, 8:8 + n]
+    fq.quant_linear(xd, qw, sw, out=view)
+    torch.cuda.synchronize()
+    y64, _, _ = oracle.quant_linear_ref(xfull[:, :k], host_bits(qw), host_bits(sw))
+    ob = host_bits(out)
+    check_close(ob[:, 8:8 + n], y64, "strided")
+    assert np.all(ob[:, :8] == 0) and np.all(ob[:, 8 + n:] == 0)
+
+
+def test_deterministic_outputs():
+    for m in (1, 8, 512):
+        qx, sx, qw, sw = _rand_operands(m, 1024, 4096, 900 + m)
+        a = _run_linear(qx, sx, qw, sw)
+        b = _run_linear(qx, sx, qw, sw)
+        assert np.array_equal(a, b)
+
+
+def test_empty_calls():
+    qw = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
+    sw = torch.ones(16, dtype=torch.float32, device="cuda")
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    y = fq.quant_linear(x, qw, sw)
+    assert y.shape == (0, 16)

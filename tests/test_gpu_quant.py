@@ -1,0 +1,133 @@
+"""GPU parity of the quantization kernels against the oracle: codes and
+float32 scales must be bit-identical.  Calls go through the C ABI via the
+Python binding."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_dynamic_amd as fq
+import oracle
+from oracle import check_bytes
+from tests.gpu_util import host_bits, to_dev_bf16
+from workloads import LAYER_SHAPES, bf16_from_f64, c1_inputs, c2_inputs, c3_inputs
+from workloads.generators import c5_rows, c5_x
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(bits, weight=False):
+    x = to_dev_bf16(bits)
+    if weight:
+        q, s = fq.quantize_weight_channelwise(x)
+    else:
+        q, s = fq.quantize_act_per_token(x)
+    torch.cuda.synchronize()
+    return host_bits(q), host_bits(s)
+
+
+def _check_rows(bits, q, s, rows=None, what="quant"):
+    ref = bits if rows is None else bits[rows]
+    rq, rs = oracle.quant_act_ref(ref)
+    gq = q if rows is None else q[rows]
+    gs = s if rows is None else s[rows]
+    check_bytes(gs.view(np.uint32), rs.view(np.uint32), what + " scales")
+    check_bytes(gq, rq, what + " codes")
+
+
+def _all_finite_bf16():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    exp = (b >> 7) & 0xFF
+    return b[exp != 0xFF]
+
+
+def test_every_bf16_value_under_many_scales():
+    """Each row holds every finite bf16 value whose magnitude is at most the
+    row's amax (larger ones replaced by +0) and the amax itself, so every
+    bf16 input meets the encoder under each row's scale."""
+    allb = _all_finite_bf16()
+    mag = oracle.bf16_bits_to_f32(allb & np.uint16(0x7FFF))
+    rng = np.random.default_rng(17)
+    amaxes = [448.0, 1.0, 896.0, 3.0, 1e-3, 2.0 ** -130, 7.0 * 2.0 ** -133,
+              1e30, 0.1, 3.3e38]
+    amaxes += list(2.0 ** rng.uniform(-120, 120, 22))
+    amax_bits = bf16_from_f64(np.array(amaxes))
+    k = ((allb.size + 1 + 7) // 8) * 8
+    rows = np.zeros((len(amaxes), k), np.uint16)
+    for r, ab in enumerate(amax_bits):
+        amax = oracle.bf16_bits_to_f32(np.array([ab]))[0]
+        keep = np.where(mag <= amax, allb, np.uint16(0))
+        rows[r, 0] = ab
+        rows[r, 1:1 + keep.size] = keep
+    q, s = _gpu_quant(rows)
+    _check_rows(rows, q, s, what="all-bf16")
+
+
+def test_c1_activations_and_weights():
+    x, w = c1_inputs()
+    q, s = _gpu_quant(x)
+    _check_rows(x, q, s, what="c1 x")
+    qw, sw = _gpu_quant(w, weight=True)
+    rq, rs = oracle.quant_weight_ref(w)
+    check_bytes(sw.view(np.uint32), rs.view(np.uint32), "c1 w scales")
+    check_bytes(qw, rq, "c1 w codes")
+
+
+@pytest.mark.parametrize("linear", range(7))
+def test_c2_weights_sampled_rows(linear):
+    _, w = c2_inputs(1, linear)
+    qw, sw = _gpu_quant(w, weight=True)
+    rows = np.random.default_rng(linear).choice(w.shape[0], 256, replace=False)
+    _check_rows(w, qw, sw, rows, what=f"w {LAYER_SHAPES[linear][0]}")
+
+
+@pytest.mark.parametrize("linear", [0, 6])
+def test_c3_activations(linear):
+    x, _ = c3_inputs(linear, m=4096)
+    q, s = _gpu_quant(x)
+    rows = np.random.default_rng(3).choice(4096, 512, replace=False)
+    _check_rows(x, q, s, rows, what="c3 x")
+
+
+def test_c5_activations_special_rows():
+    m, k = 16384, 4096
+    x = c5_x(m, k, 0)
+    q, s = _gpu_quant(x)
+    zero, big, heavy = c5_rows(m)
+    rows = np.unique(np.concatenate(
+        [zero, big, heavy, np.random.default_rng(5).choice(m, 256, replace=False)]))
+    _check_rows(x, q, s, rows, what="c5 x")
+    assert np.all(s[zero] == 0) and np.all(q[zero] == 0)
+    # saturated codes present in the heavy rows
+    assert np.mean((q[heavy] & 0x7F) == 0x7E) > 0.05
+
+
+@pytest.mark.parametrize("m,k,ld", [(1, 8, 8), (3, 24, 32), (5, 520, 528),
+                                    (7, 4104, 4104), (2, 16392, 16400),
+                                    (9, 12288, 12296), (33, 40000, 40000)])
+def test_ragged_and_strided(m, k, ld):
+    rng = np.random.default_rng(m * 7 + k)
+    full = bf16_from_f64(rng.standard_normal((m, ld)) * 10.0 ** rng.uniform(-3, 3, (m, 1)))
+    x = to_dev_bf16(full)[:, :k]
+    q, s = fq.quantize_act_per_token(x)
+    torch.cuda.synchronize()
+    _check_rows(full[:, :k], host_bits(q), host_bits(s), what=f"ragged {m}x{k}")
+
+
+def test_tiny_zero_and_negative_zero_rows():
+    rows = np.zeros((4, 64), np.uint16)
+    rows[0, :] = 0x8000                                  # all -0
+    rows[1, 5] = 0x0001                                  # smallest subnormal
+    rows[1, 6] = 0x8002
+    rows[2, :] = bf16_from_f64(np.linspace(-2.0 ** -128, 2.0 ** -129, 64))
+    rows[3, :8] = bf16_from_f64(np.array([1e-40, -1e-40, 5e-39, 0, 1, -1, 2, -448]) * 1e-30)
+    q, s = _gpu_quant(rows)
+    _check_rows(rows, q, s, what="tiny")
+    assert np.all(q[0] == 0x80) and s[0] == 0
+
+
+def test_deterministic():
+    x, _ = c3_inputs(1, m=1024)
+    a = _gpu_quant(x)
+    b = _gpu_quant(x)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
