@@ -34,7 +34,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kStepBytes = 128;        // K bytes per MFMA
-constexpr int kBatch = 8;              // MFMA steps whose loads are in flight
+constexpr int kBatch = 4;              // MFMA steps whose loads are in flight
 constexpr int kLdsRowPad = 16;
 constexpr int64_t kGemvFusedLds = 64 * 1024;
 
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave-uniform values live in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = blockIdx.x / split_k;
   const int chunk = blockIdx.x - tile * split_k;
   const int n0 = tile * 16;
@@ -82,20 +83,21 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
 
   // A operand: lane -> weight row n0 + (lane & 15), 32 bytes at 32*(lane>>4)
   // of every 128-byte step.  B operand: lane -> token (lane & 15), same K
-  // bytes; tokens >= M contribute zeros.
+  // bytes; tokens >= M read token 0's bytes and are zeroed by a select.
   const int arow = lane & 15;
   const int kq = (lane >> 4) * 32;
   const uint8_t* wptr =
       qw + static_cast<int64_t>(n0 + arow) * K + kwave + kq;
   const int tok = lane & 15;
   const bool tok_ok = tok < M;
+  const int tok_rd = tok_ok ? tok : 0;
 
   // Start the first batch of weight loads before anything else.
+  const int nfull = steps / kBatch;              // full batches
   uint4 wa[kBatch][2];
-  const int first = min(steps, kBatch);
+  if (nfull > 0) {
 #pragma unroll
-  for (int s = 0; s < kBatch; ++s) {
-    if (s < first) {
+    for (int s = 0; s < kBatch; ++s) {
       wa[s][0] = load_stream16(wptr + s * kStepBytes);
       wa[s][1] = load_stream16(wptr + s * kStepBytes + 16);
     }
@@ -138,49 +140,50 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
     __syncthreads();
   }
 
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int base = 0; base < steps; base += kBatch) {
-    const int nb = min(kBatch, steps - base);
-    // B fragments for this batch.
-    v8i xb[kBatch];
-#pragma unroll
-    for (int s = 0; s < kBatch; ++s) {
-      if (s < nb) {
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-        if (tok_ok) {
-          const int koff = kwoff + (base + s) * kStepBytes + kq;
-          if constexpr (FUSED) {
-            const uint8_t* p = lds_dyn + tok * lds_stride + koff;
-            lo = *reinterpret_cast<const uint4*>(p);
-            hi = *reinterpret_cast<const uint4*>(p + 16);
-          } else {
-            const uint8_t* p = qx + static_cast<int64_t>(tok) * K + kbeg + koff;
-            lo = *reinterpret_cast<const uint4*>(p);
-            hi = *reinterpret_cast<const uint4*>(p + 16);
-          }
-        }
-        xb[s] = to_v8i(lo, hi);
-      }
+  // B fragment of one step (k offset inside the chunk), zero for tokens >= M.
+  auto load_b = [&](int koff) -> v8i {
+    uint4 lo, hi;
+    if constexpr (FUSED) {
+      const uint8_t* p = lds_dyn + tok_rd * lds_stride + koff + kq;
+      lo = *reinterpret_cast<const uint4*>(p);
+      hi = *reinterpret_cast<const uint4*>(p + 16);
+    } else {
+      const uint8_t* p = qx + static_cast<int64_t>(tok_rd) * K + kbeg + koff + kq;
+      lo = *reinterpret_cast<const uint4*>(p);
+      hi = *reinterpret_cast<const uint4*>(p + 16);
     }
-    // MFMAs on the loaded batch, then start the next batch's loads.
+    v8i r = to_v8i(lo, hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = tok_ok ? r[i] : 0;
+    return r;
+  };
+
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = 0; b < nfull; ++b) {
     v8i wfrag[kBatch];
 #pragma unroll
-    for (int s = 0; s < kBatch; ++s)
-      if (s < nb) wfrag[s] = to_v8i(wa[s][0], wa[s][1]);
-    const int next = base + kBatch;
-    const int nn = min(kBatch, steps - next);
+    for (int s = 0; s < kBatch; ++s) wfrag[s] = to_v8i(wa[s][0], wa[s][1]);
+    if (b + 1 < nfull) {
+      const uint8_t* nxt = wptr + (b + 1) * kBatch * kStepBytes;
 #pragma unroll
-    for (int s = 0; s < kBatch; ++s) {
-      if (s < nn) {
-        wa[s][0] = load_stream16(wptr + (next + s) * kStepBytes);
-        wa[s][1] = load_stream16(wptr + (next + s) * kStepBytes + 16);
+      for (int s = 0; s < kBatch; ++s) {
+        wa[s][0] = load_stream16(nxt + s * kStepBytes);
+        wa[s][1] = load_stream16(nxt + s * kStepBytes + 16);
       }
     }
 #pragma unroll
-    for (int s = 0; s < kBatch; ++s)
-      if (s < nb)
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wfrag[s], xb[s], acc, 0, 0, 0, 0, 0, 0);
+    for (int s = 0; s < kBatch; ++s) {
+      const v8i xb = load_b(kwoff + (b * kBatch + s) * kStepBytes);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          wfrag[s], xb, acc, 0, 0, 0, 0, 0, 0);
+    }
+  }
+  for (int s = nfull * kBatch; s < steps; ++s) {
+    const v8i wf = to_v8i(load_stream16(wptr + s * kStepBytes),
+                          load_stream16(wptr + s * kStepBytes + 16));
+    const v8i xb = load_b(kwoff + s * kStepBytes);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xb, acc, 0, 0,
+                                                           0, 0, 0, 0);
   }
 
   // Add the 4 waves' tiles in wave order.  16x16 accumulator layout: lane
