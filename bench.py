@@ -1,0 +1,271 @@
+"""Benchmark of the FP8_DYNAMIC W8A8 Linear on one MI355X.
+
+One step = one pass of the whole hot path (per-token activation quantization,
+FP8 GEMM, scale epilogue) through the 7 quantized Linears of one
+self-attention layer (q, k, v, o, gate, up, down) on a 4096-token prefill
+chunk of seeded synthetic data.  ``value`` is that step's throughput in
+TFLOP/s (2*M*N*K summed over the 7 Linears; quantization flops not counted).
+
+Also measured and printed on the same JSON line:
+* ``roofline``: the dominant kernel (the FP8 GEMM) timed alone with HIP events
+  on its own stream, against the FP8 dense MFMA peak (5.0 PFLOP/s);
+* ``decode``: the decode step of one layer at M = 1 (7 fused calls replayed
+  from a HIP graph, rotating over 4 copies of the layer's weights so that the
+  weight bytes come from HBM, not from the 256 MB last-level cache), in GB/s
+  of algorithmic bytes against 8 TB/s;
+* ``cpu_baseline``: the CPU oracle timed on a bounded sample of the same
+  workload on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+PREFILL_M = 4096
+DECODE_M = 1
+DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).to("cuda")
+
+
+def time_events(torch, fn, reps):
+    """Average duration of fn() over reps calls, HIP events on the current
+    stream (the stream the library launches on)."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def setup_layer(torch, fq, m, cfg):
+    from workloads import LAYER_SHAPES
+    from workloads.generators import c3_x, outlier_act_bf16, rng_for, weight_bf16
+    layer = []
+    for j, (name, n, k) in enumerate(LAYER_SHAPES):
+        w = weight_bf16(cfg, 0, j, n, k)
+        qw, sw = fq.quantize_weight_channelwise(to_dev(w, torch))
+        if cfg == 3:
+            x = c3_x(m, k, j)
+        else:
+            x = outlier_act_bf16(rng_for(2, m, j, 0), (m, k))
+        xd = to_dev(x, torch)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        layer.append(dict(name=name, n=n, k=k, x=xd, qw=qw, sw=sw, y=y))
+    torch.cuda.synchronize()
+    return layer
+
+
+def bench_prefill(torch, fq, steps, warmup):
+    layer = setup_layer(torch, fq, PREFILL_M, 3)
+    flops = sum(2 * PREFILL_M * L["n"] * L["k"] for L in layer)
+    wsb = max(fq.workspace_bytes(PREFILL_M, L["n"], L["k"], True) for L in layer)
+    ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
+
+    def step():
+        for L in layer:
+            fq.quant_linear(L["x"], L["qw"], L["sw"], out=L["y"], workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_time = time_events(torch, step, steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Dominant kernel alone: the GEMM on pre-quantized activations.
+    for L in layer:
+        L["qx"], L["sx"] = fq.quantize_act_per_token(L["x"])
+    gemm_t, quant_t = [], []
+    for L in layer:
+        f = lambda L=L: fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
+        f()
+        gemm_t.append(time_events(torch, f, max(10, steps)))
+        q = lambda L=L: fq.quantize_act_per_token(L["x"])
+        q()
+        quant_t.append(time_events(torch, q, max(10, steps)))
+    per = {L["name"]: {"gemm_us": round(t * 1e6, 2),
+                       "gemm_tflops": round(2 * PREFILL_M * L["n"] * L["k"] / t / 1e12, 1),
+                       "quant_us": round(tq * 1e6, 2),
+                       "quant_gbs": round((3 * PREFILL_M * L["k"] + 4 * PREFILL_M) / tq / 1e9, 0)}
+           for L, t, tq in zip(layer, gemm_t, quant_t)}
+    gemm_tflops = flops / sum(gemm_t) / 1e12
+    del layer
+    torch.cuda.empty_cache()
+    return dict(step_time=step_time, wall=wall, flops=flops,
+                gemm_tflops=gemm_tflops, gemm_time=sum(gemm_t), per_linear=per)
+
+
+def bench_decode(torch, fq, reps):
+    base = setup_layer(torch, fq, DECODE_M, 2)
+    copies = [base]
+    for _ in range(DECODE_COPIES - 1):
+        copies.append([dict(L, qw=L["qw"].clone(), sw=L["sw"].clone()) for L in base])
+    nbytes = sum(L["n"] * L["k"] + 4 * L["n"] + 2 * DECODE_M * L["k"]
+                 + 2 * DECODE_M * L["n"] for L in base)
+    wsb = max(fq.workspace_bytes(DECODE_M, L["n"], L["k"], True) for L in base)
+    ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
+
+    def layer_pass(layer):
+        for L in layer:
+            fq.quant_linear(L["x"], L["qw"], L["sw"], out=L["y"], workspace=ws)
+
+    for c in copies:                       # warm-up outside capture
+        layer_pass(c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        layer_pass(copies[0])              # first use of this stream, uncaptured
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for c in copies:
+                layer_pass(c)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t = time_events(torch, g.replay, reps) / DECODE_COPIES
+    del copies, base
+    torch.cuda.empty_cache()
+    return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes)
+
+
+def cpu_baseline(target_s=16.0):
+    """The oracle as it stands, timed on a sample of the prefill workload:
+    all 7 Linears, a subset of tokens and of output channels (weights
+    quantized by the oracle beforehand, untimed, as the offline step)."""
+    import oracle
+    from workloads import LAYER_SHAPES
+    from workloads.generators import c3_x, weight_bf16
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    def run(m_s, n_frac):
+        flops, secs = 0, 0.0
+        for j, (_, n, k) in enumerate(LAYER_SHAPES):
+            n_s = max(16, n // n_frac)
+            x = c3_x(PREFILL_M, k, j, rows=m_s)
+            w = weight_bf16(3, 0, j, n, k, rows=n_s)
+            qw, sw = oracle.quant_weight_ref(w)
+            t0 = time.perf_counter()
+            oracle.quant_linear_ref(x, qw, sw)
+            secs += time.perf_counter() - t0
+            flops += 2 * m_s * n_s * k
+        return flops, secs
+
+    # Grow the sample until the timed oracle work reaches about target_s.
+    sizes = [(64, 16), (256, 8), (512, 4), (1024, 4), (2048, 4), (4096, 4)]
+    for m_s, n_frac in sizes:
+        flops, secs = run(m_s, n_frac)
+        if secs >= target_s / 2:
+            break
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"prefill M=4096 layer, {m_s} tokens x 1/{n_frac} of the "
+                      f"output channels of each of the 7 Linears; quantize + "
+                      f"fp64 matmul + epilogue; {secs:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; "
+                          "run with --gpus 1"}))
+        return 2
+    import torch
+    import fp8_w8a8_dynamic_amd as fq
+    fq.load_library()
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+
+    log("prefill ...")
+    pre = bench_prefill(torch, fq, args.steps, args.warmup)
+    tflops = pre["flops"] / pre["step_time"] / 1e12
+    log(f"prefill step {pre['step_time']*1e6:.1f} us  {tflops:.1f} TFLOP/s; "
+        f"GEMM alone {pre['gemm_tflops']:.1f} TFLOP/s")
+    dec = None
+    if not args.no_decode:
+        log("decode ...")
+        dec = bench_decode(torch, fq, max(20, args.steps))
+        log(f"decode layer {dec['layer_us']:.2f} us  {dec['gbs']:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu:
+        log("cpu oracle ...")
+        cpu = cpu_baseline()
+        log(f"cpu oracle {cpu}")
+
+    out = {
+        "metric": "FP8_DYNAMIC linear TFLOP/s @M=4096 (%MFMA peak); GB/s @M=1 (%HBM)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["step_time"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> f32 acc -> bf16",
+        "data": "synthetic (seeded; no datasets or trained weights)",
+        "config": {"workload": "prefill chunk of one self-attention layer: "
+                               "M=4096 tokens through q,k,v,o (4096|1024 x 4096), "
+                               "gate,up (12288 x 4096), down (4096 x 12288); "
+                               "fused per-token quant + FP8 GEMM + epilogue",
+                   "m": PREFILL_M, "linears": 7,
+                   "frac_of_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tflops"], 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pre["gemm_tflops"] / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "gemm_fp8_kernel",
+                     "per_linear": pre["per_linear"]},
+    }
+    if dec is not None:
+        out["decode"] = {"m": DECODE_M, "metric": "GB/s of algorithmic bytes, "
+                         "7 fused calls of one layer, HIP graph replay",
+                         "value": round(dec["gbs"], 1), "unit": "GB/s",
+                         "us_per_layer": round(dec["layer_us"], 3),
+                         "frac_of_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+                         "bytes_per_layer": dec["bytes"]}
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

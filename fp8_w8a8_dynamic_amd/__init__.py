@@ -8,9 +8,10 @@ package is its Python binding (argument marshalling only).
 """
 
 from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
-                      load_library, quant_linear, quantize_act_per_token,
+                      init_workspace, load_library, quant_linear, quantize_act_per_token,
                       quantize_weight_channelwise, workspace_bytes)
 
 __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
+           "init_workspace",
            "load_library", "quant_linear", "quantize_act_per_token",
            "quantize_weight_channelwise", "workspace_bytes"]

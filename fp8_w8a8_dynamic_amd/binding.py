@@ -138,6 +138,23 @@ def workspace_bytes(m: int, n: int, k: int, fused: bool) -> int:
     return int(load_library().fp8w8a8_workspace_bytes(m, n, k, int(fused)))
 
 
+def init_workspace(ws: torch.Tensor) -> torch.Tensor:
+    """Zero a caller-owned uint8 workspace with the library's fill kernel."""
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    _check(load_library().fp8w8a8_workspace_init(
+        ws.data_ptr(), ws.numel(), _stream_ptr(ws.device)), "workspace_init")
+    return ws
+
+
+def _pick_workspace(device, need, workspace):
+    if workspace is None:
+        return _workspaces.get(device, need)
+    if need and workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
+    return workspace
+
+
 def quantize_weight_channelwise(w: torch.Tensor):
     """bf16 W[N, K] -> (qW float8_e4m3fn [N, K], w_scale float32 [N])."""
     lib = load_library()
@@ -178,8 +195,11 @@ def _out(m, n, device, out):
     return out
 
 
-def fp8_linear(qx, x_scale, qw, w_scale, out=None):
-    """Y[M, N] = bf16((qX @ qW^T) * x_scale[:, None] * w_scale[None, :])."""
+def fp8_linear(qx, x_scale, qw, w_scale, out=None, workspace=None):
+    """Y[M, N] = bf16((qX @ qW^T) * x_scale[:, None] * w_scale[None, :]).
+
+    ``workspace``: optional caller-owned buffer (see :func:`init_workspace`);
+    by default a cached per-stream workspace is used."""
     lib = load_library()
     qx, qw = _as_codes(qx), _as_codes(qw)
     m, k, ldq = _rows(qx, "qx")
@@ -190,7 +210,7 @@ def fp8_linear(qx, x_scale, qw, w_scale, out=None):
     if m == 0 or n == 0:
         return y
     need = workspace_bytes(m, n, k, False)
-    ws = _workspaces.get(qx.device, need)
+    ws = _pick_workspace(qx.device, need, workspace)
     _check(lib.fp8w8a8_fp8_linear(
         qx.data_ptr(), x_scale.data_ptr(), qw.data_ptr(), w_scale.data_ptr(),
         m, n, k, y.data_ptr(), y.stride(0),
@@ -200,7 +220,7 @@ def fp8_linear(qx, x_scale, qw, w_scale, out=None):
     return y
 
 
-def quant_linear(x, qw, w_scale, out=None):
+def quant_linear(x, qw, w_scale, out=None, workspace=None):
     """Fused FP8_DYNAMIC forward: bf16 X[M, K] -> bf16 Y[M, N]."""
     lib = load_library()
     if x.dtype != torch.bfloat16:
@@ -214,7 +234,7 @@ def quant_linear(x, qw, w_scale, out=None):
     if m == 0 or n == 0:
         return y
     need = workspace_bytes(m, n, k, True)
-    ws = _workspaces.get(x.device, need)
+    ws = _pick_workspace(x.device, need, workspace)
     _check(lib.fp8w8a8_quant_linear(
         x.data_ptr(), ldx, qw.data_ptr(), w_scale.data_ptr(), m, n, k,
         y.data_ptr(), y.stride(0), ws.data_ptr() if ws is not None else None,

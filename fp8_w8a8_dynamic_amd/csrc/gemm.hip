@@ -72,25 +72,36 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int p0) {
   return r;
 }
 
-// Start the global -> LDS copies of one K stage (A rows then B rows).
-template <int BM, int BN>
-__device__ __forceinline__ void issue_stage(
-    uint8_t* smem, int st, int k0, int wave,
-    const uint8_t* const (&a_src)[GemmShape<BM, BN>::A_LOADS],
-    const uint8_t* const (&b_src)[GemmShape<BM, BN>::B_LOADS]) {
-  using S = GemmShape<BM, BN>;
-  uint8_t* as = smem + st * S::STAGE;
-  uint8_t* bs = as + S::A_STAGE;
-#pragma unroll
-  for (int i = 0; i < S::A_LOADS; ++i)
-    __builtin_amdgcn_global_load_lds(
-        a_src[i] + k0, (lds_void*)(as + (wave * S::A_LOADS + i) * 1024), 16, 0,
-        0);
-#pragma unroll
-  for (int i = 0; i < S::B_LOADS; ++i)
-    __builtin_amdgcn_global_load_lds(
-        b_src[i] + k0, (lds_void*)(bs + (wave * S::B_LOADS + i) * 1024), 16, 0,
-        0);
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0).  Loads
+// at offsets >= bytes return zero: this is how rows past M or N read as 0.
+__device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
+  return r;
+}
+
+// One 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): the
+// wave's 64 x 16 bytes land contiguously at LDS byte address `lds` (M0).
+// Inline asm because the compiler's wait-count insertion cannot tell the two
+// stage buffers apart and would serialize every copy with the MFMAs on the
+// other stage.  The instruction has no register result; the kernel waits for
+// the copies explicitly (vmcnt(0) + barrier) before reading the stage.
+__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff,
+                                           uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
 }
 
 template <int BM, int BN, int MINB>
@@ -104,32 +115,36 @@ __global__ __launch_bounds__(256, MINB) void gemm_fp8_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   int tm, tn;
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
+  // Descriptors cover exactly this tile's valid rows.
+  const v4i a_rsrc = make_rsrc(qx + static_cast<int64_t>(m0) * K,
+                               static_cast<uint32_t>(min(M - m0, BM)) * K);
+  const v4i b_rsrc = make_rsrc(qw + static_cast<int64_t>(n0) * K,
+                               static_cast<uint32_t>(min(N - n0, BN)) * K);
+
   // Global -> LDS assignment.  One wave instruction fills 1 KB of LDS =
   // 8 rows x 128 bytes; lane j lands at byte 16*j: row j>>3, physical chunk
   // j&7, which holds logical chunk (j&7) ^ (row&7).
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ lrow;
-  const uint8_t* a_src[S::A_LOADS];
-  const uint8_t* b_src[S::B_LOADS];
+  uint32_t a_off[S::A_LOADS], b_off[S::B_LOADS];
 #pragma unroll
-  for (int i = 0; i < S::A_LOADS; ++i) {
-    const int r = (wave * S::A_LOADS + i) * 8 + lrow;
-    const int gm = min(m0 + r, M - 1);
-    a_src[i] = qx + static_cast<int64_t>(gm) * K + lchunk * 16;
-  }
+  for (int i = 0; i < S::A_LOADS; ++i)
+    a_off[i] = static_cast<uint32_t>(((wave * S::A_LOADS + i) * 8 + lrow) * K +
+                                     lchunk * 16);
 #pragma unroll
-  for (int i = 0; i < S::B_LOADS; ++i) {
-    const int r = (wave * S::B_LOADS + i) * 8 + lrow;
-    const int gn = min(n0 + r, N - 1);
-    b_src[i] = qw + static_cast<int64_t>(gn) * K + lchunk * 16;
-  }
+  for (int i = 0; i < S::B_LOADS; ++i)
+    b_off[i] = static_cast<uint32_t>(((wave * S::B_LOADS + i) * 8 + lrow) * K +
+                                     lchunk * 16);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t a_lds = lds0 + wave * S::A_LOADS * 1024;
+  const uint32_t b_lds = lds0 + S::A_STAGE + wave * S::B_LOADS * 1024;
 
   v16f acc[S::TM][S::TN];
 #pragma unroll
@@ -148,13 +163,21 @@ __global__ __launch_bounds__(256, MINB) void gemm_fp8_kernel(
   const int b_row0 = wn * S::WN + frow;
 
   const int KT = K / kBK;
-  issue_stage<BM, BN>(smem, 0, 0, wave, a_src, b_src);
+  auto issue = [&](int st, int k0) {
+    const uint32_t so = static_cast<uint32_t>(k0);
+#pragma unroll
+    for (int i = 0; i < S::A_LOADS; ++i)
+      lds_copy16(a_rsrc, a_off[i], so, a_lds + st * S::STAGE + i * 1024);
+#pragma unroll
+    for (int i = 0; i < S::B_LOADS; ++i)
+      lds_copy16(b_rsrc, b_off[i], so, b_lds + st * S::STAGE + i * 1024);
+  };
+  issue(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
-    __syncthreads();                     // all waves' loads landed; the other
-                                         // buffer is no longer being read
-    if (kt + 1 < KT)
-      issue_stage<BM, BN>(smem, (kt + 1) & 1, (kt + 1) * kBK, wave, a_src, b_src);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+    __syncthreads();                     // all copies landed; the other stage
+                                         // is no longer being read
+    if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * kBK);
     const uint8_t* as = smem + (kt & 1) * S::STAGE;
     const uint8_t* bs = as + S::A_STAGE;
 #pragma unroll

@@ -200,28 +200,42 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
     for (int r = 0; r < 4; ++r) acc[r] += red[w][lane][r];
 
   if (split_k > 1) {
-    float4* mine = reinterpret_cast<float4*>(
-        partials + (static_cast<int64_t>(tile) * split_k + chunk) * 256);
-    mine[lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    __threadfence();
+    // Hand-off between the workgroups of one tile without whole-cache
+    // flushes: partials are written and read with device-coherent (sc1)
+    // accesses, which bypass the per-XCD caches; the writer waits for its
+    // stores to complete before bumping the arrival counter, and only the
+    // last arriver, which has seen every other increment, reads them.
+    float* mine = partials + (static_cast<int64_t>(tile) * split_k + chunk) * 256;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_store(mine + lane * 4 + r, acc[r], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): stores done
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(counters + tile, 1u);
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0, 64);
     if (prev != static_cast<unsigned>(split_k - 1)) return;
-    __threadfence();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     v4f sum = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float4* all = reinterpret_cast<const float4*>(
-        partials + static_cast<int64_t>(tile) * split_k * 256);
+    const float* all = partials + static_cast<int64_t>(tile) * split_k * 256;
     for (int c = 0; c < split_k; ++c) {
       if (c == chunk) {
         sum += acc;
       } else {
-        const float4 p = all[c * 64 + lane];
-        sum[0] += p.x; sum[1] += p.y; sum[2] += p.z; sum[3] += p.w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sum[r] += __hip_atomic_load(all + c * 256 + lane * 4 + r,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     acc = sum;
-    if (lane == 0) atomicExch(counters + tile, 0u);
+    if (lane == 0)
+      __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if (!tok_ok) return;

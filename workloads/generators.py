@@ -84,9 +84,11 @@ def outlier_act_bf16(rng, shape, frac=0.01, factor=20.0) -> np.ndarray:
     return bf16_from_f64(x)
 
 
-def weight_bf16(cfg: int, layer: int, linear: int, n: int, k: int):
-    """W[n, k] ~ N(0, 0.02) for one Linear."""
-    return normal_bf16(rng_for(cfg, layer, linear, ROLE_W), (n, k), 0.02)
+def weight_bf16(cfg: int, layer: int, linear: int, n: int, k: int, rows=None):
+    """W[n, k] ~ N(0, 0.02) for one Linear (or only its first `rows` rows,
+    which are the same numbers: draws are made row by row)."""
+    return normal_bf16(rng_for(cfg, layer, linear, ROLE_W),
+                       (n if rows is None else rows, k), 0.02)
 
 
 def c1_inputs():
@@ -105,11 +107,13 @@ def c2_inputs(m: int, linear: int):
     return x, w
 
 
-def c3_x(m: int, k: int, seed_linear: int) -> np.ndarray:
+def c3_x(m: int, k: int, seed_linear: int, rows=None) -> np.ndarray:
+    """X[m, k] of the prefill chunk (or only its first `rows` rows)."""
     rng = rng_for(3, m, seed_linear, ROLE_X)
     gain = np.power(np.float32(10.0),
                     rng.uniform(-1.0, 1.0, size=k).astype(np.float32))
-    x = rng.standard_normal((m, k), dtype=np.float32) * gain[None, :]
+    x = rng.standard_normal((m if rows is None else rows, k),
+                            dtype=np.float32) * gain[None, :]
     return bf16_from_f64(x)
 
 
