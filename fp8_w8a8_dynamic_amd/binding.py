@@ -102,12 +102,8 @@ def _rows(t: torch.Tensor, name: str):
 
 
 class _Workspaces:
-    """One zero-initialised workspace per (device, stream), grown on demand.
-
-    The library's split-K counters sit in the first 64 KiB and are left at
-    zero by every call, so a workspace is reusable by consecutive calls on its
-    stream.  A grown workspace is zeroed by the library's own fill kernel.
-    """
+    """One scratch workspace per (device, stream), grown on demand (calls on
+    one stream are ordered, so they can share it)."""
 
     def __init__(self):
         self._bufs = {}
@@ -124,9 +120,6 @@ class _Workspaces:
                 size = max(nbytes, 1 << 20)
                 size = (size + 255) // 256 * 256
                 buf = torch.empty(size, dtype=torch.uint8, device=device)
-                _check(load_library().fp8w8a8_workspace_init(
-                    buf.data_ptr(), size, stream.cuda_stream),
-                    "fp8w8a8_workspace_init")
                 self._bufs[key] = buf
             return buf
 

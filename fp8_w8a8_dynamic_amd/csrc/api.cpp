@@ -113,31 +113,20 @@ Path choose_path(int64_t m) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout, the same for every call:
-//   [0, kCounterBytes)            split-K arrival counters (zero between calls)
-//   [kCounterBytes, +partials)    float32 split-K partial tiles
-//   [.., +qx)                     quantized activations [m, k] (fused calls
-//   [.., +sx)                     that quantize in a separate kernel), scales
+// Workspace: only calls that quantize in a separate kernel before the
+// linear kernel need one; it holds the quantized activations [m, k] and
+// their scales [m] (no state survives a call).
 struct Layout {
-  size_t partials = 0, qx = 0, sx = 0, total = 0;
-  size_t partial_bytes = 0;
-  bool any = false;
+  size_t qx = 0, sx = 0, total = 0;
 };
 
 Layout layout_for(int64_t m, int64_t n, int64_t k, bool fused, Path path) {
   Layout L;
-  if (m == 0 || n == 0) return L;
-  const bool gemv = path == Path::kGemv;
-  const bool fused_in_kernel = gemv && fused && fp8w8a8::gemv_fused_fits(m, n, k);
-  const bool separate_quant = fused && !fused_in_kernel;
-  L.partial_bytes =
-      gemv ? fp8w8a8::gemv_partial_bytes(m, n, k, fused_in_kernel) : 0;
-  if (L.partial_bytes == 0 && !separate_quant) return L;
-  L.any = true;
-  L.partials = fp8w8a8::kCounterBytes;
-  L.qx = L.partials + round_up(L.partial_bytes, 256);
-  L.sx = L.qx + (separate_quant ? round_up(static_cast<size_t>(m) * k, 256) : 0);
-  L.total = L.sx + (separate_quant ? round_up(static_cast<size_t>(m) * 4, 256) : 0);
+  if (m == 0 || n == 0 || !fused) return L;
+  if (path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k)) return L;
+  L.qx = 0;
+  L.sx = round_up(static_cast<size_t>(m) * k, 256);
+  L.total = L.sx + round_up(static_cast<size_t>(m) * 4, 256);
   return L;
 }
 
@@ -206,8 +195,7 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
       overlap(ry, span(qw, n, k, k, 1)) || overlap(ry, span(w_scale, n, 1, 1, 4)))
     return FP8W8A8_ERR_ALIAS;
   const Path path = choose_path(m);
-  const Layout L = layout_for(m, n, k, false, path);
-  const size_t need = L.total;
+  const size_t need = layout_for(m, n, k, false, path).total;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
     const Range rw{reinterpret_cast<uintptr_t>(workspace),
@@ -222,11 +210,9 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
   if ((st = check_device()) != FP8W8A8_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
   if (path == Path::kGemv)
     e = fp8w8a8::launch_gemv(nullptr, 0, qx, x_scale, qw, w_scale, m, n, k, y,
-                             ldy, reinterpret_cast<unsigned*>(ws),
-                             reinterpret_cast<float*>(ws + L.partials), s);
+                             ldy, s);
   else
     e = fp8w8a8::launch_gemm(qx, x_scale, qw, w_scale, m, n, k, y, ldy, s);
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
@@ -263,12 +249,10 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
   if ((st = check_device()) != FP8W8A8_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  unsigned* counters = reinterpret_cast<unsigned*>(ws);
-  float* partials = L.any ? reinterpret_cast<float*>(ws + L.partials) : nullptr;
   hipError_t e;
   if (path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k)) {
     e = fp8w8a8::launch_gemv(x, ldx, nullptr, nullptr, qw, w_scale, m, n, k,
-                             y, ldy, counters, partials, s);
+                             y, ldy, s);
   } else {
     // Quantize into the workspace, then run the matching linear kernel.
     uint8_t* qx = ws + L.qx;
@@ -277,7 +261,7 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
     if (e == hipSuccess) {
       if (path == Path::kGemv)
         e = fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y,
-                                 ldy, counters, partials, s);
+                                 ldy, s);
       else
         e = fp8w8a8::launch_gemm(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
     }

@@ -126,20 +126,19 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
 
 /*
  * Workspace size in bytes for fp8w8a8_fp8_linear (fused == 0) or
- * fp8w8a8_quant_linear (fused != 0) at the given sizes; 0 for invalid sizes.
- * The workspace holds split-K partial sums with their arrival counters and,
- * for the fused call, the quantized activations.  Contract: the workspace
- * must be all zero before its first use (fp8w8a8_workspace_init does this);
- * every call that returns FP8W8A8_OK leaves the counters zero again, so one
- * workspace can be reused by consecutive calls on ONE stream.  Calls that
- * may run concurrently need distinct workspaces.
+ * fp8w8a8_quant_linear (fused != 0) at the given sizes; 0 when the call needs
+ * none, and 0 for invalid sizes.  The workspace is plain scratch that holds
+ * the quantized activations [m, k] and their scales [m] when a fused call
+ * quantizes in a separate kernel before the matmul; no state survives a
+ * call, so any workspace can be reused, but calls that may run concurrently
+ * need distinct workspaces.
  */
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused);
 
 /*
- * Zero-fill a workspace with a kernel on `stream` (no hipMemsetAsync, so it
- * can sit inside a captured graph).  bytes % 16 == 0, workspace 16-byte
- * aligned.
+ * Zero-fill a device buffer (e.g. a workspace) with a kernel on `stream`
+ * (no hipMemsetAsync, so it can sit inside a captured graph).
+ * bytes % 16 == 0, buffer 16-byte aligned.
  */
 int fp8w8a8_workspace_init(void* workspace, size_t bytes, void* stream);
 

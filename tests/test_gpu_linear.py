@@ -163,3 +163,24 @@ def test_empty_calls():
     x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
     y = fq.quant_linear(x, qw, sw)
     assert y.shape == (0, 16)
+
+
+GEMM_CONFIGS = ["0", "1", "2", "3"]
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 1040, 384), (513, 528, 640), (4096, 272, 256),
+                                   (1, 4096, 128)])
+def test_every_gemm_config_matches_oracle_and_each_other(m, n, k, monkeypatch):
+    """Every tile configuration accumulates each output over K in the same
+    order, so all must agree bit for bit, and with the oracle."""
+    qx, sx, qw, sw = _rand_operands(m, n, k, 4242 + m)
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", "gemm")
+    y64 = oracle.linear_ref(qx, sx, qw, sw)
+    outs = []
+    for cfg in GEMM_CONFIGS:
+        monkeypatch.setenv("FP8W8A8_GEMM_CONFIG", cfg)
+        y = _run_linear(qx, sx, qw, sw)
+        check_close(y, y64, f"gemm cfg {cfg} {m}x{n}x{k}")
+        outs.append(y)
+    for cfg, y in zip(GEMM_CONFIGS[1:], outs[1:]):
+        assert np.array_equal(y, outs[0]), f"config {cfg} differs from config 0"
