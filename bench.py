@@ -202,6 +202,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy "
+                         "(reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; "
@@ -213,6 +216,16 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.calibrate_copy:
+        # A plain elementwise kernel of known traffic: reads 256 MiB, writes
+        # 256 MiB (torch's vectorized add on uint8).
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1, out=dst)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x (268435456 B read + 268435456 B written)")
+        del src, dst
     log("prefill ...")
     pre = bench_prefill(torch, fq, args.steps, args.warmup)
     tflops = pre["flops"] / pre["step_time"] / 1e12
