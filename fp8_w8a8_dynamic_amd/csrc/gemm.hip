@@ -8,21 +8,28 @@
 // Both operands are K-contiguous ("NT"), which is what the MFMA operand
 // fragments want.  Design for gfx950:
 //   * v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> f32; every product is exact
-//     in f32, accumulation in f32);
-//   * a 256-thread workgroup (4 waves in 2x2) owns a BM x BN output tile;
-//     each wave owns (BM/2) x (BN/2) and keeps it in registers;
-//   * K advances 128 bytes per stage; stages are double-buffered in LDS and
-//     filled with global_load_lds_dwordx4 (HBM/L2 -> LDS without passing
-//     through VGPRs) while the MFMAs consume the other stage;
+//     in f32, accumulation in f32), with the weight fragment as the A operand
+//     so that a lane's accumulators hold one token and runs of consecutive
+//     output channels;
+//   * a workgroup of WGM x WGN waves owns a BM x BN output tile, each wave a
+//     (BM/WGM) x (BN/WGN) sub-tile kept in registers;
+//   * K advances 128 bytes per stage.  Stages are copied HBM/L2 -> LDS with
+//     buffer_load_dwordx4 ... lds (no trip through VGPRs) into two LDS
+//     buffers.  At the start of a stage every wave reads all its fragments of
+//     the stage into registers; one barrier later the buffer is free and is
+//     refilled with stage k+2 while the stage's MFMAs run, so two stages of
+//     copies are always in flight, with the copies spread between the MFMAs;
 //   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
-//     (row & 7), so the ds_read_b128 of 8 consecutive rows hit 8 different
-//     bank groups; the swizzle is applied on the global side (each lane
-//     fetches the chunk that belongs at its fixed LDS slot);
+//     ((row >> 1) & 7), so the 16 lanes that the LDS serves together read 16
+//     distinct bank groups; the swizzle is applied on the global side (each
+//     lane fetches the chunk that belongs at its fixed LDS slot);
 //   * workgroup -> tile mapping is XCD-aware: the hardware deals workgroups
 //     round-robin over the 8 XCDs, so consecutive logical tiles (which share
-//     operand rows in groups of 4 tile-rows) are given to one XCD and its L2.
-// Rows beyond M or N are loaded clamped to the last valid row and never
-// stored.  K must be a multiple of 128.
+//     operand rows in groups of 4 tile-rows) are given to one XCD and its L2;
+//   * the epilogue scales, rounds to bf16 and stages the tile in LDS, then
+//     writes whole row segments with 16-byte stores.
+// Rows beyond M or N read as zero (buffer descriptors bounded to the tile's
+// valid rows) and are never stored.  K must be a multiple of 128.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -33,46 +40,45 @@ namespace fp8w8a8 {
 namespace detail {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kGroupM = 4;
+constexpr int kBK = 128;     // K bytes per stage
+constexpr int kSteps = 2;    // 64-byte MFMA K-steps per stage
 
-// Tile configuration: BM x BN output tile per 256-thread workgroup (4 waves
-// in 2x2, each owning (BM/2) x (BN/2)), BK bytes of K per LDS stage, STAGES
-// stage buffers (copies run STAGES-1 stages ahead of the MFMAs).
-template <int BM, int BN, int BK, int STAGES>
+// Tile configuration: BM x BN output tile per workgroup of WGM x WGN waves.
+template <int BM, int BN, int WGM, int WGN>
 struct GemmShape {
-  static constexpr int WM = BM / 2, WN = BN / 2;    // wave tile
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   static constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA tiles
-  static constexpr int CH = BK / 16;                // 16-byte chunks per row
-  static constexpr int RPI = 1024 / BK;             // rows per 1 KB copy
-  static constexpr int A_STAGE = BM * BK, B_STAGE = BN * BK;
+  static constexpr int CH = kBK / 16;               // 16-byte chunks per row
+  static constexpr int RPI = 1024 / kBK;            // rows per 1 KB copy
+  static constexpr int A_STAGE = BM * kBK, B_STAGE = BN * kBK;
   static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int LDS = STAGES * STAGE;
-  static constexpr int A_LOADS = A_STAGE / 4096;    // 1 KB copies per wave
-  static constexpr int B_LOADS = B_STAGE / 4096;
-  static constexpr int STEPS = BK / 64;             // MFMA K-steps per stage
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int A_LOADS = A_STAGE / (1024 * WAVES);  // 1 KB copies
+  static constexpr int B_LOADS = B_STAGE / (1024 * WAVES);  // per wave
+  static constexpr int COPIES = A_LOADS + B_LOADS;          // per stage
   // Epilogue staging: each wave's WM x WN bf16 tile, rows padded by 16 B.
   static constexpr int EPI_ROW = WN * 2 + 16;
-  static constexpr int EPI = 4 * WM * EPI_ROW;
+  static constexpr int EPI = WAVES * WM * EPI_ROW;
   static constexpr int SMEM = LDS > EPI ? LDS : EPI;
-  static_assert(BK == 64 || BK == 128, "BK is 64 or 128 bytes");
-  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
   static_assert(SMEM <= 160 * 1024, "LDS budget of one CU");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 &&
+                A_LOADS * 1024 * WAVES == A_STAGE &&
+                B_LOADS * 1024 * WAVES == B_STAGE, "whole 1 KB copies per wave");
+  static_assert(TM >= 1 && TN >= 1 && (TM * TN) % 2 == 0, "wave tile");
 };
 
-// XOR swizzle of the 16-byte chunk index within a row.  gfx950's LDS serves
-// a ds_read_b128 16 lanes at a time from 64 four-byte banks (256 bytes), and
-// the 16 lanes of a fragment read read 16 consecutive rows at the same
-// logical chunk: the swizzle makes their 16 addresses fall in 16 distinct
-// 16-byte bank groups.  128-byte rows: 2 rows per 256 bytes, 8 chunk values;
-// 64-byte rows: 4 rows per 256 bytes, 4 chunk values.
-template <int BK>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (BK == 128) return (row >> 1) & 7;
-  else return (row >> 2) & 3;
-}
+// XOR swizzle of the 16-byte chunk index within a 128-byte row.  gfx950's
+// LDS serves a ds_read_b128 16 lanes at a time from 64 four-byte banks (256
+// bytes, two rows), and the 16 lanes of a fragment read read 16 consecutive
+// rows at the same logical chunk: the swizzle makes their 16 addresses fall
+// in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
@@ -95,6 +101,7 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n,
   tn = in / gsize;
 }
 
+// One 32-byte MFMA operand fragment: physical chunks p0 and p0 ^ 1 of a row.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int p0) {
   const uint4 lo = *reinterpret_cast<const uint4*>(base + p0 * 16);
   const uint4 hi = *reinterpret_cast<const uint4*>(base + (p0 ^ 1) * 16);
@@ -103,8 +110,6 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int p0) {
   r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
   return r;
 }
-
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0).  Loads
 // at offsets >= bytes return zero: this is how rows past M or N read as 0.
@@ -123,7 +128,7 @@ __device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
 // Inline asm because the compiler's wait-count insertion cannot tell the two
 // stage buffers apart and would serialize every copy with the MFMAs on the
 // other stage.  The instruction has no register result; the kernel waits for
-// the copies explicitly (vmcnt(0) + barrier) before reading the stage.
+// the copies explicitly (vmcnt + barrier) before reading the stage.
 __device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff,
                                            uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
@@ -136,19 +141,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
 }
 
-template <int BM, int BN, int BK, int STAGES, int MINB>
-__global__ __launch_bounds__(256, MINB) void gemm_fp8_kernel(
+template <int BM, int BN, int WGM, int WGN, int MINB>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw, int M,
     int N, int K, uint16_t* __restrict__ y, int64_t ldy, int tiles_m,
     int tiles_n) {
-  using S = GemmShape<BM, BN, BK, STAGES>;
+  using S = GemmShape<BM, BN, WGM, WGN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   int tm, tn;
   map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -161,20 +166,18 @@ __global__ __launch_bounds__(256, MINB) void gemm_fp8_kernel(
                                static_cast<uint32_t>(min(N - n0, BN)) * K);
 
   // Global -> LDS assignment.  One wave copy fills 1 KB of LDS = RPI rows of
-  // BK bytes; lane j lands at byte 16*j: row j / CH, physical chunk j % CH,
+  // 128 bytes; lane j lands at byte 16*j: row j / CH, physical chunk j % CH,
   // which holds logical chunk (j % CH) ^ swz(row).
   uint32_t a_off[S::A_LOADS], b_off[S::B_LOADS];
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
     const int r = (wave * S::A_LOADS + i) * S::RPI + lane / S::CH;
-    a_off[i] = static_cast<uint32_t>(
-        r * K + (((lane % S::CH) ^ swz<BK>(r)) * 16));
+    a_off[i] = static_cast<uint32_t>(r * K + (((lane % S::CH) ^ swz(r)) * 16));
   }
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i) {
     const int r = (wave * S::B_LOADS + i) * S::RPI + lane / S::CH;
-    b_off[i] = static_cast<uint32_t>(
-        r * K + (((lane % S::CH) ^ swz<BK>(r)) * 16));
+    b_off[i] = static_cast<uint32_t>(r * K + (((lane % S::CH) ^ swz(r)) * 16));
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const uint32_t a_lds = lds0 + wave * S::A_LOADS * 1024;
@@ -195,80 +198,74 @@ __global__ __launch_bounds__(256, MINB) void gemm_fp8_kernel(
   // multiples of 32.
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
-  const int fswz = swz<BK>(frow);
+  const int fswz = swz(frow);
   const int a_row0 = wm * S::WM + frow;
   const int b_row0 = wn * S::WN + frow;
 
-  const int KT = K / BK;
-  constexpr int PER_STAGE = S::A_LOADS + S::B_LOADS;  // copies per wave
-  auto issue = [&](int st, int k0) {
-    const uint32_t so = static_cast<uint32_t>(k0);
-#pragma unroll
-    for (int i = 0; i < S::A_LOADS; ++i)
-      lds_copy16(a_rsrc, a_off[i], so, a_lds + st * S::STAGE + i * 1024);
-#pragma unroll
-    for (int i = 0; i < S::B_LOADS; ++i)
-      lds_copy16(b_rsrc, b_off[i], so, b_lds + st * S::STAGE + i * 1024);
+  // Copy c (0 <= c < COPIES) of the stage starting at K byte k0 into buffer
+  // buf.
+  auto copy = [&](int c, int buf, uint32_t k0) {
+    if (c < S::A_LOADS)
+      lds_copy16(a_rsrc, a_off[c], k0, a_lds + buf * S::STAGE + c * 1024);
+    else
+      lds_copy16(b_rsrc, b_off[c - S::A_LOADS], k0,
+                 b_lds + buf * S::STAGE + (c - S::A_LOADS) * 1024);
   };
-  // Prologue: the first STAGES-1 stages.
+
+  const int KT = K / kBK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s * BK);
+  for (int c = 0; c < S::COPIES; ++c) copy(c, 0, 0);
+  if (KT > 1) {
+#pragma unroll
+    for (int c = 0; c < S::COPIES; ++c) copy(c, 1, kBK);
+  }
+  constexpr int kMfma = S::TM * S::TN * kSteps;
+  // MFMAs issued before the release barrier (time for the fragment reads to
+  // land), and the copy spacing over the remaining MFMAs.
+  constexpr int kRelease = (S::TM * S::TN) / 2;
+  constexpr int kSlots = kMfma - kRelease;
+  constexpr int kEvery = kSlots / S::COPIES > 0 ? kSlots / S::COPIES : 1;
+  constexpr int kInLoop = kSlots / kEvery < S::COPIES ? kSlots / kEvery : S::COPIES;
   for (int kt = 0; kt < KT; ++kt) {
-    // Wait until this wave's copies of stage kt have landed: the copies of
-    // the (up to STAGES-2) later stages may stay in flight.
-    const int later = min(STAGES - 2, KT - 1 - kt);
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STAGE));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STAGE));
+    // This wave's copies of stage kt have landed once only stage kt+1's are
+    // outstanding; the barrier extends that to every wave's copies.
+    if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::COPIES));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();  // all waves' copies of stage kt landed, and every wave
-                      // is done reading the stage the next copy overwrites
-    const uint8_t* as = smem + (kt % STAGES) * S::STAGE;
+    __syncthreads();
+    const int buf = kt & 1;
+    const uint8_t* as = smem + buf * S::STAGE;
     const uint8_t* bs = as + S::A_STAGE;
-    // All fragments of the stage are read first; the next stage's copies are
-    // issued while those reads are in flight; then the MFMAs run back to back
-    // with no LDS latency between them.
-    v8i af[S::STEPS][S::TM], bf[S::STEPS][S::TN];
+    v8i af[kSteps][S::TM], bf[kSteps][S::TN];
 #pragma unroll
-    for (int t = 0; t < S::TM; ++t)
-      af[0][t] = lds_frag(as + (a_row0 + 32 * t) * BK, (2 * fhalf) ^ fswz);
-#pragma unroll
-    for (int u = 0; u < S::TN; ++u)
-      bf[0][u] = lds_frag(bs + (b_row0 + 32 * u) * BK, (2 * fhalf) ^ fswz);
-    if (kt + STAGES - 1 < KT)
-      issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
-    // Step 0's MFMAs alternate with the LDS reads of step 1 (when the stage
-    // has two steps), so those reads are in flight under the MFMAs.
-    if constexpr (S::STEPS == 2) {
-      const int p1 = (4 + 2 * fhalf) ^ fswz;
+    for (int step = 0; step < kSteps; ++step) {
+      const int p = (4 * step + 2 * fhalf) ^ fswz;
 #pragma unroll
       for (int t = 0; t < S::TM; ++t)
-        af[1][t] = lds_frag(as + (a_row0 + 32 * t) * BK, p1);
+        af[step][t] = lds_frag(as + (a_row0 + 32 * t) * kBK, p);
 #pragma unroll
       for (int u = 0; u < S::TN; ++u)
-        bf[1][u] = lds_frag(bs + (b_row0 + 32 * u) * BK, p1);
+        bf[step][u] = lds_frag(bs + (b_row0 + 32 * u) * kBK, p);
     }
+    const bool refill = kt + 2 < KT;
+    const uint32_t next_k = static_cast<uint32_t>((kt + 2) * kBK);
 #pragma unroll
-    for (int t = 0; t < S::TM; ++t)
-#pragma unroll
-      for (int u = 0; u < S::TN; ++u)
-        acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            bf[0][u], af[0][t], acc[t][u], 0, 0, 0, 0, 0, 0);
-    if constexpr (S::STEPS == 2) {
-      constexpr int kReads = 2 * (S::TM + S::TN);      // ds_read_b128 count
-      constexpr int kMfma = S::TM * S::TN;
-#pragma unroll
-      for (int i = 0; i < kMfma; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+    for (int i = 0; i < kMfma; ++i) {
+      // Past this barrier every wave holds its fragments of the stage in
+      // registers, so the buffer can take stage kt+2.
+      if (i == kRelease && refill) __syncthreads();
+      const int step = i / (S::TM * S::TN);
+      const int t = (i / S::TN) % S::TM, u = i % S::TN;
+      acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          bf[step][u], af[step][t], acc[t][u], 0, 0, 0, 0, 0, 0);
+      if (i >= kRelease && (i - kRelease) % kEvery == kEvery - 1 && refill) {
+        const int c = (i - kRelease) / kEvery;
+        if (c < S::COPIES) copy(c, buf, next_k);
       }
-      if (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+    }
+    // Copies that did not fit between the MFMAs.
+    if (refill) {
 #pragma unroll
-      for (int t = 0; t < S::TM; ++t)
-#pragma unroll
-        for (int u = 0; u < S::TN; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              bf[1][u], af[1][t], acc[t][u], 0, 0, 0, 0, 0, 0);
+      for (int c = kInLoop; c < S::COPIES; ++c) copy(c, buf, next_k);
     }
   }
 
@@ -324,16 +321,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_fp8_kernel(
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, int MINB>
+template <int BM, int BN, int WGM, int WGN, int MINB>
 hipError_t launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
                       const float* sw, int64_t m, int64_t n, int64_t k,
                       uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
-  gemm_fp8_kernel<BM, BN, BK, STAGES, MINB>
-      <<<dim3(static_cast<uint32_t>(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
-          qx, sx, qw, sw, static_cast<int>(m), static_cast<int>(n),
-          static_cast<int>(k), y, ldy, tiles_m, tiles_n);
+  gemm_fp8_kernel<BM, BN, WGM, WGN, MINB>
+      <<<dim3(static_cast<uint32_t>(tiles_m * tiles_n)), dim3(64 * WGM * WGN),
+         0, stream>>>(qx, sx, qw, sw, static_cast<int>(m), static_cast<int>(n),
+                      static_cast<int>(k), y, ldy, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -349,20 +346,19 @@ hipError_t launch_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
   int cfg = -1;
   if (const char* e = std::getenv("FP8W8A8_GEMM_CONFIG")) cfg = std::atoi(e);
   if (cfg < 0) {
-    // Measured on MI355X for the 4096-token layer shapes: 128x128 tiles with
-    // two workgroups per CU are best unless K is long, where the 256x256
-    // tile's lower operand traffic per flop wins; narrow outputs (few tiles)
-    // prefer the 4-stage 64-byte-K pipeline.
+    // Measured on MI355X for the 4096-token layer shapes: 256x256 tiles of
+    // eight waves, four waves where K is long; narrow outputs (few tiles)
+    // take 128x128 tiles, two workgroups per CU.
     const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
     if (big_tiles < 128) cfg = 2;
-    else if (k > 8192 && big_tiles >= 192) cfg = 1;
-    else cfg = 3;
+    else if (k > 8192) cfg = 0;
+    else cfg = 1;
   }
   switch (cfg) {
-    case 0: return launch_cfg<256, 256, 64, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 1: return launch_cfg<256, 256, 128, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 2: return launch_cfg<128, 128, 64, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    default: return launch_cfg<128, 128, 128, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 0: return launch_cfg<256, 256, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 1: return launch_cfg<256, 256, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 2: return launch_cfg<128, 128, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    default: return launch_cfg<256, 256, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
   }
 }
 
