@@ -108,4 +108,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
 }
 
+// ---- global -> LDS copies (buffer_load_dwordx4 ... lds) -------------------
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0).  Loads
+// at offsets >= bytes return zero.
+__device__ __forceinline__ v4i_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i_t r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
+  return r;
+}
+
+// One 16-byte-per-lane copy global -> LDS: the wave's 64 x 16 bytes land
+// contiguously at LDS byte address `lds` (M0, wave-uniform).  Inline asm so
+// that the compiler's wait-count insertion leaves it alone; the instruction
+// has no register result, and callers wait for it explicitly (vmcnt, then a
+// barrier) before reading what it wrote.
+__device__ __forceinline__ void lds_copy16(v4i_t rsrc, uint32_t voff,
+                                           uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)p));
+}
+
 }  // namespace fp8w8a8

@@ -40,9 +40,8 @@ namespace fp8w8a8 {
 namespace detail {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v4i __attribute__((ext_vector_type(4)));
+typedef v4i_t v4i;
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kGroupM = 4;
 constexpr int kBK = 128;     // K bytes per stage
@@ -80,12 +79,6 @@ struct GemmShape {
 // in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) {
-  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n,
                                          int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
@@ -109,36 +102,6 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int p0) {
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
   r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
   return r;
-}
-
-// Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0).  Loads
-// at offsets >= bytes return zero: this is how rows past M or N read as 0.
-__device__ __forceinline__ v4i make_rsrc(const uint8_t* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = static_cast<int>(static_cast<uint32_t>(a));
-  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu);
-  r[2] = static_cast<int>(bytes);
-  r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
-  return r;
-}
-
-// One 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): the
-// wave's 64 x 16 bytes land contiguously at LDS byte address `lds` (M0).
-// Inline asm because the compiler's wait-count insertion cannot tell the two
-// stage buffers apart and would serialize every copy with the MFMAs on the
-// other stage.  The instruction has no register result; the kernel waits for
-// the copies explicitly (vmcnt + barrier) before reading the stage.
-__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff,
-                                           uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
 }
 
 template <int BM, int BN, int WGM, int WGN, int MINB>

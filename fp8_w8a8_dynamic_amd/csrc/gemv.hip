@@ -3,23 +3,36 @@
 // the model is quantized: in streaming decode, memory bandwidth sets the
 // response speed, and 8-bit weights halve it against BF16).
 //
-// Work decomposition: one workgroup of kWaves waves owns a tile of 16 output
-// channels and streams those 16 weight rows over the whole K; the K range is
-// dealt to its waves in 128-byte steps.  A wave issues the loads of all its
-// steps (up to kMaxSteps) at once, straight from HBM into registers: 32
-// bytes per lane per step, so each step reads whole 128-byte lines of the 16
-// rows.  Each step is one v_mfma_f32_16x16x128_f8f6f4 with A = the 16 weight
-// rows and B = the (up to 16) token rows of the activation codes; the matrix
-// cores have far more throughput than the weight stream needs.  The waves'
-// 16x16 partial tiles are added in LDS in wave order (deterministic), and
-// wave 0 applies the epilogue y = bf16(acc * sx[m] * sw[n]).  No workgroup
-// ever waits on another: there is no cross-workgroup reduction.
+// MFMA layout.  Each v_mfma_f32_16x16x128_f8f6f4 multiplies a 16-row A
+// operand (weights) by a 16-column B operand (activation codes).  With MP =
+// M rounded up to a power of two and C = 16 / MP, the 16 A rows are MP
+// weight rows x C "K classes" and the 16 B columns are MP tokens x C
+// classes; class c of a row is every C-th 16-byte chunk, so one MFMA (an
+// "item") consumes 2 KB of weights: C * 128 contiguous bytes of each of its
+// MP rows (M = 1: 2 KB of one row, read by two fully coalesced 1 KB loads).
+// Only the accumulator entries whose row class equals the column class are
+// partial dot products; their sum over the C classes is the output.  (M = 16
+// gives C = 1: the plain 16-row x 16-token tile.)  The matrix cores have
+// ample throughput for the discarded entries.
 //
-// Fused mode (bf16 activations in, M small): while its weight loads are in
-// flight the workgroup takes the amax of each token row over the whole K
-// (integer max on bf16 bits), derives the float32 scale and quantizes the
-// rows into LDS with exactly the arithmetic of the stand-alone quantization
-// kernel; the B operands are then read from LDS.
+// Work decomposition.  MP weight rows form a row group, which is cs items
+// long.  A workgroup of 16 waves owns gpw consecutive row groups and deals
+// their gpw * cs items to its waves in equal contiguous ranges, so every
+// wave streams at most 8 items (16 KB) and the whole workgroup's weights are
+// requested at once, before anything else; the grid is about one workgroup
+// per CU.  A wave accumulates the items of one row group in its MFMA
+// accumulator; a row group that lies wholly inside one wave's range is
+// finished by that wave, and one that spans several waves is summed from
+// their LDS partials in wave order (deterministic).  No workgroup waits on
+// another.
+//
+// Activations.  The workgroup stages the activation codes in LDS: in fused
+// mode (bf16 in) it loads the rows into registers before issuing the weight
+// loads (so they arrive first), takes each row's amax (integer max on bf16
+// bits), derives the float32 scale and quantizes into LDS with exactly the
+// arithmetic of the stand-alone quantization kernel, all while the weights
+// are in flight; unfused, it copies the codes.  Shapes whose codes do not
+// fit read them from global memory instead.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -33,16 +46,13 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kStepBytes = 128;        // K bytes per MFMA
-constexpr int kLdsRowPad = 16;
-constexpr int64_t kGemvFusedLds = 64 * 1024;
-
-// 16-byte load of weight bytes.  (Plain loads: the two loads of a step
-// touch the same 128-byte lines, and a non-temporal hint could let the line
-// leave L2 between them.)
-__device__ __forceinline__ uint4 load16(const uint8_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;
+constexpr int kItems = 8;              // items in flight per wave
+constexpr int kLdsRowPad = 16;         // LDS code rows: K + 16 bytes
+constexpr int64_t kStageLds = 80 * 1024;  // + 48 KB of partials
+constexpr int64_t kFusedElems = 16384;  // in-kernel quantization up to M*K
+constexpr int kFusedRegs = kFusedElems / 8 / kThreads;  // x loads per thread
 
 __device__ __forceinline__ v8i to_v8i(uint4 lo, uint4 hi) {
   v8i r;
@@ -51,167 +61,393 @@ __device__ __forceinline__ v8i to_v8i(uint4 lo, uint4 hi) {
   return r;
 }
 
-// WAVES waves per workgroup; each wave keeps the loads of up to MAXSTEPS
-// 128-byte steps in flight.
-template <bool FUSED, int WAVES, int MAXSTEPS>
-__global__ __launch_bounds__(WAVES * 64) void gemv_fp8_kernel(
+// Workgroup barrier that orders LDS only.  (__syncthreads also fences
+// global memory, which makes every wave wait for all its weight loads in
+// flight; the barriers here only publish LDS data.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Byte offset, within a row, of the 16-byte chunk that lane group g, class
+// c, half h of step s covers (C classes; see the header).
+__device__ __forceinline__ int chunk_off(int s, int h, int g, int c, int C) {
+  return s * (C * 128) + h * (C * 64) + (g * C + c) * 16;
+}
+
+// Sum over classes of a 16x16 tile held as [lane][4] (lane = column j +
+// 16 * (row >> 2), register = row & 3): output (row rr, token t).  All 16
+// candidate reads are issued together (indexes kept in range) and the ones
+// past C are dropped.
+__device__ __forceinline__ float class_sum(const float (*tile)[4], int rr,
+                                           int t, int C) {
+  float v[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const int i = (rr * C + cc) & 15, j = (t * C + cc) & 15;
+    v[cc] = tile[j + 16 * (i >> 2)][i & 3];
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) s += cc < C ? v[cc] : 0.0f;
+  return s;
+}
+
+// Sum over the 64 lanes of a wave with DPP moves (no LDS traffic); the
+// total lands in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_to_63(float v) {
+  v += dpp_f<0xb1, 0xf>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e, 0xf>(v);    // quad_perm [2,3,0,1]: quad sums
+  v += dpp_f<0x141, 0xf>(v);   // row_half_mirror: 8-lane sums
+  v += dpp_f<0x140, 0xf>(v);   // row_mirror: 16-lane (row) sums
+  v += dpp_f<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// STAGE: 0 = codes read from global memory, 1 = codes copied to LDS,
+// 2 = bf16 activations quantized into LDS (fused).  XR: activation loads per
+// thread for staging.  NI: weight items loaded per wave and batch; every
+// wave issues exactly 2 * NI weight loads per batch (items past its range
+// re-read its last item), so that the wait counts before each use are
+// static and every MFMA starts as soon as its own item has landed.
+template <int STAGE, int XR, int NI>
+__global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ qx,
     const float* __restrict__ sx, const uint8_t* __restrict__ qw,
-    const float* __restrict__ sw, int M, int K, uint16_t* __restrict__ y,
-    int64_t ldy) {
-  constexpr int kWaves = WAVES;
-  constexpr int kThreads = WAVES * 64;
-  constexpr int kMaxSteps = MAXSTEPS;
+    const float* __restrict__ sw, int M, int lg_mp, int N, int K, int gpw,
+    uint16_t* __restrict__ y, int64_t ldy) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_x[];
-  __shared__ float red[kWaves][64][4];
+  __shared__ float part[kWaves][2][64][4];   // partials of shared row groups
+  __shared__ float part1[kWaves][2];         // ... for M = 1 (one value)
+  __shared__ float fin[kWaves][64][4];       // per-wave finishing scratch
   __shared__ float s_scale[kGemvMaxM];
-  __shared__ uint32_t s_amax[kWaves][kGemvMaxM];
+  __shared__ uint32_t s_wmax[kWaves][kGemvMaxM];   // per-wave row maxima
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * 16;
-  // The K range's 128-byte steps, dealt to the waves as evenly as possible.
-  const int csteps = K / kStepBytes;
-  const int s_beg = (wave * csteps) / kWaves;
-  const int steps = ((wave + 1) * csteps) / kWaves - s_beg;
+  const int MP = 1 << lg_mp;
+  const int C = 16 >> lg_mp;
+  const int cs = (K + C * 128 - 1) / (C * 128);  // items per row group
+  const int g0 = blockIdx.x * gpw;               // first row group
+  const int gcount = min(gpw, (N >> lg_mp) - g0);
+  const int total = gcount * cs;
+  const int a = (wave * total) / kWaves, b = ((wave + 1) * total) / kWaves;
 
-  // A operand: lane -> weight row n0 + (lane & 15); its 32 bytes of every
-  // 128-byte step are bytes [16g, 16g+16) and [64+16g, 64+16g+16) with
-  // g = lane >> 4, so each of the two 16-byte loads of a step reads 64
-  // contiguous bytes of every row.  (Which K index sits in which operand byte
-  // is free as long as A and B agree.)  B operand: lane -> token (lane & 15),
-  // same K bytes; tokens >= M read token 0's bytes and are zeroed.
-  const int kq = (lane >> 4) * 16;
-  const uint8_t* wptr = qw + static_cast<int64_t>(n0 + (lane & 15)) * K +
-                        s_beg * kStepBytes + kq;
-  const int tok = lane & 15;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int r = i16 / C, c = i16 % C;            // A: weight row, class
+  const int tok = i16 / C;                       // B: token (same class c)
   const bool tok_ok = tok < M;
-  const int tok_rd = tok_ok ? tok : 0;
+  // LDS code rows: K + 16 bytes; copied rows (STAGE 1) are padded to whole
+  // 1 KB copies first.
+  const int lds_stride = (STAGE == 1 ? (K + 1023) / 1024 * 1024 : K) + kLdsRowPad;
 
-  // Issue the first batch of weight loads before anything else.
-  uint4 wa[kMaxSteps][2];
+  // 1) Staging loads of the activations, issued first.
+  uint4 xv[STAGE == 2 ? XR : 1];
+  uint32_t after = 0;   // produced after the staging loads (see below)
+  if constexpr (STAGE == 2) {
+    const int kv8 = K / 8;
 #pragma unroll
-  for (int s = 0; s < kMaxSteps; ++s)
-    if (s < steps) {
-      wa[s][0] = load16(wptr + s * kStepBytes);
-      wa[s][1] = load16(wptr + s * kStepBytes + 64);
+    for (int i = 0; i < XR; ++i) {
+      // Clamped index: every lane loads (a valid address); only in-range
+      // elements are used.
+      const int e = min(tid + i * kThreads, M * kv8 - 1);
+      const int m = e / kv8, v = e - m * kv8;
+      xv[i] = *reinterpret_cast<const uint4*>(x + m * ldx + v * 8);
     }
+    // Each wave clears its own row maxima (wave-private: no barrier).
+    if (lane < kGemvMaxM) s_wmax[wave][lane] = 0u;
+  } else if constexpr (STAGE == 1) {
+    // 1 KB copies of the code rows straight into LDS, dealt to the waves.
+    // Lanes past a row's end copy the next row's first bytes into this
+    // row's padding (never read); past the last row the descriptor reads 0.
+    const v4i_t rs = make_rsrc(qx, static_cast<uint32_t>(M * K));
+    const int nch = (K + 1023) / 1024;
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_x));
+    for (int q = wave; q < M * nch; q += kWaves) {
+      const int m = q / nch, ch = q - m * nch;
+      lds_copy16(rs, static_cast<uint32_t>(m * K + ch * 1024 + lane * 16), 0u,
+                 l0 + m * lds_stride + ch * 1024);
+    }
+  }
+  // The weight addresses below take `after`, written by an asm statement
+  // that follows the staging loads: the weight loads cannot be issued before
+  // them, so waiting for "2 * NI outstanding" covers every staging load.
+  asm volatile("s_mov_b32 %0, 0" : "=s"(after) : : "memory");
 
-  const int lds_stride = K + kLdsRowPad;
-  if constexpr (FUSED) {
-    // 1) amax of each token row over the full K (integer max on bf16 bits).
-    const int nvec = K / 8;
-    for (int m = 0; m < M; ++m) {
-      const uint4* xr = reinterpret_cast<const uint4*>(x + m * ldx);
-      uint32_t mm = 0;
-      for (int v = tid; v < nvec; v += kThreads) {
-        const uint4 t = xr[v];
-        mm = pk_max_u16(mm, bf16x2_abs_bits(t.x));
-        mm = pk_max_u16(mm, bf16x2_abs_bits(t.y));
-        mm = pk_max_u16(mm, bf16x2_abs_bits(t.z));
-        mm = pk_max_u16(mm, bf16x2_abs_bits(t.w));
+  // 2) Weight loads of this wave's first NI items.  Item it is step
+  // (it % cs) of row group (it / cs).  The first kEarly items go out now;
+  // the rest after the activation codes are staged, so that every wave
+  // reaches the staging barriers quickly (a wave blocks while the memory
+  // pipeline is full, and kEarly items per wave keep it full meanwhile).
+  constexpr int kEarly = NI < 2 ? NI : 2;
+  uint4 wa[NI][2];
+  const int last = b > a ? b - 1 : min(a, total - 1);
+  auto load_item = [&](int s, int first, uint32_t dep) {
+    const int it = min(first + s, last);
+    const int gl = it / cs, st = it - gl * cs;
+    const uint8_t* rp =
+        qw + static_cast<int64_t>((g0 + gl) * MP + r) * K + dep;
+    // Chunks past K (a partial last step) re-read the row's last chunk:
+    // their B operand is zero, so they add nothing.  The loads carry no
+    // condition, which keeps their number, and the waits, static.
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      wa[s][h] = *reinterpret_cast<const uint4*>(
+          rp + min(chunk_off(st, h, g, c, C), K - 16));
+  };
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < kEarly; ++s) load_item(s, a, after);
+  // A use of the loaded registers on a path never taken (K > 0): the loads
+  // must stay here, ahead of the barriers below, instead of being sunk to
+  // their MFMAs.  It costs one scalar compare and forces no wait on the
+  // path taken.
+  if (K <= 0) {
+    uint32_t z = 0;
+#pragma unroll
+    for (int s = 0; s < kEarly; ++s) z ^= wa[s][0].x ^ wa[s][1].x;
+    y[0] = static_cast<uint16_t>(z);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3) Activation codes into LDS.
+  if constexpr (STAGE == 2) {
+    // Row amax (integer max on bf16 magnitude bits): each wave into its own
+    // slots, then one barrier, after which every thread takes the max over
+    // the waves for the rows it quantizes.
+    const int kv8 = K / 8;
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int e0 = i * kThreads + wave * 64;   // first element of the wave
+      if (e0 < M * kv8) {
+        const int e = e0 + lane;
+        const bool ok = e < M * kv8;
+        uint32_t mm = 0;
+        if (ok) {
+          mm = pk_max_u16(bf16x2_abs_bits(xv[i].x), bf16x2_abs_bits(xv[i].y));
+          mm = pk_max_u16(mm, bf16x2_abs_bits(xv[i].z));
+          mm = pk_max_u16(mm, bf16x2_abs_bits(xv[i].w));
+          mm = max(mm & 0xffffu, mm >> 16);
+        }
+        const int m_first = e0 / kv8;
+        const int m_last = min(e0 + 63, M * kv8 - 1) / kv8;
+        if (m_first == m_last) {
+          const uint32_t wm = wave_max_u32(mm);
+          if (lane == 0) s_wmax[wave][m_first] = max(s_wmax[wave][m_first], wm);
+        } else if (ok) {
+          atomicMax(&s_wmax[wave][e / kv8], mm);
+        }
       }
-      const uint32_t wmax = wave_max_u32(max(mm & 0xffffu, mm >> 16));
-      if (lane == 0) s_amax[wave][m] = wmax;
     }
-    __syncthreads();
-    if (tid < M) {
-      uint32_t a = s_amax[0][tid];
+    lds_barrier();
+    auto scale_row = [&](int m) {
+      uint32_t am = 0;
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) a = max(a, s_amax[w][tid]);
-      s_scale[tid] = row_scale(__uint_as_float(a << 16));
-    }
-    __syncthreads();
-    // 2) quantize every token row into LDS (codes, row stride K + pad).
-    for (int m = 0; m < M; ++m) {
-      const uint4* xr = reinterpret_cast<const uint4*>(x + m * ldx);
-      const float s = s_scale[m];
-      for (int v = tid; v < nvec; v += kThreads)
+      for (int w = 0; w < kWaves; ++w) am = max(am, s_wmax[w][m]);
+      return row_scale(__uint_as_float(am << 16));
+    };
+    if (tid < M) s_scale[tid] = scale_row(tid);   // for the epilogue
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < M * kv8) {
+        const int m = e / kv8, v = e - m * kv8;
         *reinterpret_cast<uint2*>(lds_x + m * lds_stride + v * 8) =
-            quantize8(xr[v], s);
+            quantize8(xv[i], scale_row(m));
+      }
     }
-    __syncthreads();
+    lds_barrier();
+  } else if constexpr (STAGE == 1) {
+    // This wave's copies are older than its 2 * kEarly weight loads.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kEarly));
+    lds_barrier();
   }
 
-  // B fragment of one step (k offset within the row), zero for tokens >= M.
-  auto load_b = [&](int koff) -> v8i {
-    uint4 lo, hi;
-    if constexpr (FUSED) {
-      const uint8_t* p = lds_x + tok_rd * lds_stride + koff + kq;
-      lo = *reinterpret_cast<const uint4*>(p);
-      hi = *reinterpret_cast<const uint4*>(p + 64);
-    } else {
-      const uint8_t* p = qx + static_cast<int64_t>(tok_rd) * K + koff + kq;
-      lo = *reinterpret_cast<const uint4*>(p);
-      hi = *reinterpret_cast<const uint4*>(p + 64);
-    }
-    v8i r = to_v8i(lo, hi);
+  // The remaining items of the first batch; their addresses depend on an
+  // asm statement after the staging barriers, so they cannot be hoisted
+  // above them (nor above the manual wait of the LDS copies).
+  if constexpr (NI > kEarly) {
+    uint32_t after2;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(after2) : : "memory");
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = tok_ok ? r[i] : 0;
-    return r;
+    for (int s = kEarly; s < NI; ++s) load_item(s, a, after2);
+  }
+
+  // B fragment of step st (zero for tokens >= M and for chunks past K).
+  auto load_b = [&](int st) -> v8i {
+    uint4 hv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int off = chunk_off(st, h, g, c, C);
+      const bool ok = tok_ok && off < K;
+      const int o = ok ? off : 0;
+      const int t = tok_ok ? tok : 0;
+      uint4 v;
+      if constexpr (STAGE == 0)
+        v = *reinterpret_cast<const uint4*>(qx + static_cast<int64_t>(t) * K + o);
+      else
+        v = *reinterpret_cast<const uint4*>(lds_x + t * lds_stride + o);
+      hv[h] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+    return to_v8i(hv[0], hv[1]);
   };
 
+  auto scale_of = [&](int t) { return STAGE == 2 ? s_scale[t] : sx[t]; };
+  const int outs = MP * M;   // outputs of one row group
+
+  // A row group is done with this wave's contribution: finish it here if it
+  // lies wholly inside [a, b), else leave the partial for the workgroup.
+  const int g_first = a / cs;
+  auto flush = [&](int gl, const v4f& acc) {
+    const bool inside = gl * cs >= a && (gl + 1) * cs <= b;
+    if (C == 16) {
+      // M = 1: the output is the sum of the diagonal, which lane l holds in
+      // register (l & 15) - 4 * (l >> 4) when that is in 0..3.
+      const int qd = (lane & 15) - 4 * (lane >> 4);
+      float d = qd == 0 ? acc[0] : qd == 1 ? acc[1] : qd == 2 ? acc[2]
+              : qd == 3 ? acc[3] : 0.0f;
+      d = wave_sum_to_63(d);
+      if (lane == 63) {
+        if (inside) {
+          const int n = g0 + gl;
+          y[n] = f32_to_bf16_bits(d * sw[n] * scale_of(0));
+        } else {
+          part1[wave][gl == g_first ? 0 : 1] = d;
+        }
+      }
+      return;
+    }
+    if (inside) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fin[wave][lane][q] = acc[q];
+      __builtin_amdgcn_wave_barrier();
+      for (int o = lane; o < outs; o += 64) {
+        const int rr = o % MP, t = o / MP;
+        const int n = (g0 + gl) * MP + rr;
+        const float v = class_sum(fin[wave], rr, t, C);
+        y[static_cast<int64_t>(t) * ldy + n] =
+            f32_to_bf16_bits(v * sw[n] * scale_of(t));
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      const int si = gl == g_first ? 0 : 1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[wave][si][lane][q] = acc[q];
+    }
+  };
+
+  // 4) The items: one MFMA each, row group by row group (the accumulator is
+  // flushed where a row group or this wave's range ends).  More than NI
+  // items per wave (a row group longer than the workgroup can hold) are
+  // loaded batch by batch.
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int base = 0; base < steps; base += kMaxSteps) {
-    v8i wf[kMaxSteps];
+  auto run_batch = [&](int base) {             // items [base, base + nb)
+    const int nb = min(NI, b - base);
+    int s0 = 0;
+    while (s0 < nb) {
+      const int gl = (base + s0) / cs;
+      const int s1 = min(nb, (gl + 1) * cs - base);   // end of the group here
+      const int st0 = base - gl * cs;                 // step of slot 0
 #pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s) wf[s] = to_v8i(wa[s][0], wa[s][1]);
-    // Next batch's loads go out before this batch's MFMAs.
-    const int nb = base + kMaxSteps;
-#pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s)
-      if (nb + s < steps) {
-        wa[s][0] = load16(wptr + (nb + s) * kStepBytes);
-        wa[s][1] = load16(wptr + (nb + s) * kStepBytes + 64);
+      for (int s = 0; s < NI; ++s)
+        if (s >= s0 && s < s1)
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              to_v8i(wa[s][0], wa[s][1]), load_b(st0 + s), acc,
+              0, 0, 0, 0, 0, 0);
+      if (base + s1 == (gl + 1) * cs || base + s1 == b) {
+        flush(gl, acc);
+        acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       }
+      s0 = s1;
+    }
+  };
+  // The first batch in straight-line code (its loads are the ones issued
+  // above), later batches in a loop.
+  if (a < b) run_batch(a);
+  for (int base = a + NI; base < b; base += NI) {
 #pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s)
-      if (base + s < steps) {
-        const v8i xb = load_b((s_beg + base + s) * kStepBytes);
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wf[s], xb, acc, 0, 0, 0, 0, 0, 0);
-      }
+    for (int s = 0; s < NI; ++s) load_item(s, base, 0u);
+    run_batch(base);
   }
 
-  // Add the waves' tiles in wave order.  16x16 accumulator layout: lane
-  // holds column (lane & 15) = token and rows 4*(lane>>4) + r = channel.
-#pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][lane][r] = acc[r];
-  __syncthreads();
-  if (wave != 0) return;
-  v4f sum = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sum[r] += red[w][lane][r];
-  if (!tok_ok) return;
-  const float xs = FUSED ? s_scale[tok] : sx[tok];
-  const int nb0 = n0 + 4 * (lane >> 4);
-  const float4 ws = *reinterpret_cast<const float4*>(sw + nb0);
-  uint2 out;
-  out.x = pack_bf16x2(sum[0] * ws.x * xs, sum[1] * ws.y * xs);
-  out.y = pack_bf16x2(sum[2] * ws.z * xs, sum[3] * ws.w * xs);
-  *reinterpret_cast<uint2*>(y + static_cast<int64_t>(tok) * ldy + nb0) = out;
+  // 5) Row groups shared by several waves: sum the partials in wave order.
+  lds_barrier();
+  for (int o = tid; o < gcount * outs; o += kThreads) {
+    const int gl = o / outs, rr = o % MP, t = (o % outs) / MP;
+    const int lo = gl * cs, hi = lo + cs;
+    // Waves whose (non-empty) ranges meet the group: w_lo .. w_hi.
+    int w_lo = kWaves, w_hi = -1;
+    for (int w = 0; w < kWaves; ++w) {
+      const int aw = (w * total) / kWaves, bw = ((w + 1) * total) / kWaves;
+      if (aw < bw && aw < hi && bw > lo) {
+        w_lo = min(w_lo, w);
+        w_hi = w;
+      }
+    }
+    if (w_hi > w_lo) {
+      float v = 0.0f;
+      for (int w = w_lo; w <= w_hi; ++w) {
+        const int aw = (w * total) / kWaves, bw = ((w + 1) * total) / kWaves;
+        if (aw < bw) {
+          const int si = gl == aw / cs ? 0 : 1;
+          v += C == 16 ? part1[w][si] : class_sum(part[w][si], rr, t, C);
+        }
+      }
+      const int n = (g0 + gl) * MP + rr;
+      y[static_cast<int64_t>(t) * ldy + n] = f32_to_bf16_bits(v * sw[n] * scale_of(t));
+    }
+  }
 }
 
 }  // namespace detail
 using namespace detail;
 
+// Fused (in-kernel) quantization pays for re-quantizing the activations in
+// every workgroup; measured on MI355X it beats a separate quantization
+// kernel up to about 16K activation elements.
 bool gemv_fused_fits(int64_t m, int64_t n, int64_t k) {
   (void)n;
-  return m * (k + kLdsRowPad) <= kGemvFusedLds;
+  return m * k <= kFusedElems &&
+         m * (k / 8) <= static_cast<int64_t>(kFusedRegs) * kThreads &&
+         m * (k + kLdsRowPad) <= kStageLds;
 }
 
-template <bool FUSED, int WAVES, int MAXSTEPS>
+template <int STAGE, int XR, int NI>
+hipError_t launch_ni(const uint16_t* x, int64_t ldx, const uint8_t* qx,
+                     const float* sx, const uint8_t* qw, const float* sw,
+                     int64_t m, int lg_mp, int64_t n, int64_t k, int gpw,
+                     uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const int64_t groups = n >> lg_mp;
+  const dim3 grid(static_cast<uint32_t>((groups + gpw - 1) / gpw));
+  const size_t lds = STAGE == 0 ? 0
+                   : static_cast<size_t>(m) *
+                         ((STAGE == 1 ? (k + 1023) / 1024 * 1024 : k) + kLdsRowPad);
+  gemv_fp8_kernel<STAGE, XR, NI><<<grid, dim3(kThreads), lds, stream>>>(
+      x, ldx, qx, sx, qw, sw, static_cast<int>(m), lg_mp, static_cast<int>(n),
+      static_cast<int>(k), gpw, y, ldy);
+  return hipGetLastError();
+}
+
+template <int STAGE, int XR>
 hipError_t launch_one(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                       const float* sx, const uint8_t* qw, const float* sw,
-                      int64_t m, int64_t n, int64_t k, uint16_t* y,
-                      int64_t ldy, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(n / 16));
-  const size_t lds = FUSED ? static_cast<size_t>(m) * (k + kLdsRowPad) : 0;
-  gemv_fp8_kernel<FUSED, WAVES, MAXSTEPS><<<grid, dim3(WAVES * 64), lds, stream>>>(
-      x, ldx, qx, sx, qw, sw, static_cast<int>(m), static_cast<int>(k), y, ldy);
-  return hipGetLastError();
+                      int64_t m, int lg_mp, int64_t n, int64_t k, int gpw,
+                      int ni, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  switch (ni) {
+    case 1: return launch_ni<STAGE, XR, 1>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+    case 2: return launch_ni<STAGE, XR, 2>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+    case 3: return launch_ni<STAGE, XR, 3>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+    case 4: return launch_ni<STAGE, XR, 4>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+    case 6: return launch_ni<STAGE, XR, 6>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+    default: return launch_ni<STAGE, XR, 8>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+  }
 }
 
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
@@ -219,17 +455,44 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                        int64_t m, int64_t n, int64_t k, uint16_t* y,
                        int64_t ldy, hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
-  // Many tiles: small workgroups, several resident per CU, each wave with a
-  // deep queue of loads.  Few tiles: one wide workgroup per tile so that the
-  // tile's K range is streamed by 16 waves at once.
-  int variant = n / 16 >= 512 ? 0 : 1;
-  if (const char* e = std::getenv("FP8W8A8_GEMV_VARIANT")) variant = std::atoi(e) & 1;
-  const bool fused = x != nullptr;
-  if (variant == 0)
-    return fused ? launch_one<true, 4, 8>(x, ldx, qx, sx, qw, sw, m, n, k, y, ldy, stream)
-                 : launch_one<false, 4, 8>(x, ldx, qx, sx, qw, sw, m, n, k, y, ldy, stream);
-  return fused ? launch_one<true, 16, 4>(x, ldx, qx, sx, qw, sw, m, n, k, y, ldy, stream)
-               : launch_one<false, 16, 4>(x, ldx, qx, sx, qw, sw, m, n, k, y, ldy, stream);
+  int lg_mp = 0;
+  while ((1 << lg_mp) < m) ++lg_mp;
+  // Row groups per workgroup.  Measured on MI355X: whole row groups per
+  // wave (none shared between waves) and about one workgroup per CU are
+  // best, as long as that leaves >= 64 workgroups and a wave's groups fit
+  // one batch of loads; otherwise about one workgroup per CU, with groups
+  // shared between waves.
+  const int64_t groups = n >> lg_mp;
+  const int64_t cs = (k + (2048 >> lg_mp) - 1) / (2048 >> lg_mp);
+  int64_t gpw;
+  if (cs <= kItems && groups >= 64 * kWaves) {
+    int64_t per_wave = (groups + 256 * kWaves - 1) / (256 * kWaves);
+    if (per_wave > kItems / cs) per_wave = kItems / cs;
+    gpw = kWaves * per_wave;
+  } else {
+    gpw = (groups + 255) / 256;
+    const int64_t cap = (kWaves * kItems) / cs;
+    if (gpw > cap) gpw = cap;
+    if (gpw < 1) gpw = 1;
+  }
+  // FP8W8A8_GEMV_GPW overrides (a tuning aid; every choice computes the
+  // same result up to float32 summation order).
+  if (const char* e = std::getenv("FP8W8A8_GEMV_GPW")) {
+    const int64_t v = std::atoll(e);
+    if (v >= 1 && v <= groups) gpw = v;
+  }
+  const int gp = static_cast<int>(gpw);
+  // Items per wave (the most any wave of a full workgroup gets).
+  const int64_t per_wave = (gpw * cs + kWaves - 1) / kWaves;
+  const int ni = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 3 ? 3
+               : per_wave <= 4 ? 4 : per_wave <= 6 ? 6 : kItems;
+  if (x != nullptr) {
+    if (!gemv_fused_fits(m, n, k)) return hipErrorInvalidValue;
+    return launch_one<2, kFusedRegs>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gp, ni, y, ldy, stream);
+  }
+  if (m * ((k + 1023) / 1024 * 1024 + kLdsRowPad) <= kStageLds)
+    return launch_one<1, 1>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gp, ni, y, ldy, stream);
+  return launch_one<0, 1>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gp, ni, y, ldy, stream);
 }
 
 }  // namespace fp8w8a8

@@ -61,6 +61,32 @@ def test_forced_path_cross_check(m, path, monkeypatch):
     check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"{path} m={m}")
 
 
+GEMV_CASES = [(1, 48, 384), (2, 16, 640), (3, 272, 4096), (4, 48, 2176),
+              (5, 1040, 1024), (8, 48, 256), (9, 64, 12288), (16, 272, 384),
+              (1, 1024, 12288), (16, 1024, 4096)]
+
+
+@pytest.mark.parametrize("gpw", ["1", "2", "3", "7"])
+@pytest.mark.parametrize("m,n,k", GEMV_CASES)
+def test_every_gemv_grouping(gpw, m, n, k, monkeypatch):
+    """Every row-group count per workgroup of the decode kernel (which moves
+    the row-group boundaries between its waves, and past 8 items per wave
+    switches to batched loads), on ragged token counts and K not a multiple
+    of the 2 KB class span, unfused and fused (bf16 in), against the
+    oracle."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", "gemv")
+    monkeypatch.setenv("FP8W8A8_GEMV_GPW", gpw)
+    qx, sx, qw, sw = _rand_operands(m, n, k, 31 * m + n + k)
+    y = _run_linear(qx, sx, qw, sw)
+    check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"gemv gpw {gpw} {m}x{n}x{k}")
+    rng = np.random.default_rng(m + k)
+    x = bf16_from_f64(rng.standard_normal((m, k)) * 3.0)
+    yf = fq.quant_linear(to_dev_bf16(x), to_dev_u8(qw), to_dev_f32(sw))
+    torch.cuda.synchronize()
+    y64, _, _ = oracle.quant_linear_ref(x, qw, sw)
+    check_close(host_bits(yf), y64, f"fused gemv gpw {gpw} {m}x{n}x{k}")
+
+
 def _quant_weights_gpu(w_bits):
     qw, sw = fq.quantize_weight_channelwise(to_dev_bf16(w_bits))
     return qw, sw
@@ -123,7 +149,7 @@ def test_c5_long_prefill_sampled_rows(linear):
 
 
 def test_workspace_reuse_across_shapes():
-    """Split-K counters must be back at zero after every call."""
+    """One workspace serves calls of different shapes in a row."""
     shapes = [(1, 1024, 4096), (300, 1040, 512), (4, 4096, 12288),
               (1, 1024, 4096), (16, 48, 384), (1, 1024, 4096)]
     for i, (m, n, k) in enumerate(shapes):
