@@ -9,10 +9,15 @@ TFLOP/s (2*M*N*K summed over the 7 Linears; quantization flops not counted).
 Also measured and printed on the same JSON line:
 * ``roofline``: the dominant kernel (the FP8 GEMM) timed alone with HIP events
   on its own stream, against the FP8 dense MFMA peak (5.0 PFLOP/s);
+  (the step itself is replayed from a HIP graph of its 7 fused calls;)
 * ``decode``: the decode step of one layer at M = 1 (7 fused calls replayed
   from a HIP graph, rotating over 4 copies of the layer's weights so that the
   weight bytes come from HBM, not from the 256 MB last-level cache), in GB/s
   of algorithmic bytes against 8 TB/s;
+* ``packed``: the same two measurements with the layer's Linears packed the
+  way the checkpoint's packed modules are (q|k|v as one 6144 x 4096 Linear,
+  gate|up as one 24576 x 4096 Linear), so that each distinct input is
+  quantized once and a layer is 4 calls instead of 7;
 * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the same
   workload on the host's cores.
 
@@ -36,6 +41,21 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 PREFILL_M = 4096
 DECODE_M = 1
 DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
+
+# HBM bytes of one prefill step's 7 GEMM dispatches, from rocprofv3
+# FETCH_SIZE (x2, calibrated) + WRITE_SIZE passes over this script (see
+# profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM source
+# with this SHA-1; reported as null once the source differs.
+GEMM_TRAFFIC = {"gemm_hip_sha1": "adf3b3cf2dee7ee529c7bc580a370a5687f88f02",
+                "bytes_per_step": 1493734 * 1024}
+
+
+def gemm_traffic():
+    import hashlib
+    path = os.path.join(ROOT, "fp8_w8a8_dynamic_amd", "csrc", "gemm.hip")
+    with open(path, "rb") as f:
+        sha = hashlib.sha1(f.read()).hexdigest()
+    return GEMM_TRAFFIC["bytes_per_step"] if sha == GEMM_TRAFFIC["gemm_hip_sha1"] else None
 
 
 def log(*a):
@@ -61,7 +81,11 @@ def time_events(torch, fn, reps):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def setup_layer(torch, fq, m, cfg):
+def setup_layer(torch, fq, m, cfg, packed=False):
+    """The 7 Linears of one layer (seeded weights quantized on the GPU, one
+    seeded input per Linear); packed: q|k|v and gate|up concatenated along
+    the output channels (rows of W and of the channel scales), taking the
+    input of q and of gate respectively."""
     from workloads import LAYER_SHAPES
     from workloads.generators import c3_x, outlier_act_bf16, rng_for, weight_bf16
     layer = []
@@ -73,22 +97,47 @@ def setup_layer(torch, fq, m, cfg):
         else:
             x = outlier_act_bf16(rng_for(2, m, j, 0), (m, k))
         xd = to_dev(x, torch)
-        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        layer.append(dict(name=name, n=n, k=k, x=xd, qw=qw, sw=sw, y=y))
+        layer.append(dict(name=name, n=n, k=k, x=xd, qw=qw, sw=sw))
+    if packed:
+        def pack(idx, name):
+            parts = [layer[i] for i in idx]
+            return dict(name=name, n=sum(L["n"] for L in parts), k=parts[0]["k"],
+                        x=parts[0]["x"],
+                        qw=torch.cat([L["qw"].view(torch.uint8) for L in parts]),
+                        sw=torch.cat([L["sw"] for L in parts]))
+        layer = [pack([0, 1, 2], "qkv_proj"), layer[3],
+                 pack([4, 5], "gate_up_proj"), layer[6]]
+    for L in layer:
+        L["y"] = torch.empty((m, L["n"]), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
     return layer
 
 
-def bench_prefill(torch, fq, steps, warmup):
-    layer = setup_layer(torch, fq, PREFILL_M, 3)
+def bench_prefill(torch, fq, steps, warmup, packed=False):
+    layer = setup_layer(torch, fq, PREFILL_M, 3, packed)
     flops = sum(2 * PREFILL_M * L["n"] * L["k"] for L in layer)
     wsb = max(fq.workspace_bytes(PREFILL_M, L["n"], L["k"], True) for L in layer)
     ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
 
-    def step():
+    def calls():
         for L in layer:
             fq.quant_linear(L["x"], L["qw"], L["sw"], out=L["y"], workspace=ws)
 
+    # The step's calls are captured once in a HIP graph and replayed (as a
+    # serving loop would), so host-side launch cost stays out of the timing.
+    for _ in range(max(1, warmup)):
+        calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        calls()                            # first use of this stream, uncaptured
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            calls()
+    torch.cuda.synchronize()
+    step = g.replay
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -96,15 +145,33 @@ def bench_prefill(torch, fq, steps, warmup):
     step_time = time_events(torch, step, steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if packed:
+        del layer
+        torch.cuda.empty_cache()
+        return dict(step_time=step_time, wall=wall, flops=flops)
 
-    # Dominant kernel alone: the GEMM on pre-quantized activations.
+    # Dominant kernel: the GEMM on pre-quantized activations, timed per
+    # launch with HIP events on the launching stream while the 7 GEMMs of the
+    # layer run in sequence (as in the step: operands rotate through 7
+    # Linears, 300+ MB, more than the last-level cache holds).
     for L in layer:
         L["qx"], L["sx"] = fq.quantize_act_per_token(L["x"])
-    gemm_t, quant_t = [], []
+    s = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layer] for _ in range(steps)]
     for L in layer:
-        f = lambda L=L: fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
-        f()
-        gemm_t.append(time_events(torch, f, max(10, steps)))
+        fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
+    torch.cuda.synchronize()
+    for it in range(steps):
+        for j, L in enumerate(layer):
+            ev[it][j][0].record(s)
+            fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
+            ev[it][j][1].record(s)
+    torch.cuda.synchronize()
+    gemm_t = [sum(ev[it][j][0].elapsed_time(ev[it][j][1]) for it in range(steps))
+              * 1e-3 / steps for j in range(len(layer))]
+    quant_t = []
+    for L in layer:
         q = lambda L=L: fq.quantize_act_per_token(L["x"])
         q()
         quant_t.append(time_events(torch, q, max(10, steps)))
@@ -120,11 +187,12 @@ def bench_prefill(torch, fq, steps, warmup):
                 gemm_tflops=gemm_tflops, gemm_time=sum(gemm_t), per_linear=per)
 
 
-def bench_decode(torch, fq, reps):
-    base = setup_layer(torch, fq, DECODE_M, 2)
+def bench_decode(torch, fq, reps, packed=False):
+    base = setup_layer(torch, fq, DECODE_M, 2, packed)
     copies = [base]
     for _ in range(DECODE_COPIES - 1):
-        copies.append([dict(L, qw=L["qw"].clone(), sw=L["sw"].clone()) for L in base])
+        copies.append([dict(L, qw=L["qw"].clone(), sw=L["sw"].clone(),
+                            y=torch.empty_like(L["y"])) for L in base])
     nbytes = sum(L["n"] * L["k"] + 4 * L["n"] + 2 * DECODE_M * L["k"]
                  + 2 * DECODE_M * L["n"] for L in base)
     wsb = max(fq.workspace_bytes(DECODE_M, L["n"], L["k"], True) for L in base)
@@ -183,7 +251,7 @@ def cpu_baseline(target_s=16.0):
         return flops, secs
 
     # Grow the sample until the timed oracle work reaches about target_s.
-    sizes = [(64, 16), (256, 8), (512, 4), (1024, 4), (2048, 4), (4096, 4)]
+    sizes = [(64, 16), (256, 8), (512, 4), (1024, 4), (2048, 4), (4096, 4), (4096, 2)]
     for m_s, n_frac in sizes:
         flops, secs = run(m_s, n_frac)
         if secs >= target_s / 2:
@@ -236,6 +304,20 @@ def main():
         log("decode ...")
         dec = bench_decode(torch, fq, max(20, args.steps))
         log(f"decode layer {dec['layer_us']:.2f} us  {dec['gbs']:.0f} GB/s")
+    log("packed layer ...")
+    pre_p = bench_prefill(torch, fq, args.steps, args.warmup, packed=True)
+    packed = {"linears": "qkv_proj (6144x4096), o_proj, gate_up_proj (24576x4096), "
+                         "down_proj: 4 calls, one quantization per distinct input",
+              "prefill": {"value": round(pre_p["flops"] / pre_p["step_time"] / 1e12, 2),
+                          "unit": "TFLOP/s",
+                          "ms_per_step": round(pre_p["step_time"] * 1e3, 4)}}
+    log(f"packed prefill {packed['prefill']}")
+    if not args.no_decode:
+        dec_p = bench_decode(torch, fq, max(20, args.steps), packed=True)
+        packed["decode"] = {"value": round(dec_p["gbs"], 1), "unit": "GB/s",
+                            "us_per_layer": round(dec_p["layer_us"], 3),
+                            "frac_of_hbm": round(dec_p["gbs"] / HBM_PEAK_GBS, 4)}
+        log(f"packed decode {packed['decode']}")
     cpu = None
     if not args.no_cpu:
         log("cpu oracle ...")
@@ -264,7 +346,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tflops"], 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre["gemm_tflops"] / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_fp8_kernel",
+                     "traffic": gemm_traffic(),
+                     "traffic_scope": "HBM bytes of one step's 7 GEMM dispatches "
+                                      "(rocprofv3 FETCH_SIZE x2 + WRITE_SIZE); "
+                                      "algorithmic 663 MB",
+                     "kernel": "gemm_fp8_kernel",
                      "per_linear": pre["per_linear"]},
     }
     if dec is not None:
@@ -274,6 +360,7 @@ def main():
                          "us_per_layer": round(dec["layer_us"], 3),
                          "frac_of_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                          "bytes_per_layer": dec["bytes"]}
+    out["packed"] = packed
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

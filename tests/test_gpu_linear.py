@@ -210,3 +210,28 @@ def test_every_gemm_config_matches_oracle_and_each_other(m, n, k, monkeypatch):
         outs.append(y)
     for cfg, y in zip(GEMM_CONFIGS[1:], outs[1:]):
         assert np.array_equal(y, outs[0]), f"config {cfg} differs from config 0"
+
+
+@pytest.mark.parametrize("m", [1, 4, 300])
+def test_packed_qkv_equals_separate_calls(m):
+    """Packed modules (q|k|v as one Linear with the rows of W and of the
+    channel scales concatenated) quantize the shared input once; every
+    output channel is the same dot product as in the separate calls, so the
+    packed output must match the oracle and, where each output's summation
+    order does not depend on N (M = 1 and the tiled GEMM), the separate calls
+    bit for bit."""
+    rng = np.random.default_rng(7000 + m)
+    k = 512
+    ws = [bf16_from_f64(rng.standard_normal((n, k)) * 0.02) for n in (256, 64, 64)]
+    x = bf16_from_f64(rng.standard_normal((m, k)))
+    parts = [_quant_weights_gpu(w) for w in ws]
+    qw = torch.cat([p[0].view(torch.uint8) for p in parts])
+    sw = torch.cat([p[1] for p in parts])
+    xd = to_dev_bf16(x)
+    yp = host_bits(fq.quant_linear(xd, qw, sw))
+    ys = [host_bits(fq.quant_linear(xd, p[0], p[1])) for p in parts]
+    torch.cuda.synchronize()
+    y64, _, _ = oracle.quant_linear_ref(x, host_bits(qw), host_bits(sw))
+    check_close(yp, y64, f"packed qkv m={m}")
+    if m != 4:
+        assert np.array_equal(yp, np.concatenate(ys, axis=1))
