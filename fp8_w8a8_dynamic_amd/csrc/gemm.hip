@@ -15,10 +15,11 @@
 //     (BM/WGM) x (BN/WGN) sub-tile kept in registers;
 //   * K advances 128 bytes per stage.  Stages are copied HBM/L2 -> LDS with
 //     buffer_load_dwordx4 ... lds (no trip through VGPRs) into two LDS
-//     buffers.  At the start of a stage every wave reads all its fragments of
-//     the stage into registers; one barrier later the buffer is free and is
-//     refilled with stage k+2 while the stage's MFMAs run, so two stages of
-//     copies are always in flight, with the copies spread between the MFMAs;
+//     buffers.  Every stage's fragments are read into registers early (the
+//     second half of a stage's reads overlaps the previous stage's MFMAs);
+//     once all waves hold them a barrier frees the buffer, which is refilled
+//     with stage k+2 while the MFMAs run, so two stages of copies are always
+//     in flight, with the copies spread between the MFMAs;
 //   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
 //     ((row >> 1) & 7), so the 16 lanes that the LDS serves together read 16
 //     distinct bank groups; the swizzle is applied on the global side (each
@@ -45,7 +46,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kGroupM = 4;
 constexpr int kBK = 128;     // K bytes per stage
-constexpr int kSteps = 2;    // 64-byte MFMA K-steps per stage
 
 // Tile configuration: BM x BN output tile per workgroup of WGM x WGN waves.
 template <int BM, int BN, int WGM, int WGN>
@@ -182,53 +182,75 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
 #pragma unroll
     for (int c = 0; c < S::COPIES; ++c) copy(c, 1, kBK);
   }
-  constexpr int kMfma = S::TM * S::TN * kSteps;
-  // MFMAs issued before the release barrier (time for the fragment reads to
-  // land), and the copy spacing over the remaining MFMAs.
-  constexpr int kRelease = (S::TM * S::TN) / 2;
-  constexpr int kSlots = kMfma - kRelease;
-  constexpr int kEvery = kSlots / S::COPIES > 0 ? kSlots / S::COPIES : 1;
-  constexpr int kInLoop = kSlots / kEvery < S::COPIES ? kSlots / kEvery : S::COPIES;
-  for (int kt = 0; kt < KT; ++kt) {
-    // This wave's copies of stage kt have landed once only stage kt+1's are
-    // outstanding; the barrier extends that to every wave's copies.
-    if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::COPIES));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    const int buf = kt & 1;
-    const uint8_t* as = smem + buf * S::STAGE;
+  // Main loop.  Per stage, each wave runs T MFMAs of step 0 then T of step
+  // 1 (T = TM * TN).  A wave drains its LDS reads at roughly 1 KB per 40
+  // clocks, so the reads are spread so that no MFMA waits on them:
+  //   * the stage's step-1 fragments are read at its start, its step-0
+  //     fragments were read during the previous stage;
+  //   * after kRel MFMAs (the step-1 reads have landed) a barrier releases the
+  //     buffer, and the copies of stage kt+2 into it go out one or two per
+  //     MFMA;
+  //   * at MFMA kNext (step 0 done, its registers free) the wave waits for
+  //     stage kt+1's copies (all but the kBefore newest outstanding), a
+  //     barrier makes every wave's copies visible, and the next stage's
+  //     step-0 fragments are read under the remaining step-1 MFMAs.
+  // kRel and kNext were tuned on MI355X (3/4 and 5/4 of T).
+  constexpr int T = S::TM * S::TN;
+  constexpr int kMfma = 2 * T;
+  constexpr int kRel = T * 12 / 16;
+  constexpr int kNext = T * 20 / 16;
+  static_assert(kNext >= T && kNext > kRel && kNext < kMfma, "pipeline points");
+  constexpr int kSlots = kMfma - kRel;
+  constexpr int kPer = (S::COPIES + kSlots - 1) / kSlots;   // copies per MFMA
+  constexpr int kBefore =
+      (kNext - kRel) * kPer < S::COPIES ? (kNext - kRel) * kPer : S::COPIES;
+  const int p0 = (2 * fhalf) ^ fswz, p1 = (4 + 2 * fhalf) ^ fswz;
+  v8i af0[S::TM], bf0[S::TN], af1[S::TM], bf1[S::TN];
+  // Fragments of one step, in the order the MFMAs consume them.
+  auto read_step = [&](v8i* af, v8i* bf, const uint8_t* as, int p) {
     const uint8_t* bs = as + S::A_STAGE;
-    v8i af[kSteps][S::TM], bf[kSteps][S::TN];
+    af[0] = lds_frag(as + a_row0 * kBK, p);
 #pragma unroll
-    for (int step = 0; step < kSteps; ++step) {
-      const int p = (4 * step + 2 * fhalf) ^ fswz;
+    for (int u = 0; u < S::TN; ++u) bf[u] = lds_frag(bs + (b_row0 + 32 * u) * kBK, p);
 #pragma unroll
-      for (int t = 0; t < S::TM; ++t)
-        af[step][t] = lds_frag(as + (a_row0 + 32 * t) * kBK, p);
-#pragma unroll
-      for (int u = 0; u < S::TN; ++u)
-        bf[step][u] = lds_frag(bs + (b_row0 + 32 * u) * kBK, p);
-    }
+    for (int t = 1; t < S::TM; ++t) af[t] = lds_frag(as + (a_row0 + 32 * t) * kBK, p);
+  };
+  if (KT > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::COPIES));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  read_step(af0, bf0, smem, p0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    read_step(af1, bf1, smem + buf * S::STAGE, p1);
     const bool refill = kt + 2 < KT;
+    const bool more = kt + 1 < KT;
     const uint32_t next_k = static_cast<uint32_t>((kt + 2) * kBK);
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
-      // Past this barrier every wave holds its fragments of the stage in
-      // registers, so the buffer can take stage kt+2.
-      if (i == kRelease && refill) __syncthreads();
-      const int step = i / (S::TM * S::TN);
-      const int t = (i / S::TN) % S::TM, u = i % S::TN;
-      acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          bf[step][u], af[step][t], acc[t][u], 0, 0, 0, 0, 0, 0);
-      if (i >= kRelease && (i - kRelease) % kEvery == kEvery - 1 && refill) {
-        const int c = (i - kRelease) / kEvery;
-        if (c < S::COPIES) copy(c, buf, next_k);
+      // Every wave holds this stage's fragments: the buffer takes stage kt+2.
+      if (i == kRel && refill) __syncthreads();
+      if (i == kNext && more) {
+        // Stage kt+1 has landed once only stage kt+2's first kBefore copies
+        // are outstanding.
+        if (refill) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBefore));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        read_step(af0, bf0, smem + (buf ^ 1) * S::STAGE, p0);
       }
-    }
-    // Copies that did not fit between the MFMAs.
-    if (refill) {
+      const int t = (i / S::TN) % S::TM, u = i % S::TN;
+      if (i < T)
+        acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bf0[u], af0[t], acc[t][u], 0, 0, 0, 0, 0, 0);
+      else
+        acc[t][u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bf1[u], af1[t], acc[t][u], 0, 0, 0, 0, 0, 0);
+      if (refill && i >= kRel) {
 #pragma unroll
-      for (int c = kInLoop; c < S::COPIES; ++c) copy(c, buf, next_k);
+        for (int j = 0; j < kPer; ++j) {
+          const int c = (i - kRel) * kPer + j;
+          if (c < S::COPIES) copy(c, buf, next_k);
+        }
+      }
     }
   }
 
@@ -310,12 +332,10 @@ hipError_t launch_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
   if (const char* e = std::getenv("FP8W8A8_GEMM_CONFIG")) cfg = std::atoi(e);
   if (cfg < 0) {
     // Measured on MI355X for the 4096-token layer shapes: 256x256 tiles of
-    // eight waves, four waves where K is long; narrow outputs (few tiles)
-    // take 128x128 tiles, two workgroups per CU.
+    // eight waves (4x2); narrow outputs (few tiles) take 128x128 tiles, two
+    // workgroups per CU.
     const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-    if (big_tiles < 128) cfg = 2;
-    else if (k > 8192) cfg = 0;
-    else cfg = 1;
+    cfg = big_tiles < 128 ? 2 : 3;
   }
   switch (cfg) {
     case 0: return launch_cfg<256, 256, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
