@@ -47,8 +47,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kGroupM = 4;
 constexpr int kBK = 128;     // K bytes per stage
 
-// Tile configuration: BM x BN output tile per workgroup of WGM x WGN waves.
-template <int BM, int BN, int WGM, int WGN>
+// Tile configuration: BM x BN output tile per workgroup of WGM x WGN waves,
+// NB stage buffers in LDS (stages in flight).
+template <int BM, int BN, int WGM, int WGN, int NB>
 struct GemmShape {
   static constexpr int WAVES = WGM * WGN;
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
@@ -57,7 +58,8 @@ struct GemmShape {
   static constexpr int RPI = 1024 / kBK;            // rows per 1 KB copy
   static constexpr int A_STAGE = BM * kBK, B_STAGE = BN * kBK;
   static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NB * STAGE;
+  static_assert(NB == 2 || NB == 4, "two or four stage buffers");
   static constexpr int A_LOADS = A_STAGE / (1024 * WAVES);  // 1 KB copies
   static constexpr int B_LOADS = B_STAGE / (1024 * WAVES);  // per wave
   static constexpr int COPIES = A_LOADS + B_LOADS;          // per stage
@@ -104,13 +106,13 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int p0) {
   return r;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB>
+template <int BM, int BN, int WGM, int WGN, int NB, int MINB>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw, int M,
     int N, int K, uint16_t* __restrict__ y, int64_t ldy, int tiles_m,
     int tiles_n) {
-  using S = GemmShape<BM, BN, WGM, WGN>;
+  using S = GemmShape<BM, BN, WGM, WGN, NB>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::SMEM];
 
   const int tid = threadIdx.x;
@@ -177,11 +179,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
 
   const int KT = K / kBK;
 #pragma unroll
-  for (int c = 0; c < S::COPIES; ++c) copy(c, 0, 0);
-  if (KT > 1) {
+  for (int st = 0; st < NB; ++st)
+    if (st < KT) {
 #pragma unroll
-    for (int c = 0; c < S::COPIES; ++c) copy(c, 1, kBK);
-  }
+      for (int c = 0; c < S::COPIES; ++c) copy(c, st, static_cast<uint32_t>(st * kBK));
+    }
   // Main loop.  Per stage, each wave runs T MFMAs of step 0 then T of step
   // 1 (T = TM * TN).  A wave drains its LDS reads at roughly 1 KB per 40
   // clocks, so the reads are spread so that no MFMA waits on them:
@@ -215,27 +217,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
 #pragma unroll
     for (int t = 1; t < S::TM; ++t) af[t] = lds_frag(as + (a_row0 + 32 * t) * kBK, p);
   };
-  if (KT > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::COPIES));
+  // (Waits outside the steady state fall back to "nothing outstanding".)
+  if (KT >= NB) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 1) * S::COPIES));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   read_step(af0, bf0, smem, p0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
+    const int buf = kt & (NB - 1);
     read_step(af1, bf1, smem + buf * S::STAGE, p1);
-    const bool refill = kt + 2 < KT;
+    const bool refill = kt + NB < KT;
     const bool more = kt + 1 < KT;
-    const uint32_t next_k = static_cast<uint32_t>((kt + 2) * kBK);
+    const uint32_t next_k = static_cast<uint32_t>((kt + NB) * kBK);
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
-      // Every wave holds this stage's fragments: the buffer takes stage kt+2.
+      // Every wave holds this stage's fragments: the buffer takes stage
+      // kt+NB.
       if (i == kRel && refill) __syncthreads();
       if (i == kNext && more) {
-        // Stage kt+1 has landed once only stage kt+2's first kBefore copies
-        // are outstanding.
-        if (refill) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBefore));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // Stage kt+1 has landed once only stages kt+2 .. kt+NB-1 and the
+        // first kBefore copies of stage kt+NB are outstanding.
+        if (refill)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((NB - 2) * S::COPIES + kBefore));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
-        read_step(af0, bf0, smem + (buf ^ 1) * S::STAGE, p0);
+        read_step(af0, bf0, smem + ((kt + 1) & (NB - 1)) * S::STAGE, p0);
       }
       const int t = (i / S::TN) % S::TM, u = i % S::TN;
       if (i < T)
@@ -306,13 +312,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB>
+template <int BM, int BN, int WGM, int WGN, int NB, int MINB>
 hipError_t launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
                       const float* sw, int64_t m, int64_t n, int64_t k,
                       uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
-  gemm_fp8_kernel<BM, BN, WGM, WGN, MINB>
+  gemm_fp8_kernel<BM, BN, WGM, WGN, NB, MINB>
       <<<dim3(static_cast<uint32_t>(tiles_m * tiles_n)), dim3(64 * WGM * WGN),
          0, stream>>>(qx, sx, qw, sw, static_cast<int>(m), static_cast<int>(n),
                       static_cast<int>(k), y, ldy, tiles_m, tiles_n);
@@ -331,17 +337,20 @@ hipError_t launch_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
   int cfg = -1;
   if (const char* e = std::getenv("FP8W8A8_GEMM_CONFIG")) cfg = std::atoi(e);
   if (cfg < 0) {
-    // Measured on MI355X for the 4096-token layer shapes: 256x256 tiles of
-    // eight waves (4x2); narrow outputs (few tiles) take 128x128 tiles, two
-    // workgroups per CU.
+    // Measured on MI355X for the 4096-token layer shapes with operands
+    // arriving from HBM: 256x256 tiles of eight waves (4x2); narrow outputs
+    // (few tiles, one per CU) take 128x128 tiles with four stages in flight,
+    // whose pipeline is otherwise bound by the copies' latency.
     const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-    cfg = big_tiles < 128 ? 2 : 3;
+    cfg = big_tiles < 128 ? 4 : 3;
   }
   switch (cfg) {
-    case 0: return launch_cfg<256, 256, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 1: return launch_cfg<256, 256, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 2: return launch_cfg<128, 128, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    default: return launch_cfg<256, 256, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 0: return launch_cfg<256, 256, 2, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 1: return launch_cfg<256, 256, 2, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 2: return launch_cfg<128, 128, 2, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 3: return launch_cfg<256, 256, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    case 4: return launch_cfg<128, 128, 2, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+    default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
   }
 }
 
