@@ -215,7 +215,7 @@ def bench_decode(torch, fq, reps, packed=False):
             for c in copies:
                 layer_pass(c)
     torch.cuda.synchronize()
-    for _ in range(3):
+    for _ in range(max(3, reps // 2)):
         g.replay()
     torch.cuda.synchronize()
     t = time_events(torch, g.replay, reps) / DECODE_COPIES
@@ -266,8 +266,11 @@ def cpu_baseline(target_s=16.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU's clocks ramp for several milliseconds after an idle period:
+    # the warm-up is long enough (tens of ms of work) that the timed steps
+    # see the steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

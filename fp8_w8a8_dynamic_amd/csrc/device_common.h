@@ -51,6 +51,41 @@ __device__ __forceinline__ float quotient(float v, float scale) {
   return v / scale;
 }
 
+// One row's divisor.  Every element of a row is divided by the same scale,
+// so the reciprocal part of the IEEE float32 division can be done once per
+// row.  gfx950's correctly rounded division is: r = rcp(s) refined by one
+// Newton step, q0 = v*r, then two residual corrections q += fma(-s, q, v)*r,
+// with range scaling of v and s (v_div_scale / v_div_fmas) and a special
+// case pass (v_div_fixup) around it.  For 2^-60 <= s <= 2^60 and any element
+// with |v / s| >= 2^-11 the scaling is inactive (s and 1/s normal, quotient
+// normal, v above 2^-71) and the fixup returns its input with the sign of v,
+// so the unscaled sequence below yields the identical float32 quotient;
+// smaller quotients encode to a signed zero either way (the E4M3 midpoint
+// nearest zero is 2^-10).  Other scales (zero, subnormal or extreme) take the
+// plain division.
+struct RowDivisor {
+  float s, r;
+  bool fast;
+};
+
+__device__ __forceinline__ RowDivisor make_divisor(float s) {
+  RowDivisor d;
+  d.s = s;
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  d.r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+  d.fast = s >= 0x1p-60f && s <= 0x1p60f;
+  return d;
+}
+
+__device__ __forceinline__ float quotient_fast(float v, const RowDivisor& d) {
+  const float q0 = v * d.r;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-d.s, q0, v), d.r, q0);
+  const float q = __builtin_fmaf(__builtin_fmaf(-d.s, q1, v), d.r, q1);
+  // Sign of v (so that -0 stays -0), magnitude of q.
+  return __uint_as_float((__float_as_uint(q) & 0x7fffffffu) |
+                         (__float_as_uint(v) & 0x80000000u));
+}
+
 // Four float32 quotients -> four E4M3 codes packed little-endian in a dword
 // (code of `a` in the lowest byte).  The clamp to +-448 makes the hardware
 // conversion's round-to-nearest-even saturate instead of overflowing.
@@ -65,9 +100,17 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c,
   return static_cast<uint32_t>(w);
 }
 
-// Quantize 8 bf16 (one 16-byte vector) with a row scale -> 8 codes.
-__device__ __forceinline__ uint2 quantize8(uint4 v, float scale) {
+// Quantize 8 bf16 (one 16-byte vector) with a row's divisor -> 8 codes.
+__device__ __forceinline__ uint2 quantize8(uint4 v, const RowDivisor& d) {
   uint2 out;
+  if (d.fast) {
+    out.x = encode4(quotient_fast(bf16_lo(v.x), d), quotient_fast(bf16_hi(v.x), d),
+                    quotient_fast(bf16_lo(v.y), d), quotient_fast(bf16_hi(v.y), d));
+    out.y = encode4(quotient_fast(bf16_lo(v.z), d), quotient_fast(bf16_hi(v.z), d),
+                    quotient_fast(bf16_lo(v.w), d), quotient_fast(bf16_hi(v.w), d));
+    return out;
+  }
+  const float scale = d.s;
   if (scale == 0.0f) {
     // amax == 0: every element is +-0; the codes are the sign bits.
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
       if (e < M * kv8) {
         const int m = e / kv8, v = e - m * kv8;
         *reinterpret_cast<uint2*>(lds_x + m * lds_stride + v * 8) =
-            quantize8(xv[i], scale_row(m));
+            quantize8(xv[i], make_divisor(scale_row(m)));
       }
     }
     lds_barrier();

@@ -6,7 +6,8 @@
 // loads, into registers; the magnitude maximum is reduced on the bf16 bit
 // patterns (integer order equals value order for non-negative floats) and
 // then across the wave; the scale amax/448 is one IEEE division; each
-// element is divided by the scale (IEEE), clamped to +-448 and converted
+// element is divided by the scale (the IEEE quotient, with the reciprocal
+// part hoisted out of the row: make_divisor), clamped to +-448 and converted
 // with round-to-nearest-even by v_cvt_pk_fp8_f32; codes leave as 8-byte
 // stores that are contiguous across the wave.  HBM traffic is the algorithmic
 // 2 bytes in + 1 byte out per element + 4 bytes of scale per row.
@@ -45,11 +46,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
   const uint32_t mrow = wave_max_u32(max(m & 0xffffu, m >> 16));
   const float s = row_scale(__uint_as_float(mrow << 16));
+  const RowDivisor d = make_divisor(s);
   uint2* dst = reinterpret_cast<uint2*>(q + row * static_cast<int64_t>(k));
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int idx = i * 64 + lane;
-    if (idx < nvec) dst[idx] = quantize8(v[i], s);
+    if (idx < nvec) dst[idx] = quantize8(v[i], d);
   }
   if (lane == 0) scale[row] = s;
 }
@@ -75,8 +77,9 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(
   }
   const uint32_t mrow = wave_max_u32(max(m & 0xffffu, m >> 16));
   const float s = row_scale(__uint_as_float(mrow << 16));
+  const RowDivisor d = make_divisor(s);
   uint2* dst = reinterpret_cast<uint2*>(q + row * k);
-  for (int64_t idx = lane; idx < nvec; idx += 64) dst[idx] = quantize8(src[idx], s);
+  for (int64_t idx = lane; idx < nvec; idx += 64) dst[idx] = quantize8(src[idx], d);
   if (lane == 0) scale[row] = s;
 }
 

@@ -50,7 +50,12 @@ def test_every_bf16_value_under_many_scales():
     rng = np.random.default_rng(17)
     amaxes = [448.0, 1.0, 896.0, 3.0, 1e-3, 2.0 ** -130, 7.0 * 2.0 ** -133,
               1e30, 0.1, 3.3e38]
-    amaxes += list(2.0 ** rng.uniform(-120, 120, 22))
+    # Scales at the edges of the kernels' hoisted-reciprocal range
+    # [2^-60, 2^60] and one bf16 step either side.
+    for e in (-60, 60):
+        for f in (1.0 - 2.0 ** -7, 1.0, 1.0 + 2.0 ** -6):
+            amaxes.append(448.0 * 2.0 ** e * f)
+    amaxes += list(2.0 ** rng.uniform(-120, 120, 40))
     amax_bits = bf16_from_f64(np.array(amaxes))
     k = ((allb.size + 1 + 7) // 8) * 8
     rows = np.zeros((len(amaxes), k), np.uint16)
