@@ -46,8 +46,8 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # FETCH_SIZE (x2, calibrated) + WRITE_SIZE passes over this script (see
 # profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM source
 # with this SHA-1; reported as null once the source differs.
-GEMM_TRAFFIC = {"gemm_hip_sha1": "adf3b3cf2dee7ee529c7bc580a370a5687f88f02",
-                "bytes_per_step": 1493734 * 1024}
+GEMM_TRAFFIC = {"gemm_hip_sha1": "25b56a643e4b64b1276acba846b3e134c3f32443",
+                "bytes_per_step": 1493002 * 1024}
 
 
 def gemm_traffic():
