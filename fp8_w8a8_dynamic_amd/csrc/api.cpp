@@ -113,20 +113,30 @@ Path choose_path(int64_t m) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace: only calls that quantize in a separate kernel before the
-// linear kernel need one; it holds the quantized activations [m, k] and
-// their scales [m] (no state survives a call).
+// Workspace (no state survives a call): a fused call that quantizes in a
+// separate kernel before the linear kernel keeps the quantized activations
+// [m, k] and their scales [m] there; a GEMM whose plan splits K keeps its
+// float32 partial sums [splits, m, n] there.
 struct Layout {
-  size_t qx = 0, sx = 0, total = 0;
+  size_t qx = 0, sx = 0, part = 0, total = 0;
 };
 
-Layout layout_for(int64_t m, int64_t n, int64_t k, bool fused, Path path) {
+Layout layout_for(int64_t m, int64_t n, int64_t k, bool fused, Path path,
+                  const fp8w8a8::GemmPlan& plan) {
   Layout L;
-  if (m == 0 || n == 0 || !fused) return L;
-  if (path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k)) return L;
-  L.qx = 0;
-  L.sx = round_up(static_cast<size_t>(m) * k, 256);
-  L.total = L.sx + round_up(static_cast<size_t>(m) * 4, 256);
+  if (m == 0 || n == 0) return L;
+  if (fused && !(path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k))) {
+    L.qx = 0;
+    L.sx = round_up(static_cast<size_t>(m) * k, 256);
+    L.total = L.sx + round_up(static_cast<size_t>(m) * 4, 256);
+  }
+  if (path == Path::kGemm) {
+    const size_t pb = fp8w8a8::gemm_partial_bytes(plan, m, n);
+    if (pb > 0) {
+      L.part = L.total;
+      L.total += round_up(pb, 256);
+    }
+  }
   return L;
 }
 
@@ -176,7 +186,8 @@ int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
 
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
-  return layout_for(m, n, k, fused != 0, choose_path(m)).total;
+  return layout_for(m, n, k, fused != 0, choose_path(m),
+                    fp8w8a8::plan_gemm(m, n, k)).total;
 }
 
 int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
@@ -195,7 +206,9 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
       overlap(ry, span(qw, n, k, k, 1)) || overlap(ry, span(w_scale, n, 1, 1, 4)))
     return FP8W8A8_ERR_ALIAS;
   const Path path = choose_path(m);
-  const size_t need = layout_for(m, n, k, false, path).total;
+  const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
+  const Layout L = layout_for(m, n, k, false, path, plan);
+  const size_t need = L.total;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
     const Range rw{reinterpret_cast<uintptr_t>(workspace),
@@ -214,7 +227,10 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
     e = fp8w8a8::launch_gemv(nullptr, 0, qx, x_scale, qw, w_scale, m, n, k, y,
                              ldy, s);
   else
-    e = fp8w8a8::launch_gemm(qx, x_scale, qw, w_scale, m, n, k, y, ldy, s);
+    e = fp8w8a8::launch_gemm(plan, qx, x_scale, qw, w_scale, m, n, k, y, ldy,
+                             reinterpret_cast<float*>(
+                                 static_cast<uint8_t*>(workspace) + L.part),
+                             s);
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
@@ -235,7 +251,8 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
       overlap(ry, span(w_scale, n, 1, 1, 4)))
     return FP8W8A8_ERR_ALIAS;
   const Path path = choose_path(m);
-  const Layout L = layout_for(m, n, k, true, path);
+  const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
+  const Layout L = layout_for(m, n, k, true, path, plan);
   const size_t need = L.total;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
@@ -263,7 +280,8 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
         e = fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y,
                                  ldy, s);
       else
-        e = fp8w8a8::launch_gemm(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
+        e = fp8w8a8::launch_gemm(plan, qx, sx, qw, w_scale, m, n, k, y, ldy,
+                                 reinterpret_cast<float*>(ws + L.part), s);
     }
   }
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);

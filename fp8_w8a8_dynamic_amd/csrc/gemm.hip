@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw, int M,
     int N, int K, uint16_t* __restrict__ y, int64_t ldy, int tiles_m,
-    int tiles_n) {
+    int tiles_n, float* __restrict__ part) {
   using S = GemmShape<BM, BN, WGM, WGN, NB>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::SMEM];
 
@@ -177,12 +177,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
                  b_lds + buf * S::STAGE + (c - S::A_LOADS) * 1024);
   };
 
-  const int KT = K / kBK;
+  // K split blockIdx.y of gridDim.y takes stages [kt0, kt0 + KT) (all of
+  // K when gridDim.y == 1).
+  const int KT_all = K / kBK;
+  const int kt0 = static_cast<int>(blockIdx.y) * KT_all / static_cast<int>(gridDim.y);
+  const int KT = (static_cast<int>(blockIdx.y) + 1) * KT_all / static_cast<int>(gridDim.y) - kt0;
+  const uint32_t kbase = static_cast<uint32_t>(kt0 * kBK);
 #pragma unroll
   for (int st = 0; st < NB; ++st)
     if (st < KT) {
 #pragma unroll
-      for (int c = 0; c < S::COPIES; ++c) copy(c, st, static_cast<uint32_t>(st * kBK));
+      for (int c = 0; c < S::COPIES; ++c)
+        copy(c, st, kbase + static_cast<uint32_t>(st * kBK));
     }
   // Main loop.  Per stage, each wave runs T MFMAs of step 0 then T of step
   // 1 (T = TM * TN).  A wave drains its LDS reads at roughly 1 KB per 40
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
     read_step(af1, bf1, smem + buf * S::STAGE, p1);
     const bool refill = kt + NB < KT;
     const bool more = kt + 1 < KT;
-    const uint32_t next_k = static_cast<uint32_t>((kt + NB) * kBK);
+    const uint32_t next_k = kbase + static_cast<uint32_t>((kt + NB) * kBK);
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
       // Every wave holds this stage's fragments: the buffer takes stage
@@ -267,10 +273,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   // scales its values, packs four bf16 (8 bytes) into this wave's region of
   // LDS laid out [token][channel], and the wave then writes whole rows back
   // with 16-byte stores (coalesced row segments of 2*WN bytes).
-  __syncthreads();  // every wave is done with the stage buffers
-  uint8_t* ep = smem + wave * (S::WM * S::EPI_ROW);
   const int tok0 = m0 + wm * S::WM;
   const int ch0 = n0 + wn * S::WN;
+  if (part != nullptr) {
+    // K split: the raw float32 sums of this split go to part[split][m][n]
+    // (16 bytes = 4 consecutive channels per lane and (t, u, q)); the
+    // reduction kernel adds the splits in order and applies the scales.
+    float* pb = part + static_cast<int64_t>(blockIdx.y) * M * N;
+#pragma unroll
+    for (int t = 0; t < S::TM; ++t) {
+      const int gm = tok0 + 32 * t + frow;
+#pragma unroll
+      for (int u = 0; u < S::TN; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int gn = ch0 + 32 * u + 8 * q + 4 * fhalf;
+          if (gm < M && gn < N)
+            *reinterpret_cast<float4*>(pb + static_cast<int64_t>(gm) * N + gn) =
+                make_float4(acc[t][u][4 * q + 0], acc[t][u][4 * q + 1],
+                            acc[t][u][4 * q + 2], acc[t][u][4 * q + 3]);
+        }
+    }
+    return;
+  }
+  __syncthreads();  // every wave is done with the stage buffers
+  uint8_t* ep = smem + wave * (S::WM * S::EPI_ROW);
   // Channel scales of this lane: 4 consecutive channels per (u, q).
   float4 ws[S::TN][4];
 #pragma unroll
@@ -312,45 +339,125 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   }
 }
 
+// Sum of the K splits in split order, then the epilogue of the unsplit
+// kernel: y = bf16_rne(sum * sw[n] * sx[m]).  One thread per 4 consecutive
+// channels (n % 16 == 0, so a group never leaves its row).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    const float* __restrict__ part, int splits, const float* __restrict__ sx,
+    const float* __restrict__ sw, int M, int N, uint16_t* __restrict__ y,
+    int64_t ldy) {
+  const int64_t groups = static_cast<int64_t>(M) * (N / 4);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t plane = static_cast<int64_t>(M) * N;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       g < groups; g += stride) {
+    const int m = static_cast<int>(g / (N / 4));
+    const int n = static_cast<int>(g - static_cast<int64_t>(m) * (N / 4)) * 4;
+    const float* p = part + static_cast<int64_t>(m) * N + n;
+    float4 a = *reinterpret_cast<const float4*>(p);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 b = *reinterpret_cast<const float4*>(p + sp * plane);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    const float4 w = *reinterpret_cast<const float4*>(sw + n);
+    const float xs = sx[m];
+    uint2 pk;
+    pk.x = pack_bf16x2(a.x * w.x * xs, a.y * w.y * xs);
+    pk.y = pack_bf16x2(a.z * w.z * xs, a.w * w.w * xs);
+    *reinterpret_cast<uint2*>(y + static_cast<int64_t>(m) * ldy + n) = pk;
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int NB, int MINB>
 hipError_t launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
                       const float* sw, int64_t m, int64_t n, int64_t k,
-                      uint16_t* y, int64_t ldy, hipStream_t stream) {
+                      uint16_t* y, int64_t ldy, int splits, float* part,
+                      hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
   gemm_fp8_kernel<BM, BN, WGM, WGN, NB, MINB>
-      <<<dim3(static_cast<uint32_t>(tiles_m * tiles_n)), dim3(64 * WGM * WGN),
-         0, stream>>>(qx, sx, qw, sw, static_cast<int>(m), static_cast<int>(n),
-                      static_cast<int>(k), y, ldy, tiles_m, tiles_n);
+      <<<dim3(static_cast<uint32_t>(tiles_m * tiles_n), static_cast<uint32_t>(splits)),
+         dim3(64 * WGM * WGN), 0, stream>>>(
+          qx, sx, qw, sw, static_cast<int>(m), static_cast<int>(n),
+          static_cast<int>(k), y, ldy, tiles_m, tiles_n,
+          splits > 1 ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  int64_t blocks = (m * (n / 4) + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  splitk_reduce_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream>>>(
+      part, splits, sx, sw, static_cast<int>(m), static_cast<int>(n), y, ldy);
   return hipGetLastError();
 }
 
 }  // namespace detail
 using namespace detail;
 
-// Tile configurations; FP8W8A8_GEMM_CONFIG=<index> overrides the choice
-// (a tuning aid; every configuration computes the same result).
-hipError_t launch_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
-                       const float* sw, int64_t m, int64_t n, int64_t k,
-                       uint16_t* y, int64_t ldy, hipStream_t stream) {
-  if (m == 0 || n == 0) return hipSuccess;
-  int cfg = -1;
-  if (const char* e = std::getenv("FP8W8A8_GEMM_CONFIG")) cfg = std::atoi(e);
-  if (cfg < 0) {
-    // Measured on MI355X for the 4096-token layer shapes with operands
-    // arriving from HBM: 256x256 tiles of eight waves (4x2); narrow outputs
-    // (few tiles, one per CU) take 128x128 tiles with four stages in flight,
-    // whose pipeline is otherwise bound by the copies' latency.
-    const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-    cfg = big_tiles < 128 ? 4 : 3;
+// Tile configuration and K splits.  FP8W8A8_GEMM_CONFIG=<index> overrides
+// the configuration, and with it FP8W8A8_GEMM_SPLITS=<n> the number of K
+// splits (1 if unset) -- tuning aids; every configuration computes the same
+// result, and the splits change only the float32 summation order.
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
+  GemmPlan p{3, 1};
+  if (m <= 0 || n <= 0 || k < kBK) return p;
+  if (const char* e = std::getenv("FP8W8A8_GEMM_CONFIG")) {
+    p.cfg = std::atoi(e);
+    if (p.cfg >= 0) {
+      if (const char* sp = std::getenv("FP8W8A8_GEMM_SPLITS")) {
+        int v = std::atoi(sp);
+        const int kt = static_cast<int>(k / kBK);
+        if (v > kt) v = kt;
+        if (v > kMaxSplits) v = kMaxSplits;
+        p.splits = v < 1 ? 1 : v;
+      }
+      return p;
+    }
   }
-  switch (cfg) {
-    case 0: return launch_cfg<256, 256, 2, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 1: return launch_cfg<256, 256, 2, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 2: return launch_cfg<128, 128, 2, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 3: return launch_cfg<256, 256, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    case 4: return launch_cfg<128, 128, 2, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
-    default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, stream);
+  // Measured on MI355X for the 4096-token layer shapes with operands
+  // arriving from HBM: 256x256 tiles of eight waves (4x2); narrow outputs
+  // (few tiles, one per CU) take 128x128 tiles with four stages in flight,
+  // whose pipeline is otherwise bound by the copies' latency.
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  p.cfg = big_tiles < 128 ? 4 : 3;
+  const int64_t tiles4 = ((m + 127) / 128) * ((n + 127) / 128);
+  if (big_tiles < 128 && tiles4 < 128) {
+    // Few tokens (m up to a few hundred): too few output tiles to keep the
+    // CUs streaming the weights.  128x64 tiles (one workgroup per CU), and
+    // K split so that about one workgroup per CU results, at most 8 ways
+    // (measured at m = 64 and 256 on the layer's shapes: more splits cost
+    // more in partial-sum traffic than they gain); the splits' float32
+    // partial sums go through the workspace to a reduction kernel.
+    p.cfg = 5;
+    const int64_t tiles5 = ((m + 127) / 128) * ((n + 63) / 64);
+    const int64_t kt = k / kBK;
+    int64_t sp = 256 / tiles5;
+    if (sp > 8) sp = 8;
+    if (sp > kt) sp = kt;
+    p.splits = static_cast<int>(sp < 1 ? 1 : sp);
+  }
+  return p;
+}
+
+size_t gemm_partial_bytes(const GemmPlan& p, int64_t m, int64_t n) {
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * m * n * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(const GemmPlan& p, const uint8_t* qx, const float* sx,
+                       const uint8_t* qw, const float* sw, int64_t m, int64_t n,
+                       int64_t k, uint16_t* y, int64_t ldy, float* part,
+                       hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+  const int sp = p.splits;
+  switch (p.cfg) {
+    case 0: return launch_cfg<256, 256, 2, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 1: return launch_cfg<256, 256, 2, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 2: return launch_cfg<128, 128, 2, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 3: return launch_cfg<256, 256, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 4: return launch_cfg<128, 128, 2, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 6: return launch_cfg<64, 128, 2, 2, 2, 3>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 7: return launch_cfg<64, 64, 2, 1, 2, 4>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
   }
 }
 

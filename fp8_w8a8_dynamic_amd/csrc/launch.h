@@ -16,9 +16,21 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t k,
                              hipStream_t stream);
 
 // Prefill GEMM: y[m,n] = bf16(sum_k qx[m,k] qw[n,k] * sx[m] * sw[n]).
-hipError_t launch_gemm(const uint8_t* qx, const float* sx, const uint8_t* qw,
-                       const float* sw, int64_t m, int64_t n, int64_t k,
-                       uint16_t* y, int64_t ldy, hipStream_t stream);
+// The plan fixes the tile configuration and the number of K splits; with
+// splits > 1 the GEMM writes float32 partial sums [splits, m, n] to `part`
+// (gemm_partial_bytes) and a second kernel adds them in split order and
+// applies the scales.
+constexpr int kMaxSplits = 64;
+struct GemmPlan {
+  int cfg;
+  int splits;
+};
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k);
+size_t gemm_partial_bytes(const GemmPlan& p, int64_t m, int64_t n);
+hipError_t launch_gemm(const GemmPlan& p, const uint8_t* qx, const float* sx,
+                       const uint8_t* qw, const float* sw, int64_t m, int64_t n,
+                       int64_t k, uint16_t* y, int64_t ldy, float* part,
+                       hipStream_t stream);
 
 // Decode GEMV (m <= kGemvMaxM).  If x != nullptr the activations are
 // quantized inside the kernel (fused; only where gemv_fused_fits), otherwise

@@ -129,9 +129,12 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
  * fp8w8a8_quant_linear (fused != 0) at the given sizes; 0 when the call needs
  * none, and 0 for invalid sizes.  The workspace is plain scratch that holds
  * the quantized activations [m, k] and their scales [m] when a fused call
- * quantizes in a separate kernel before the matmul; no state survives a
- * call, so any workspace can be reused, but calls that may run concurrently
- * need distinct workspaces.
+ * quantizes in a separate kernel before the matmul, and float32 partial sums
+ * [splits, m, n] when the matmul splits K over several workgroups (shapes
+ * with few output tiles, i.e. m from 17 to a few hundred; the splits are
+ * added in a fixed order, so results are deterministic); no state survives
+ * a call, so any workspace can be reused, but calls that may run
+ * concurrently need distinct workspaces.
  */
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused);
 

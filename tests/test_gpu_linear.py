@@ -183,6 +183,39 @@ def test_deterministic_outputs():
         assert np.array_equal(a, b)
 
 
+SPLIT_SHAPES = [(17, 4096, 4096), (64, 1024, 4096), (64, 4112, 12288),
+                (100, 272, 384), (129, 2048, 1152), (256, 4096, 4096),
+                (100, 6144, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
+def test_split_k_gemm(m, n, k):
+    """Token counts with few output tiles split K over workgroups (float32
+    partial sums in the workspace, added in split order by a second
+    kernel): against the oracle, ragged m and n, uneven splits of K, and
+    bit-identical on a second run."""
+    assert fq.workspace_bytes(m, n, k, False) >= m * n * 4 * 2, "plan does not split K"
+    qx, sx, qw, sw = _rand_operands(m, n, k, 7 * m + n + k)
+    y = _run_linear(qx, sx, qw, sw)
+    check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"split-K {m}x{n}x{k}")
+    assert np.array_equal(y, _run_linear(qx, sx, qw, sw))
+
+
+@pytest.mark.parametrize("m,linear", [(64, 0), (64, 6), (256, 1), (33, 4)])
+def test_split_k_fused_layer_shapes(m, linear):
+    """The fused call at mid-sized token counts (workspace holding the
+    quantized activations and the partial sums) on the layer's shapes."""
+    _, n, k = LAYER_SHAPES[linear]
+    rng = np.random.default_rng(40 + m + linear)
+    x = bf16_from_f64(rng.standard_normal((m, k)))
+    w = weight_bf16(2, 0, linear, n, k)
+    qw, sw = _quant_weights_gpu(w)
+    y = fq.quant_linear(to_dev_bf16(x), qw, sw)
+    torch.cuda.synchronize()
+    y64, _, _ = oracle.quant_linear_ref(x, host_bits(qw), host_bits(sw))
+    check_close(host_bits(y), y64, f"fused split-K m={m} {LAYER_SHAPES[linear][0]}")
+
+
 def test_empty_calls():
     qw = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
     sw = torch.ones(16, dtype=torch.float32, device="cuda")
