@@ -231,6 +231,52 @@ def bench_decode(torch, fq, reps, packed=False):
     return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes)
 
 
+def bench_stack(torch, fq, m, passes):
+    """The 36-layer stack at m tokens: 252 fused calls per pass over
+    6.946 GB of FP8 weights resident in HBM, with the stack's data flow
+    (q, k, v, o, gate, up read the layer input, down reads up's output, and
+    down's output is the next layer's input).  Weight codes are seeded
+    random bytes (NaN codes excluded) with random channel scales: the timing
+    does not depend on the values, and quantizing 6.9 GB of bf16 weights
+    first would dominate the run."""
+    from workloads import LAYER_SHAPES
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    layers = []
+    for _ in range(36):
+        lw = []
+        for _, n, k in LAYER_SHAPES:
+            c = torch.randint(0, 256, (n, k), dtype=torch.uint8, device="cuda", generator=gen)
+            c[(c & 0x7F) == 0x7F] -= 1
+            lw.append((c, torch.rand(n, device="cuda", generator=gen) * 1e-3 + 1e-4))
+        layers.append(lw)
+    x0 = torch.randn(m, 4096, device="cuda", generator=gen).to(torch.bfloat16)
+    ys = [torch.empty(m, n, dtype=torch.bfloat16, device="cuda") for _, n, _ in LAYER_SHAPES]
+    xs = [x0] + [torch.empty(m, 4096, dtype=torch.bfloat16, device="cuda") for _ in range(36)]
+    wsb = max(fq.workspace_bytes(m, n, k, True) for _, n, k in LAYER_SHAPES)
+    ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
+
+    def one_pass():
+        for li, lw in enumerate(layers):
+            x = xs[li]
+            for j in range(6):
+                fq.quant_linear(x, lw[j][0], lw[j][1], out=ys[j], workspace=ws)
+            fq.quant_linear(ys[5], lw[6][0], lw[6][1], out=xs[li + 1], workspace=ws)
+
+    for _ in range(3):
+        one_pass()
+    torch.cuda.synchronize()
+    t = time_events(torch, one_pass, passes)
+    nbytes = 36 * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for _, n, k in LAYER_SHAPES)
+    flops = 36 * sum(2 * m * n * k for _, n, k in LAYER_SHAPES)
+    del layers, xs, ys
+    torch.cuda.empty_cache()
+    return {"m": m, "ms_per_pass": round(t * 1e3, 4), "gbs": round(nbytes / t / 1e9, 1),
+            "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(flops / t / 1e12, 2),
+            "frac_of_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline(target_s=16.0):
     """The oracle as it stands, timed on a sample of the prefill workload:
     all 7 Linears, a subset of tokens and of output channels (weights
@@ -280,6 +326,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 36-layer stack leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy "
                          "(reference for the HBM byte counters)")
@@ -328,6 +375,11 @@ def main():
                             "us_per_layer": round(dec_p["layer_us"], 3),
                             "frac_of_hbm": round(dec_p["gbs"] / HBM_PEAK_GBS, 4)}
         log(f"packed decode {packed['decode']}")
+    stack = None
+    if not args.no_stack:
+        log("36-layer stack ...")
+        stack = [bench_stack(torch, fq, m, max(5, args.steps // 20)) for m in (64, 256)]
+        log(f"stack {stack}")
     cpu = None
     if not args.no_cpu:
         log("cpu oracle ...")
@@ -371,6 +423,12 @@ def main():
                          "frac_of_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                          "bytes_per_layer": dec["bytes"]}
     out["packed"] = packed
+    if stack is not None:
+        out["stack_36_layers"] = {
+            "metric": "one pass of the 36-layer stack (252 fused calls, 6.946 GB of "
+                      "FP8 weights in HBM, layer outputs chained): GB/s of algorithmic "
+                      "bytes and TFLOP/s",
+            "passes": stack}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
