@@ -330,8 +330,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   constexpr int CPR = S::WN * 2 / 16;
   constexpr int RPW = 64 / CPR;
   const int rr = lane / CPR, cc = lane % CPR;
+  // (When CPR does not divide 64 the last lanes sit out.)
 #pragma unroll 4
-  for (int row = rr; row < S::WM; row += RPW) {
+  for (int row = rr; row < S::WM && lane < RPW * CPR; row += RPW) {
     const uint4 v = *reinterpret_cast<const uint4*>(ep + row * S::EPI_ROW + cc * 16);
     const int gm = tok0 + row, gn = ch0 + cc * 8;
     if (gm < M && gn < N)
@@ -419,6 +420,16 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
   // whose pipeline is otherwise bound by the copies' latency.
   const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
   p.cfg = big_tiles < 128 ? 4 : 3;
+  if (p.cfg == 3) {
+    // Whole rounds of one tile per CU (256 CUs): where 256x256 tiles leave a
+    // partial last round, 256x192 tiles (0.8 of the time per tile,
+    // measured) may fill the rounds better -- e.g. a packed qkv projection,
+    // N = 6144: 384 tiles of 256x256 (1.5 rounds) against 512 of 256x192.
+    const int64_t tiles8 = ((m + 255) / 256) * ((n + 191) / 192);
+    const double t3 = static_cast<double>((big_tiles + 255) / 256);
+    const double t8 = 0.8 * static_cast<double>((tiles8 + 255) / 256);
+    if (t8 < t3) p.cfg = 8;
+  }
   const int64_t tiles4 = ((m + 127) / 128) * ((n + 127) / 128);
   if (big_tiles < 128 && tiles4 < 128) {
     // Few tokens (m up to a few hundred): too few output tiles to keep the
@@ -457,6 +468,7 @@ hipError_t launch_gemm(const GemmPlan& p, const uint8_t* qx, const float* sx,
     case 4: return launch_cfg<128, 128, 2, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
     case 6: return launch_cfg<64, 128, 2, 2, 2, 3>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
     case 7: return launch_cfg<64, 64, 2, 1, 2, 4>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+    case 8: return launch_cfg<256, 192, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
     default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
   }
 }

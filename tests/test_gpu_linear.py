@@ -224,7 +224,7 @@ def test_empty_calls():
     assert y.shape == (0, 16)
 
 
-GEMM_CONFIGS = ["0", "1", "2", "3", "4", "5"]
+GEMM_CONFIGS = ["0", "1", "2", "3", "4", "5", "6", "7", "8"]
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 1040, 384), (513, 528, 640), (4096, 272, 256),
