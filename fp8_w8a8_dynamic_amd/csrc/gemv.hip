@@ -457,27 +457,48 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
   if (m == 0 || n == 0) return hipSuccess;
   int lg_mp = 0;
   while ((1 << lg_mp) < m) ++lg_mp;
-  // Row groups per workgroup.  Measured on MI355X: whole row groups per
-  // wave (none shared between waves) and about one workgroup per CU are
-  // best, as long as that leaves >= 64 workgroups and a wave's groups fit
-  // one batch of loads.  Where one workgroup per CU would need more groups
-  // per wave than a batch holds, the groups are split evenly over 2, 3, ...
-  // workgroups per CU (a count that leaves some CUs one workgroup more than
-  // others costs a whole extra workgroup time: 24576 x 4096 took 27.4 us
-  // with 384 workgroups, 22.5 us with 512).  Otherwise about one workgroup
-  // per CU, with groups shared between waves.
+  // Row groups per workgroup, measured on MI355X at M = 1, 2, 4, 8 on the
+  // layer's shapes.  The workgroup count aims at one per CU but no fewer
+  // than ~64 KB of weights per workgroup (64 to 256 workgroups): every
+  // workgroup pays for staging the activations, so small matrices (k/v,
+  // 4 MB) stream fastest from 64 workgroups, and e.g. q at M = 4 from 256
+  // rather than 64 (12.1 -> 9.9 us).  Where a workgroup holds at least one
+  // row group per wave and the groups fit one batch of loads, they are
+  // dealt whole to the waves (none shared); where one workgroup per CU
+  // would then need more groups per wave than a batch holds, the groups are
+  // split evenly over 2, 3, ... workgroups per CU (a count that leaves some
+  // CUs one workgroup more than others costs a whole extra workgroup time:
+  // 24576 x 4096 took 27.4 us with 384 workgroups, 22.5 us with 512).
+  // Otherwise groups are shared between waves, up to one batch per wave.
   const int64_t groups = n >> lg_mp;
   const int64_t cs = (k + (2048 >> lg_mp) - 1) / (2048 >> lg_mp);
-  int64_t gpw;
-  if (cs <= kItems && groups >= 64 * kWaves) {
-    const int64_t need = (groups + 256 * kWaves - 1) / (256 * kWaves);
+  int64_t wgs = n * k / 65536;
+  if (wgs > 256) wgs = 256;
+  if (wgs < 64) wgs = 64;
+  int64_t gpw = (groups + wgs - 1) / wgs;
+  // Share of the last round of one workgroup per CU that is filled.
+  auto filled = [&](int64_t g) {
+    const int64_t c = (groups + g - 1) / g;
+    return c <= 256 ? 1.0 : static_cast<double>(c) / (256.0 * ((c + 255) / 256));
+  };
+  // Largest of unit, 2 unit, ... top with the fullest last round.
+  auto best_fill = [&](int64_t unit, int64_t top) {
+    int64_t pick = unit;
+    for (int64_t g = unit; g <= top; g += unit)
+      if (filled(g) >= filled(pick)) pick = g;
+    return pick;
+  };
+  const int64_t cap = (kWaves * kItems) / cs;   // one batch per wave
+  if (cs <= kItems && gpw >= kWaves) {
+    const int64_t need = (gpw + kWaves - 1) / kWaves;
     const int64_t fit = kItems / cs;
-    const int64_t rounds = (need + fit - 1) / fit;
-    gpw = kWaves * ((need + rounds - 1) / rounds);
+    gpw = need <= fit ? kWaves * need : best_fill(kWaves, kWaves * fit);
+    if (filled(gpw) < 1.0) {
+      const int64_t shared = best_fill(1, cap);
+      if (filled(shared) > filled(gpw)) gpw = shared;
+    }
   } else {
-    gpw = (groups + 255) / 256;
-    const int64_t cap = (kWaves * kItems) / cs;
-    if (gpw > cap) gpw = cap;
+    if (gpw > cap) gpw = best_fill(1, cap);
     if (gpw < 1) gpw = 1;
   }
   // FP8W8A8_GEMV_GPW overrides (a tuning aid; every choice computes the
