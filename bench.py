@@ -46,8 +46,8 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # FETCH_SIZE (x2, calibrated) + WRITE_SIZE passes over this script (see
 # profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM source
 # with this SHA-1; reported as null once the source differs.
-GEMM_TRAFFIC = {"gemm_hip_sha1": "25b56a643e4b64b1276acba846b3e134c3f32443",
-                "bytes_per_step": 1493002 * 1024}
+GEMM_TRAFFIC = {"gemm_hip_sha1": "eba943d142c2bdfc874cc52c8eb625268b17364a",
+                "bytes_per_step": 1493156 * 1024}
 
 
 def gemm_traffic():
