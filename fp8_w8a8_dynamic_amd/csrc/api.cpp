@@ -97,18 +97,27 @@ int check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t ldy) {
   return FP8W8A8_OK;
 }
 
-enum class Path { kGemv, kGemm };
+enum class Path { kGemv, kGemvTok, kGemm };
 
-// Decode-sized inputs stream the weights through the split-K MFMA GEMV;
-// everything else takes the tiled MFMA GEMM.  FP8W8A8_FORCE_PATH=gemm|gemv
-// overrides the choice (the GEMV only where m <= 16) so that the two kernels
-// can be cross-checked on identical inputs.
-Path choose_path(int64_t m) {
+// Decode-sized inputs stream the weights through the split-K MFMA GEMV
+// (m <= 16); a little above that, up to 32 tokens, the token-group GEMV
+// beats the GEMM for weight matrices up to 16 MiB (each of its workgroups
+// re-reads all activation codes, which larger N make too costly: measured on
+// the layer's shapes at m = 17-64); everything else takes the tiled MFMA
+// GEMM.  FP8W8A8_FORCE_PATH=gemm|gemv|tok overrides the choice (each only
+// within its range of m) so that the kernels can be cross-checked on
+// identical inputs.
+Path choose_path(int64_t m, int64_t n, int64_t k) {
   const char* force = std::getenv("FP8W8A8_FORCE_PATH");
   if (force && std::strcmp(force, "gemm") == 0) return Path::kGemm;
   if (force && std::strcmp(force, "gemv") == 0 && m <= kGemvMaxM)
     return Path::kGemv;
-  return m <= kGemvMaxM ? Path::kGemv : Path::kGemm;
+  if (force && std::strcmp(force, "tok") == 0 && m > kGemvMaxM &&
+      m <= fp8w8a8::kGemvTokMaxM)
+    return Path::kGemvTok;
+  if (m <= kGemvMaxM) return Path::kGemv;
+  if (m <= 32 && n * k <= (int64_t{1} << 24)) return Path::kGemvTok;
+  return Path::kGemm;
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -186,7 +195,7 @@ int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
 
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
-  return layout_for(m, n, k, fused != 0, choose_path(m),
+  return layout_for(m, n, k, fused != 0, choose_path(m, n, k),
                     fp8w8a8::plan_gemm(m, n, k)).total;
 }
 
@@ -205,7 +214,7 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
   if (overlap(ry, span(qx, m, k, k, 1)) || overlap(ry, span(x_scale, m, 1, 1, 4)) ||
       overlap(ry, span(qw, n, k, k, 1)) || overlap(ry, span(w_scale, n, 1, 1, 4)))
     return FP8W8A8_ERR_ALIAS;
-  const Path path = choose_path(m);
+  const Path path = choose_path(m, n, k);
   const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
   const Layout L = layout_for(m, n, k, false, path, plan);
   const size_t need = L.total;
@@ -226,6 +235,8 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
   if (path == Path::kGemv)
     e = fp8w8a8::launch_gemv(nullptr, 0, qx, x_scale, qw, w_scale, m, n, k, y,
                              ldy, s);
+  else if (path == Path::kGemvTok)
+    e = fp8w8a8::launch_gemv_tok(qx, x_scale, qw, w_scale, m, n, k, y, ldy, s);
   else
     e = fp8w8a8::launch_gemm(plan, qx, x_scale, qw, w_scale, m, n, k, y, ldy,
                              reinterpret_cast<float*>(
@@ -250,7 +261,7 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
   if (overlap(ry, rx) || overlap(ry, span(qw, n, k, k, 1)) ||
       overlap(ry, span(w_scale, n, 1, 1, 4)))
     return FP8W8A8_ERR_ALIAS;
-  const Path path = choose_path(m);
+  const Path path = choose_path(m, n, k);
   const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
   const Layout L = layout_for(m, n, k, true, path, plan);
   const size_t need = L.total;
@@ -279,6 +290,8 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
       if (path == Path::kGemv)
         e = fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y,
                                  ldy, s);
+      else if (path == Path::kGemvTok)
+        e = fp8w8a8::launch_gemv_tok(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
       else
         e = fp8w8a8::launch_gemm(plan, qx, sx, qw, w_scale, m, n, k, y, ldy,
                                  reinterpret_cast<float*>(ws + L.part), s);

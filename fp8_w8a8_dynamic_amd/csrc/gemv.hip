@@ -406,8 +406,135 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
   }
 }
 
+// Token-group GEMV for 16 < M <= 64 (T = ceil(M / 16) groups of 16 tokens):
+// the same v_mfma_f32_16x16x128_f8f6f4 with one K class (the A operand is 16
+// weight rows x 128 K bytes, the B operand 16 tokens x the same 128 bytes),
+// each weight fragment feeding T MFMAs.  A 4-wave workgroup owns 16 weight
+// rows (one row group) over all of K; the waves split K four ways, load
+// weights and activation codes straight into registers (the codes of one
+// K range are read by one wave only, so LDS staging would buy nothing) in
+// batches of kTokBatch items with the next batch in flight, and add their
+// sums in LDS in wave order.  One kernel, no workspace partial sums.
+constexpr int kTokWaves = 4;
+
+template <int T>
+__global__ __launch_bounds__(kTokWaves * 64) void gemv_tok_kernel(
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx,
+    const uint8_t* __restrict__ qw, const float* __restrict__ sw, int M,
+    int K, uint16_t* __restrict__ y, int64_t ldy) {
+  constexpr int kB = T <= 2 ? 4 : 2;                // items per batch
+  __shared__ float red[kTokWaves][T][64][4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int ks = K / 128;                           // items of the row group
+  const int s0 = wave * ks / kTokWaves, s1 = (wave + 1) * ks / kTokWaves;
+  // Lane (r, g) holds bytes g*16 .. +15 and 64 + g*16 .. +15 of each
+  // 128-byte step, for weight row n0 + r and for token 16 t + r: the same
+  // K order on both operands.
+  const uint8_t* wrow = qw + static_cast<int64_t>(n0 + r) * K + g * 16;
+  const uint8_t* xrow[T];
+  bool tok_ok[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int tok = 16 * t + r;
+    tok_ok[t] = tok < M;
+    xrow[t] = qx + static_cast<int64_t>(tok_ok[t] ? tok : 0) * K + g * 16;
+  }
+  v4f acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint4 wa[2][kB][2], xb[2][kB][T][2];
+  // Items past the wave's range re-read its last item (a static number of
+  // loads); their MFMAs are skipped.
+  auto load = [&](int buf, int s) {
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int si = min(s + i, s1 - 1) * 128;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        wa[buf][i][h] = *reinterpret_cast<const uint4*>(wrow + si + h * 64);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          xb[buf][i][t][h] = *reinterpret_cast<const uint4*>(xrow[t] + si + h * 64);
+      }
+    }
+  };
+  auto run = [&](int buf, int s) {
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (s + i < s1) {
+        const v8i a = to_v8i(wa[buf][i][0], wa[buf][i][1]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const v8i b = tok_ok[t] ? to_v8i(xb[buf][i][t][0], xb[buf][i][t][1])
+                                  : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a, b, acc[t], 0, 0, 0, 0, 0, 0);
+        }
+      }
+  };
+  if (s0 < s1) {
+    load(0, s0);
+    for (int s = s0; s < s1; s += 2 * kB) {
+      if (s + kB < s1) load(1, s + kB);
+      run(0, s);
+      if (s + kB < s1) {
+        if (s + 2 * kB < s1) load(0, s + 2 * kB);
+        run(1, s + kB);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][t][lane][q] = acc[t][q];
+  __syncthreads();
+  // Lane l's accumulator q is the dot product of weight row 4 (l >> 4) + q
+  // and token l & 15 of its group: 4 consecutive outputs of one token.
+  for (int o = tid; o < T * 64; o += kTokWaves * 64) {
+    const int t = o / 64, l = o % 64;
+    const int tok = 16 * t + (l & 15);
+    if (tok < M) {
+      const int n = n0 + 4 * (l >> 4);
+      const float xs = sx[tok];
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float a = red[0][t][l][q];
+#pragma unroll
+        for (int w = 1; w < kTokWaves; ++w) a += red[w][t][l][q];
+        v[q] = a * sw[n + q] * xs;
+      }
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(y + static_cast<int64_t>(tok) * ldy + n) = pk;
+    }
+  }
+}
+
 }  // namespace detail
 using namespace detail;
+
+hipError_t launch_gemv_tok(const uint8_t* qx, const float* sx,
+                           const uint8_t* qw, const float* sw, int64_t m,
+                           int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                           hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (m <= kGemvMaxM || m > kGemvTokMaxM) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n / 16)), block(kTokWaves * 64);
+  const int mi = static_cast<int>(m), ki = static_cast<int>(k);
+  switch ((m + 15) / 16) {
+    case 2: gemv_tok_kernel<2><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
+    case 3: gemv_tok_kernel<3><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
+    default: gemv_tok_kernel<4><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
+  }
+  return hipGetLastError();
+}
 
 // Fused (in-kernel) quantization pays for re-quantizing the activations in
 // every workgroup; measured on MI355X it beats a separate quantization

@@ -42,6 +42,13 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                        int64_t m, int64_t n, int64_t k, uint16_t* y,
                        int64_t ldy, hipStream_t stream);
 
+// Token-group GEMV, kGemvMaxM < m <= kGemvTokMaxM, on quantized activations.
+constexpr int kGemvTokMaxM = 64;
+hipError_t launch_gemv_tok(const uint8_t* qx, const float* sx,
+                           const uint8_t* qw, const float* sw, int64_t m,
+                           int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                           hipStream_t stream);
+
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace fp8w8a8

@@ -189,11 +189,12 @@ SPLIT_SHAPES = [(17, 4096, 4096), (64, 1024, 4096), (64, 4112, 12288),
 
 
 @pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
-def test_split_k_gemm(m, n, k):
+def test_split_k_gemm(m, n, k, monkeypatch):
     """Token counts with few output tiles split K over workgroups (float32
     partial sums in the workspace, added in split order by a second
     kernel): against the oracle, ragged m and n, uneven splits of K, and
     bit-identical on a second run."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", "gemm")
     assert fq.workspace_bytes(m, n, k, False) >= m * n * 4 * 2, "plan does not split K"
     qx, sx, qw, sw = _rand_operands(m, n, k, 7 * m + n + k)
     y = _run_linear(qx, sx, qw, sw)
@@ -214,6 +215,34 @@ def test_split_k_fused_layer_shapes(m, linear):
     torch.cuda.synchronize()
     y64, _, _ = oracle.quant_linear_ref(x, host_bits(qw), host_bits(sw))
     check_close(host_bits(y), y64, f"fused split-K m={m} {LAYER_SHAPES[linear][0]}")
+
+
+TOK_SHAPES = [(17, 16, 128), (31, 272, 384), (32, 1040, 4096), (33, 48, 640),
+              (48, 4096, 4096), (63, 1024, 12288), (64, 4112, 1152),
+              (64, 4096, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", TOK_SHAPES)
+def test_token_group_gemv(m, n, k, monkeypatch):
+    """16 < m <= 64: the token-group GEMV (2-4 groups of 16 tokens, K split
+    over a workgroup's waves, ragged token groups, K ranges of unequal
+    length) against the oracle, and bit-identical on a second run."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", "tok")
+    qx, sx, qw, sw = _rand_operands(m, n, k, 11 * m + n + k)
+    y = _run_linear(qx, sx, qw, sw)
+    check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"tok {m}x{n}x{k}")
+    assert np.array_equal(y, _run_linear(qx, sx, qw, sw))
+
+
+@pytest.mark.parametrize("m", [17, 40, 64])
+@pytest.mark.parametrize("path", ["gemm", "tok"])
+def test_token_group_gemv_vs_gemm(m, path, monkeypatch):
+    """The token-group GEMV and the (split-K) GEMM on identical inputs, both
+    against the oracle."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", path)
+    qx, sx, qw, sw = _rand_operands(m, 1024, 4096, 300 + m)
+    y = _run_linear(qx, sx, qw, sw)
+    check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"{path} m={m}")
 
 
 def test_empty_calls():
