@@ -99,24 +99,25 @@ int check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t ldy) {
 
 enum class Path { kGemv, kGemvTok, kGemm };
 
-// Decode-sized inputs stream the weights through the split-K MFMA GEMV
-// (m <= 16); a little above that, up to 32 tokens, the token-group GEMV
-// beats the GEMM for weight matrices up to 16 MiB (each of its workgroups
-// re-reads all activation codes, which larger N make too costly: measured on
-// the layer's shapes at m = 17-64); everything else takes the tiled MFMA
-// GEMM.  FP8W8A8_FORCE_PATH=gemm|gemv|tok overrides the choice (each only
-// within its range of m) so that the kernels can be cross-checked on
-// identical inputs.
+// Decode-sized inputs stream the weights through the K-class MFMA GEMV
+// (m <= 4; it can also run up to 16); from 5 to 16 tokens, and up to 32 for
+// weight matrices up to 16 MiB, the token-group GEMV is faster (measured on
+// the layer's shapes: e.g. one layer at m = 16 in 108.6 us against 130.4;
+// beyond that each of its workgroups re-reading all activation codes costs
+// too much); everything else takes the tiled MFMA GEMM.
+// FP8W8A8_FORCE_PATH=gemm|gemv|tok overrides the choice (each only within
+// its range of m) so that the kernels can be cross-checked on identical
+// inputs.
 Path choose_path(int64_t m, int64_t n, int64_t k) {
   const char* force = std::getenv("FP8W8A8_FORCE_PATH");
   if (force && std::strcmp(force, "gemm") == 0) return Path::kGemm;
   if (force && std::strcmp(force, "gemv") == 0 && m <= kGemvMaxM)
     return Path::kGemv;
-  if (force && std::strcmp(force, "tok") == 0 && m > kGemvMaxM &&
-      m <= fp8w8a8::kGemvTokMaxM)
+  if (force && std::strcmp(force, "tok") == 0 && m <= fp8w8a8::kGemvTokMaxM)
     return Path::kGemvTok;
-  if (m <= kGemvMaxM) return Path::kGemv;
-  if (m <= 32 && n * k <= (int64_t{1} << 24)) return Path::kGemvTok;
+  if (m <= 4) return Path::kGemv;
+  if (m <= kGemvMaxM || (m <= 32 && n * k <= (int64_t{1} << 24)))
+    return Path::kGemvTok;
   return Path::kGemm;
 }
 

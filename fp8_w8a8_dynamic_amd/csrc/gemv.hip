@@ -525,10 +525,11 @@ hipError_t launch_gemv_tok(const uint8_t* qx, const float* sx,
                            int64_t n, int64_t k, uint16_t* y, int64_t ldy,
                            hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (m <= kGemvMaxM || m > kGemvTokMaxM) return hipErrorInvalidValue;
+  if (m > kGemvTokMaxM) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n / 16)), block(kTokWaves * 64);
   const int mi = static_cast<int>(m), ki = static_cast<int>(k);
   switch ((m + 15) / 16) {
+    case 1: gemv_tok_kernel<1><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
     case 2: gemv_tok_kernel<2><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
     case 3: gemv_tok_kernel<3><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
     default: gemv_tok_kernel<4><<<grid, block, 0, stream>>>(qx, sx, qw, sw, mi, ki, y, ldy); break;
