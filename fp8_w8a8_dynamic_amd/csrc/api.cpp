@@ -90,9 +90,13 @@ int check_quant_args(const uint16_t* src, int64_t rows, int64_t k, int64_t ld,
   return FP8W8A8_OK;
 }
 
+// The matmul kernels address a tile's rows with 32-bit buffer offsets
+// (up to 256 rows x k bytes per descriptor), which bounds k.
+constexpr int64_t kMaxLinearK = int64_t{1} << 22;
+
 int check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t ldy) {
   if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || n % 16 != 0 ||
-      k < 128 || k > kMaxDim || k % 128 != 0 || ldy < n || ldy % 8 != 0)
+      k < 128 || k > kMaxLinearK || k % 128 != 0 || ldy < n || ldy % 8 != 0)
     return FP8W8A8_ERR_SHAPE;
   return FP8W8A8_OK;
 }

@@ -101,8 +101,8 @@ int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
  *   y            bf16 [m, n], row stride ldy >= n, ldy % 8 == 0 (output)
  *   workspace    device scratch of at least
  *                fp8w8a8_workspace_bytes(m, n, k, 0) bytes; see below
- * Rules: m, n >= 0; n % 16 == 0; k >= 128, k % 128 == 0; all pointers
- * 16-byte aligned.
+ * Rules: m, n >= 0; n % 16 == 0; 128 <= k <= 4194304, k % 128 == 0; all
+ * pointers 16-byte aligned.
  */
 int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
                        const uint8_t* qw, const float* w_scale, int64_t m,

@@ -77,6 +77,7 @@ def test_linear_validation(lib):
     assert _lin(lib, n=24) == ESHAPE            # n % 16
     assert _lin(lib, k=192) == ESHAPE           # k % 128
     assert _lin(lib, k=0) == ESHAPE
+    assert _lin(lib, k=(1 << 22) + 128) == ESHAPE   # beyond 32-bit tile offsets
     assert _lin(lib, m=-1) == ESHAPE
     assert _lin(lib, ldy=32) == ESHAPE          # ldy < n
     assert _lin(lib, ldy=68) == ESHAPE          # ldy % 8
@@ -84,9 +85,12 @@ def test_linear_validation(lib):
     assert _lin(lib, y=A + 64) == EALIAS        # y overlaps qx
     assert _lin(lib, m=0) == OK
     assert _lin(lib, n=0) == OK
-    # the pre-quantized linear never needs scratch
+    # the pre-quantized linear needs scratch only where the GEMM splits K
+    # (few output tiles: float32 partial sums of at least two splits)
     assert lib.fp8w8a8_workspace_bytes(1, 64, 4096, 0) == 0
+    assert lib.fp8w8a8_workspace_bytes(16, 4096, 4096, 0) == 0
     assert lib.fp8w8a8_workspace_bytes(4096, 4096, 4096, 0) == 0
+    assert lib.fp8w8a8_workspace_bytes(64, 4096, 4096, 0) >= 2 * 64 * 4096 * 4
 
 
 def test_quant_linear_validation(lib):
