@@ -81,6 +81,31 @@ def time_events(torch, fn, reps):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
+def time_chunks(torch, fn, reps, chunks=5):
+    """time_events over reps calls, with an event between `chunks` equal
+    slices of them (no synchronization in between): returns the average per
+    call over all reps and the average per call of each slice."""
+    s = torch.cuda.current_stream()
+    cuts = [round(i * reps / chunks) for i in range(chunks + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in cuts]
+    ev[0].record(s)
+    for i in range(chunks):
+        for _ in range(cuts[i + 1] - cuts[i]):
+            fn()
+        ev[i + 1].record(s)
+    ev[-1].synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 / max(1, cuts[i + 1] - cuts[i])
+           for i in range(chunks)]
+    return ev[0].elapsed_time(ev[-1]) * 1e-3 / reps, per
+
+
+def spread(rates):
+    """Median, p10 and p90 of the rates of the timed slices."""
+    return {"median": round(float(np.median(rates)), 2),
+            "p10": round(float(np.percentile(rates, 10)), 2),
+            "p90": round(float(np.percentile(rates, 90)), 2), "slices": len(rates)}
+
+
 def setup_layer(torch, fq, m, cfg, packed=False):
     """The 7 Linears of one layer (seeded weights quantized on the GPU, one
     seeded input per Linear); packed: q|k|v and gate|up concatenated along
@@ -142,13 +167,14 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_time = time_events(torch, step, steps)
+    step_time, slices = time_chunks(torch, step, steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    slice_tflops = [flops / t / 1e12 for t in slices]
     if packed:
         del layer
         torch.cuda.empty_cache()
-        return dict(step_time=step_time, wall=wall, flops=flops)
+        return dict(step_time=step_time, wall=wall, flops=flops, slices=slice_tflops)
 
     # Dominant kernel: the GEMM on pre-quantized activations, timed with HIP
     # events on the launching stream while the 7 GEMMs of the layer run in
@@ -190,7 +216,7 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
     gemm_tflops = flops / gemm_region / 1e12
     del layer
     torch.cuda.empty_cache()
-    return dict(step_time=step_time, wall=wall, flops=flops,
+    return dict(step_time=step_time, wall=wall, flops=flops, slices=slice_tflops,
                 gemm_tflops=gemm_tflops, gemm_time=gemm_region, per_linear=per)
 
 
@@ -225,10 +251,12 @@ def bench_decode(torch, fq, reps, packed=False):
     for _ in range(max(3, reps // 2)):
         g.replay()
     torch.cuda.synchronize()
-    t = time_events(torch, g.replay, reps) / DECODE_COPIES
+    t, slices = time_chunks(torch, g.replay, reps)
+    t /= DECODE_COPIES
     del copies, base
     torch.cuda.empty_cache()
-    return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes)
+    return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes,
+                slices=[nbytes * DECODE_COPIES / ts / 1e9 for ts in slices])
 
 
 def bench_stack(torch, fq, m, passes):
@@ -367,11 +395,13 @@ def main():
                          "down_proj: 4 calls, one quantization per distinct input",
               "prefill": {"value": round(pre_p["flops"] / pre_p["step_time"] / 1e12, 2),
                           "unit": "TFLOP/s",
-                          "ms_per_step": round(pre_p["step_time"] * 1e3, 4)}}
+                          "ms_per_step": round(pre_p["step_time"] * 1e3, 4),
+                          "slice_tflops": spread(pre_p["slices"])}}
     log(f"packed prefill {packed['prefill']}")
     if not args.no_decode:
         dec_p = bench_decode(torch, fq, max(20, args.steps), packed=True)
-        packed["decode"] = {"value": round(dec_p["gbs"], 1), "unit": "GB/s",
+        packed["decode"] = {"slice_gbs": spread(dec_p["slices"]),
+                            "value": round(dec_p["gbs"], 1), "unit": "GB/s",
                             "us_per_layer": round(dec_p["layer_us"], 3),
                             "frac_of_hbm": round(dec_p["gbs"] / HBM_PEAK_GBS, 4)}
         log(f"packed decode {packed['decode']}")
@@ -404,7 +434,8 @@ def main():
                                "gate,up (12288 x 4096), down (4096 x 12288); "
                                "fused per-token quant + FP8 GEMM + epilogue",
                    "m": PREFILL_M, "linears": 7,
-                   "frac_of_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)},
+                   "frac_of_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+                   "slice_tflops": spread(pre["slices"])},
         "roofline": {"bound": "mfma", "achieved": round(pre["gemm_tflops"], 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre["gemm_tflops"] / FP8_PEAK_TFLOPS, 4),
@@ -421,7 +452,8 @@ def main():
                          "value": round(dec["gbs"], 1), "unit": "GB/s",
                          "us_per_layer": round(dec["layer_us"], 3),
                          "frac_of_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4),
-                         "bytes_per_layer": dec["bytes"]}
+                         "bytes_per_layer": dec["bytes"],
+                         "slice_gbs": spread(dec["slices"])}
     out["packed"] = packed
     if stack is not None:
         out["stack_36_layers"] = {
