@@ -245,6 +245,64 @@ def test_token_group_gemv_vs_gemm(m, path, monkeypatch):
     check_close(y, oracle.linear_ref(qx, sx, qw, sw), f"{path} m={m}")
 
 
+FINITE_CODES = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+
+
+def _pairs_case(tok_codes, n_codes, k, k0):
+    """One-hot operands: token m holds code tok_codes[m] and weight row n
+    holds n_codes[n], both at K position k0 and zero elsewhere, unit scales:
+    every output is a single E4M3 x E4M3 product, exact in float32, so the
+    bf16 output must equal the oracle's bf16 rounding bit for bit."""
+    m, n = len(tok_codes), len(n_codes)
+    qx = np.zeros((m, k), np.uint8)
+    qw = np.zeros((n, k), np.uint8)
+    qx[:, k0] = tok_codes
+    qw[:, k0] = n_codes
+    return qx, np.ones(m, np.float32), qw, np.ones(n, np.float32)
+
+
+def _check_pairs(qx, sx, qw, sw, what):
+    y = _run_linear(qx, sx, qw, sw).copy()
+    want = oracle.f64_to_bf16_bits(oracle.linear_ref(qx, sx, qw, sw))
+    y[y == 0x8000] = 0                     # a single product of -0 sums to +0
+    want = want.copy()
+    want[want == 0x8000] = 0
+    check_bytes(y, want, what)
+
+
+@pytest.mark.parametrize("path,cfg", [("gemm", "3"), ("gemm", "4"), ("gemm", "8"),
+                                      ("gemm", "-1"), ("tok", None)])
+def test_all_code_pairs_exact_tiles(path, cfg, monkeypatch):
+    """All 254 x 254 finite code pairs through the MFMA tiles (the GEMM's
+    configurations, its split-K plan, the token-group GEMV), at K positions
+    that reach every 16-byte chunk and both MFMA K halves of a 128-byte
+    step."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", path)
+    if cfg is not None and cfg != "-1":
+        monkeypatch.setenv("FP8W8A8_GEMM_CONFIG", cfg)
+    codes_n = np.concatenate([FINITE_CODES, np.zeros(2, np.uint8)])   # n = 256
+    k = 1024 if cfg == "-1" else 256
+    tok_sets = [FINITE_CODES] if path == "gemm" else \
+        [FINITE_CODES[i:i + 64] for i in range(0, 254, 64)]
+    for k0 in ([0, 17, 63, 64, 100, 127, 128 + 31, 255] + ([700, 1023] if k > 256 else [])):
+        for toks in tok_sets:
+            qx, sx, qw, sw = _pairs_case(toks, codes_n, k, k0)
+            _check_pairs(qx, sx, qw, sw, f"{path} cfg {cfg} k0={k0}")
+
+
+def test_all_code_pairs_exact_decode_gemv(monkeypatch):
+    """All 254 x 254 finite code pairs through the K-class decode GEMV (4
+    tokens per call, so four K classes per MFMA), at K positions in every
+    class and 16-byte chunk of the first 2 KB."""
+    monkeypatch.setenv("FP8W8A8_FORCE_PATH", "gemv")
+    codes_n = np.concatenate([FINITE_CODES, np.zeros(2, np.uint8)])
+    k = 2048
+    for k0 in range(0, 2048, 176):
+        for i in range(0, 254, 4):
+            qx, sx, qw, sw = _pairs_case(FINITE_CODES[i:i + 4], codes_n, k, k0)
+            _check_pairs(qx, sx, qw, sw, f"gemv k0={k0} tokens {i}")
+
+
 def test_empty_calls():
     qw = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
     sw = torch.ones(16, dtype=torch.float32, device="cuda")
