@@ -203,6 +203,7 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
         for L in layer:
             fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
     gemm_region = time_events(torch, gemms, steps)
+    lib_tflops = library_gemm_tflops(torch, layer, flops, steps)
     quant_t = []
     for L in layer:
         q = lambda L=L: fq.quantize_act_per_token(L["x"])
@@ -217,7 +218,28 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
     del layer
     torch.cuda.empty_cache()
     return dict(step_time=step_time, wall=wall, flops=flops, slices=slice_tflops,
-                gemm_tflops=gemm_tflops, gemm_time=gemm_region, per_linear=per)
+                gemm_tflops=gemm_tflops, gemm_time=gemm_region, per_linear=per,
+                lib_tflops=lib_tflops)
+
+
+def library_gemm_tflops(torch, layer, flops, steps):
+    """For comparison only: the vendor library's FP8 GEMM (hipBLASLt behind
+    torch._scaled_mm) on the same quantized operands, with the same
+    per-token x per-channel float32 scales and bf16 output, timed the same
+    way (the 7 GEMMs back to back).  None where torch does not offer it."""
+    try:
+        ops = [(L["qx"].view(torch.float8_e4m3fn), L["qw"].view(torch.float8_e4m3fn).t(),
+                L["sx"].view(-1, 1), L["sw"].view(1, -1)) for L in layer]
+
+        def seq():
+            for a, b, sa, sb in ops:
+                torch._scaled_mm(a, b, scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        seq()
+        torch.cuda.synchronize()
+        return round(flops / time_events(torch, seq, steps) / 1e12, 2)
+    except Exception as e:                 # not offered by this torch build
+        log(f"library comparison skipped: {type(e).__name__}: {e}")
+        return None
 
 
 def bench_decode(torch, fq, reps, packed=False):
@@ -444,6 +466,8 @@ def main():
                                       "(rocprofv3 FETCH_SIZE x2 + WRITE_SIZE); "
                                       "algorithmic 663 MB",
                      "kernel": "gemm_fp8_kernel",
+                     "library_same_operands_tflops": pre.get("lib_tflops"),
+                     "library": "hipBLASLt via torch._scaled_mm, row-wise scales (comparison only)",
                      "per_linear": pre["per_linear"]},
     }
     if dec is not None:
