@@ -132,12 +132,23 @@ __device__ __forceinline__ uint2 quantize8(uint4 v, const RowDivisor& d) {
   return out;
 }
 
-// Max over the 64 lanes of a wave (result valid in every lane).
+// Max over the 64 lanes of a wave (result valid in every lane), with DPP
+// moves (no LDS round trips): quad, 8-lane, 16-lane (row) maxima, then the
+// row broadcasts fold rows 0-2 into row 3, so lane 63 holds the maximum.
+// Lanes a move does not write keep 0, the identity of an unsigned max.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(x), CTRL, ROW_MASK, 0xf, false));
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1)
-    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
-  return v;
+  v = max(v, dpp_u32<0xb1, 0xf>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4e, 0xf>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141, 0xf>(v));   // row_half_mirror
+  v = max(v, dpp_u32<0x140, 0xf>(v));   // row_mirror
+  v = max(v, dpp_u32<0x142, 0xa>(v));   // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_u32<0x143, 0xc>(v));   // row_bcast:31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // float32 -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32).
