@@ -44,17 +44,22 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 
 # HBM bytes of one prefill step's 7 GEMM dispatches, from rocprofv3
 # FETCH_SIZE (x2, calibrated) + WRITE_SIZE passes over this script (see
-# profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM source
-# with this SHA-1; reported as null once the source differs.
-GEMM_TRAFFIC = {"gemm_hip_sha1": "eba943d142c2bdfc874cc52c8eb625268b17364a",
+# profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM code
+# whose SHA-1 (comments and blank lines stripped) is given here; reported as
+# null once the code differs.
+GEMM_TRAFFIC = {"gemm_hip_sha1": "e766db1e35120c34317c809469a94491d0471fc0",
                 "bytes_per_step": 1493156 * 1024}
 
 
 def gemm_traffic():
+    """GEMM_TRAFFIC's bytes if gemm.hip's code (comments and blank lines
+    aside) is still the code the counters were taken on, else None."""
     import hashlib
+    import re
     path = os.path.join(ROOT, "fp8_w8a8_dynamic_amd", "csrc", "gemm.hip")
-    with open(path, "rb") as f:
-        sha = hashlib.sha1(f.read()).hexdigest()
+    with open(path) as f:
+        code = [re.sub(r"//.*", "", line).rstrip() for line in f]
+    sha = hashlib.sha1("\n".join(c for c in code if c).encode()).hexdigest()
     return GEMM_TRAFFIC["bytes_per_step"] if sha == GEMM_TRAFFIC["gemm_hip_sha1"] else None
 
 

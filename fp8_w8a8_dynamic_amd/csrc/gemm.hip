@@ -14,12 +14,12 @@
 //   * a workgroup of WGM x WGN waves owns a BM x BN output tile, each wave a
 //     (BM/WGM) x (BN/WGN) sub-tile kept in registers;
 //   * K advances 128 bytes per stage.  Stages are copied HBM/L2 -> LDS with
-//     buffer_load_dwordx4 ... lds (no trip through VGPRs) into two LDS
-//     buffers.  Every stage's fragments are read into registers early (the
-//     second half of a stage's reads overlaps the previous stage's MFMAs);
-//     once all waves hold them a barrier frees the buffer, which is refilled
-//     with stage k+2 while the MFMAs run, so two stages of copies are always
-//     in flight, with the copies spread between the MFMAs;
+//     buffer_load_dwordx4 ... lds (no trip through VGPRs) into NB (2 or 4)
+//     LDS buffers.  Every stage's fragments are read into registers early
+//     (the second half of a stage's reads overlaps the previous stage's
+//     MFMAs); once all waves hold them a barrier frees the buffer, which is
+//     refilled with stage k+NB while the MFMAs run, so NB stages of copies
+//     are always in flight, with the copies spread between the MFMAs;
 //   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
 //     ((row >> 1) & 7), so the 16 lanes that the LDS serves together read 16
 //     distinct bank groups; the swizzle is applied on the global side (each
@@ -28,7 +28,11 @@
 //     round-robin over the 8 XCDs, so consecutive logical tiles (which share
 //     operand rows in groups of 4 tile-rows) are given to one XCD and its L2;
 //   * the epilogue scales, rounds to bf16 and stages the tile in LDS, then
-//     writes whole row segments with 16-byte stores.
+//     writes whole row segments with 16-byte stores;
+//   * shapes with few output tiles (a few hundred tokens or less) split K
+//     over gridDim.y workgroups per tile; each split stores its raw float32
+//     sums and splitk_reduce_kernel adds the splits in order and applies the
+//     epilogue (deterministic, no cross-workgroup synchronization).
 // Rows beyond M or N read as zero (buffer descriptors bounded to the tile's
 // valid rows) and are never stored.  K must be a multiple of 128.
 #include <cstdlib>
