@@ -1,7 +1,9 @@
-// Decode-sized FP8_DYNAMIC Linear (1 <= M <= 16 tokens), bound by the HBM
-// bytes of the E4M3 weights (MOSS-VL-Realtime-FP8 article, section on why
-// the model is quantized: in streaming decode, memory bandwidth sets the
-// response speed, and 8-bit weights halve it against BF16).
+// Decode-sized FP8_DYNAMIC Linear (1 <= M <= 16 tokens for the K-class
+// kernel below, up to 64 for the token-group kernel at the end of the
+// file), bound by the HBM bytes of the E4M3 weights (MOSS-VL-Realtime-FP8
+// article, section on why the model is quantized: in streaming decode,
+// memory bandwidth sets the response speed, and 8-bit weights halve it
+// against BF16).
 //
 // MFMA layout.  Each v_mfma_f32_16x16x128_f8f6f4 multiplies a 16-row A
 // operand (weights) by a 16-column B operand (activation codes).  With MP =
