@@ -84,6 +84,17 @@ def _stream_ptr(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _scales(t: torch.Tensor, count: int, device, name: str) -> torch.Tensor:
+    """float32 scales: one per row, contiguous, on the operands' device (the
+    kernels read exactly `count` of them)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 tensor")
+    if t.device != device or t.numel() != count or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {count} "
+                         f"elements on {device}")
+    return t
+
+
 def _as_codes(t: torch.Tensor) -> torch.Tensor:
     """Accept E4M3 tensors as float8_e4m3fn or as raw uint8 bytes."""
     if t.dtype == torch.float8_e4m3fn:
@@ -183,8 +194,10 @@ def quantize_act_per_token(x: torch.Tensor):
 def _out(m, n, device, out):
     if out is None:
         return torch.empty((m, n), dtype=torch.bfloat16, device=device)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (m, n) or out.stride(1) != 1:
-        raise ValueError("out must be bfloat16 [M, N] with contiguous rows")
+    if (out.dtype != torch.bfloat16 or tuple(out.shape) != (m, n) or out.stride(1) != 1
+            or out.device != device):
+        raise ValueError("out must be bfloat16 [M, N] with contiguous rows, on the "
+                         "operands' device")
     return out
 
 
@@ -199,6 +212,10 @@ def fp8_linear(qx, x_scale, qw, w_scale, out=None, workspace=None):
     n, k2, ldw = _rows(qw, "qw")
     if k2 != k or ldq != k or ldw != k:
         raise ValueError("qx [M, K] and qw [N, K] must be contiguous with one K")
+    if qw.device != qx.device:
+        raise ValueError("qx and qw must be on one device")
+    x_scale = _scales(x_scale, m, qx.device, "x_scale")
+    w_scale = _scales(w_scale, n, qx.device, "w_scale")
     y = _out(m, n, qx.device, out)
     if m == 0 or n == 0:
         return y
@@ -223,6 +240,9 @@ def quant_linear(x, qw, w_scale, out=None, workspace=None):
     n, k2, ldw = _rows(qw, "qw")
     if k2 != k or ldw != k:
         raise ValueError("qw must be contiguous [N, K] with the K of x")
+    if qw.device != x.device:
+        raise ValueError("x and qw must be on one device")
+    w_scale = _scales(w_scale, n, x.device, "w_scale")
     y = _out(m, n, x.device, out)
     if m == 0 or n == 0:
         return y

@@ -303,6 +303,29 @@ def test_all_code_pairs_exact_decode_gemv(monkeypatch):
             _check_pairs(qx, sx, qw, sw, f"gemv k0={k0} tokens {i}")
 
 
+def test_binding_rejects_bad_scales_and_outputs():
+    """The binding checks what the kernels would read past: scale dtype,
+    length and contiguity, and the output's dtype, shape and device."""
+    qx = torch.zeros((4, 128), dtype=torch.uint8, device="cuda")
+    qw = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
+    sx = torch.ones(4, dtype=torch.float32, device="cuda")
+    sw = torch.ones(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        fq.fp8_linear(qx, sx.to(torch.bfloat16), qw, sw)
+    with pytest.raises(ValueError):
+        fq.fp8_linear(qx, sx[:3], qw, sw)
+    with pytest.raises(ValueError):
+        fq.fp8_linear(qx, sx, qw, torch.ones(32, device="cuda")[::2])
+    with pytest.raises(ValueError):
+        fq.fp8_linear(qx, sx, qw, sw, out=torch.empty((4, 8), dtype=torch.bfloat16, device="cuda"))
+    x = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fq.quant_linear(x, qw, torch.ones(15, device="cuda"))
+    y = fq.fp8_linear(qx, sx, qw, sw)
+    torch.cuda.synchronize()
+    assert y.shape == (4, 16) and not torch.any(y.float() != 0).item()
+
+
 def test_empty_calls():
     qw = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
     sw = torch.ones(16, dtype=torch.float32, device="cuda")
