@@ -21,11 +21,14 @@ Modules
 e4m3    256-entry decode table and the nearest-value encoder.
 quant   per-token activation and per-output-channel weight quantization.
 linear  fp64 matmul of decoded codes and the scale epilogue.
+norm    BF16 RMSNorm and the per-token quantization of its output (the
+        fusion ahead of the q/k/v and gate/up Linears).
 check   the pass criteria (bit-exact bytes, elementwise output tolerance).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, hand-derived golden values, brute force in exact rational
-arithmetic, and torch's independent CPU ``float8_e4m3fn`` cast).
+arithmetic, torch's independent CPU ``float8_e4m3fn`` cast, and torch's
+float64 ``rms_norm`` for the normalization).
 """
 
 from .e4m3 import (DECODE_TABLE, FINITE_MAX, decode, encode, encode_exact,

@@ -29,6 +29,9 @@ the model's Linear shapes and of the token counts those workloads produce):
 * c5: a 16384-token prefill; X Student-t with 3 degrees of freedom, 0.1 % of
   rows all +0 (row 0 always), 0.1 % of rows x1e4, 0.1 % of rows with 10 % of
   their entries set to +-(row amax).
+* norm: the RMSNorm input ahead of q/k/v and gate/up: residual-stream rows
+  X[m, k] ~ N(0,1) * g[k], g[k] = 10^U(-1, 1) (outlier channels, as c3), and
+  the norm weight gamma[k] ~ N(1, 0.25).
 """
 
 import math
@@ -51,7 +54,8 @@ LAYER_SHAPES = (
 )
 LINEAR_NAMES = tuple(s[0] for s in LAYER_SHAPES)
 N_SELF_ATTN_LAYERS = 36
-ROLE_X, ROLE_W = 0, 1
+ROLE_X, ROLE_W, ROLE_GAMMA = 0, 1, 2
+CFG_NORM = 6
 
 
 def rng_for(cfg: int, a: int, b: int, role: int) -> np.random.Generator:
@@ -165,3 +169,12 @@ def c5_x(m: int, k: int, seed_linear: int) -> np.ndarray:
 def c5_inputs(linear: int, m: int = 16384):
     _, n, k = LAYER_SHAPES[linear]
     return c5_x(m, k, linear), weight_bf16(5, 0, linear, n, k)
+
+
+def norm_inputs(m: int, k: int = HIDDEN, seed: int = 0):
+    """(x [m, k], gamma [k]) bf16 bits for the RMSNorm ahead of a Linear."""
+    rng = rng_for(CFG_NORM, seed, k, ROLE_X)
+    ch = np.power(np.float32(10.0), rng.uniform(-1.0, 1.0, k).astype(np.float32))
+    x = rng.standard_normal((m, k), dtype=np.float32) * ch[None, :]
+    gamma = rng_for(CFG_NORM, seed, k, ROLE_GAMMA).standard_normal(k, dtype=np.float32)
+    return bf16_from_f64(x), bf16_from_f64(np.float32(1.0) + np.float32(0.25) * gamma)
