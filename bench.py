@@ -18,6 +18,9 @@ Also measured and printed on the same JSON line:
   way the checkpoint's packed modules are (q|k|v as one 6144 x 4096 Linear,
   gate|up as one 24576 x 4096 Linear), so that each distinct input is
   quantized once and a layer is 4 calls instead of 7;
+* ``rmsnorm_quant``: the fused BF16 RMSNorm -> per-token quantization
+  kernel (the norm ahead of q/k/v and gate/up) at M = 4096 and M = 1, in GB/s
+  of algorithmic bytes against 8 TB/s, beside the unfused sequence;
 * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the same
   workload on the host's cores.
 
@@ -45,22 +48,29 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # HBM bytes of one prefill step's 7 GEMM dispatches, from rocprofv3
 # FETCH_SIZE (x2, calibrated) + WRITE_SIZE passes over this script (see
 # profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM code
-# whose SHA-1 (comments and blank lines stripped) is given here; reported as
-# null once the code differs.
-GEMM_TRAFFIC = {"gemm_hip_sha1": "e766db1e35120c34317c809469a94491d0471fc0",
+# (gemm.hip and device_common.h) whose SHA-1, comments and blank lines
+# stripped, is given here; reported as null once the code differs.
+GEMM_TRAFFIC = {"gemm_code_sha1": "pending",
                 "bytes_per_step": 1493156 * 1024}
 
 
-def gemm_traffic():
-    """GEMM_TRAFFIC's bytes if gemm.hip's code (comments and blank lines
-    aside) is still the code the counters were taken on, else None."""
+def gemm_code_sha1():
+    """SHA-1 of the GEMM's source (gemm.hip and the device helpers it
+    includes), comments and blank lines stripped."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "fp8_w8a8_dynamic_amd", "csrc", "gemm.hip")
-    with open(path) as f:
-        code = [re.sub(r"//.*", "", line).rstrip() for line in f]
-    sha = hashlib.sha1("\n".join(c for c in code if c).encode()).hexdigest()
-    return GEMM_TRAFFIC["bytes_per_step"] if sha == GEMM_TRAFFIC["gemm_hip_sha1"] else None
+    code = []
+    for name in ("gemm.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "fp8_w8a8_dynamic_amd", "csrc", name)) as f:
+            code += [re.sub(r"//.*", "", line).rstrip() for line in f]
+    return hashlib.sha1("\n".join(c for c in code if c).encode()).hexdigest()
+
+
+def gemm_traffic():
+    """GEMM_TRAFFIC's bytes if the GEMM's code is still the code the counters
+    were taken on, else None."""
+    ok = gemm_code_sha1() == GEMM_TRAFFIC["gemm_code_sha1"]
+    return GEMM_TRAFFIC["bytes_per_step"] if ok else None
 
 
 def log(*a):
@@ -332,6 +342,67 @@ def bench_stack(torch, fq, m, passes):
             "frac_of_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
 
 
+def graph_of(torch, fn, calls):
+    """A HIP graph of `calls` back-to-back fn() calls (outputs allocated at
+    capture and reused by every replay), so that replays time the kernels
+    without the host's per-call overhead."""
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        fn()                               # first use of this stream, uncaptured
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(calls):
+                fn()
+    torch.cuda.synchronize()
+    return g
+
+
+NORM_CALLS_PER_GRAPH = 20
+
+
+def bench_norm(torch, fq, reps, m=PREFILL_M, k=4096, eps=1e-6):
+    """The fused BF16 RMSNorm -> per-token quantization (the input norm of
+    q/k/v and of gate/up) on m tokens of hidden size k: GB/s of algorithmic
+    bytes (x and gamma in; codes, scales and, when stored, the bf16 norm
+    output out), with and without the bf16 output, and the unfused sequence
+    (torch's bf16 rms_norm, then this library's quantizer) for comparison.
+    Each figure is a HIP-graph replay of NORM_CALLS_PER_GRAPH calls, timed
+    with events on the replay stream."""
+    from workloads import norm_inputs
+    xb, gb = norm_inputs(m, k, seed=0)
+    x, g = to_dev(xb, torch), to_dev(gb, torch)
+    y = torch.empty_like(x)
+    base = 2 * m * k + 2 * k + m * k + 4 * m
+
+    def unfused():
+        n = torch.nn.functional.rms_norm(x, (k,), weight=g, eps=eps)
+        fq.quantize_act_per_token(n)
+
+    res = {}
+    for name, fn, nbytes in (
+            ("fused", lambda: fq.rmsnorm_quantize(x, g, eps), base),
+            ("fused_with_normed_output",
+             lambda: fq.rmsnorm_quantize(x, g, eps, out=y), base + 2 * m * k),
+            ("unfused_torch_rms_norm_then_quantize", unfused, base)):
+        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
+        for _ in range(max(10, reps // 10)):
+            gr.replay()
+        torch.cuda.synchronize()
+        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
+        t /= NORM_CALLS_PER_GRAPH
+        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
+                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes,
+                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
+                                          for ts in slices])}
+        del gr
+    del x, g, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s=16.0):
     """The oracle as it stands, timed on a sample of the prefill workload:
     all 7 Linears, a subset of tokens and of output channels (weights
@@ -437,6 +508,10 @@ def main():
         log("36-layer stack ...")
         stack = [bench_stack(torch, fq, m, max(5, args.steps // 20)) for m in (64, 256)]
         log(f"stack {stack}")
+    log("rmsnorm -> quant ...")
+    norm = bench_norm(torch, fq, args.steps)
+    norm_dec = bench_norm(torch, fq, args.steps, m=DECODE_M)
+    log(f"rmsnorm quant {norm}; M=1 {norm_dec['fused']['us']} us")
     cpu = None
     if not args.no_cpu:
         log("cpu oracle ...")
@@ -490,6 +565,14 @@ def main():
                       "FP8 weights in HBM, layer outputs chained): GB/s of algorithmic "
                       "bytes and TFLOP/s",
             "passes": stack}
+    f = norm["fused"]
+    out["rmsnorm_quant"] = {
+        "workload": f"BF16 RMSNorm fused with per-token FP8 quantization of its output, "
+                    f"M={PREFILL_M}, hidden 4096 (the input norm of q/k/v and gate/up)",
+        "roofline": {"bound": "hbm", "achieved": f["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": f["frac_of_hbm"], "traffic": None,
+                     "kernel": "rmsnorm_quant_kernel"},
+        "m4096": norm, "m1_us": norm_dec["fused"]["us"]}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -25,6 +25,9 @@ SIGNATURES = {
         (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fp8w8a8_quantize_act_per_token":
         (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fp8w8a8_rmsnorm_quantize":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, ctypes.c_float,
+                        _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_fp8_linear":
         (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -189,6 +192,39 @@ def quantize_act_per_token(x: torch.Tensor):
         x.data_ptr(), m, k, ld, qx.data_ptr(), sx.data_ptr(),
         _stream_ptr(x.device)), "quantize_act_per_token")
     return qx.view(torch.float8_e4m3fn), sx
+
+
+def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                     return_normed: bool = False, out: torch.Tensor = None):
+    """BF16 RMSNorm of X[M, K] with weight gamma[K], then the per-token
+    quantization of the norm's bf16 output.
+
+    Returns ``(qX float8_e4m3fn [M, K], x_scale float32 [M])``, plus the
+    bf16 norm output [M, K] as a third item when ``return_normed`` is set or
+    ``out`` (a bf16 [M, K] tensor with contiguous rows) is given."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
+        raise TypeError("x and gamma must be bfloat16")
+    m, k, ld = _rows(x, "x")
+    if (gamma.dim() != 1 or gamma.numel() != k or not gamma.is_contiguous()
+            or gamma.device != x.device):
+        raise ValueError(f"gamma must be a contiguous bf16 tensor of {k} elements "
+                         f"on {x.device}")
+    eps = float(eps)
+    qx = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((m,), dtype=torch.float32, device=x.device)
+    y = None
+    if return_normed or out is not None:
+        y = _out(m, k, x.device, out)
+    if m > 0:
+        _check(lib.fp8w8a8_rmsnorm_quantize(
+            x.data_ptr(), m, k, ld, gamma.data_ptr(), eps, qx.data_ptr(),
+            sx.data_ptr(), y.data_ptr() if y is not None else None,
+            y.stride(0) if y is not None else 0, _stream_ptr(x.device)),
+            "rmsnorm_quantize")
+    if y is None:
+        return qx.view(torch.float8_e4m3fn), sx
+    return qx.view(torch.float8_e4m3fn), sx, y
 
 
 def _out(m, n, device, out):

@@ -198,6 +198,38 @@ int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
+int fp8w8a8_rmsnorm_quantize(const uint16_t* x, int64_t m, int64_t k,
+                             int64_t ldx, const uint16_t* gamma, float eps,
+                             uint8_t* qx, float* x_scale, uint16_t* y,
+                             int64_t ldy, void* stream) {
+  if (!x || !gamma || !qx || !x_scale) return FP8W8A8_ERR_NULL;
+  if (m < 0 || m > kMaxDim || k < 8 || k > kMaxDim || k % 8 != 0 || ldx < k ||
+      ldx % 8 != 0 || (y && (ldy < k || ldy % 8 != 0)) ||
+      !(eps >= 0.0f && eps <= 3.4028235e38f))
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(qx) ||
+      (y && !aligned16(y)) || (reinterpret_cast<uintptr_t>(x_scale) & 3u) != 0)
+    return FP8W8A8_ERR_ALIGN;
+  const Range rx = span(x, m, k, ldx, 2);
+  const Range rg = span(gamma, 1, k, k, 2);
+  const Range rq = span(qx, m, k, k, 1);
+  const Range rs = span(x_scale, m, 1, 1, 4);
+  const Range ry = y ? span(y, m, k, ldy, 2) : Range{0, 0};
+  const Range outs[3] = {rq, rs, ry};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], rx) || overlap(outs[i], rg)) return FP8W8A8_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FP8W8A8_ERR_ALIAS;
+  }
+  if (m == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_rmsnorm_quant(
+      x, m, k, ldx, gamma, eps, qx, x_scale, y, ldy,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
   return layout_for(m, n, k, fused != 0, choose_path(m, n, k),

@@ -15,6 +15,15 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t k,
                              int64_t ld, uint8_t* q, float* scale,
                              hipStream_t stream);
 
+// RMSNorm of each row of x [rows, k] with weight gamma [k], then the
+// per-row quantization of the bf16 result: codes [rows, k] contiguous, one
+// float32 scale per row, and the bf16 result itself into y (row stride ldy)
+// when y != nullptr.
+hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t rows, int64_t k,
+                                int64_t ldx, const uint16_t* gamma, float eps,
+                                uint8_t* q, float* scale, uint16_t* y,
+                                int64_t ldy, hipStream_t stream);
+
 // Prefill GEMM: y[m,n] = bf16(sum_k qx[m,k] qw[n,k] * sx[m] * sw[n]).
 // The plan fixes the tile configuration and the number of K splits; with
 // splits > 1 the GEMM writes float32 partial sums [splits, m, n] to `part`

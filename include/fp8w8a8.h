@@ -91,6 +91,37 @@ int fp8w8a8_quantize_act_per_token(const uint16_t* x, int64_t m, int64_t k,
                                    void* stream);
 
 /*
+ * BF16 RMSNorm fused with the per-token quantization of its output: the norm
+ * that precedes the q/k/v and gate/up Linears stays BF16 while those Linears
+ * are FP8_DYNAMIC (MOSS-VL-Realtime-FP8 article, component / precision map),
+ * and the norm's output row is the row whose amax the per-token scale needs.
+ *   x        bf16 [m, k], row stride ldx >= k, ldx % 8 == 0     (input)
+ *   gamma    bf16 [k], the norm weight                          (input)
+ *   eps      float32, finite, >= 0                              (input)
+ *   qx       E4M3 [m, k], contiguous                            (output)
+ *   x_scale  float32 [m]                                        (output)
+ *   y        bf16 [m, k], row stride ldy >= k, ldy % 8 == 0, the norm's
+ *            output, or NULL to skip storing it (ldy then ignored) (output)
+ * Per row (readings where the pages give no formula):
+ *   t = bf16( x / sqrt(mean_k(x^2) + eps) )     evaluated in float32 with a
+ *       power-of-two prescaling of the row (no overflow or underflow for
+ *       any finite bf16 row) and a float64 square root, so t may differ by
+ *       one bf16 step from the exactly rounded value where the exact value
+ *       lies within float32 rounding error of a bf16 rounding boundary;
+ *   y = bf16( gamma * t )                        (rounded once, exactly);
+ *   qx, x_scale = the per-token quantization of y, bit-identical to
+ *       fp8w8a8_quantize_act_per_token applied to y.
+ * qx and x_scale feed fp8w8a8_fp8_linear directly.
+ * Rules: m >= 0, k >= 8, k % 8 == 0; x, gamma, qx, y 16-byte aligned,
+ * x_scale 4-byte aligned; gamma * t must stay finite.  Outputs must not
+ * overlap the inputs or each other.
+ */
+int fp8w8a8_rmsnorm_quantize(const uint16_t* x, int64_t m, int64_t k,
+                             int64_t ldx, const uint16_t* gamma, float eps,
+                             uint8_t* qx, float* x_scale, uint16_t* y,
+                             int64_t ldy, void* stream);
+
+/*
  * The W8A8 Linear on already-quantized operands ("the quantized kernels" of
  * README "FP8-Dynamic"):
  *   y[m,n] = bf16_rne( (sum_k dec(qx[m,k]) * dec(qw[n,k])) * x_scale[m]

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 8
+    assert len(names) == 9
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -64,6 +64,39 @@ def test_quant_validation(lib, fn):
     assert _q(lib, fn, src, 4, 64, 64, q, q + 16) == EALIAS    # s inside q
     # empty is a valid no-op and needs no device
     assert _q(lib, fn, src, 0, 64, 64, q, s) == OK
+
+
+def _norm(lib, x=A, m=4, k=64, ldx=64, g=2 * A, eps=1e-6, q=64 * A, s=128 * A,
+          y=256 * A, ldy=64):
+    return lib.fp8w8a8_rmsnorm_quantize(x, m, k, ldx, g, eps, q, s, y, ldy, None)
+
+
+def test_rmsnorm_quantize_validation(lib):
+    assert _norm(lib, x=None) == ENULL
+    assert _norm(lib, g=None) == ENULL
+    assert _norm(lib, q=None) == ENULL
+    assert _norm(lib, s=None) == ENULL
+    assert _norm(lib, m=-1) == ESHAPE
+    assert _norm(lib, k=0) == ESHAPE
+    assert _norm(lib, k=60, ldx=64, ldy=64) == ESHAPE      # k % 8
+    assert _norm(lib, ldx=32) == ESHAPE                     # ldx < k
+    assert _norm(lib, ldx=68) == ESHAPE                     # ldx % 8
+    assert _norm(lib, ldy=32) == ESHAPE                     # ldy < k
+    assert _norm(lib, ldy=72 + 4) == ESHAPE                 # ldy % 8
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert _norm(lib, eps=eps) == ESHAPE
+    assert _norm(lib, x=A + 8) == EALIGN
+    assert _norm(lib, g=2 * A + 8) == EALIGN
+    assert _norm(lib, q=64 * A + 4) == EALIGN
+    assert _norm(lib, y=256 * A + 2) == EALIGN
+    assert _norm(lib, s=128 * A + 2) == EALIGN
+    assert _norm(lib, q=A + 64) == EALIAS                   # codes inside x
+    assert _norm(lib, s=2 * A) == EALIAS                    # scales over gamma
+    assert _norm(lib, y=64 * A + 128) == EALIAS             # y inside codes
+    assert _norm(lib, s=256 * A + 16) == EALIAS             # scales inside y
+    # empty is a valid no-op and needs no device, with or without y
+    assert _norm(lib, m=0) == OK
+    assert _norm(lib, m=0, y=None, ldy=0) == OK
 
 
 def _lin(lib, qx=A, sx=2 * A, qw=4 * A, sw=8 * A, m=32, n=64, k=256,
