@@ -23,12 +23,15 @@ quant   per-token activation and per-output-channel weight quantization.
 linear  fp64 matmul of decoded codes and the scale epilogue.
 norm    BF16 RMSNorm and the per-token quantization of its output (the
         fusion ahead of the q/k/v and gate/up Linears).
+swiglu  the SiLU-gated activation between gate/up and down and the
+        per-token quantization of its output (down_proj's input).
 check   the pass criteria (bit-exact bytes, elementwise output tolerance).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (closed forms, hand-derived golden values, brute force in exact rational
 arithmetic, torch's independent CPU ``float8_e4m3fn`` cast, and torch's
-float64 ``rms_norm`` for the normalization).
+float64 ``rms_norm`` for the normalization, scipy's ``expit`` and
+50-digit decimal arithmetic for the activation).
 """
 
 from .e4m3 import (DECODE_TABLE, FINITE_MAX, decode, encode, encode_exact,
