@@ -21,6 +21,8 @@ Also measured and printed on the same JSON line:
 * ``rmsnorm_quant``: the fused BF16 RMSNorm -> per-token quantization
   kernel (the norm ahead of q/k/v and gate/up) at M = 4096 and M = 1, in GB/s
   of algorithmic bytes against 8 TB/s, beside the unfused sequence;
+* ``swiglu_quant``: the fused SiLU-gated activation -> per-token quantization
+  kernel (down_proj's input) at M = 4096 and M = 1, likewise;
 * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the same
   workload on the host's cores.
 
@@ -403,6 +405,47 @@ def bench_norm(torch, fq, reps, m=PREFILL_M, k=4096, eps=1e-6):
     return res
 
 
+def bench_swiglu(torch, fq, reps, m=PREFILL_M, n=12288):
+    """The fused SiLU-gated activation -> per-token quantization (down_proj's
+    input) on m tokens of width n, reading the two halves of a packed
+    gate_up output [m, 2n]: GB/s of algorithmic bytes (gate and up in; codes
+    and scales out; plus h when stored), beside the unfused sequence (torch's
+    bf16 silu and multiply, then this library's quantizer).  HIP-graph
+    replays, as for the norm."""
+    from workloads import swiglu_inputs
+    gb, ub = swiglu_inputs(m, n, seed=0)
+    gu = to_dev(np.concatenate([gb, ub], axis=1), torch)
+    g, u = gu[:, :n], gu[:, n:]
+    h = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    base = 4 * m * n + m * n + 4 * m
+
+    def unfused():
+        a = torch.nn.functional.silu(g) * u
+        fq.quantize_act_per_token(a)
+
+    res = {}
+    for name, fn, nbytes in (
+            ("fused", lambda: fq.swiglu_quantize(g, u), base),
+            ("fused_with_h_output", lambda: fq.swiglu_quantize(g, u, out=h),
+             base + 2 * m * n),
+            ("unfused_torch_silu_mul_then_quantize", unfused, base)):
+        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
+        for _ in range(max(10, reps // 10)):
+            gr.replay()
+        torch.cuda.synchronize()
+        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
+        t /= NORM_CALLS_PER_GRAPH
+        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
+                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes,
+                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
+                                          for ts in slices])}
+        del gr
+    del gu, g, u, h
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s=16.0):
     """The oracle as it stands, timed on a sample of the prefill workload:
     all 7 Linears, a subset of tokens and of output channels (weights
@@ -512,6 +555,10 @@ def main():
     norm = bench_norm(torch, fq, args.steps)
     norm_dec = bench_norm(torch, fq, args.steps, m=DECODE_M)
     log(f"rmsnorm quant {norm}; M=1 {norm_dec['fused']['us']} us")
+    log("swiglu -> quant ...")
+    swi = bench_swiglu(torch, fq, args.steps)
+    swi_dec = bench_swiglu(torch, fq, args.steps, m=DECODE_M)
+    log(f"swiglu quant {swi}; M=1 {swi_dec['fused']['us']} us")
     cpu = None
     if not args.no_cpu:
         log("cpu oracle ...")
@@ -573,6 +620,15 @@ def main():
                      "unit": "GB/s", "frac": f["frac_of_hbm"], "traffic": None,
                      "kernel": "rmsnorm_quant_kernel"},
         "m4096": norm, "m1_us": norm_dec["fused"]["us"]}
+    f = swi["fused"]
+    out["swiglu_quant"] = {
+        "workload": f"SiLU-gated activation fused with per-token FP8 quantization of its "
+                    f"output, M={PREFILL_M}, width 12288 (gate/up halves of the packed "
+                    f"gate_up output -> down_proj's input)",
+        "roofline": {"bound": "hbm", "achieved": f["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": f["frac_of_hbm"], "traffic": None,
+                     "kernel": "swiglu_quant_kernel"},
+        "m4096": swi, "m1_us": swi_dec["fused"]["us"]}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

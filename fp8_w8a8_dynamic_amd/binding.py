@@ -28,6 +28,9 @@ SIGNATURES = {
     "fp8w8a8_rmsnorm_quantize":
         (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, ctypes.c_float,
                         _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "fp8w8a8_swiglu_quantize":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp,
+                        _c_vp, _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_fp8_linear":
         (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -225,6 +228,37 @@ def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float,
     if y is None:
         return qx.view(torch.float8_e4m3fn), sx
     return qx.view(torch.float8_e4m3fn), sx, y
+
+
+def swiglu_quantize(gate: torch.Tensor, up: torch.Tensor,
+                    return_h: bool = False, out: torch.Tensor = None):
+    """h = bf16(bf16(silu(gate)) * up) over [M, N], then the per-token
+    quantization of h (the input of down_proj).  gate and up may be strided
+    views, e.g. the two halves of gate_up_proj's output.
+
+    Returns ``(qH float8_e4m3fn [M, N], h_scale float32 [M])``, plus h (bf16
+    [M, N]) as a third item when ``return_h`` is set or ``out`` is given."""
+    lib = load_library()
+    if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
+        raise TypeError("gate and up must be bfloat16")
+    m, n, ldg = _rows(gate, "gate")
+    m2, n2, ldu = _rows(up, "up")
+    if (m2, n2) != (m, n) or up.device != gate.device:
+        raise ValueError("gate and up must have one shape and one device")
+    qh = torch.empty((m, n), dtype=torch.uint8, device=gate.device)
+    sh = torch.empty((m,), dtype=torch.float32, device=gate.device)
+    h = None
+    if return_h or out is not None:
+        h = _out(m, n, gate.device, out)
+    if m > 0:
+        _check(lib.fp8w8a8_swiglu_quantize(
+            gate.data_ptr(), ldg, up.data_ptr(), ldu, m, n, qh.data_ptr(),
+            sh.data_ptr(), h.data_ptr() if h is not None else None,
+            h.stride(0) if h is not None else 0, _stream_ptr(gate.device)),
+            "swiglu_quantize")
+    if h is None:
+        return qh.view(torch.float8_e4m3fn), sh
+    return qh.view(torch.float8_e4m3fn), sh, h
 
 
 def _out(m, n, device, out):

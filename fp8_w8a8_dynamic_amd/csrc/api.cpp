@@ -230,6 +230,35 @@ int fp8w8a8_rmsnorm_quantize(const uint16_t* x, int64_t m, int64_t k,
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
+int fp8w8a8_swiglu_quantize(const uint16_t* gate, int64_t ldg,
+                            const uint16_t* up, int64_t ldu, int64_t m,
+                            int64_t n, uint8_t* qh, float* h_scale,
+                            uint16_t* h, int64_t ldh, void* stream) {
+  if (!gate || !up || !qh || !h_scale) return FP8W8A8_ERR_NULL;
+  if (m < 0 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 || ldg < n ||
+      ldg % 8 != 0 || ldu < n || ldu % 8 != 0 || (h && (ldh < n || ldh % 8 != 0)))
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(qh) || (h && !aligned16(h)) ||
+      (reinterpret_cast<uintptr_t>(h_scale) & 3u) != 0)
+    return FP8W8A8_ERR_ALIGN;
+  const Range rg = span(gate, m, n, ldg, 2);
+  const Range ru = span(up, m, n, ldu, 2);
+  const Range outs[3] = {span(qh, m, n, n, 1), span(h_scale, m, 1, 1, 4),
+                         h ? span(h, m, n, ldh, 2) : Range{0, 0}};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], rg) || overlap(outs[i], ru)) return FP8W8A8_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FP8W8A8_ERR_ALIAS;
+  }
+  if (m == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_swiglu_quant(gate, ldg, up, ldu, m, n, qh,
+                                              h_scale, h, ldh,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
   return layout_for(m, n, k, fused != 0, choose_path(m, n, k),

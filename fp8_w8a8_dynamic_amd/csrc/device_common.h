@@ -122,27 +122,30 @@ __device__ __forceinline__ uint32_t sign_bytes(uint32_t w0, uint32_t w1) {
 }
 
 // Quantize 8 bf16 (one 16-byte vector) of a row with that row's divisor ->
-// 8 codes.  The fast path divides magnitudes and inserts the sign bits
-// afterwards (so -0 and negative values whose quotient underflows keep
-// their sign, as the IEEE quotient's sign does).
-__device__ __forceinline__ uint2 quantize8(uint4 v, const RowDivisor& d) {
+// 8 codes.  Fast path (d.fast): magnitudes are divided and the sign bits
+// inserted afterwards (so -0 and negative values whose quotient underflows
+// keep their sign, as the IEEE quotient's sign does).
+__device__ __forceinline__ uint2 quantize8_fast(uint4 v, const RowDivisor& d) {
   uint2 out;
-  if (d.fast) {
-    out.x = encode4_mag(quotient_mag(__builtin_fabsf(bf16_lo(v.x)), d),
-                        quotient_mag(__builtin_fabsf(bf16_hi(v.x)), d),
-                        quotient_mag(__builtin_fabsf(bf16_lo(v.y)), d),
-                        quotient_mag(__builtin_fabsf(bf16_hi(v.y)), d)) |
-            sign_bytes(v.x, v.y);
-    out.y = encode4_mag(quotient_mag(__builtin_fabsf(bf16_lo(v.z)), d),
-                        quotient_mag(__builtin_fabsf(bf16_hi(v.z)), d),
-                        quotient_mag(__builtin_fabsf(bf16_lo(v.w)), d),
-                        quotient_mag(__builtin_fabsf(bf16_hi(v.w)), d)) |
-            sign_bytes(v.z, v.w);
-    return out;
-  }
+  out.x = encode4_mag(quotient_mag(__builtin_fabsf(bf16_lo(v.x)), d),
+                      quotient_mag(__builtin_fabsf(bf16_hi(v.x)), d),
+                      quotient_mag(__builtin_fabsf(bf16_lo(v.y)), d),
+                      quotient_mag(__builtin_fabsf(bf16_hi(v.y)), d)) |
+          sign_bytes(v.x, v.y);
+  out.y = encode4_mag(quotient_mag(__builtin_fabsf(bf16_lo(v.z)), d),
+                      quotient_mag(__builtin_fabsf(bf16_hi(v.z)), d),
+                      quotient_mag(__builtin_fabsf(bf16_lo(v.w)), d),
+                      quotient_mag(__builtin_fabsf(bf16_hi(v.w)), d)) |
+          sign_bytes(v.z, v.w);
+  return out;
+}
+
+// General path: the IEEE float32 quotient, clamped, for any scale; a zero
+// scale (amax == 0: every element is +-0) gives the sign bits as codes.
+__device__ __forceinline__ uint2 quantize8_general(uint4 v, const RowDivisor& d) {
+  uint2 out;
   const float scale = d.s;
   if (scale == 0.0f) {
-    // amax == 0: every element is +-0; the codes are the sign bits.
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t r[2];
 #pragma unroll
@@ -160,6 +163,25 @@ __device__ __forceinline__ uint2 quantize8(uint4 v, const RowDivisor& d) {
   out.y = encode4(quotient(bf16_lo(v.z), scale), quotient(bf16_hi(v.z), scale),
                   quotient(bf16_lo(v.w), scale), quotient(bf16_hi(v.w), scale));
   return out;
+}
+
+__device__ __forceinline__ uint2 quantize8(uint4 v, const RowDivisor& d) {
+  return d.fast ? quantize8_fast(v, d) : quantize8_general(v, d);
+}
+
+// A row's NV vectors (8 bf16 each) -> NV x 8 codes, with the fast/general
+// choice made once for the row.
+template <int NV>
+__device__ __forceinline__ void quantize_row(const uint4 (&v)[NV],
+                                             const RowDivisor& d,
+                                             uint2 (&out)[NV]) {
+  if (d.fast) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) out[i] = quantize8_fast(v[i], d);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) out[i] = quantize8_general(v[i], d);
+  }
 }
 
 // Max over the 64 lanes of a wave (result valid in every lane), with DPP
@@ -219,6 +241,38 @@ __device__ __forceinline__ v4i_t make_rsrc(const uint8_t* base, uint32_t bytes) 
   r[2] = static_cast<int>(bytes);
   r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
   return r;
+}
+
+// Register loads and stores through a buffer resource covering one row:
+// the range check is the descriptor's, so a row's ragged tail needs no
+// branches (loads past the end return 0, stores past the end are dropped,
+// neither touches memory), and straight-line code keeps the compiler's
+// wait counts exact.  `base` must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base,
+                                                          uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u32_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r,
+                                            uint32_t off) {
+  const v4u32_t t = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void buf_store8(uint2 v, __amdgpu_buffer_rsrc_t r,
+                                           uint32_t off) {
+  const v2u32_t t = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(t, r, static_cast<int>(off), 0, 0);
+}
+
+__device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r,
+                                            uint32_t off) {
+  const v4u32_t t = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(t, r, static_cast<int>(off), 0, 0);
 }
 
 // One 16-byte-per-lane copy global -> LDS: the wave's 64 x 16 bytes land

@@ -24,6 +24,14 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t rows, int64_t k,
                                 uint8_t* q, float* scale, uint16_t* y,
                                 int64_t ldy, hipStream_t stream);
 
+// h = bf16(bf16(silu(gate)) * up) over [rows, n], then the per-row
+// quantization of h: codes [rows, n] contiguous, one float32 scale per row,
+// and h itself into `h` (row stride ldh) when h != nullptr.
+hipError_t launch_swiglu_quant(const uint16_t* gate, int64_t ldg,
+                               const uint16_t* up, int64_t ldu, int64_t rows,
+                               int64_t n, uint8_t* q, float* scale,
+                               uint16_t* h, int64_t ldh, hipStream_t stream);
+
 // Prefill GEMM: y[m,n] = bf16(sum_k qx[m,k] qw[n,k] * sx[m] * sw[n]).
 // The plan fixes the tile configuration and the number of K splits; with
 // splits > 1 the GEMM writes float32 partial sums [splits, m, n] to `part`

@@ -11,7 +11,8 @@
 // codes and the scale are written once, and the bf16 norm output is written
 // only when the caller asks for it.
 //
-// One wavefront owns one row of k elements:
+// One wavefront owns one row of k elements (buffer loads and stores, whose
+// descriptors clip the ragged tail; padding lanes hold zeros throughout):
 //   1. ss = sum x^2 in float32 (per-lane sums, then a DPP tree); a row whose
 //      sum leaves [2^-60, 2^127] (squares that underflow or overflow float32)
 //      takes a rare path: p = 2^-e, e the (clamped) exponent of the row's
@@ -169,23 +170,17 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ gamma, float eps, uint8_t* __restrict__ q,
     float* __restrict__ scale, uint16_t* __restrict__ y, int64_t ldy) {
   const int lane = threadIdx.x & 63;
-  const int64_t row =
-      static_cast<int64_t>(blockIdx.x) * kNormRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kNormRowsPerBlock +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
-  const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx);
-  const uint4* gsrc = reinterpret_cast<const uint4*>(gamma);
-  const int nvec = k >> 3;  // 8 bf16 per 16-byte vector
+  const uint32_t row_bytes = static_cast<uint32_t>(k) * 2u;
+  const auto src = row_rsrc(x + row * ldx, row_bytes);
+  const auto gsrc = row_rsrc(gamma, row_bytes);
   uint4 v[NV], g[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * 64 + lane;
-    v[i] = idx < nvec ? src[idx] : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (i * 64 + lane) * 16u);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * 64 + lane;
-    g[i] = idx < nvec ? gsrc[idx] : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < NV; ++i) g[i] = buf_load16(gsrc, (i * 64 + lane) * 16u);
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) ss = sumsq8(v[i], ss);
@@ -211,20 +206,15 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     for (int i = 0; i < NV; ++i) v[i] = norm8<false>(v[i], g[i], nf.p, nf.f, am);
   }
   const float s = scale_from_products(am);
-  const RowDivisor d = make_divisor(s);
-  uint2* dst = reinterpret_cast<uint2*>(q + row * static_cast<int64_t>(k));
+  uint2 codes[NV];
+  quantize_row<NV>(v, make_divisor(s), codes);
+  const auto dst = row_rsrc(q + row * static_cast<int64_t>(k), static_cast<uint32_t>(k));
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * 64 + lane;
-    if (idx < nvec) dst[idx] = quantize8(v[i], d);
-  }
+  for (int i = 0; i < NV; ++i) buf_store8(codes[i], dst, (i * 64 + lane) * 8u);
   if (y != nullptr) {
-    uint4* ydst = reinterpret_cast<uint4*>(y + row * ldy);
+    const auto ydst = row_rsrc(y + row * ldy, row_bytes);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int idx = i * 64 + lane;
-      if (idx < nvec) ydst[idx] = v[i];
-    }
+    for (int i = 0; i < NV; ++i) buf_store16(v[i], ydst, (i * 64 + lane) * 16u);
   }
   if (lane == 0) scale[row] = s;
 }

@@ -3,7 +3,7 @@
 // "FP8-Dynamic" recipe; the same arithmetic on rows of X[M,K] or W[N,K]).
 //
 // One wavefront owns one row.  The row is read from HBM once, with 16-byte
-// loads, into registers; the magnitude maximum is reduced on the bf16 bit
+// buffer loads (the descriptor clips the ragged tail), into registers; the magnitude maximum is reduced on the bf16 bit
 // patterns (integer order equals value order for non-negative floats) and
 // then across the wave; the scale amax/448 is one IEEE division; each
 // element is divided by the scale (the IEEE quotient, with the reciprocal
@@ -25,18 +25,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int k, int64_t ld,
     uint8_t* __restrict__ q, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int64_t row =
-      static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
-  const uint4* src = reinterpret_cast<const uint4*>(x + row * ld);
-  const int nvec = k >> 3;  // 8 bf16 per 16-byte vector
+  const auto src = row_rsrc(x + row * ld, static_cast<uint32_t>(k) * 2u);
   uint4 v[NV];
-  uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * 64 + lane;
-    v[i] = idx < nvec ? src[idx] : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (i * 64 + lane) * 16u);
+  uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     m = pk_max_u16(m, bf16x2_abs_bits(v[i].x));
@@ -46,13 +42,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
   const uint32_t mrow = wave_max_u32(max(m & 0xffffu, m >> 16));
   const float s = row_scale(__uint_as_float(mrow << 16));
-  const RowDivisor d = make_divisor(s);
-  uint2* dst = reinterpret_cast<uint2*>(q + row * static_cast<int64_t>(k));
+  uint2 codes[NV];
+  quantize_row<NV>(v, make_divisor(s), codes);
+  const auto dst = row_rsrc(q + row * static_cast<int64_t>(k), static_cast<uint32_t>(k));
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * 64 + lane;
-    if (idx < nvec) dst[idx] = quantize8(v[i], d);
-  }
+  for (int i = 0; i < NV; ++i) buf_store8(codes[i], dst, (i * 64 + lane) * 8u);
   if (lane == 0) scale[row] = s;
 }
 

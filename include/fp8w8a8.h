@@ -122,6 +122,38 @@ int fp8w8a8_rmsnorm_quantize(const uint16_t* x, int64_t m, int64_t k,
                              int64_t ldy, void* stream);
 
 /*
+ * The MLP activation fused with the per-token quantization of its output,
+ * the input of down_proj.  gate_proj/up_proj (packed as gate_up_proj) and
+ * down_proj are FP8_DYNAMIC Linears (MOSS-VL quantization README,
+ * "FP8-Dynamic" and its packed-module mapping); the activation between
+ * them stays BF16 (MOSS-VL-Realtime-FP8 article, component / precision map).
+ *   gate     bf16 [m, n], row stride ldg >= n, ldg % 8 == 0       (input)
+ *   up       bf16 [m, n], row stride ldu >= n, ldu % 8 == 0       (input)
+ *            (for gate_up_proj's output Y [m, 2n]: gate = Y, up = Y + n,
+ *            ldg = ldu = 2n)
+ *   qh       E4M3 [m, n], contiguous                               (output)
+ *   h_scale  float32 [m]                                           (output)
+ *   h        bf16 [m, n], row stride ldh >= n, ldh % 8 == 0, the
+ *            activation itself, or NULL to skip storing it       (output)
+ * Per element (the pages do not name the activation; the gated SiLU is the
+ * reading):
+ *   s = bf16(silu(g)), silu(g) = g / (1 + exp(-g)), evaluated in float32
+ *       (relative error below 2^-16 for every finite g whose result is a
+ *       normal float), so s may differ by one bf16 step from the exactly
+ *       rounded value where the exact value lies that close to a bf16
+ *       rounding boundary;
+ *   h = bf16(s * u)                              (rounded once, exactly);
+ *   qh, h_scale = the per-token quantization of h, bit-identical to
+ *       fp8w8a8_quantize_act_per_token applied to h.
+ * Rules: m >= 0, n >= 8, n % 8 == 0; gate, up, qh, h 16-byte aligned,
+ * h_scale 4-byte aligned; outputs must not overlap the inputs or each other.
+ */
+int fp8w8a8_swiglu_quantize(const uint16_t* gate, int64_t ldg,
+                            const uint16_t* up, int64_t ldu, int64_t m,
+                            int64_t n, uint8_t* qh, float* h_scale,
+                            uint16_t* h, int64_t ldh, void* stream);
+
+/*
  * The W8A8 Linear on already-quantized operands ("the quantized kernels" of
  * README "FP8-Dynamic"):
  *   y[m,n] = bf16_rne( (sum_k dec(qx[m,k]) * dec(qw[n,k])) * x_scale[m]

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -97,6 +97,34 @@ def test_rmsnorm_quantize_validation(lib):
     # empty is a valid no-op and needs no device, with or without y
     assert _norm(lib, m=0) == OK
     assert _norm(lib, m=0, y=None, ldy=0) == OK
+
+
+def _swi(lib, g=A, ldg=128, u=A + 128, ldu=128, m=4, n=64, q=64 * A, s=128 * A,
+         h=256 * A, ldh=64):
+    return lib.fp8w8a8_swiglu_quantize(g, ldg, u, ldu, m, n, q, s, h, ldh, None)
+
+
+def test_swiglu_quantize_validation(lib):
+    assert _swi(lib, g=None) == ENULL
+    assert _swi(lib, u=None) == ENULL
+    assert _swi(lib, q=None) == ENULL
+    assert _swi(lib, s=None) == ENULL
+    assert _swi(lib, m=-1) == ESHAPE
+    assert _swi(lib, n=0) == ESHAPE
+    assert _swi(lib, n=60, ldh=64) == ESHAPE                 # n % 8
+    assert _swi(lib, ldg=32) == ESHAPE
+    assert _swi(lib, ldu=132) == ESHAPE
+    assert _swi(lib, ldh=32) == ESHAPE
+    assert _swi(lib, g=A + 8) == EALIGN
+    assert _swi(lib, u=A + 136) == EALIGN
+    assert _swi(lib, q=64 * A + 8) == EALIGN
+    assert _swi(lib, h=256 * A + 4) == EALIGN
+    assert _swi(lib, s=128 * A + 1) == EALIGN
+    assert _swi(lib, q=A + 256) == EALIAS                    # codes over gate/up rows
+    assert _swi(lib, h=64 * A + 64) == EALIAS                # h over codes
+    assert _swi(lib, s=256 * A) == EALIAS                    # scales over h
+    assert _swi(lib, m=0) == OK
+    assert _swi(lib, m=0, h=None, ldh=0) == OK
 
 
 def _lin(lib, qx=A, sx=2 * A, qw=4 * A, sw=8 * A, m=32, n=64, k=256,

@@ -29,6 +29,9 @@ the model's Linear shapes and of the token counts those workloads produce):
 * c5: a 16384-token prefill; X Student-t with 3 degrees of freedom, 0.1 % of
   rows all +0 (row 0 always), 0.1 % of rows x1e4, 0.1 % of rows with 10 % of
   their entries set to +-(row amax).
+* swiglu: gate_up_proj's output ahead of the activation: gate ~ 1.5 N(0,1)
+  with 1 % of entries x10, up ~ 1.5 N(0,1) (the spread of a K = 4096 dot
+  product of c3-like activations with N(0, 0.02) weights).
 * norm: the RMSNorm input ahead of q/k/v and gate/up: residual-stream rows
   X[m, k] ~ N(0,1) * g[k], g[k] = 10^U(-1, 1) (outlier channels, as c3), and
   the norm weight gamma[k] ~ N(1, 0.25).
@@ -56,6 +59,7 @@ LINEAR_NAMES = tuple(s[0] for s in LAYER_SHAPES)
 N_SELF_ATTN_LAYERS = 36
 ROLE_X, ROLE_W, ROLE_GAMMA = 0, 1, 2
 CFG_NORM = 6
+CFG_SWIGLU = 7
 
 
 def rng_for(cfg: int, a: int, b: int, role: int) -> np.random.Generator:
@@ -178,3 +182,13 @@ def norm_inputs(m: int, k: int = HIDDEN, seed: int = 0):
     x = rng.standard_normal((m, k), dtype=np.float32) * ch[None, :]
     gamma = rng_for(CFG_NORM, seed, k, ROLE_GAMMA).standard_normal(k, dtype=np.float32)
     return bf16_from_f64(x), bf16_from_f64(np.float32(1.0) + np.float32(0.25) * gamma)
+
+
+def swiglu_inputs(m: int, n: int, seed: int = 0):
+    """(gate [m, n], up [m, n]) bf16 bits: the two halves of gate_up_proj's
+    output for m tokens."""
+    rng = rng_for(CFG_SWIGLU, seed, n, ROLE_X)
+    g = rng.standard_normal((m, n), dtype=np.float32) * np.float32(1.5)
+    g[rng.random((m, n), dtype=np.float32) < np.float32(0.01)] *= np.float32(10.0)
+    u = rng_for(CFG_SWIGLU, seed, n, ROLE_W).standard_normal((m, n), dtype=np.float32)
+    return bf16_from_f64(g), bf16_from_f64(u * np.float32(1.5))
