@@ -170,17 +170,17 @@ __device__ __forceinline__ uint2 quantize8(uint4 v, const RowDivisor& d) {
 }
 
 // A row's NV vectors (8 bf16 each) -> NV x 8 codes, with the fast/general
-// choice made once for the row.
-template <int NV>
+// choice made once for the row; store(i, codes) receives each vector's
+// codes as soon as they are formed (keeps few of them live at once).
+template <int NV, typename Store>
 __device__ __forceinline__ void quantize_row(const uint4 (&v)[NV],
-                                             const RowDivisor& d,
-                                             uint2 (&out)[NV]) {
+                                             const RowDivisor& d, Store store) {
   if (d.fast) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) out[i] = quantize8_fast(v[i], d);
+    for (int i = 0; i < NV; ++i) store(i, quantize8_fast(v[i], d));
   } else {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) out[i] = quantize8_general(v[i], d);
+    for (int i = 0; i < NV; ++i) store(i, quantize8_general(v[i], d));
   }
 }
 

@@ -13,7 +13,8 @@
 //
 // One wavefront owns one row of k elements (buffer loads and stores, whose
 // descriptors clip the ragged tail; padding lanes hold zeros throughout):
-//   1. ss = sum x^2 in float32 (per-lane sums, then a DPP tree); a row whose
+//   1. ss = sum x^2 in float32 (per-lane v_dot2 sums of bf16 pairs, then a
+//      DPP tree, then across the row's waves in LDS); a row whose
 //      sum leaves [2^-60, 2^127] (squares that underflow or overflow float32)
 //      takes a rare path: p = 2^-e, e the (clamped) exponent of the row's
 //      amax, every x p is exact and below 2 in magnitude, and ss is taken
@@ -33,6 +34,8 @@
 // HBM traffic per row: 2k bytes in, k bytes of codes + 4 bytes of scale out
 // (+ 2k bytes if y is stored); gamma (2k bytes, shared by all rows) is read
 // from L2.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -76,15 +79,21 @@ __device__ __forceinline__ float pow2_for_amax(uint32_t amax_bits) {
   return __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
 }
 
+typedef __bf16 bf16x2_dot_t __attribute__((ext_vector_type(2)));
+
+// Sum of squares of 8 packed bf16 with v_dot2c_f32_bf16 (two exact bf16
+// products added to the float32 accumulator per instruction).  Subnormal
+// bf16 inputs may count as zero here; their squares are below 2^-252, which
+// is negligible next to any sum this path keeps (at least 2^-60; smaller
+// sums take the rare, exactly scaled path).
 __device__ __forceinline__ float sumsq8(uint4 v, float s) {
-  s = __builtin_fmaf(bf16_lo(v.x), bf16_lo(v.x), s);
-  s = __builtin_fmaf(bf16_hi(v.x), bf16_hi(v.x), s);
-  s = __builtin_fmaf(bf16_lo(v.y), bf16_lo(v.y), s);
-  s = __builtin_fmaf(bf16_hi(v.y), bf16_hi(v.y), s);
-  s = __builtin_fmaf(bf16_lo(v.z), bf16_lo(v.z), s);
-  s = __builtin_fmaf(bf16_hi(v.z), bf16_hi(v.z), s);
-  s = __builtin_fmaf(bf16_lo(v.w), bf16_lo(v.w), s);
-  return __builtin_fmaf(bf16_hi(v.w), bf16_hi(v.w), s);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_dot_t a = __builtin_bit_cast(bf16x2_dot_t, w[i]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a, a, s, false);
+  }
+  return s;
 }
 
 __device__ __forceinline__ float sumsq8_scaled(uint4 v, float p, float s) {
@@ -142,10 +151,13 @@ __device__ __forceinline__ uint4 norm8(uint4 x, uint4 g, float p, float f,
 
 // The row's scale from max |gamma t| over the row: the bf16 rounding is
 // monotonic, so max |y| = bf16(max |gamma t|).
+__device__ __forceinline__ float scale_from_row_max(float am) {
+  return row_scale(__uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(am)) << 16));
+}
+
 __device__ __forceinline__ float scale_from_products(float am) {
-  const uint32_t m = wave_max_u32(__float_as_uint(am));  // non-negative floats
-  return row_scale(__uint_as_float(
-      static_cast<uint32_t>(f32_to_bf16_bits(__uint_as_float(m))) << 16));
+  // non-negative floats order like their bit patterns
+  return scale_from_row_max(__uint_as_float(wave_max_u32(__float_as_uint(am))));
 }
 
 // Row-uniform factor p and whether p * f is a normal float.
@@ -164,37 +176,82 @@ __device__ __forceinline__ NormFactor make_norm_factor(float ss, int64_t k,
   return n;
 }
 
-template <int NV>
+// Sum (SUM) or max (!SUM, non-negative floats) of one value per wave over
+// the S waves that share a row; `slot` is this exchange's own LDS array.
+// Every wave of the workgroup calls it (the barrier is unconditional).
+template <int S, bool SUM>
+__device__ __forceinline__ float row_combine(float v, float* slot, int wave) {
+  if (S == 1) return v;
+  if ((threadIdx.x & 63) == 0) slot[wave] = v;
+  __syncthreads();
+  const int first = (wave / S) * S;
+  float r = slot[first];
+#pragma unroll
+  for (int j = 1; j < S; ++j)
+    r = SUM ? r + slot[first + j] : __builtin_fmaxf(r, slot[first + j]);
+  return r;
+}
+
+// A row of k elements is split over S waves of a workgroup (4 / S rows per
+// workgroup), each wave holding NV 16-byte vectors of the row per lane.
+template <int NV, int S>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int k, int64_t ldx,
     const uint16_t* __restrict__ gamma, float eps, uint8_t* __restrict__ q,
     float* __restrict__ scale, uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ float s_ss[4], s_amx[4], s_ss2[4], s_amy[4];
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kNormRowsPerBlock +
-                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint32_t row_bytes = static_cast<uint32_t>(k) * 2u;
-  const auto src = row_rsrc(x + row * ldx, row_bytes);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (4 / S) + wave / S;
+  const int part = wave % S;
+  // Waves past the last row still take part in the exchanges, with empty
+  // descriptors (no memory is touched).
+  const bool live = row < rows;
+  const int64_t r = live ? row : 0;
+  const uint32_t row_bytes = live ? static_cast<uint32_t>(k) * 2u : 0u;
+  const auto src = row_rsrc(x + r * ldx, row_bytes);
   const auto gsrc = row_rsrc(gamma, row_bytes);
+  const uint32_t v0 = static_cast<uint32_t>(part * NV * 64 + lane);
   uint4 v[NV], g[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (i * 64 + lane) * 16u);
+  for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (v0 + i * 64) * 16u);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) g[i] = buf_load16(gsrc, (i * 64 + lane) * 16u);
+  for (int i = 0; i < NV; ++i) g[i] = buf_load16(gsrc, (v0 + i * 64) * 16u);
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) ss = sumsq8(v[i], ss);
-  ss = wave_sum_f32(ss);
+  ss = row_combine<S, true>(wave_sum_f32(ss), s_ss, wave);
   float p = 1.0f;
-  if (!sumsq_in_range(ss)) {
+  const bool rare = !sumsq_in_range(ss);   // uniform over the row's waves
+  if (S == 1) {
+    if (rare) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) m = amax8_bits(v[i], m);
+      p = pow2_for_amax(wave_max_u32(max(m & 0xffffu, m >> 16)));
+      float ss2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) ss2 = sumsq8_scaled(v[i], p, ss2);
+      ss = wave_sum_f32(ss2);
+    }
+  } else {
+    // The rare path's two exchanges run for every row (their barriers must
+    // be reached by all waves); only rows that need them use the results.
     uint32_t m = 0;
+    if (rare) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) m = amax8_bits(v[i], m);
-    p = pow2_for_amax(wave_max_u32(max(m & 0xffffu, m >> 16)));
-    ss = 0.0f;
+      for (int i = 0; i < NV; ++i) m = amax8_bits(v[i], m);
+    }
+    const float amx = row_combine<S, false>(
+        __uint_as_float(wave_max_u32(max(m & 0xffffu, m >> 16)) << 16), s_amx, wave);
+    if (rare) p = pow2_for_amax(__float_as_uint(amx) >> 16);
+    float ss2 = 0.0f;
+    if (rare) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) ss = sumsq8_scaled(v[i], p, ss);
-    ss = wave_sum_f32(ss);
+      for (int i = 0; i < NV; ++i) ss2 = sumsq8_scaled(v[i], p, ss2);
+    }
+    ss2 = row_combine<S, true>(wave_sum_f32(ss2), s_ss2, wave);
+    if (rare) ss = ss2;
   }
   const NormFactor nf = make_norm_factor(ss, k, eps, p);
   float am = 0.0f;
@@ -205,18 +262,20 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = norm8<false>(v[i], g[i], nf.p, nf.f, am);
   }
-  const float s = scale_from_products(am);
-  uint2 codes[NV];
-  quantize_row<NV>(v, make_divisor(s), codes);
-  const auto dst = row_rsrc(q + row * static_cast<int64_t>(k), static_cast<uint32_t>(k));
-#pragma unroll
-  for (int i = 0; i < NV; ++i) buf_store8(codes[i], dst, (i * 64 + lane) * 8u);
+  am = row_combine<S, false>(__uint_as_float(wave_max_u32(__float_as_uint(am))),
+                             s_amy, wave);
+  const float s = scale_from_row_max(am);
+  const auto dst = row_rsrc(q + r * static_cast<int64_t>(k),
+                            live ? static_cast<uint32_t>(k) : 0u);
+  quantize_row<NV>(v, make_divisor(s), [&](int i, uint2 c) {
+    buf_store8(c, dst, (v0 + i * 64) * 8u);
+  });
   if (y != nullptr) {
-    const auto ydst = row_rsrc(y + row * ldy, row_bytes);
+    const auto ydst = row_rsrc(y + r * ldy, row_bytes);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) buf_store16(v[i], ydst, (i * 64 + lane) * 16u);
+    for (int i = 0; i < NV; ++i) buf_store16(v[i], ydst, (v0 + i * 64) * 16u);
   }
-  if (lane == 0) scale[row] = s;
+  if (live && part == 0 && lane == 0) scale[row] = s;
 }
 
 // Rows longer than the register-resident variants: the same arithmetic in
@@ -264,37 +323,67 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_long_kernel(
   if (lane == 0) scale[row] = s;
 }
 
-template <int NV>
+template <int NV, int S>
 hipError_t launch_norm_nv(const uint16_t* x, int64_t rows, int64_t k,
                           int64_t ldx, const uint16_t* gamma, float eps,
                           uint8_t* q, float* scale, uint16_t* y, int64_t ldy,
                           hipStream_t stream) {
-  const int64_t blocks = (rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock;
-  rmsnorm_quant_kernel<NV><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                             stream>>>(x, rows, static_cast<int>(k), ldx, gamma,
-                                       eps, q, scale, y, ldy);
+  constexpr int kRows = 4 / S;
+  const int64_t blocks = (rows + kRows - 1) / kRows;
+  rmsnorm_quant_kernel<NV, S><<<dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                                0, stream>>>(x, rows, static_cast<int>(k), ldx,
+                                             gamma, eps, q, scale, y, ldy);
   return hipGetLastError();
 }
 
 }  // namespace detail
 using namespace detail;
 
+// Waves per row: FP8W8A8_NORM_SPLIT=1|2|4 overrides the choice (tuning and
+// tests); rows up to 4 x 12 vectors per lane take the register kernels.
+int norm_split(int64_t rows, int64_t per_lane) {
+  if (const char* e = std::getenv("FP8W8A8_NORM_SPLIT")) {
+    const int v = std::atoi(e);
+    if (v == 1 || v == 2 || v == 4) return v;
+  }
+  // Measured at k = 4096 on MI355X: one wave per row is fastest once there
+  // are thousands of rows (12.0 us at 4096 rows against 13.4 us split over
+  // four), four waves per row when rows are few (2.8 us against 3.8 us for
+  // one row, 3.2 against 3.8 for 64).
+  if (per_lane < 4) return 1;
+  return rows >= 2048 ? 1 : (rows >= 512 ? 2 : 4);
+}
+
 hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t rows, int64_t k,
                                 int64_t ldx, const uint16_t* gamma, float eps,
                                 uint8_t* q, float* scale, uint16_t* y,
                                 int64_t ldy, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const int64_t per_lane = (k / 8 + 63) / 64;
-  if (per_lane <= 1)
-    return launch_norm_nv<1>(x, rows, k, ldx, gamma, eps, q, scale, y, ldy, stream);
-  if (per_lane <= 2)
-    return launch_norm_nv<2>(x, rows, k, ldx, gamma, eps, q, scale, y, ldy, stream);
-  if (per_lane <= 4)
-    return launch_norm_nv<4>(x, rows, k, ldx, gamma, eps, q, scale, y, ldy, stream);
-  if (per_lane <= 8)
-    return launch_norm_nv<8>(x, rows, k, ldx, gamma, eps, q, scale, y, ldy, stream);
-  if (per_lane <= 12)
-    return launch_norm_nv<12>(x, rows, k, ldx, gamma, eps, q, scale, y, ldy, stream);
+  const int64_t per_lane = (k / 8 + 63) / 64;   // vectors per lane, one wave
+  const int split = norm_split(rows, per_lane);
+  const int64_t pw = (per_lane + split - 1) / split;   // per wave
+#define FP8W8A8_NORM(NV, S) \
+  return launch_norm_nv<NV, S>(x, rows, k, ldx, gamma, eps, q, scale, y, ldy, stream)
+  if (split == 1) {
+    if (pw <= 1) FP8W8A8_NORM(1, 1);
+    if (pw <= 2) FP8W8A8_NORM(2, 1);
+    if (pw <= 4) FP8W8A8_NORM(4, 1);
+    if (pw <= 8) FP8W8A8_NORM(8, 1);
+    if (pw <= 12) FP8W8A8_NORM(12, 1);
+  } else if (split == 2) {
+    if (pw <= 1) FP8W8A8_NORM(1, 2);
+    if (pw <= 2) FP8W8A8_NORM(2, 2);
+    if (pw <= 4) FP8W8A8_NORM(4, 2);
+    if (pw <= 8) FP8W8A8_NORM(8, 2);
+    if (pw <= 12) FP8W8A8_NORM(12, 2);
+  } else {
+    if (pw <= 1) FP8W8A8_NORM(1, 4);
+    if (pw <= 2) FP8W8A8_NORM(2, 4);
+    if (pw <= 4) FP8W8A8_NORM(4, 4);
+    if (pw <= 8) FP8W8A8_NORM(8, 4);
+    if (pw <= 12) FP8W8A8_NORM(12, 4);
+  }
+#undef FP8W8A8_NORM
   const int64_t blocks = (rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock;
   rmsnorm_quant_long_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                               stream>>>(x, rows, k, ldx, gamma, eps, q, scale, y,

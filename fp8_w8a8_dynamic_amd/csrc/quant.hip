@@ -42,11 +42,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
   const uint32_t mrow = wave_max_u32(max(m & 0xffffu, m >> 16));
   const float s = row_scale(__uint_as_float(mrow << 16));
-  uint2 codes[NV];
-  quantize_row<NV>(v, make_divisor(s), codes);
   const auto dst = row_rsrc(q + row * static_cast<int64_t>(k), static_cast<uint32_t>(k));
-#pragma unroll
-  for (int i = 0; i < NV; ++i) buf_store8(codes[i], dst, (i * 64 + lane) * 8u);
+  quantize_row<NV>(v, make_divisor(s), [&](int i, uint2 c) {
+    buf_store8(c, dst, (i * 64 + lane) * 8u);
+  });
   if (lane == 0) scale[row] = s;
 }
 

@@ -125,12 +125,11 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
   // max |h| = bf16(max |s u|): the rounding is monotonic.
   const float s = row_scale(__uint_as_float(
       static_cast<uint32_t>(f32_to_bf16_bits(__uint_as_float(m))) << 16));
-  uint2 codes[NV];
-  quantize_row<NV>(g, make_divisor(s), codes);
   const auto dst = row_rsrc(q + r * static_cast<int64_t>(n),
                             live ? static_cast<uint32_t>(n) : 0u);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) buf_store8(codes[i], dst, (v0 + i * 64) * 8u);
+  quantize_row<NV>(g, make_divisor(s), [&](int i, uint2 c) {
+    buf_store8(c, dst, (v0 + i * 64) * 8u);
+  });
   if (h != nullptr) {
     const auto hdst = row_rsrc(h + r * ldh, row_bytes);
 #pragma unroll

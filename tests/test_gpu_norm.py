@@ -98,9 +98,16 @@ def check_norm(x_bits, g_bits, eps, qx, sx, y, what):
     return n_mis
 
 
-def test_prefill_chunk_full_size():
-    """The input norm of a 4096-token prefill chunk (hidden 4096), in the
-    launch configuration the benchmark times."""
+SPLITS = ["1", "2", "4"]
+
+
+@pytest.mark.parametrize("split", [None] + SPLITS)
+def test_prefill_chunk_full_size(split, monkeypatch):
+    """The input norm of a 4096-token prefill chunk (hidden 4096): in the
+    launch configuration the benchmark times (split None: the library's
+    choice) and with each row split over 1, 2 or 4 waves."""
+    if split is not None:
+        monkeypatch.setenv("FP8W8A8_NORM_SPLIT", split)
     x, g = norm_inputs(4096, 4096, seed=0)
     qx, sx, y = _gpu_norm(x, g, 1e-6)
     n = check_norm(x, g, 1e-6, qx, sx, y, "prefill 4096x4096")
@@ -111,37 +118,50 @@ SHAPES = [(1, 4096), (3, 8), (5, 16), (7, 520), (64, 512), (5, 2048),
           (33, 4104), (2, 8192), (9, 12288), (6, 12296), (3, 16400)]
 
 
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("m,k", SHAPES)
-def test_shapes_and_kernel_variants(m, k):
+def test_shapes_and_kernel_variants(m, k, split, monkeypatch):
     """Every register-resident variant (up to 8, 16, 32, 64 and 96 elements
-    per lane), ragged tails, and the four-pass kernel for longer rows."""
+    per lane and wave, rows split over 1, 2 or 4 waves, idle waves in the
+    last workgroup), ragged tails, and the multi-pass kernel for longer
+    rows."""
+    monkeypatch.setenv("FP8W8A8_NORM_SPLIT", split)
     x, g = norm_inputs(m, k, seed=m + k)
     qx, sx, y = _gpu_norm(x, g, 1e-6)
     check_norm(x, g, 1e-6, qx, sx, y, f"{m}x{k}")
 
 
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-2, 1.0, 1e30])
-def test_eps_values(eps):
+def test_eps_values(eps, split, monkeypatch):
+    monkeypatch.setenv("FP8W8A8_NORM_SPLIT", split)
     x, g = norm_inputs(16, 1024, seed=21)
     qx, sx, y = _gpu_norm(x, g, eps)
     check_norm(x, g, eps, qx, sx, y, f"eps {eps}")
 
 
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("scale", [2.0 ** -120, 2.0 ** -70, 1e-20, 1e20, 2.0 ** 100,
                                    3e38])
 @pytest.mark.parametrize("eps", [0.0, 1e-6])
-def test_extreme_row_magnitudes(scale, eps):
+def test_extreme_row_magnitudes(scale, eps, split, monkeypatch):
     """Rows whose float32 sum of squares would overflow or underflow without
-    the power-of-two prescaling (and, with eps, rows that eps dominates)."""
+    the power-of-two prescaling (and, with eps, rows that eps dominates),
+    next to ordinary rows in the same workgroup."""
+    monkeypatch.setenv("FP8W8A8_NORM_SPLIT", split)
     rng = np.random.default_rng(31)
     k = 768
-    x = bf16_from_f64(rng.standard_normal((4, k)) * scale * 0.25)
+    x = bf16_from_f64(rng.standard_normal((6, k)) * scale * 0.25)
+    x[1] = bf16_from_f64(rng.standard_normal(k))              # an ordinary row
+    x[4] = bf16_from_f64(rng.standard_normal(k) * 3.0)
     g = bf16_from_f64(1.0 + 0.25 * rng.standard_normal(k))
     qx, sx, y = _gpu_norm(x, g, eps)
     check_norm(x, g, eps, qx, sx, y, f"rows x{scale:g} eps {eps}")
 
 
-def test_zero_rows_and_signed_zeros():
+@pytest.mark.parametrize("split", SPLITS)
+def test_zero_rows_and_signed_zeros(split, monkeypatch):
+    monkeypatch.setenv("FP8W8A8_NORM_SPLIT", split)
     k = 256
     g = bf16_from_f64(np.linspace(-2.0, 2.0, k))
     x = np.zeros((4, k), np.uint16)
@@ -153,8 +173,10 @@ def test_zero_rows_and_signed_zeros():
         assert np.all(sx[:3] == 0)
 
 
-def test_subnormal_rows():
-    k = 64
+@pytest.mark.parametrize("split", SPLITS)
+def test_subnormal_rows(split, monkeypatch):
+    monkeypatch.setenv("FP8W8A8_NORM_SPLIT", split)
+    k = 512
     rng = np.random.default_rng(41)
     x = rng.integers(0, 128, (6, k)).astype(np.uint16)       # bf16 subnormals
     x |= (rng.integers(0, 2, (6, k)).astype(np.uint16) << 15)
