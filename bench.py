@@ -23,6 +23,9 @@ Also measured and printed on the same JSON line:
   of algorithmic bytes against 8 TB/s, beside the unfused sequence;
 * ``swiglu_quant``: the fused SiLU-gated activation -> per-token quantization
   kernel (down_proj's input) at M = 4096 and M = 1, likewise;
+* ``layer_with_fusions``: one layer's whole Linear path with the fused norms
+  and activation (norm -> q|k|v, o, norm -> gate|up, SwiGLU -> down) at
+  M = 4096 and M = 1, beside the unfused chain;
 * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the same
   workload on the host's cores.
 
@@ -47,32 +50,48 @@ PREFILL_M = 4096
 DECODE_M = 1
 DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 
-# HBM bytes of one prefill step's 7 GEMM dispatches, from rocprofv3
-# FETCH_SIZE (x2, calibrated) + WRITE_SIZE passes over this script (see
-# profiles/hbm_traffic_counters_prefill_layer.txt), valid for the GEMM code
-# (gemm.hip and device_common.h) whose SHA-1, comments and blank lines
-# stripped, is given here; reported as null once the code differs.
-GEMM_TRAFFIC = {"gemm_code_sha1": "pending",
-                "bytes_per_step": 1493156 * 1024}
+# HBM bytes per launch (or per prefill step, for the GEMM: its 7 dispatches)
+# from rocprofv3 FETCH_SIZE (x2, calibrated) and WRITE_SIZE passes over this
+# script (profiles/hbm_traffic_counters_prefill_layer.txt), each valid for the
+# source whose SHA-1 (comments and blank lines stripped) is given; reported
+# as null once that code differs.
+KERNEL_TRAFFIC = {
+    "gemm": {"files": ("gemm.hip", "device_common.h"),
+             "sha1": "9683d2565fe3d221443e7f712aa839b0dbba9bd6",
+             "bytes": 1492966 * 1024},
+    "rmsnorm_quant": {"files": ("norm.hip", "device_common.h"),
+                      "sha1": "7b56739909f3606c5939c9a9598f4fdb7af37bf0",
+                      "bytes": (16502 * 2 + 16416) * 1024},
+    "swiglu_quant": {"files": ("swiglu.hip", "device_common.h"),
+                     "sha1": "5a78ec8fcf4d58acdd7ba7fef8056f929ac9c383",
+                     "bytes": (98454 * 2 + 49287) * 1024},
+}
 
 
-def gemm_code_sha1():
-    """SHA-1 of the GEMM's source (gemm.hip and the device helpers it
-    includes), comments and blank lines stripped."""
+def code_sha1(files):
+    """SHA-1 of the given csrc files, comments and blank lines stripped."""
     import hashlib
     import re
     code = []
-    for name in ("gemm.hip", "device_common.h"):
+    for name in files:
         with open(os.path.join(ROOT, "fp8_w8a8_dynamic_amd", "csrc", name)) as f:
             code += [re.sub(r"//.*", "", line).rstrip() for line in f]
     return hashlib.sha1("\n".join(c for c in code if c).encode()).hexdigest()
 
 
+def kernel_traffic(name):
+    """The counted HBM bytes of `name` if its code is still the code the
+    counters were taken on, else None."""
+    t = KERNEL_TRAFFIC[name]
+    return t["bytes"] if code_sha1(t["files"]) == t["sha1"] else None
+
+
+def gemm_code_sha1():
+    return code_sha1(KERNEL_TRAFFIC["gemm"]["files"])
+
+
 def gemm_traffic():
-    """GEMM_TRAFFIC's bytes if the GEMM's code is still the code the counters
-    were taken on, else None."""
-    ok = gemm_code_sha1() == GEMM_TRAFFIC["gemm_code_sha1"]
-    return GEMM_TRAFFIC["bytes_per_step"] if ok else None
+    return kernel_traffic("gemm")
 
 
 def log(*a):
@@ -446,6 +465,73 @@ def bench_swiglu(torch, fq, reps, m=PREFILL_M, n=12288):
     return res
 
 
+def bench_fused_layer(torch, fq, m, steps, copies=1, eps=1e-6):
+    """One layer's Linear path with the adjacent fusions, HIP-graph replays:
+        rmsnorm_quantize(x1)       -> fp8_linear(q|k|v)        [6144 x 4096]
+        quant_linear(attention out)                            (o_proj)
+        rmsnorm_quantize(x2)       -> fp8_linear(gate|up)      [24576 x 4096]
+        swiglu_quantize(gate, up)  -> fp8_linear(down)         [4096 x 12288]
+    beside the same chain with torch's bf16 rms_norm and silu * up feeding
+    quant_linear.  Attention and the residual adds are not part of it (their
+    inputs are seeded data).  `copies` layers with distinct weights run per
+    replay so that decode-sized steps read their weights from HBM."""
+    from workloads import norm_inputs
+    base = setup_layer(torch, fq, m, 3 if m == PREFILL_M else 2, packed=True)
+    layers = [base]
+    for _ in range(copies - 1):
+        layers.append([dict(L, qw=L["qw"].clone(), sw=L["sw"].clone(),
+                            y=torch.empty_like(L["y"])) for L in base])
+    _, g1 = norm_inputs(1, 4096, seed=11)
+    _, g2 = norm_inputs(1, 4096, seed=12)
+    g1, g2 = to_dev(g1, torch), to_dev(g2, torch)
+    qkv, o, gu, down = base
+    inter = gu["n"] // 2
+    wsb = max(fq.workspace_bytes(m, L["n"], L["k"], True) for L in base)
+    ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
+    flops = sum(2 * m * L["n"] * L["k"] for L in base)
+    nbytes = (sum(L["n"] * L["k"] + 4 * L["n"] + 2 * m * L["k"] + 2 * m * L["n"] for L in base)
+              + 2 * (2 * 4096) + 2 * 2 * m * inter)      # gammas, gate/up re-read
+
+    def fused(layer):
+        qkv, o, gu, down = layer
+        qx, sx = fq.rmsnorm_quantize(qkv["x"], g1, eps)
+        fq.fp8_linear(qx, sx, qkv["qw"], qkv["sw"], out=qkv["y"], workspace=ws)
+        fq.quant_linear(o["x"], o["qw"], o["sw"], out=o["y"], workspace=ws)
+        qx, sx = fq.rmsnorm_quantize(gu["x"], g2, eps)
+        fq.fp8_linear(qx, sx, gu["qw"], gu["sw"], out=gu["y"], workspace=ws)
+        qh, sh = fq.swiglu_quantize(gu["y"][:, :inter], gu["y"][:, inter:])
+        fq.fp8_linear(qh, sh, down["qw"], down["sw"], out=down["y"], workspace=ws)
+
+    def unfused(layer):
+        qkv, o, gu, down = layer
+        n1 = torch.nn.functional.rms_norm(qkv["x"], (4096,), weight=g1, eps=eps)
+        fq.quant_linear(n1, qkv["qw"], qkv["sw"], out=qkv["y"], workspace=ws)
+        fq.quant_linear(o["x"], o["qw"], o["sw"], out=o["y"], workspace=ws)
+        n2 = torch.nn.functional.rms_norm(gu["x"], (4096,), weight=g2, eps=eps)
+        fq.quant_linear(n2, gu["qw"], gu["sw"], out=gu["y"], workspace=ws)
+        a = torch.nn.functional.silu(gu["y"][:, :inter]) * gu["y"][:, inter:]
+        fq.quant_linear(a, down["qw"], down["sw"], out=down["y"], workspace=ws)
+
+    res = {}
+    for name, fn in (("fused", fused), ("unfused_torch_norm_and_silu", unfused)):
+        gr = graph_of(torch, lambda: [fn(L) for L in layers], 1)
+        for _ in range(max(5, steps // 4)):
+            gr.replay()
+        torch.cuda.synchronize()
+        t, slices = time_chunks(torch, gr.replay, steps)
+        t /= copies
+        res[name] = {"us_per_layer": round(t * 1e6, 2),
+                     "tflops": round(flops / t / 1e12, 2),
+                     "gbs": round(nbytes / t / 1e9, 1),
+                     "slice_us": spread([ts * 1e6 / copies for ts in slices])}
+        del gr
+    del layers, base
+    torch.cuda.empty_cache()
+    res["flops_per_layer"] = flops
+    res["bytes_per_layer"] = nbytes
+    return res
+
+
 def cpu_baseline(target_s=16.0):
     """The oracle as it stands, timed on a sample of the prefill workload:
     all 7 Linears, a subset of tokens and of output channels (weights
@@ -559,6 +645,12 @@ def main():
     swi = bench_swiglu(torch, fq, args.steps)
     swi_dec = bench_swiglu(torch, fq, args.steps, m=DECODE_M)
     log(f"swiglu quant {swi}; M=1 {swi_dec['fused']['us']} us")
+    log("layer with fused norms and activation ...")
+    fl = bench_fused_layer(torch, fq, PREFILL_M, max(20, args.steps // 4))
+    fl_dec = None
+    if not args.no_decode:
+        fl_dec = bench_fused_layer(torch, fq, DECODE_M, max(20, args.steps), DECODE_COPIES)
+    log(f"fused layer M=4096 {fl}; M=1 {fl_dec}")
     cpu = None
     if not args.no_cpu:
         log("cpu oracle ...")
@@ -617,7 +709,11 @@ def main():
         "workload": f"BF16 RMSNorm fused with per-token FP8 quantization of its output, "
                     f"M={PREFILL_M}, hidden 4096 (the input norm of q/k/v and gate/up)",
         "roofline": {"bound": "hbm", "achieved": f["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": f["frac_of_hbm"], "traffic": None,
+                     "unit": "GB/s", "frac": f["frac_of_hbm"],
+                     "traffic": kernel_traffic("rmsnorm_quant"),
+                     "traffic_scope": "HBM bytes of one launch without the norm output "
+                                      "(rocprofv3 FETCH_SIZE x2 + WRITE_SIZE); "
+                                      "algorithmic 50,356,224",
                      "kernel": "rmsnorm_quant_kernel"},
         "m4096": norm, "m1_us": norm_dec["fused"]["us"]}
     f = swi["fused"]
@@ -626,9 +722,19 @@ def main():
                     f"output, M={PREFILL_M}, width 12288 (gate/up halves of the packed "
                     f"gate_up output -> down_proj's input)",
         "roofline": {"bound": "hbm", "achieved": f["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": f["frac_of_hbm"], "traffic": None,
+                     "unit": "GB/s", "frac": f["frac_of_hbm"],
+                     "traffic": kernel_traffic("swiglu_quant"),
+                     "traffic_scope": "HBM bytes of one launch without the activation "
+                                      "output (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE); "
+                                      "algorithmic 251,674,624",
                      "kernel": "swiglu_quant_kernel"},
         "m4096": swi, "m1_us": swi_dec["fused"]["us"]}
+    out["layer_with_fusions"] = {
+        "workload": "one layer's Linear path with the adjacent fusions: RMSNorm->quant "
+                    "-> q|k|v, o, RMSNorm->quant -> gate|up, SwiGLU->quant -> down "
+                    "(attention and residual adds excluded), beside the same chain with "
+                    "torch bf16 rms_norm / silu*up feeding quant_linear",
+        "m4096": fl, "m1": fl_dec}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
