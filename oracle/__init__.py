@@ -25,6 +25,8 @@ norm    BF16 RMSNorm and the per-token quantization of its output (the
         fusion ahead of the q/k/v and gate/up Linears).
 swiglu  the SiLU-gated activation between gate/up and down and the
         per-token quantization of its output (down_proj's input).
+kvcache the FP8 E4M3 key/value-cache codec (group-wise dynamic scales,
+        float32 read-back rounded to bf16).
 check   the pass criteria (bit-exact bytes, elementwise output tolerance).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
