@@ -23,6 +23,8 @@ Also measured and printed on the same JSON line:
   of algorithmic bytes against 8 TB/s, beside the unfused sequence;
 * ``swiglu_quant``: the fused SiLU-gated activation -> per-token quantization
   kernel (down_proj's input) at M = 4096 and M = 1, likewise;
+* ``kv_cache_fp8``: the FP8 E4M3 KV-cache codec (quantizing a 4096-token
+  chunk into the cache, reading a 32768-token window back), GB/s;
 * ``layer_with_fusions``: one layer's whole Linear path with the fused norms
   and activation (norm -> q|k|v, o, norm -> gate|up, SwiGLU -> down) at
   M = 4096 and M = 1, beside the unfused chain;
@@ -532,6 +534,42 @@ def bench_fused_layer(torch, fq, m, steps, copies=1, eps=1e-6):
     return res
 
 
+def bench_kv(torch, fq, reps, t_write=PREFILL_M, t_read=32768, width=1024, group=128):
+    """The FP8 E4M3 KV-cache codec: quantizing one prefill chunk's K (or V)
+    rows into the cache (t_write tokens x 8 KV heads x 128) and reading a
+    t_read-token window back to bf16, one scale per head; GB/s of
+    algorithmic bytes (bf16 in/out, codes, scales), HIP-graph replays."""
+    from workloads import kv_inputs
+    x = to_dev(kv_inputs(t_write, width, seed=0), torch)
+    cache = torch.empty((t_read, width), dtype=torch.uint8, device="cuda")
+    cscale = torch.empty((t_read, width // group), dtype=torch.float32, device="cuda")
+    win = to_dev(kv_inputs(t_read, width, seed=1), torch)
+    fq.kv_quantize_fp8(win, group, cache, cscale)
+    out = torch.empty((t_read, width), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for name, fn, nbytes in (
+            ("quantize", lambda: fq.kv_quantize_fp8(x, group, cache[:t_write],
+                                                    cscale[:t_write]),
+             3 * t_write * width + 4 * t_write * width // group),
+            ("dequantize", lambda: fq.kv_dequantize_fp8(cache, cscale, group, out=out),
+             3 * t_read * width + 4 * t_read * width // group)):
+        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
+        for _ in range(max(10, reps // 10)):
+            gr.replay()
+        torch.cuda.synchronize()
+        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
+        t /= NORM_CALLS_PER_GRAPH
+        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
+                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes,
+                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
+                                          for ts in slices])}
+        del gr
+    del x, cache, cscale, win, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s=16.0):
     """The oracle as it stands, timed on a sample of the prefill workload:
     all 7 Linears, a subset of tokens and of output channels (weights
@@ -645,6 +683,9 @@ def main():
     swi = bench_swiglu(torch, fq, args.steps)
     swi_dec = bench_swiglu(torch, fq, args.steps, m=DECODE_M)
     log(f"swiglu quant {swi}; M=1 {swi_dec['fused']['us']} us")
+    log("kv cache codec ...")
+    kv = bench_kv(torch, fq, args.steps)
+    log(f"kv fp8 {kv}")
     log("layer with fused norms and activation ...")
     fl = bench_fused_layer(torch, fq, PREFILL_M, max(20, args.steps // 4))
     fl_dec = None
@@ -729,6 +770,15 @@ def main():
                                       "algorithmic 251,674,624",
                      "kernel": "swiglu_quant_kernel"},
         "m4096": swi, "m1_us": swi_dec["fused"]["us"]}
+    d = kv["dequantize"]
+    out["kv_cache_fp8"] = {
+        "workload": "FP8 E4M3 KV-cache codec, 8 KV heads x 128, one scale per "
+                    "(token, head): quantize a 4096-token chunk into the cache, read a "
+                    "32768-token window back to bf16",
+        "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d["frac_of_hbm"], "traffic": None,
+                     "kernel": "kv_dequant_kernel"},
+        "quantize": kv["quantize"], "dequantize": d}
     out["layer_with_fusions"] = {
         "workload": "one layer's Linear path with the adjacent fusions: RMSNorm->quant "
                     "-> q|k|v, o, RMSNorm->quant -> gate|up, SwiGLU->quant -> down "

@@ -31,6 +31,10 @@ SIGNATURES = {
     "fp8w8a8_swiglu_quantize":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp,
                         _c_vp, _c_vp, _c_i64, _c_vp]),
+    "fp8w8a8_kv_quantize_fp8":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fp8w8a8_kv_dequantize_fp8":
+        (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_fp8_linear":
         (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -259,6 +263,56 @@ def swiglu_quantize(gate: torch.Tensor, up: torch.Tensor,
     if h is None:
         return qh.view(torch.float8_e4m3fn), sh
     return qh.view(torch.float8_e4m3fn), sh, h
+
+
+def kv_quantize_fp8(kv: torch.Tensor, group: int = 128, codes: torch.Tensor = None,
+                    scales: torch.Tensor = None):
+    """K or V rows [T, W] (bf16, W = kv_heads * head_dim) -> (codes
+    float8_e4m3fn [T, W], scales float32 [T, W // group]).  ``codes`` and
+    ``scales`` may be given (e.g. slices of a cache's tail: contiguous
+    [T, W] / [T, W // group] views)."""
+    lib = load_library()
+    if kv.dtype != torch.bfloat16:
+        raise TypeError("kv must be bfloat16")
+    t, w, ld = _rows(kv, "kv")
+    if group <= 0 or w % group != 0:
+        raise ValueError("the row width must be a multiple of the group")
+    codes = torch.empty((t, w), dtype=torch.uint8, device=kv.device) if codes is None \
+        else _as_codes(codes)
+    scales = torch.empty((t, w // group), dtype=torch.float32, device=kv.device) \
+        if scales is None else scales
+    if (tuple(codes.shape) != (t, w) or not codes.is_contiguous()
+            or codes.device != kv.device):
+        raise ValueError(f"codes must be a contiguous [{t}, {w}] tensor on {kv.device}")
+    if (scales.dtype != torch.float32 or tuple(scales.shape) != (t, w // group)
+            or not scales.is_contiguous() or scales.device != kv.device):
+        raise ValueError(f"scales must be a contiguous float32 [{t}, {w // group}] tensor")
+    if t > 0:
+        _check(lib.fp8w8a8_kv_quantize_fp8(
+            kv.data_ptr(), t, w, ld, group, codes.data_ptr(), scales.data_ptr(),
+            _stream_ptr(kv.device)), "kv_quantize_fp8")
+    return codes.view(torch.float8_e4m3fn), scales
+
+
+def kv_dequantize_fp8(codes: torch.Tensor, scales: torch.Tensor, group: int = 128,
+                      out: torch.Tensor = None):
+    """(codes [T, W], scales [T, W // group]) -> bf16 [T, W] =
+    bf16(dec(code) * scale)."""
+    lib = load_library()
+    codes = _as_codes(codes)
+    t, w, ldc = _rows(codes, "codes")
+    if ldc != w:
+        raise ValueError("codes must be contiguous")
+    if group <= 0 or w % group != 0:
+        raise ValueError("the row width must be a multiple of the group")
+    scales = _scales(scales.reshape(-1) if scales.is_contiguous() else scales,
+                     t * (w // group), codes.device, "scales")
+    y = _out(t, w, codes.device, out)
+    if t > 0:
+        _check(lib.fp8w8a8_kv_dequantize_fp8(
+            codes.data_ptr(), scales.data_ptr(), t, w, group, y.data_ptr(),
+            y.stride(0), _stream_ptr(codes.device)), "kv_dequantize_fp8")
+    return y
 
 
 def _out(m, n, device, out):

@@ -20,8 +20,8 @@ LIB_NAME = "libfp8w8a8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quant.hip", "norm.hip", "swiglu.hip", "gemm.hip",
-           "gemv.hip"]
+SOURCES = ["api.cpp", "quant.hip", "norm.hip", "swiglu.hip", "kvcache.hip",
+           "gemm.hip", "gemv.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 # No fast-math and no denormal flushing: the quantizer must see IEEE float32

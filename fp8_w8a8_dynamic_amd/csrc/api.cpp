@@ -259,6 +259,55 @@ int fp8w8a8_swiglu_quantize(const uint16_t* gate, int64_t ldg,
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
+bool kv_group_ok(int64_t width, int64_t group) {
+  return group >= 8 && group <= 512 && (group & (group - 1)) == 0 &&
+         width % group == 0;
+}
+
+int fp8w8a8_kv_quantize_fp8(const uint16_t* kv, int64_t rows, int64_t width,
+                            int64_t ld, int64_t group, uint8_t* codes,
+                            float* scales, void* stream) {
+  if (!kv || !codes || !scales) return FP8W8A8_ERR_NULL;
+  if (rows < 0 || rows > kMaxDim || width < 8 || width > kMaxDim ||
+      width % 8 != 0 || !kv_group_ok(width, group) || ld < width || ld % 8 != 0)
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(kv) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return FP8W8A8_ERR_ALIGN;
+  const Range rx = span(kv, rows, width, ld, 2);
+  const Range rc = span(codes, rows, width, width, 1);
+  const Range rs = span(scales, rows, width / group, width / group, 4);
+  if (overlap(rc, rx) || overlap(rs, rx) || overlap(rc, rs)) return FP8W8A8_ERR_ALIAS;
+  if (rows == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_kv_quantize(kv, rows, width, ld, group, codes,
+                                             scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_kv_dequantize_fp8(const uint8_t* codes, const float* scales,
+                              int64_t rows, int64_t width, int64_t group,
+                              uint16_t* out, int64_t ldo, void* stream) {
+  if (!codes || !scales || !out) return FP8W8A8_ERR_NULL;
+  if (rows < 0 || rows > kMaxDim || width < 8 || width > kMaxDim ||
+      width % 8 != 0 || !kv_group_ok(width, group) || ldo < width || ldo % 8 != 0)
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return FP8W8A8_ERR_ALIGN;
+  const Range ro = span(out, rows, width, ldo, 2);
+  if (overlap(ro, span(codes, rows, width, width, 1)) ||
+      overlap(ro, span(scales, rows, width / group, width / group, 4)))
+    return FP8W8A8_ERR_ALIAS;
+  if (rows == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_kv_dequantize(codes, scales, rows, width, group,
+                                               out, ldo, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
   return layout_for(m, n, k, fused != 0, choose_path(m, n, k),

@@ -32,6 +32,15 @@ hipError_t launch_swiglu_quant(const uint16_t* gate, int64_t ldg,
                                int64_t n, uint8_t* q, float* scale,
                                uint16_t* h, int64_t ldh, hipStream_t stream);
 
+// FP8 KV-cache codec: rows of `width` values in groups of `group` (a power
+// of two from 8 to 512 dividing width), one scale per group.
+hipError_t launch_kv_quantize(const uint16_t* kv, int64_t rows, int64_t width,
+                              int64_t ld, int64_t group, uint8_t* codes,
+                              float* scales, hipStream_t stream);
+hipError_t launch_kv_dequantize(const uint8_t* codes, const float* scales,
+                                int64_t rows, int64_t width, int64_t group,
+                                uint16_t* out, int64_t ldo, hipStream_t stream);
+
 // Prefill GEMM: y[m,n] = bf16(sum_k qx[m,k] qw[n,k] * sx[m] * sw[n]).
 // The plan fixes the tile configuration and the number of K splits; with
 // splits > 1 the GEMM writes float32 partial sums [splits, m, n] to `part`

@@ -154,6 +154,36 @@ int fp8w8a8_swiglu_quantize(const uint16_t* gate, int64_t ldg,
                             uint16_t* h, int64_t ldh, void* stream);
 
 /*
+ * FP8 E4M3 key/value-cache codec.  With the FP8 checkpoint under SGLang the
+ * KV cache uses the engine's own dtype, e.g. --kv-cache-dtype fp8_e4m3
+ * (MOSS-VL quantization README, "KV cache"); the pages give only the dtype.
+ * Readings: each token's K (or V) row of `width` values (kv_heads x
+ * head_dim) is quantized in groups of `group` consecutive values, each group
+ * with one dynamic float32 scale = amax / 448 and codes exactly as
+ * fp8w8a8_quantize_act_per_token would give for that group as a row; reading
+ * back gives bf16(fl32(dec(code) * scale)).
+ *
+ * fp8w8a8_kv_quantize_fp8 (appending rows to a cache):
+ *   kv       bf16 [rows, width], row stride ld >= width, ld % 8 == 0 (input)
+ *   codes    E4M3 [rows, width], contiguous                          (output)
+ *   scales   float32 [rows, width / group], contiguous               (output)
+ * fp8w8a8_kv_dequantize_fp8 (reading a cache window back):
+ *   codes, scales as above                                           (input)
+ *   out      bf16 [rows, width], row stride ldo >= width, ldo % 8 == 0 (output)
+ * Rules: rows >= 0; width >= 8, width % 8 == 0; group a power of two from 8
+ * to 512 with width % group == 0; kv and out 16-byte aligned, codes 8-byte
+ * aligned, scales 4-byte aligned; outputs must not overlap the inputs or
+ * each other.  (To write rows t0.. of a cache, pass codes + t0 * width and
+ * scales + t0 * width / group.)
+ */
+int fp8w8a8_kv_quantize_fp8(const uint16_t* kv, int64_t rows, int64_t width,
+                            int64_t ld, int64_t group, uint8_t* codes,
+                            float* scales, void* stream);
+int fp8w8a8_kv_dequantize_fp8(const uint8_t* codes, const float* scales,
+                              int64_t rows, int64_t width, int64_t group,
+                              uint16_t* out, int64_t ldo, void* stream);
+
+/*
  * The W8A8 Linear on already-quantized operands ("the quantized kernels" of
  * README "FP8-Dynamic"):
  *   y[m,n] = bf16_rne( (sum_k dec(qx[m,k]) * dec(qw[n,k])) * x_scale[m]

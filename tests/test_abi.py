@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -125,6 +125,40 @@ def test_swiglu_quantize_validation(lib):
     assert _swi(lib, s=256 * A) == EALIAS                    # scales over h
     assert _swi(lib, m=0) == OK
     assert _swi(lib, m=0, h=None, ldh=0) == OK
+
+
+def _kvq(lib, x=A, t=4, w=1024, ld=1024, g=128, c=64 * A, s=128 * A):
+    return lib.fp8w8a8_kv_quantize_fp8(x, t, w, ld, g, c, s, None)
+
+
+def _kvd(lib, c=A, s=2 * A, t=4, w=1024, g=128, o=64 * A, ldo=1024):
+    return lib.fp8w8a8_kv_dequantize_fp8(c, s, t, w, g, o, ldo, None)
+
+
+def test_kv_codec_validation(lib):
+    assert _kvq(lib, x=None) == ENULL
+    assert _kvq(lib, c=None) == ENULL
+    assert _kvq(lib, s=None) == ENULL
+    assert _kvq(lib, t=-1) == ESHAPE
+    assert _kvq(lib, w=4, ld=8, g=8) == ESHAPE
+    for g in (0, 4, 96, 1024, 48):
+        assert _kvq(lib, g=g) == ESHAPE                       # power of two, 8..512
+    assert _kvq(lib, w=1000, ld=1000, g=16) == ESHAPE         # 1000 % 16
+    assert _kvq(lib, ld=1000) == ESHAPE
+    assert _kvq(lib, x=A + 8) == EALIGN
+    assert _kvq(lib, c=64 * A + 4) == EALIGN
+    assert _kvq(lib, s=128 * A + 2) == EALIGN
+    assert _kvq(lib, c=A + 4096) == EALIAS                    # codes inside kv
+    assert _kvq(lib, s=64 * A + 512) == EALIAS                # scales inside codes
+    assert _kvq(lib, t=0) == OK
+    assert _kvd(lib, c=None) == ENULL
+    assert _kvd(lib, o=None) == ENULL
+    assert _kvd(lib, g=12) == ESHAPE
+    assert _kvd(lib, ldo=1020) == ESHAPE
+    assert _kvd(lib, o=64 * A + 8) == EALIGN
+    assert _kvd(lib, c=A + 4) == EALIGN
+    assert _kvd(lib, o=A + 16) == EALIAS                      # out over codes
+    assert _kvd(lib, t=0) == OK
 
 
 def _lin(lib, qx=A, sx=2 * A, qw=4 * A, sw=8 * A, m=32, n=64, k=256,

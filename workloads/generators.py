@@ -32,6 +32,9 @@ the model's Linear shapes and of the token counts those workloads produce):
 * swiglu: gate_up_proj's output ahead of the activation: gate ~ 1.5 N(0,1)
   with 1 % of entries x10, up ~ 1.5 N(0,1) (the spread of a K = 4096 dot
   product of c3-like activations with N(0, 0.02) weights).
+* kv: K or V rows of the cache, kv_heads x head_dim = 1024 wide:
+  N(0,1) x 10^U(-0.5, 0.5) per channel (k_proj / v_proj outputs with
+  channels of different spread).
 * norm: the RMSNorm input ahead of q/k/v and gate/up: residual-stream rows
   X[m, k] ~ N(0,1) * g[k], g[k] = 10^U(-1, 1) (outlier channels, as c3), and
   the norm weight gamma[k] ~ N(1, 0.25).
@@ -60,6 +63,7 @@ N_SELF_ATTN_LAYERS = 36
 ROLE_X, ROLE_W, ROLE_GAMMA = 0, 1, 2
 CFG_NORM = 6
 CFG_SWIGLU = 7
+CFG_KV = 8
 
 
 def rng_for(cfg: int, a: int, b: int, role: int) -> np.random.Generator:
@@ -192,3 +196,10 @@ def swiglu_inputs(m: int, n: int, seed: int = 0):
     g[rng.random((m, n), dtype=np.float32) < np.float32(0.01)] *= np.float32(10.0)
     u = rng_for(CFG_SWIGLU, seed, n, ROLE_W).standard_normal((m, n), dtype=np.float32)
     return bf16_from_f64(g), bf16_from_f64(u * np.float32(1.5))
+
+
+def kv_inputs(t: int, width: int = KV_WIDTH, seed: int = 0):
+    """K or V rows [t, width] bf16 bits for t tokens."""
+    rng = rng_for(CFG_KV, seed, width, ROLE_X)
+    ch = np.power(np.float32(10.0), rng.uniform(-0.5, 0.5, width).astype(np.float32))
+    return bf16_from_f64(rng.standard_normal((t, width), dtype=np.float32) * ch[None, :])
