@@ -26,7 +26,8 @@ norm    BF16 RMSNorm and the per-token quantization of its output (the
 swiglu  the SiLU-gated activation between gate/up and down and the
         per-token quantization of its output (down_proj's input).
 kvcache the FP8 E4M3 key/value-cache codec (group-wise dynamic scales,
-        float32 read-back rounded to bf16).
+        float32 read-back rounded to bf16) and the INT8 group-wise cache
+        with a BF16 residual window (asymmetric min-max reading of HQQ).
 check   the pass criteria (bit-exact bytes, elementwise output tolerance).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
