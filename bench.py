@@ -25,6 +25,8 @@ Also measured and printed on the same JSON line:
   kernel (down_proj's input) at M = 4096 and M = 1, likewise;
 * ``kv_cache_fp8``: the FP8 E4M3 KV-cache codec (quantizing a 4096-token
   chunk into the cache, reading a 32768-token window back), GB/s;
+* ``kv_cache_int8``: the INT8 group-64 KV cache with its 128-token BF16
+  residual window (quantizing into the store; reading history + tail);
 * ``layer_with_fusions``: one layer's whole Linear path with the fused norms
   and activation (norm -> q|k|v, o, norm -> gate|up, SwiGLU -> down) at
   M = 4096 and M = 1, beside the unfused chain;
@@ -570,6 +572,46 @@ def bench_kv(torch, fq, reps, t_write=PREFILL_M, t_read=32768, width=1024, group
     return res
 
 
+def bench_kv_int8(torch, fq, reps, t_write=PREFILL_M, t_read=32768, width=1024,
+                  group=64, residual=128):
+    """The INT8 group-wise KV cache with its BF16 residual window (groups of
+    64, newest 128 positions in bf16): quantizing t_write tokens into the
+    INT8 store, and the cache read of a t_read-token window (t_read - 128
+    dequantized history rows followed by the 128-row bf16 tail); GB/s of
+    algorithmic bytes, HIP-graph replays."""
+    from workloads import kv_inputs
+    x = to_dev(kv_inputs(t_write, width, seed=0), torch)
+    hist = t_read - residual
+    win = to_dev(kv_inputs(t_read, width, seed=1), torch)
+    codes, sc, mn = fq.kv_quantize_int8(win[:hist], group)
+    tail = win[hist:]
+    out = torch.empty((t_read, width), dtype=torch.bfloat16, device="cuda")
+    g = width // group
+    res = {}
+    for name, fn, nbytes in (
+            ("quantize", lambda: fq.kv_quantize_int8(x, group, codes[:t_write],
+                                                     sc[:t_write], mn[:t_write]),
+             3 * t_write * width + 8 * t_write * g),
+            ("read_history_and_tail",
+             lambda: fq.kv_read_int8(codes, sc, mn, tail=tail, group=group, out=out),
+             hist * width + 8 * hist * g + 2 * residual * width + 2 * t_read * width)):
+        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
+        for _ in range(max(10, reps // 10)):
+            gr.replay()
+        torch.cuda.synchronize()
+        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
+        t /= NORM_CALLS_PER_GRAPH
+        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
+                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes,
+                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
+                                          for ts in slices])}
+        del gr
+    del x, win, codes, sc, mn, tail, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s=16.0):
     """The oracle as it stands, timed on a sample of the prefill workload:
     all 7 Linears, a subset of tokens and of output channels (weights
@@ -686,6 +728,8 @@ def main():
     log("kv cache codec ...")
     kv = bench_kv(torch, fq, args.steps)
     log(f"kv fp8 {kv}")
+    kv8 = bench_kv_int8(torch, fq, args.steps)
+    log(f"kv int8 {kv8}")
     log("layer with fused norms and activation ...")
     fl = bench_fused_layer(torch, fq, PREFILL_M, max(20, args.steps // 4))
     fl_dec = None
@@ -779,6 +823,15 @@ def main():
                      "unit": "GB/s", "frac": d["frac_of_hbm"], "traffic": None,
                      "kernel": "kv_dequant_kernel"},
         "quantize": kv["quantize"], "dequantize": d}
+    d = kv8["read_history_and_tail"]
+    out["kv_cache_int8"] = {
+        "workload": "INT8 group-wise KV cache (groups of 64, min-max) with the newest 128 "
+                    "positions in bf16: quantize a 4096-token chunk into the INT8 store, "
+                    "read a 32768-token window (32640 history + 128 tail) back to bf16",
+        "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d["frac_of_hbm"], "traffic": None,
+                     "kernel": "kv_int8_read_kernel"},
+        "quantize": kv8["quantize"], "read": d}
     out["layer_with_fusions"] = {
         "workload": "one layer's Linear path with the adjacent fusions: RMSNorm->quant "
                     "-> q|k|v, o, RMSNorm->quant -> gate|up, SwiGLU->quant -> down "

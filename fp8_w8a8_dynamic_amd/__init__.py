@@ -4,20 +4,23 @@ Per-token dynamic E4M3 activations x channel-wise static E4M3 weights, float32
 accumulation, token-scale x channel-scale epilogue to bfloat16, as in the
 FP8-Dynamic recipe of the MOSS-VL quantization README, and the BF16 RMSNorm
 ahead of the q/k/v and gate/up Linears and the MLP activation ahead of
-down_proj, each fused with the per-token quantization of its output, and an
-FP8 E4M3 key/value-cache codec.  The work happens in hand-written HIP kernels behind the C ABI
+down_proj, each fused with the per-token quantization of its output, and the
+key/value-cache codecs (FP8 E4M3; INT8 group-wise with a BF16 residual
+window).  The work happens in hand-written HIP kernels behind the C ABI
 of ``include/fp8w8a8.h``; this package is its Python binding (argument
 marshalling only).
 """
 
 from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
-                      init_workspace, kv_dequantize_fp8, kv_quantize_fp8, load_library,
+                      init_workspace, kv_dequantize_fp8, kv_quantize_fp8,
+                      kv_quantize_int8, kv_read_int8, load_library,
                       quant_linear, quantize_act_per_token,
                       quantize_weight_channelwise, rmsnorm_quantize, swiglu_quantize,
                       workspace_bytes)
 
 __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
            "init_workspace", "kv_dequantize_fp8", "kv_quantize_fp8",
+           "kv_quantize_int8", "kv_read_int8",
            "load_library", "quant_linear",
            "quantize_act_per_token", "quantize_weight_channelwise",
            "rmsnorm_quantize", "swiglu_quantize", "workspace_bytes"]

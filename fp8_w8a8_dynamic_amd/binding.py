@@ -35,6 +35,12 @@ SIGNATURES = {
         (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fp8w8a8_kv_dequantize_fp8":
         (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
+    "fp8w8a8_kv_quantize_int8":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp,
+                        _c_vp]),
+    "fp8w8a8_kv_read_int8":
+        (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64,
+                        _c_i64, _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_fp8_linear":
         (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -312,6 +318,72 @@ def kv_dequantize_fp8(codes: torch.Tensor, scales: torch.Tensor, group: int = 12
         _check(lib.fp8w8a8_kv_dequantize_fp8(
             codes.data_ptr(), scales.data_ptr(), t, w, group, y.data_ptr(),
             y.stride(0), _stream_ptr(codes.device)), "kv_dequantize_fp8")
+    return y
+
+
+def _group_params(t, count, device, name, given):
+    if given is None:
+        return torch.empty((t, count), dtype=torch.float32, device=device)
+    if (given.dtype != torch.float32 or tuple(given.shape) != (t, count)
+            or not given.is_contiguous() or given.device != device):
+        raise ValueError(f"{name} must be a contiguous float32 [{t}, {count}] tensor")
+    return given
+
+
+def kv_quantize_int8(kv: torch.Tensor, group: int = 64, codes: torch.Tensor = None,
+                     scales: torch.Tensor = None, mins: torch.Tensor = None):
+    """K or V rows [T, W] (bf16) -> (codes uint8 [T, W], scales float32
+    [T, W // group], mins float32 [T, W // group]), asymmetric min-max per
+    group.  Outputs may be given (e.g. the next rows of a cache's INT8
+    store)."""
+    lib = load_library()
+    if kv.dtype != torch.bfloat16:
+        raise TypeError("kv must be bfloat16")
+    t, w, ld = _rows(kv, "kv")
+    if group <= 0 or w % group != 0:
+        raise ValueError("the row width must be a multiple of the group")
+    codes = torch.empty((t, w), dtype=torch.uint8, device=kv.device) if codes is None \
+        else codes
+    if (codes.dtype != torch.uint8 or tuple(codes.shape) != (t, w)
+            or not codes.is_contiguous() or codes.device != kv.device):
+        raise ValueError(f"codes must be a contiguous uint8 [{t}, {w}] tensor")
+    scales = _group_params(t, w // group, kv.device, "scales", scales)
+    mins = _group_params(t, w // group, kv.device, "mins", mins)
+    if t > 0:
+        _check(lib.fp8w8a8_kv_quantize_int8(
+            kv.data_ptr(), t, w, ld, group, codes.data_ptr(), scales.data_ptr(),
+            mins.data_ptr(), _stream_ptr(kv.device)), "kv_quantize_int8")
+    return codes, scales, mins
+
+
+def kv_read_int8(codes: torch.Tensor, scales: torch.Tensor, mins: torch.Tensor,
+                 tail: torch.Tensor = None, group: int = 64, out: torch.Tensor = None):
+    """The cache read: the dequantized INT8 history [H, W] followed by the
+    bf16 residual rows ``tail`` [R, W] -> bf16 [H + R, W]."""
+    lib = load_library()
+    if codes.dtype != torch.uint8:
+        raise TypeError("codes must be uint8")
+    h, w, ldc = _rows(codes, "codes")
+    if ldc != w:
+        raise ValueError("codes must be contiguous")
+    if group <= 0 or w % group != 0:
+        raise ValueError("the row width must be a multiple of the group")
+    scales = _group_params(h, w // group, codes.device, "scales", scales)
+    mins = _group_params(h, w // group, codes.device, "mins", mins)
+    r, ldt = 0, w
+    if tail is not None:
+        if tail.dtype != torch.bfloat16:
+            raise TypeError("tail must be bfloat16")
+        r, w2, ldt = _rows(tail, "tail")
+        if w2 != w or tail.device != codes.device:
+            raise ValueError("tail must have the history's width and device")
+    y = _out(h + r, w, codes.device, out)
+    if h + r > 0:
+        _check(lib.fp8w8a8_kv_read_int8(
+            codes.data_ptr() if h else None, scales.data_ptr() if h else None,
+            mins.data_ptr() if h else None, h,
+            tail.data_ptr() if r else None, r, ldt, w, group, y.data_ptr(),
+            y.stride(0), _stream_ptr(codes.device)), "kv_read_int8")
     return y
 
 

@@ -308,6 +308,67 @@ int fp8w8a8_kv_dequantize_fp8(const uint8_t* codes, const float* scales,
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
+int fp8w8a8_kv_quantize_int8(const uint16_t* kv, int64_t rows, int64_t width,
+                             int64_t ld, int64_t group, uint8_t* codes,
+                             float* scales, float* mins, void* stream) {
+  if (!kv || !codes || !scales || !mins) return FP8W8A8_ERR_NULL;
+  if (rows < 0 || rows > kMaxDim || width < 8 || width > kMaxDim ||
+      width % 8 != 0 || !kv_group_ok(width, group) || ld < width || ld % 8 != 0)
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(kv) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(mins) & 3u) != 0)
+    return FP8W8A8_ERR_ALIGN;
+  const int64_t g = width / group;
+  const Range rx = span(kv, rows, width, ld, 2);
+  const Range outs[3] = {span(codes, rows, width, width, 1), span(scales, rows, g, g, 4),
+                         span(mins, rows, g, g, 4)};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], rx)) return FP8W8A8_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FP8W8A8_ERR_ALIAS;
+  }
+  if (rows == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_kv_quantize_int8(kv, rows, width, ld, group, codes,
+                                                  scales, mins,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_kv_read_int8(const uint8_t* codes, const float* scales,
+                         const float* mins, int64_t hist,
+                         const uint16_t* tail, int64_t tail_rows, int64_t ldt,
+                         int64_t width, int64_t group, uint16_t* out,
+                         int64_t ldo, void* stream) {
+  if (!out || (hist > 0 && (!codes || !scales || !mins)) || (tail_rows > 0 && !tail))
+    return FP8W8A8_ERR_NULL;
+  if (hist < 0 || tail_rows < 0 || hist > kMaxDim || tail_rows > kMaxDim ||
+      hist + tail_rows > kMaxDim || width < 8 || width > kMaxDim || width % 8 != 0 ||
+      !kv_group_ok(width, group) || ldo < width || ldo % 8 != 0 ||
+      (tail_rows > 0 && (ldt < width || ldt % 8 != 0)))
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(out) || (tail_rows > 0 && !aligned16(tail)) ||
+      (hist > 0 && ((reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
+                    (reinterpret_cast<uintptr_t>(scales) & 3u) != 0 ||
+                    (reinterpret_cast<uintptr_t>(mins) & 3u) != 0)))
+    return FP8W8A8_ERR_ALIGN;
+  const int64_t g = width / group;
+  const Range ro = span(out, hist + tail_rows, width, ldo, 2);
+  if (overlap(ro, span(codes, hist, width, width, 1)) ||
+      overlap(ro, span(scales, hist, g, g, 4)) || overlap(ro, span(mins, hist, g, g, 4)) ||
+      overlap(ro, span(tail, tail_rows, width, ldt, 2)))
+    return FP8W8A8_ERR_ALIAS;
+  if (hist + tail_rows == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_kv_read_int8(codes, scales, mins, hist, tail,
+                                              tail_rows, ldt, width, group, out, ldo,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
   return layout_for(m, n, k, fused != 0, choose_path(m, n, k),

@@ -40,6 +40,17 @@ hipError_t launch_kv_quantize(const uint16_t* kv, int64_t rows, int64_t width,
 hipError_t launch_kv_dequantize(const uint8_t* codes, const float* scales,
                                 int64_t rows, int64_t width, int64_t group,
                                 uint16_t* out, int64_t ldo, hipStream_t stream);
+// INT8 group-wise cache: codes, one scale and one minimum per group; the
+// read writes the dequantized history rows, then the bf16 tail rows.
+hipError_t launch_kv_quantize_int8(const uint16_t* kv, int64_t rows,
+                                   int64_t width, int64_t ld, int64_t group,
+                                   uint8_t* codes, float* scales, float* mins,
+                                   hipStream_t stream);
+hipError_t launch_kv_read_int8(const uint8_t* codes, const float* scales,
+                               const float* mins, int64_t hist,
+                               const uint16_t* tail, int64_t tail_rows,
+                               int64_t ldt, int64_t width, int64_t group,
+                               uint16_t* out, int64_t ldo, hipStream_t stream);
 
 // Prefill GEMM: y[m,n] = bf16(sum_k qx[m,k] qw[n,k] * sx[m] * sw[n]).
 // The plan fixes the tile configuration and the number of K splits; with

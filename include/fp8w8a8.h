@@ -184,6 +184,46 @@ int fp8w8a8_kv_dequantize_fp8(const uint8_t* codes, const float* scales,
                               uint16_t* out, int64_t ldo, void* stream);
 
 /*
+ * INT8 group-wise key/value cache with a BF16 residual window.  The
+ * checkpoint's Transformers path keeps the KV cache as HQQ INT8 with groups
+ * of 64 and the newest 128 positions in BF16; reading it dequantizes the
+ * history and appends that tail (MOSS-VL quantization README, "KV cache";
+ * MOSS-VL-Realtime-FP8 article, KV-cache section).  HQQ's solver is not on
+ * the pages; the reading is its asymmetric min-max starting point, each step
+ * one IEEE float32 operation:
+ *   per group:  s = fl32(fl32(max - min) / 255), stored with min (a zero
+ *               max or min is taken as +0: the codes keep no sign of zero)
+ *               q = clamp(rne(fl32(fl32(x - min) / s)), 0, 255)  (0 if s == 0)
+ *   read back:  bf16(fl32(fl32(q * s) + min))
+ * The caller keeps the newest tokens (up to the residual length, 128) as
+ * bf16 and moves older ones into the INT8 store with
+ * fp8w8a8_kv_quantize_int8 (at codes + t0 * width, scales / mins +
+ * t0 * width / group).
+ *
+ * fp8w8a8_kv_quantize_int8:
+ *   kv       bf16 [rows, width], row stride ld >= width, ld % 8 == 0 (input)
+ *   codes    uint8 [rows, width], contiguous                         (output)
+ *   scales, mins  float32 [rows, width / group], contiguous          (output)
+ * fp8w8a8_kv_read_int8 (the cache read: history, then tail):
+ *   codes, scales, mins  the INT8 store, hist rows                   (input)
+ *   tail     bf16 [tail_rows, width], row stride ldt >= width, ldt % 8 == 0;
+ *            may be NULL when tail_rows == 0                         (input)
+ *   out      bf16 [hist + tail_rows, width], row stride ldo          (output)
+ * Rules as for the FP8 codec (group a power of two from 8 to 512 dividing
+ * width; the pages' group is 64); codes/scales/mins may be NULL when
+ * hist == 0; tail 16-byte aligned.  A group whose max - min overflows
+ * float32 (values beyond about +-1.7e38) gives unspecified codes.
+ */
+int fp8w8a8_kv_quantize_int8(const uint16_t* kv, int64_t rows, int64_t width,
+                             int64_t ld, int64_t group, uint8_t* codes,
+                             float* scales, float* mins, void* stream);
+int fp8w8a8_kv_read_int8(const uint8_t* codes, const float* scales,
+                         const float* mins, int64_t hist,
+                         const uint16_t* tail, int64_t tail_rows, int64_t ldt,
+                         int64_t width, int64_t group, uint16_t* out,
+                         int64_t ldo, void* stream);
+
+/*
  * The W8A8 Linear on already-quantized operands ("the quantized kernels" of
  * README "FP8-Dynamic"):
  *   y[m,n] = bf16_rne( (sum_k dec(qx[m,k]) * dec(qw[n,k])) * x_scale[m]

@@ -82,7 +82,8 @@ def kv_fp8_dequant_ref(codes: np.ndarray, scales: np.ndarray, group: int):
 # Readings (the pages give no formulas; HQQ's solver is not on them):
 # * asymmetric min-max per group of `group` consecutive values of a token's
 #   row (the starting point of HQQ's fit, without its iterative refinement):
-#   mn = min, mx = max, scale = fl32(fl32(mx - mn) / 255), codes uint8
+#   mn = min, mx = max (a zero extreme taken as +0: affine codes keep no sign
+#   of zero), scale = fl32(fl32(mx - mn) / 255), codes uint8
 #   q = clamp(rne(fl32(fl32(x - mn) / scale)), 0, 255); a constant group
 #   (scale 0) gets q = 0;
 # * reading back: bf16(fl32(fl32(q * scale) + mn)), each step one IEEE
@@ -104,8 +105,9 @@ def kv_int8_quant_ref(kv_bf16_bits: np.ndarray, group: int):
     if not np.all(np.isfinite(x)):
         raise ValueError("inputs must be finite")
     g = x.reshape(r, w // group, group)
-    mn = g.min(axis=2)
-    mx = g.max(axis=2)
+    # + 0 makes a zero extreme +0 (the min or max of +0 and -0 is either)
+    mn = (g.min(axis=2) + np.float32(0.0)).astype(np.float32)
+    mx = (g.max(axis=2) + np.float32(0.0)).astype(np.float32)
     rng_ = (mx - mn).astype(np.float32)
     scale = (rng_ / np.float32(255.0)).astype(np.float32)
     assert scale.dtype == np.float32

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -159,6 +159,28 @@ def test_kv_codec_validation(lib):
     assert _kvd(lib, c=A + 4) == EALIGN
     assert _kvd(lib, o=A + 16) == EALIAS                      # out over codes
     assert _kvd(lib, t=0) == OK
+
+
+def test_kv_int8_validation(lib):
+    q = lambda **k: lib.fp8w8a8_kv_quantize_int8(
+        k.get("x", A), k.get("t", 4), k.get("w", 1024), k.get("ld", 1024), k.get("g", 64),
+        k.get("c", 64 * A), k.get("s", 128 * A), k.get("m", 192 * A), None)
+    assert q(x=None) == ENULL and q(m=None) == ENULL
+    assert q(g=48) == ESHAPE and q(g=1024) == ESHAPE and q(ld=1020) == ESHAPE
+    assert q(m=192 * A + 2) == EALIGN
+    assert q(m=128 * A + 32) == EALIAS                        # mins over scales
+    assert q(t=0) == OK
+    r = lambda **k: lib.fp8w8a8_kv_read_int8(
+        k.get("c", A), k.get("s", 2 * A), k.get("m", 3 * A), k.get("h", 4),
+        k.get("tl", 64 * A), k.get("tr", 2), k.get("ldt", 1024), k.get("w", 1024),
+        k.get("g", 64), k.get("o", 128 * A), k.get("ldo", 1024), None)
+    assert r(o=None) == ENULL
+    assert r(c=None) == ENULL and r(tl=None) == ENULL
+    assert r(c=None, s=None, m=None, h=0, o=128 * A, tr=0, tl=None) == OK   # empty
+    assert r(h=-1) == ESHAPE and r(ldt=1000) == ESHAPE and r(g=24) == ESHAPE
+    assert r(tl=64 * A + 8) == EALIGN
+    assert r(o=64 * A) == EALIAS                              # out over the tail
+    assert r(c=None, s=None, m=None, h=0, tr=0, tl=None, o=128 * A + 8) == EALIGN
 
 
 def _lin(lib, qx=A, sx=2 * A, qw=4 * A, sw=8 * A, m=32, n=64, k=256,
