@@ -639,7 +639,8 @@ def cpu_baseline(target_s=16.0):
         return flops, secs
 
     # Grow the sample until the timed oracle work reaches about target_s.
-    sizes = [(64, 16), (256, 8), (512, 4), (1024, 4), (2048, 4), (4096, 4), (4096, 2)]
+    sizes = [(64, 16), (256, 8), (512, 4), (1024, 4), (2048, 4), (4096, 4), (4096, 2),
+             (4096, 1)]
     for m_s, n_frac in sizes:
         flops, secs = run(m_s, n_frac)
         if secs >= target_s / 2:
