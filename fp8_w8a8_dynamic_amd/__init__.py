@@ -14,7 +14,8 @@ marshalling only).
 from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
                       init_workspace, kv_dequantize_fp8, kv_quantize_fp8,
                       kv_quantize_int8, kv_read_int8, load_library,
-                      quant_linear, quantize_act_per_token,
+                      quant_linear, quantize_act_per_token, rmsnorm_quant_linear,
+                      swiglu_quant_linear,
                       quantize_weight_channelwise, rmsnorm_quantize, swiglu_quantize,
                       workspace_bytes)
 
@@ -23,4 +24,5 @@ __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
            "kv_quantize_int8", "kv_read_int8",
            "load_library", "quant_linear",
            "quantize_act_per_token", "quantize_weight_channelwise",
-           "rmsnorm_quantize", "swiglu_quantize", "workspace_bytes"]
+           "rmsnorm_quantize", "rmsnorm_quant_linear", "swiglu_quantize",
+           "swiglu_quant_linear", "workspace_bytes"]

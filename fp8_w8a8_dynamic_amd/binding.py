@@ -47,6 +47,12 @@ SIGNATURES = {
     "fp8w8a8_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_rmsnorm_quant_linear":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_i64,
+                        _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_swiglu_quant_linear":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64,
+                        _c_i64, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
     "fp8w8a8_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, ctypes.c_int]),
     "fp8w8a8_workspace_init": (ctypes.c_int, [_c_vp, _c_sz, _c_vp]),
     "fp8w8a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -154,7 +160,9 @@ class _Workspaces:
 _workspaces = _Workspaces()
 
 
-def workspace_bytes(m: int, n: int, k: int, fused: bool) -> int:
+def workspace_bytes(m: int, n: int, k: int, fused) -> int:
+    """Workspace for fp8_linear (fused 0 / False), quant_linear (1 / True),
+    rmsnorm_quant_linear (2) or swiglu_quant_linear (3)."""
     return int(load_library().fp8w8a8_workspace_bytes(m, n, k, int(fused)))
 
 
@@ -449,4 +457,60 @@ def quant_linear(x, qw, w_scale, out=None, workspace=None):
         y.data_ptr(), y.stride(0), ws.data_ptr() if ws is not None else None,
         ws.numel() if ws is not None else 0, _stream_ptr(x.device)),
         "quant_linear")
+    return y
+
+
+def rmsnorm_quant_linear(x, gamma, eps, qw, w_scale, out=None, workspace=None):
+    """RMSNorm of x [M, K] with weight gamma [K], then the FP8_DYNAMIC
+    Linear: bit-identical to fp8_linear(*rmsnorm_quantize(x, gamma, eps),
+    qw, w_scale), one kernel at decode sizes."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
+        raise TypeError("x and gamma must be bfloat16")
+    qw = _as_codes(qw)
+    m, k, ldx = _rows(x, "x")
+    n, k2, ldw = _rows(qw, "qw")
+    if k2 != k or ldw != k or qw.device != x.device:
+        raise ValueError("qw must be contiguous [N, K] with the K of x, on x's device")
+    if (gamma.dim() != 1 or gamma.numel() != k or not gamma.is_contiguous()
+            or gamma.device != x.device):
+        raise ValueError(f"gamma must be a contiguous bf16 tensor of {k} elements")
+    w_scale = _scales(w_scale, n, x.device, "w_scale")
+    y = _out(m, n, x.device, out)
+    if m == 0 or n == 0:
+        return y
+    ws = _pick_workspace(x.device, workspace_bytes(m, n, k, 2), workspace)
+    _check(lib.fp8w8a8_rmsnorm_quant_linear(
+        x.data_ptr(), ldx, gamma.data_ptr(), float(eps), qw.data_ptr(),
+        w_scale.data_ptr(), m, n, k, y.data_ptr(), y.stride(0),
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream_ptr(x.device)), "rmsnorm_quant_linear")
+    return y
+
+
+def swiglu_quant_linear(gate, up, qw, w_scale, out=None, workspace=None):
+    """h = bf16(bf16(silu(gate)) * up), then the FP8_DYNAMIC Linear:
+    bit-identical to fp8_linear(*swiglu_quantize(gate, up), qw, w_scale),
+    one kernel at decode sizes."""
+    lib = load_library()
+    if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
+        raise TypeError("gate and up must be bfloat16")
+    qw = _as_codes(qw)
+    m, k, ldg = _rows(gate, "gate")
+    m2, k3, ldu = _rows(up, "up")
+    n, k2, ldw = _rows(qw, "qw")
+    if (m2, k3) != (m, k) or k2 != k or ldw != k:
+        raise ValueError("gate, up [M, K] and qw [N, K] must agree")
+    if up.device != gate.device or qw.device != gate.device:
+        raise ValueError("gate, up and qw must be on one device")
+    w_scale = _scales(w_scale, n, gate.device, "w_scale")
+    y = _out(m, n, gate.device, out)
+    if m == 0 or n == 0:
+        return y
+    ws = _pick_workspace(gate.device, workspace_bytes(m, n, k, 3), workspace)
+    _check(lib.fp8w8a8_swiglu_quant_linear(
+        gate.data_ptr(), ldg, up.data_ptr(), ldu, qw.data_ptr(), w_scale.data_ptr(),
+        m, n, k, y.data_ptr(), y.stride(0),
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream_ptr(gate.device)), "swiglu_quant_linear")
     return y

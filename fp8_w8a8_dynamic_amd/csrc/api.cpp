@@ -135,11 +135,26 @@ struct Layout {
   size_t qx = 0, sx = 0, part = 0, total = 0;
 };
 
-Layout layout_for(int64_t m, int64_t n, int64_t k, bool fused, Path path,
+// What precedes the matmul inside one call: nothing (codes given), the
+// per-token quantizer, or the RMSNorm / SiLU-gated activation with it.
+enum class Pre { kNone = 0, kQuant = 1, kRmsNorm = 2, kSwiGlu = 3 };
+
+// Whether the decode GEMV does the pre-step in its own staging (no
+// workspace for codes).
+bool pre_in_gemv(Pre pre, int64_t m, int64_t n, int64_t k) {
+  switch (pre) {
+    case Pre::kQuant: return fp8w8a8::gemv_fused_fits(m, n, k);
+    case Pre::kRmsNorm: return fp8w8a8::gemv_pre_fits(fp8w8a8::kPreRmsNorm, m, n, k);
+    case Pre::kSwiGlu: return fp8w8a8::gemv_pre_fits(fp8w8a8::kPreSwiGlu, m, n, k);
+    default: return false;
+  }
+}
+
+Layout layout_for(int64_t m, int64_t n, int64_t k, Pre pre, Path path,
                   const fp8w8a8::GemmPlan& plan) {
   Layout L;
   if (m == 0 || n == 0) return L;
-  if (fused && !(path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k))) {
+  if (pre != Pre::kNone && !(path == Path::kGemv && pre_in_gemv(pre, m, n, k))) {
     L.qx = 0;
     L.sx = round_up(static_cast<size_t>(m) * k, 256);
     L.total = L.sx + round_up(static_cast<size_t>(m) * 4, 256);
@@ -371,7 +386,10 @@ int fp8w8a8_kv_read_int8(const uint8_t* codes, const float* scales,
 
 size_t fp8w8a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int fused) {
   if (check_linear_shape(m, n, k, n) != FP8W8A8_OK) return 0;
-  return layout_for(m, n, k, fused != 0, choose_path(m, n, k),
+  const Pre pre = fused == 0 ? Pre::kNone
+                : fused == 2 ? Pre::kRmsNorm
+                : fused == 3 ? Pre::kSwiGlu : Pre::kQuant;
+  return layout_for(m, n, k, pre, choose_path(m, n, k),
                     fp8w8a8::plan_gemm(m, n, k)).total;
 }
 
@@ -392,7 +410,7 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
     return FP8W8A8_ERR_ALIAS;
   const Path path = choose_path(m, n, k);
   const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
-  const Layout L = layout_for(m, n, k, false, path, plan);
+  const Layout L = layout_for(m, n, k, Pre::kNone, path, plan);
   const size_t need = L.total;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
@@ -439,7 +457,7 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
     return FP8W8A8_ERR_ALIAS;
   const Path path = choose_path(m, n, k);
   const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
-  const Layout L = layout_for(m, n, k, true, path, plan);
+  const Layout L = layout_for(m, n, k, Pre::kQuant, path, plan);
   const size_t need = L.total;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
@@ -474,6 +492,101 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
     }
   }
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The linear kernel for `path` on staged codes (qx, sx).
+hipError_t linear_on_codes(Path path, const fp8w8a8::GemmPlan& plan,
+                           const uint8_t* qx, const float* sx, const uint8_t* qw,
+                           const float* w_scale, int64_t m, int64_t n, int64_t k,
+                           uint16_t* y, int64_t ldy, float* part, hipStream_t s) {
+  if (path == Path::kGemv)
+    return fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y, ldy, s);
+  if (path == Path::kGemvTok)
+    return fp8w8a8::launch_gemv_tok(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
+  return fp8w8a8::launch_gemm(plan, qx, sx, qw, w_scale, m, n, k, y, ldy, part, s);
+}
+
+// RMSNorm or SiLU-gated activation, then the Linear: x [m, k] (ldx) with
+// x2 = gamma [k] (kRmsNorm) or up [m, k] (ld2, kSwiGlu).
+int pre_linear(Pre pre, const uint16_t* x, int64_t ldx, const uint16_t* x2,
+               int64_t ld2, float eps, const uint8_t* qw, const float* w_scale,
+               int64_t m, int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !x2 || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
+  int st = check_linear_shape(m, n, k, ldy);
+  if (st != FP8W8A8_OK) return st;
+  if (ldx < k || ldx % 8 != 0) return FP8W8A8_ERR_SHAPE;
+  if (pre == Pre::kSwiGlu && (ld2 < k || ld2 % 8 != 0)) return FP8W8A8_ERR_SHAPE;
+  if (pre == Pre::kRmsNorm && !(eps >= 0.0f && eps <= 3.4028235e38f))
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(x2) || !aligned16(qw) || !aligned16(w_scale) ||
+      !aligned16(y) || (workspace && !aligned16(workspace)))
+    return FP8W8A8_ERR_ALIGN;
+  const Range ry = span(y, m, n, ldy, 2);
+  const Range rx = span(x, m, k, ldx, 2);
+  const Range r2 = pre == Pre::kRmsNorm ? span(x2, 1, k, k, 2) : span(x2, m, k, ld2, 2);
+  if (overlap(ry, rx) || overlap(ry, r2) || overlap(ry, span(qw, n, k, k, 1)) ||
+      overlap(ry, span(w_scale, n, 1, 1, 4)))
+    return FP8W8A8_ERR_ALIAS;
+  const Path path = choose_path(m, n, k);
+  const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
+  const Layout L = layout_for(m, n, k, pre, path, plan);
+  if (L.total > 0) {
+    if (!workspace || workspace_bytes < L.total) return FP8W8A8_ERR_WORKSPACE;
+    const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + L.total};
+    if (overlap(rw, ry) || overlap(rw, rx) || overlap(rw, r2) ||
+        overlap(rw, span(qw, n, k, k, 1)) || overlap(rw, span(w_scale, n, 1, 1, 4)))
+      return FP8W8A8_ERR_ALIAS;
+  }
+  if (m == 0 || n == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int gpre = pre == Pre::kRmsNorm ? fp8w8a8::kPreRmsNorm : fp8w8a8::kPreSwiGlu;
+  hipError_t e;
+  if (path == Path::kGemv && pre_in_gemv(pre, m, n, k)) {
+    e = fp8w8a8::launch_gemv_pre(gpre, x, ldx, x2, ld2, eps, qw, w_scale, m, n, k,
+                                 y, ldy, s);
+  } else {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* qx = ws + L.qx;
+    float* sx = reinterpret_cast<float*>(ws + L.sx);
+    e = pre == Pre::kRmsNorm
+            ? fp8w8a8::launch_rmsnorm_quant(x, m, k, ldx, x2, eps, qx, sx, nullptr, 0, s)
+            : fp8w8a8::launch_swiglu_quant(x, ldx, x2, ld2, m, k, qx, sx, nullptr, 0, s);
+    if (e == hipSuccess)
+      e = linear_on_codes(path, plan, qx, sx, qw, w_scale, m, n, k, y, ldy,
+                          reinterpret_cast<float*>(ws + L.part), s);
+  }
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8w8a8_rmsnorm_quant_linear(const uint16_t* x, int64_t ldx,
+                                 const uint16_t* gamma, float eps,
+                                 const uint8_t* qw, const float* w_scale,
+                                 int64_t m, int64_t n, int64_t k, uint16_t* y,
+                                 int64_t ldy, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return pre_linear(Pre::kRmsNorm, x, ldx, gamma, 0, eps, qw, w_scale, m, n, k, y,
+                    ldy, workspace, workspace_bytes, stream);
+}
+
+int fp8w8a8_swiglu_quant_linear(const uint16_t* gate, int64_t ldg,
+                                const uint16_t* up, int64_t ldu,
+                                const uint8_t* qw, const float* w_scale,
+                                int64_t m, int64_t n, int64_t k, uint16_t* y,
+                                int64_t ldy, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return pre_linear(Pre::kSwiGlu, gate, ldg, up, ldu, 0.0f, qw, w_scale, m, n, k, y,
+                    ldy, workspace, workspace_bytes, stream);
 }
 
 int fp8w8a8_workspace_init(void* workspace, size_t bytes, void* stream) {

@@ -34,11 +34,16 @@
 // bits), derives the float32 scale and quantizes into LDS with exactly the
 // arithmetic of the stand-alone quantization kernel, all while the weights
 // are in flight; unfused, it copies the codes.  Shapes whose codes do not
-// fit read them from global memory instead.
+// fit read them from global memory instead.  Two more fused modes put the
+// BF16 step in front of the quantization into the staging: the RMSNorm
+// (x and gamma; the row sums in the block order of row_ops.h, through LDS)
+// and the SiLU-gated activation (gate and up), each with the arithmetic of
+// its stand-alone kernel, so the codes are those the two-step path makes.
 #include <cstdlib>
 
 #include "device_common.h"
 #include "launch.h"
+#include "row_ops.h"
 
 namespace fp8w8a8 {
 
@@ -55,6 +60,7 @@ constexpr int kLdsRowPad = 16;         // LDS code rows: K + 16 bytes
 constexpr int64_t kStageLds = 80 * 1024;  // + 48 KB of partials
 constexpr int64_t kFusedElems = 16384;  // in-kernel quantization up to M*K
 constexpr int kFusedRegs = kFusedElems / 8 / kThreads;  // x loads per thread
+constexpr int kMaxNormBlocksPerRow = kFusedElems / 512;  // fused RMSNorm staging
 
 __device__ __forceinline__ v8i to_v8i(uint4 lo, uint4 hi) {
   v8i r;
@@ -113,7 +119,9 @@ __device__ __forceinline__ float wave_sum_to_63(float v) {
 }
 
 // STAGE: 0 = codes read from global memory, 1 = codes copied to LDS,
-// 2 = bf16 activations quantized into LDS (fused).  XR: activation loads per
+// 2 = bf16 activations quantized into LDS (fused), 3 = RMSNorm of x with
+// weight x2 (eps) then quantized (needs K % 512 == 0), 4 = SiLU-gated
+// activation of gate x and up x2 (row stride ld2) then quantized.  XR: activation loads per
 // thread for staging.  NI: weight items loaded per wave and batch; every
 // wave issues exactly 2 * NI weight loads per batch (items past its range
 // re-read its last item), so that the wait counts before each use are
@@ -123,7 +131,8 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ qx,
     const float* __restrict__ sx, const uint8_t* __restrict__ qw,
     const float* __restrict__ sw, int M, int lg_mp, int N, int K, int gpw,
-    uint16_t* __restrict__ y, int64_t ldy) {
+    uint16_t* __restrict__ y, int64_t ldy, const uint16_t* __restrict__ x2,
+    int64_t ld2, float eps) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_x[];
   __shared__ float part[kWaves][2][64][4];   // partials of shared row groups
   __shared__ float part1[kWaves][2];         // ... for M = 1 (one value)
@@ -151,9 +160,10 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
   const int lds_stride = (STAGE == 1 ? (K + 1023) / 1024 * 1024 : K) + kLdsRowPad;
 
   // 1) Staging loads of the activations, issued first.
-  uint4 xv[STAGE == 2 ? XR : 1];
+  uint4 xv[STAGE >= 2 ? XR : 1];
+  uint4 x2v[STAGE >= 3 ? XR : 1];
   uint32_t after = 0;   // produced after the staging loads (see below)
-  if constexpr (STAGE == 2) {
+  if constexpr (STAGE >= 2) {
     const int kv8 = K / 8;
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -162,6 +172,10 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
       const int e = min(tid + i * kThreads, M * kv8 - 1);
       const int m = e / kv8, v = e - m * kv8;
       xv[i] = *reinterpret_cast<const uint4*>(x + m * ldx + v * 8);
+      if constexpr (STAGE == 3)
+        x2v[i] = *reinterpret_cast<const uint4*>(x2 + v * 8);          // gamma
+      else if constexpr (STAGE == 4)
+        x2v[i] = *reinterpret_cast<const uint4*>(x2 + m * ld2 + v * 8);  // up
     }
     // Each wave clears its own row maxima (wave-private: no barrier).
     if (lane < kGemvMaxM) s_wmax[wave][lane] = 0u;
@@ -220,7 +234,92 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
   __builtin_amdgcn_sched_barrier(0);
 
   // 3) Activation codes into LDS.
-  if constexpr (STAGE == 2) {
+  if constexpr (STAGE == 4) {
+    // h = bf16(bf16(silu(gate)) * up) in place; the silu form is chosen per
+    // wave slot, which changes no result (row_ops.h).
+    const int kv8 = K / 8;
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int e0 = i * kThreads + wave * 64;
+      if (e0 < M * kv8) {
+        const bool ok = e0 + lane < M * kv8;
+        float unused = 0.0f;
+        xv[i] = __builtin_amdgcn_ballot_w64(ok && any_deep8(xv[i])) == 0
+                    ? swiglu8<true>(xv[i], x2v[i], unused)
+                    : swiglu8<false>(xv[i], x2v[i], unused);
+      }
+    }
+  } else if constexpr (STAGE == 3) {
+    // y = bf16(gamma * bf16(x / sqrt(mean(x^2) + eps))) in place.  With
+    // K % 512 == 0 a wave slot is one whole 512-value block of one row: its
+    // sum is block_sumsq, and the blocks of a row are added in order after
+    // one barrier, exactly as the stand-alone norm kernel adds them.
+    __shared__ float s_blk[kGemvMaxM][kMaxNormBlocksPerRow];
+    __shared__ float s_blk2[kGemvMaxM][kMaxNormBlocksPerRow];
+    __shared__ uint32_t s_amx[kWaves][kGemvMaxM];
+    const int kv8 = K / 8, nblk = kv8 / 64;
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int e0 = i * kThreads + wave * 64;
+      if (e0 < M * kv8) {
+        const int m = e0 / kv8, b = (e0 - m * kv8) / 64;
+        const float bs = block_sumsq(xv[i]);
+        if (lane == 0) s_blk[m][b] = bs;
+      }
+    }
+    if (lane < kGemvMaxM) s_amx[wave][lane] = 0u;
+    lds_barrier();
+    auto row_ss = [&](const float (*blk)[kMaxNormBlocksPerRow], int m) {
+      float ss = 0.0f;
+      for (int b = 0; b < nblk; ++b) ss += blk[m][b];
+      return ss;
+    };
+    bool rare_any = false;                       // uniform: every thread reads
+    for (int m = 0; m < M; ++m) rare_any |= !sumsq_in_range(row_ss(s_blk, m));
+    if (rare_any) {
+      // The rare, exactly scaled path (rows whose float32 sum of squares
+      // under- or overflows): p from the row's amax, then the scaled sums.
+#pragma unroll
+      for (int i = 0; i < XR; ++i) {
+        const int e0 = i * kThreads + wave * 64;
+        if (e0 < M * kv8) {
+          const uint32_t mm = amax8_bits(xv[i], 0u);
+          const uint32_t wm = wave_max_u32(max(mm & 0xffffu, mm >> 16));
+          if (lane == 0) s_amx[wave][e0 / kv8] = max(s_amx[wave][e0 / kv8], wm);
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < XR; ++i) {
+        const int e0 = i * kThreads + wave * 64;
+        if (e0 < M * kv8) {
+          const int m = e0 / kv8, b = (e0 - m * kv8) / 64;
+          uint32_t am = 0;
+          for (int w = 0; w < kWaves; ++w) am = max(am, s_amx[w][m]);
+          const float bs = block_sumsq_scaled(xv[i], pow2_for_amax(am));
+          if (lane == 0) s_blk2[m][b] = bs;
+        }
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int e0 = i * kThreads + wave * 64;
+      if (e0 < M * kv8) {
+        const int m = e0 / kv8;
+        float ss = row_ss(s_blk, m), p = 1.0f;
+        if (!sumsq_in_range(ss)) {
+          uint32_t am = 0;
+          for (int w = 0; w < kWaves; ++w) am = max(am, s_amx[w][m]);
+          p = pow2_for_amax(am);
+          ss = row_ss(s_blk2, m);
+        }
+        float unused = 0.0f;
+        xv[i] = norm8(xv[i], x2v[i], make_norm_factor(ss, K, eps, p), unused);
+      }
+    }
+  }
+  if constexpr (STAGE >= 2) {
     // Row amax (integer max on bf16 magnitude bits): each wave into its own
     // slots, then one barrier, after which every thread takes the max over
     // the waves for the rows it quantizes.
@@ -301,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
     return to_v8i(hv[0], hv[1]);
   };
 
-  auto scale_of = [&](int t) { return STAGE == 2 ? s_scale[t] : sx[t]; };
+  auto scale_of = [&](int t) { return STAGE >= 2 ? s_scale[t] : sx[t]; };
   const int outs = MP * M;   // outputs of one row group
 
   // A row group is done with this wave's contribution: finish it here if it
@@ -549,11 +648,19 @@ bool gemv_fused_fits(int64_t m, int64_t n, int64_t k) {
          m * (k + kLdsRowPad) <= kStageLds;
 }
 
+// The fused pre-step's extra operand: gamma and eps (STAGE 3) or up (STAGE 4).
+struct GemvPre {
+  const uint16_t* x2;
+  int64_t ld2;
+  float eps;
+};
+
 template <int STAGE, int XR, int NI>
 hipError_t launch_ni(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                      const float* sx, const uint8_t* qw, const float* sw,
                      int64_t m, int lg_mp, int64_t n, int64_t k, int gpw,
-                     uint16_t* y, int64_t ldy, hipStream_t stream) {
+                     uint16_t* y, int64_t ldy, const GemvPre& pre,
+                     hipStream_t stream) {
   const int64_t groups = n >> lg_mp;
   const dim3 grid(static_cast<uint32_t>((groups + gpw - 1) / gpw));
   const size_t lds = STAGE == 0 ? 0
@@ -561,7 +668,7 @@ hipError_t launch_ni(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                          ((STAGE == 1 ? (k + 1023) / 1024 * 1024 : k) + kLdsRowPad);
   gemv_fp8_kernel<STAGE, XR, NI><<<grid, dim3(kThreads), lds, stream>>>(
       x, ldx, qx, sx, qw, sw, static_cast<int>(m), lg_mp, static_cast<int>(n),
-      static_cast<int>(k), gpw, y, ldy);
+      static_cast<int>(k), gpw, y, ldy, pre.x2, pre.ld2, pre.eps);
   return hipGetLastError();
 }
 
@@ -569,22 +676,26 @@ template <int STAGE, int XR>
 hipError_t launch_one(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                       const float* sx, const uint8_t* qw, const float* sw,
                       int64_t m, int lg_mp, int64_t n, int64_t k, int gpw,
-                      int ni, uint16_t* y, int64_t ldy, hipStream_t stream) {
+                      int ni, uint16_t* y, int64_t ldy, const GemvPre& pre,
+                      hipStream_t stream) {
+#define FP8W8A8_GEMV_NI(NI) \
+  return launch_ni<STAGE, XR, NI>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, pre, stream)
   switch (ni) {
-    case 1: return launch_ni<STAGE, XR, 1>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
-    case 2: return launch_ni<STAGE, XR, 2>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
-    case 3: return launch_ni<STAGE, XR, 3>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
-    case 4: return launch_ni<STAGE, XR, 4>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
-    case 6: return launch_ni<STAGE, XR, 6>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
-    default: return launch_ni<STAGE, XR, 8>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gpw, y, ldy, stream);
+    case 1: FP8W8A8_GEMV_NI(1);
+    case 2: FP8W8A8_GEMV_NI(2);
+    case 3: FP8W8A8_GEMV_NI(3);
+    case 4: FP8W8A8_GEMV_NI(4);
+    case 6: FP8W8A8_GEMV_NI(6);
+    default: FP8W8A8_GEMV_NI(8);
   }
+#undef FP8W8A8_GEMV_NI
 }
 
-hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
-                       const float* sx, const uint8_t* qw, const float* sw,
-                       int64_t m, int64_t n, int64_t k, uint16_t* y,
-                       int64_t ldy, hipStream_t stream) {
-  if (m == 0 || n == 0) return hipSuccess;
+struct GemvPlan {
+  int lg_mp, gpw, ni;
+};
+
+GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
   int lg_mp = 0;
   while ((1 << lg_mp) < m) ++lg_mp;
   // Row groups per workgroup, measured on MI355X at M = 1, 2, 4, 8 on the
@@ -637,18 +748,52 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
     const int64_t v = std::atoll(e);
     if (v >= 1 && v <= groups) gpw = v;
   }
-  const int gp = static_cast<int>(gpw);
   // Items per wave (the most any wave of a full workgroup gets).
   const int64_t per_wave = (gpw * cs + kWaves - 1) / kWaves;
   const int ni = per_wave <= 1 ? 1 : per_wave <= 2 ? 2 : per_wave <= 3 ? 3
                : per_wave <= 4 ? 4 : per_wave <= 6 ? 6 : kItems;
+  return GemvPlan{lg_mp, static_cast<int>(gpw), ni};
+}
+
+hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
+                       const float* sx, const uint8_t* qw, const float* sw,
+                       int64_t m, int64_t n, int64_t k, uint16_t* y,
+                       int64_t ldy, hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  const GemvPlan pl = plan_gemv(m, n, k);
+  const GemvPre none{nullptr, 0, 0.0f};
   if (x != nullptr) {
     if (!gemv_fused_fits(m, n, k)) return hipErrorInvalidValue;
-    return launch_one<2, kFusedRegs>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gp, ni, y, ldy, stream);
+    return launch_one<2, kFusedRegs>(x, ldx, qx, sx, qw, sw, m, pl.lg_mp, n, k,
+                                     pl.gpw, pl.ni, y, ldy, none, stream);
   }
   if (m * ((k + 1023) / 1024 * 1024 + kLdsRowPad) <= kStageLds)
-    return launch_one<1, 1>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gp, ni, y, ldy, stream);
-  return launch_one<0, 1>(x, ldx, qx, sx, qw, sw, m, lg_mp, n, k, gp, ni, y, ldy, stream);
+    return launch_one<1, 1>(x, ldx, qx, sx, qw, sw, m, pl.lg_mp, n, k, pl.gpw,
+                            pl.ni, y, ldy, none, stream);
+  return launch_one<0, 1>(x, ldx, qx, sx, qw, sw, m, pl.lg_mp, n, k, pl.gpw,
+                          pl.ni, y, ldy, none, stream);
+}
+
+bool gemv_pre_fits(int pre, int64_t m, int64_t n, int64_t k) {
+  if (!gemv_fused_fits(m, n, k) || m > kGemvMaxM) return false;
+  if (pre == kPreRmsNorm) return k % 512 == 0 && k / 512 <= kMaxNormBlocksPerRow;
+  return pre == kPreSwiGlu;
+}
+
+hipError_t launch_gemv_pre(int pre, const uint16_t* x, int64_t ldx,
+                           const uint16_t* x2, int64_t ld2, float eps,
+                           const uint8_t* qw, const float* sw, int64_t m,
+                           int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                           hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (!gemv_pre_fits(pre, m, n, k)) return hipErrorInvalidValue;
+  const GemvPlan pl = plan_gemv(m, n, k);
+  const GemvPre extra{x2, ld2, eps};
+  if (pre == kPreRmsNorm)
+    return launch_one<3, kFusedRegs>(x, ldx, nullptr, nullptr, qw, sw, m, pl.lg_mp,
+                                     n, k, pl.gpw, pl.ni, y, ldy, extra, stream);
+  return launch_one<4, kFusedRegs>(x, ldx, nullptr, nullptr, qw, sw, m, pl.lg_mp, n,
+                                   k, pl.gpw, pl.ni, y, ldy, extra, stream);
 }
 
 }  // namespace fp8w8a8

@@ -79,6 +79,19 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                        int64_t m, int64_t n, int64_t k, uint16_t* y,
                        int64_t ldy, hipStream_t stream);
 
+// Decode GEMV with a BF16 pre-step fused into its activation staging:
+// kPreRmsNorm (x, gamma = x2, eps; needs k % 512 == 0) or kPreSwiGlu
+// (gate = x, up = x2 with row stride ld2).  The codes are bit-identical to
+// those of launch_rmsnorm_quant / launch_swiglu_quant.
+constexpr int kPreRmsNorm = 1;
+constexpr int kPreSwiGlu = 2;
+bool gemv_pre_fits(int pre, int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemv_pre(int pre, const uint16_t* x, int64_t ldx,
+                           const uint16_t* x2, int64_t ld2, float eps,
+                           const uint8_t* qw, const float* sw, int64_t m,
+                           int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                           hipStream_t stream);
+
 // Token-group GEMV, kGemvMaxM < m <= kGemvTokMaxM, on quantized activations.
 constexpr int kGemvTokMaxM = 64;
 hipError_t launch_gemv_tok(const uint8_t* qx, const float* sx,

@@ -13,8 +13,10 @@
 //
 // One wavefront owns one row of k elements (buffer loads and stores, whose
 // descriptors clip the ragged tail; padding lanes hold zeros throughout):
-//   1. ss = sum x^2 in float32 (per-lane v_dot2 sums of bf16 pairs, then a
-//      DPP tree, then across the row's waves in LDS); a row whose
+//   1. ss = sum x^2 in float32 in the fixed block order of row_ops.h (per
+//      512-value block a v_dot2 chain per lane and a DPP tree; blocks added
+//      in order, across the row's waves through LDS), so every layout, and
+//      the decode GEMV's staging, gives the same sum; a row whose
 //      sum leaves [2^-60, 2^127] (squares that underflow or overflow float32)
 //      takes a rare path: p = 2^-e, e the (clamped) exponent of the row's
 //      amax, every x p is exact and below 2 in magnitude, and ss is taken
@@ -38,143 +40,13 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "row_ops.h"
 
 namespace fp8w8a8 {
 
 namespace detail {
 
-constexpr int kNormRowsPerBlock = 4;  // 4 waves, one row each
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL,
-                                                    ROW_MASK, 0xf, false));
-}
-
-// Sum over the 64 lanes (same DPP pattern as wave_max_u32: lanes that a
-// move does not write add the 0 it leaves).  The order of the additions is
-// fixed, so the result is deterministic.
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  v += dpp_f32<0xb1, 0xf>(v);
-  v += dpp_f32<0x4e, 0xf>(v);
-  v += dpp_f32<0x141, 0xf>(v);
-  v += dpp_f32<0x140, 0xf>(v);
-  v += dpp_f32<0x142, 0xa>(v);
-  v += dpp_f32<0x143, 0xc>(v);
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-__device__ __forceinline__ uint32_t amax8_bits(uint4 v, uint32_t m) {
-  m = pk_max_u16(m, bf16x2_abs_bits(v.x));
-  m = pk_max_u16(m, bf16x2_abs_bits(v.y));
-  m = pk_max_u16(m, bf16x2_abs_bits(v.z));
-  m = pk_max_u16(m, bf16x2_abs_bits(v.w));
-  return m;
-}
-
-// Row-uniform factor p = 2^-e from the row's amax bit pattern (15 bits).
-__device__ __forceinline__ float pow2_for_amax(uint32_t amax_bits) {
-  int e = static_cast<int>(amax_bits >> 7) - 127;
-  e = e < -126 ? -126 : (e > 126 ? 126 : e);
-  return __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
-}
-
-typedef __bf16 bf16x2_dot_t __attribute__((ext_vector_type(2)));
-
-// Sum of squares of 8 packed bf16 with v_dot2c_f32_bf16 (two exact bf16
-// products added to the float32 accumulator per instruction).  Subnormal
-// bf16 inputs may count as zero here; their squares are below 2^-252, which
-// is negligible next to any sum this path keeps (at least 2^-60; smaller
-// sums take the rare, exactly scaled path).
-__device__ __forceinline__ float sumsq8(uint4 v, float s) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2_dot_t a = __builtin_bit_cast(bf16x2_dot_t, w[i]);
-    s = __builtin_amdgcn_fdot2_f32_bf16(a, a, s, false);
-  }
-  return s;
-}
-
-__device__ __forceinline__ float sumsq8_scaled(uint4 v, float p, float s) {
-  const float e[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = __builtin_fmaf(e[i] * p, e[i] * p, s);
-  return s;
-}
-
-// True when the row's float32 sum of squares is trustworthy unscaled.
-__device__ __forceinline__ bool sumsq_in_range(float ss) {
-  return ss >= 0x1p-60f && ss <= 0x1p127f;
-}
-
-// f with f * p = 1 / sqrt(mean(x^2) + eps), from the (scaled) sum of squares.
-__device__ __forceinline__ float norm_factor(float ss, int64_t k, float eps,
-                                             float p) {
-  const float ms = ss / static_cast<float>(k);
-  const double pd = static_cast<double>(p);
-  const double d = __builtin_sqrt(static_cast<double>(ms) +
-                                  static_cast<double>(eps) * pd * pd);
-  return d > 0.0 ? static_cast<float>(1.0 / d) : 1.0f;
-}
-
-// t = bf16(x * c) (ONE_MUL) or bf16((x * p) * f), then y = bf16(gamma t) for
-// two packed elements; am accumulates max |gamma t|.
-template <bool ONE_MUL>
-__device__ __forceinline__ uint32_t norm2(uint32_t x, uint32_t g, float p,
-                                          float f, float& am) {
-  float a = bf16_lo(x), b = bf16_hi(x);
-  if (ONE_MUL) {
-    a *= f;
-    b *= f;
-  } else {
-    a = (a * p) * f;
-    b = (b * p) * f;
-  }
-  const uint32_t t = pack_bf16x2(a, b);
-  const float ya = bf16_lo(g) * bf16_lo(t), yb = bf16_hi(g) * bf16_hi(t);
-  am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(ya), __builtin_fabsf(yb)));
-  return pack_bf16x2(ya, yb);
-}
-
-template <bool ONE_MUL>
-__device__ __forceinline__ uint4 norm8(uint4 x, uint4 g, float p, float f,
-                                       float& am) {
-  uint4 r;
-  r.x = norm2<ONE_MUL>(x.x, g.x, p, f, am);
-  r.y = norm2<ONE_MUL>(x.y, g.y, p, f, am);
-  r.z = norm2<ONE_MUL>(x.z, g.z, p, f, am);
-  r.w = norm2<ONE_MUL>(x.w, g.w, p, f, am);
-  return r;
-}
-
-// The row's scale from max |gamma t| over the row: the bf16 rounding is
-// monotonic, so max |y| = bf16(max |gamma t|).
-__device__ __forceinline__ float scale_from_row_max(float am) {
-  return row_scale(__uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(am)) << 16));
-}
-
-__device__ __forceinline__ float scale_from_products(float am) {
-  // non-negative floats order like their bit patterns
-  return scale_from_row_max(__uint_as_float(wave_max_u32(__float_as_uint(am))));
-}
-
-// Row-uniform factor p and whether p * f is a normal float.
-struct NormFactor {
-  float p, f, pf;
-  bool one_mul;
-};
-
-__device__ __forceinline__ NormFactor make_norm_factor(float ss, int64_t k,
-                                                       float eps, float p) {
-  NormFactor n;
-  n.p = p;
-  n.f = norm_factor(ss, k, eps, p);
-  n.pf = p * n.f;
-  n.one_mul = n.pf >= 0x1p-126f && n.pf <= 0x1p127f;
-  return n;
-}
+constexpr int kNormRowsPerBlock = 4;  // one-wave-per-row layouts
 
 // Sum (SUM) or max (!SUM, non-negative floats) of one value per wave over
 // the S waves that share a row; `slot` is this exchange's own LDS array.
@@ -192,6 +64,35 @@ __device__ __forceinline__ float row_combine(float v, float* slot, int wave) {
   return r;
 }
 
+// The row's sum of squares in block order: this wave holds blocks
+// part * NV .. part * NV + NV - 1 (vector i of a lane is in block
+// part * NV + i); with S > 1 the block sums meet in LDS (blk: this row's
+// S * NV slots) and every wave adds all of them in order.  Unconditional
+// barrier for S > 1.
+template <int NV, int S, bool SCALED>
+__device__ __forceinline__ float row_sumsq(const uint4 (&v)[NV], float p,
+                                           float* blk, int part) {
+  float b[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    b[i] = SCALED ? block_sumsq_scaled(v[i], p) : block_sumsq(v[i]);
+  if (S == 1) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ss += b[i];
+    return ss;
+  }
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) blk[part * NV + i] = b[i];
+  }
+  __syncthreads();
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < S * NV; ++j) ss += blk[j];
+  return ss;
+}
+
 // A row of k elements is split over S waves of a workgroup (4 / S rows per
 // workgroup), each wave holding NV 16-byte vectors of the row per lane.
 template <int NV, int S>
@@ -199,10 +100,11 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int k, int64_t ldx,
     const uint16_t* __restrict__ gamma, float eps, uint8_t* __restrict__ q,
     float* __restrict__ scale, uint16_t* __restrict__ y, int64_t ldy) {
-  __shared__ float s_ss[4], s_amx[4], s_ss2[4], s_amy[4];
+  __shared__ float s_blk[4][S * NV], s_blk2[4][S * NV], s_amx[4], s_amy[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (4 / S) + wave / S;
+  const int rloc = wave / S;                     // row within the workgroup
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (4 / S) + rloc;
   const int part = wave % S;
   // Waves past the last row still take part in the exchanges, with empty
   // descriptors (no memory is touched).
@@ -217,10 +119,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (v0 + i * 64) * 16u);
 #pragma unroll
   for (int i = 0; i < NV; ++i) g[i] = buf_load16(gsrc, (v0 + i * 64) * 16u);
-  float ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) ss = sumsq8(v[i], ss);
-  ss = row_combine<S, true>(wave_sum_f32(ss), s_ss, wave);
+  float ss = row_sumsq<NV, S, false>(v, 1.0f, s_blk[rloc], part);
   float p = 1.0f;
   const bool rare = !sumsq_in_range(ss);   // uniform over the row's waves
   if (S == 1) {
@@ -229,14 +128,11 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
 #pragma unroll
       for (int i = 0; i < NV; ++i) m = amax8_bits(v[i], m);
       p = pow2_for_amax(wave_max_u32(max(m & 0xffffu, m >> 16)));
-      float ss2 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) ss2 = sumsq8_scaled(v[i], p, ss2);
-      ss = wave_sum_f32(ss2);
+      ss = row_sumsq<NV, 1, true>(v, p, nullptr, 0);
     }
   } else {
-    // The rare path's two exchanges run for every row (their barriers must
-    // be reached by all waves); only rows that need them use the results.
+    // The rare path's exchanges run for every row (their barriers must be
+    // reached by all waves); only rows that need them use the results.
     uint32_t m = 0;
     if (rare) {
 #pragma unroll
@@ -245,12 +141,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     const float amx = row_combine<S, false>(
         __uint_as_float(wave_max_u32(max(m & 0xffffu, m >> 16)) << 16), s_amx, wave);
     if (rare) p = pow2_for_amax(__float_as_uint(amx) >> 16);
-    float ss2 = 0.0f;
-    if (rare) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) ss2 = sumsq8_scaled(v[i], p, ss2);
-    }
-    ss2 = row_combine<S, true>(wave_sum_f32(ss2), s_ss2, wave);
+    const float ss2 = row_sumsq<NV, S, true>(v, p, s_blk2[rloc], part);
     if (rare) ss = ss2;
   }
   const NormFactor nf = make_norm_factor(ss, k, eps, p);
@@ -278,40 +169,41 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   if (live && part == 0 && lane == 0) scale[row] = s;
 }
 
-// Rows longer than the register-resident variants: the same arithmetic in
-// three passes over the row (sum of squares, amax of y, output; a fourth for
-// the amax of x on the rare rescaled path), the later ones reading the row
-// again from L2.  (x * 1) * (p f) is the same product as x * (p f).
+// Rows longer than the register-resident variants: the same arithmetic,
+// block by block, in three passes over the row (sum of squares, amax of y,
+// output; a fourth for the amax of x on the rare, rescaled path), the later
+// ones reading the row again from L2.  (x * 1) * (p f) is the same product
+// as x * (p f).
 __global__ __launch_bounds__(256) void rmsnorm_quant_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
     const uint16_t* __restrict__ gamma, float eps, uint8_t* __restrict__ q,
     float* __restrict__ scale, uint16_t* __restrict__ y, int64_t ldy) {
   const int lane = threadIdx.x & 63;
-  const int64_t row =
-      static_cast<int64_t>(blockIdx.x) * kNormRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kNormRowsPerBlock +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
   const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx);
   const uint4* gsrc = reinterpret_cast<const uint4*>(gamma);
   const int64_t nvec = k >> 3;
+  auto xv = [&](int64_t idx) { return idx < nvec ? src[idx] : make_uint4(0, 0, 0, 0); };
+  auto gv = [&](int64_t idx) { return idx < nvec ? gsrc[idx] : make_uint4(0, 0, 0, 0); };
   float ss = 0.0f;
-  for (int64_t idx = lane; idx < nvec; idx += 64) ss = sumsq8(src[idx], ss);
-  ss = wave_sum_f32(ss);
+  for (int64_t base = 0; base < nvec; base += 64) ss += block_sumsq(xv(base + lane));
   float p = 1.0f;
   if (!sumsq_in_range(ss)) {
     uint32_t m = 0;
-    for (int64_t idx = lane; idx < nvec; idx += 64) m = amax8_bits(src[idx], m);
+    for (int64_t base = 0; base < nvec; base += 64) m = amax8_bits(xv(base + lane), m);
     p = pow2_for_amax(wave_max_u32(max(m & 0xffffu, m >> 16)));
     ss = 0.0f;
-    for (int64_t idx = lane; idx < nvec; idx += 64)
-      ss = sumsq8_scaled(src[idx], p, ss);
-    ss = wave_sum_f32(ss);
+    for (int64_t base = 0; base < nvec; base += 64)
+      ss += block_sumsq_scaled(xv(base + lane), p);
   }
   const NormFactor nf = make_norm_factor(ss, k, eps, p);
   const float pa = nf.one_mul ? 1.0f : nf.p, fa = nf.one_mul ? nf.pf : nf.f;
   float am = 0.0f;
-  for (int64_t idx = lane; idx < nvec; idx += 64)
-    norm8<false>(src[idx], gsrc[idx], pa, fa, am);
-  const float s = scale_from_products(am);
+  for (int64_t base = 0; base < nvec; base += 64)
+    norm8<false>(xv(base + lane), gv(base + lane), pa, fa, am);
+  const float s = scale_from_row_max(__uint_as_float(wave_max_u32(__float_as_uint(am))));
   const RowDivisor d = make_divisor(s);
   uint2* dst = reinterpret_cast<uint2*>(q + row * k);
   uint4* ydst = y != nullptr ? reinterpret_cast<uint4*>(y + row * ldy) : nullptr;

@@ -13,13 +13,11 @@
 // and up once, forms h in registers, takes the row's amax and writes the
 // codes and the scale; h itself is written only on request.
 //
-// silu in float32: y = -g log2(e), E = 2^y (v_exp_f32), silu = g * rcp(1 + E)
-// for g >= -44 (E <= 2^64, relative error about |y| 2^-24 from the rounding
-// of y plus a few ulps).  Below -44, 1 + E is E to float32 precision and
-// silu(g) = g e^g (1 - e^g + ...) = g e^g to 2^-63, evaluated as
-// g * 2^-64 * 2^(g log2(e) + 64) so that no step underflows before the last
-// (v_ldexp_f32 rounds into the subnormals correctly).  The choice is made
-// per wave over its slice of the row, so the common case pays for one form.
+// silu in float32 (row_ops.h): g * rcp(1 + 2^(-g log2 e)) for g >= -44
+// (relative error about |g| 2^-24 from the rounding of the exponent plus a
+// few ulps), an exponent-shifted g e^g below.  The choice is made per wave
+// over its slice of the row, so the common case pays for one form; it
+// changes no result.
 //
 // Layout: a row of i elements is split over S waves of a workgroup (S = 1,
 // 2 or 4; 4 / S rows per workgroup of 4 waves), each wave holding NV
@@ -28,56 +26,11 @@
 // ragged tail (padding lanes hold g = u = 0, hence h = 0).
 #include "device_common.h"
 #include "launch.h"
+#include "row_ops.h"
 
 namespace fp8w8a8 {
 
 namespace detail {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSiluSplit = -44.0f;
-
-__device__ __forceinline__ float silu_common(float g) {
-  const float e = __builtin_amdgcn_exp2f(g * -kLog2e);
-  return g * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-__device__ __forceinline__ float silu_any(float g) {
-  const float t = g * kLog2e;
-  const float deep = g * __builtin_ldexpf(__builtin_amdgcn_exp2f(t + 64.0f), -64);
-  return g >= kSiluSplit ? silu_common(g) : deep;
-}
-
-// h = bf16(bf16(silu(g)) * u) for two packed elements; am accumulates the
-// largest |bf16(silu(g)) * u|.
-template <bool COMMON>
-__device__ __forceinline__ uint32_t swiglu2(uint32_t g2, uint32_t u2, float& am) {
-  const float ga = bf16_lo(g2), gb = bf16_hi(g2);
-  const uint32_t s = COMMON ? pack_bf16x2(silu_common(ga), silu_common(gb))
-                            : pack_bf16x2(silu_any(ga), silu_any(gb));
-  const float ha = bf16_lo(s) * bf16_lo(u2), hb = bf16_hi(s) * bf16_hi(u2);
-  am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(ha), __builtin_fabsf(hb)));
-  return pack_bf16x2(ha, hb);
-}
-
-template <bool COMMON>
-__device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u, float& am) {
-  uint4 h;
-  h.x = swiglu2<COMMON>(g.x, u.x, am);
-  h.y = swiglu2<COMMON>(g.y, u.y, am);
-  h.z = swiglu2<COMMON>(g.z, u.z, am);
-  h.w = swiglu2<COMMON>(g.w, u.w, am);
-  return h;
-}
-
-// Whether any of the 8 packed gate values is below kSiluSplit.
-__device__ __forceinline__ bool any_deep8(uint4 g) {
-  const float m = __builtin_fminf(
-      __builtin_fminf(__builtin_fminf(bf16_lo(g.x), bf16_hi(g.x)),
-                      __builtin_fminf(bf16_lo(g.y), bf16_hi(g.y))),
-      __builtin_fminf(__builtin_fminf(bf16_lo(g.z), bf16_hi(g.z)),
-                      __builtin_fminf(bf16_lo(g.w), bf16_hi(g.w))));
-  return m < kSiluSplit;
-}
 
 template <int NV, int S>
 __global__ __launch_bounds__(256) void swiglu_quant_kernel(

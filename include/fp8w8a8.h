@@ -258,8 +258,38 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
                          size_t workspace_bytes, void* stream);
 
 /*
- * Workspace size in bytes for fp8w8a8_fp8_linear (fused == 0) or
- * fp8w8a8_quant_linear (fused != 0) at the given sizes; 0 when the call needs
+ * The adjacent fusions followed by the Linear, in one call: exactly
+ * fp8w8a8_rmsnorm_quantize(x, gamma, eps) (or fp8w8a8_swiglu_quantize(gate,
+ * up)) followed by fp8w8a8_fp8_linear, with bit-identical output.  At decode
+ * sizes (m <= 4 and m * k <= 16384; for the norm also k % 512 == 0) the
+ * norm or activation runs inside the decode GEMV's activation staging, one
+ * kernel in all; otherwise its codes go through the workspace.
+ *   x / gate bf16 [m, k], row stride ldx / ldg >= k, % 8 == 0        (input)
+ *   gamma    bf16 [k]                                                (input)
+ *   up       bf16 [m, k], row stride ldu >= k, ldu % 8 == 0          (input)
+ *   qw, w_scale, y, ldy as for fp8w8a8_fp8_linear
+ *   workspace    at least fp8w8a8_workspace_bytes(m, n, k, 2) (norm) or
+ *                (m, n, k, 3) (activation) bytes
+ * Rules as for fp8w8a8_fp8_linear and for the two fused steps.
+ */
+int fp8w8a8_rmsnorm_quant_linear(const uint16_t* x, int64_t ldx,
+                                 const uint16_t* gamma, float eps,
+                                 const uint8_t* qw, const float* w_scale,
+                                 int64_t m, int64_t n, int64_t k, uint16_t* y,
+                                 int64_t ldy, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+int fp8w8a8_swiglu_quant_linear(const uint16_t* gate, int64_t ldg,
+                                const uint16_t* up, int64_t ldu,
+                                const uint8_t* qw, const float* w_scale,
+                                int64_t m, int64_t n, int64_t k, uint16_t* y,
+                                int64_t ldy, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace size in bytes for fp8w8a8_fp8_linear (fused == 0),
+ * fp8w8a8_quant_linear (fused == 1, or any value other than 0, 2, 3),
+ * fp8w8a8_rmsnorm_quant_linear (fused == 2) or
+ * fp8w8a8_swiglu_quant_linear (fused == 3) at the given sizes; 0 when the call needs
  * none, and 0 for invalid sizes.  The workspace is plain scratch that holds
  * the quantized activations [m, k] and their scales [m] when a fused call
  * quantizes in a separate kernel before the matmul, and float32 partial sums

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -181,6 +181,40 @@ def test_kv_int8_validation(lib):
     assert r(tl=64 * A + 8) == EALIGN
     assert r(o=64 * A) == EALIAS                              # out over the tail
     assert r(c=None, s=None, m=None, h=0, tr=0, tl=None, o=128 * A + 8) == EALIGN
+
+
+def test_pre_linear_validation(lib):
+    nrm = lambda **k: lib.fp8w8a8_rmsnorm_quant_linear(
+        k.get("x", A), k.get("ldx", 256), k.get("g", 2 * A), k.get("eps", 1e-6),
+        k.get("qw", 4 * A), k.get("sw", 8 * A), k.get("m", 32), k.get("n", 64),
+        k.get("k", 256), k.get("y", 16 * A), k.get("ldy", 64), k.get("ws", None),
+        k.get("wsb", 0), None)
+    assert nrm(x=None) == ENULL and nrm(g=None) == ENULL
+    assert nrm(k=192, ldx=192) == ESHAPE                       # k % 128
+    assert nrm(n=24) == ESHAPE
+    assert nrm(ldx=200) == ESHAPE
+    assert nrm(eps=-1.0) == ESHAPE and nrm(eps=float("nan")) == ESHAPE
+    assert nrm(g=2 * A + 8) == EALIGN
+    assert nrm(y=A + 512) == EALIAS                            # y over x
+    assert nrm(y=2 * A) == EALIAS                              # y over gamma
+    assert nrm() == EWS                                        # m = 32 needs a workspace
+    assert nrm(m=0) == EWS or nrm(m=0, ws=64 * A, wsb=1 << 20) == OK
+    swi = lambda **k: lib.fp8w8a8_swiglu_quant_linear(
+        k.get("g", A), k.get("ldg", 256), k.get("u", 2 * A), k.get("ldu", 256),
+        k.get("qw", 4 * A), k.get("sw", 8 * A), k.get("m", 32), k.get("n", 64),
+        k.get("k", 256), k.get("y", 16 * A), k.get("ldy", 64), k.get("ws", None),
+        k.get("wsb", 0), None)
+    assert swi(u=None) == ENULL
+    assert swi(ldu=200) == ESHAPE
+    assert swi(u=2 * A + 4) == EALIGN
+    assert swi(y=2 * A + 256) == EALIAS                        # y over up
+    assert swi() == EWS
+    ws_norm = lib.fp8w8a8_workspace_bytes(32, 64, 256, 2)
+    assert ws_norm == lib.fp8w8a8_workspace_bytes(32, 64, 256, 1) > 0
+    assert lib.fp8w8a8_workspace_bytes(1, 4096, 4096, 2) == 0   # fused into the GEMV
+    assert lib.fp8w8a8_workspace_bytes(1, 4096, 4224, 2) > 0    # k % 512 != 0
+    assert lib.fp8w8a8_workspace_bytes(1, 4096, 4224, 3) == 0
+    assert lib.fp8w8a8_workspace_bytes(2, 4096, 12288, 3) > 0   # m * k too large
 
 
 def _lin(lib, qx=A, sx=2 * A, qw=4 * A, sw=8 * A, m=32, n=64, k=256,
