@@ -29,7 +29,9 @@ Also measured and printed on the same JSON line:
   residual window (quantizing into the store; reading history + tail);
 * ``layer_with_fusions``: one layer's whole Linear path with the fused norms
   and activation (norm -> q|k|v, o, norm -> gate|up, SwiGLU -> down) at
-  M = 4096 and M = 1, beside the unfused chain;
+  M = 4096 and M = 1 through the single-call entries (at M = 1 the norm and
+  the activation run inside the GEMV), beside the same chain as separate
+  calls and beside the unfused chain;
 * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the same
   workload on the host's cores.
 
@@ -61,14 +63,20 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # as null once that code differs.
 KERNEL_TRAFFIC = {
     "gemm": {"files": ("gemm.hip", "device_common.h"),
-             "sha1": "9683d2565fe3d221443e7f712aa839b0dbba9bd6",
-             "bytes": 1492966 * 1024},
-    "rmsnorm_quant": {"files": ("norm.hip", "device_common.h"),
-                      "sha1": "7b56739909f3606c5939c9a9598f4fdb7af37bf0",
-                      "bytes": (16502 * 2 + 16416) * 1024},
-    "swiglu_quant": {"files": ("swiglu.hip", "device_common.h"),
-                     "sha1": "5a78ec8fcf4d58acdd7ba7fef8056f929ac9c383",
-                     "bytes": (98454 * 2 + 49287) * 1024},
+             "sha1": "1ee7953892b20a2b7773e2512e426ed8c1c835f5",
+             "bytes": 1493114 * 1024},
+    "rmsnorm_quant": {"files": ("norm.hip", "row_ops.h", "device_common.h"),
+                      "sha1": "b705eec0b08b238db4b13d64c022f7e387fd5c51",
+                      "bytes": (16492 * 2 + 16416) * 1024},
+    "swiglu_quant": {"files": ("swiglu.hip", "row_ops.h", "device_common.h"),
+                     "sha1": "ec70ba76bffcc6b866b9ec5dbc6dd93875e57d26",
+                     "bytes": (98412 * 2 + 49280) * 1024},
+    "kv_dequant": {"files": ("kvcache.hip", "device_common.h"),
+                   "sha1": "83d24ec97a97cb29dc032c3d41475d8a58bd8239",
+                   "bytes": (16908 * 2 + 65629) * 1024},
+    "kv_int8_read": {"files": ("kvcache.hip", "device_common.h"),
+                     "sha1": "83d24ec97a97cb29dc032c3d41475d8a58bd8239",
+                     "bytes": (18501 * 2 + 65619) * 1024},
 }
 
 
@@ -385,6 +393,49 @@ def graph_of(torch, fn, calls):
 
 
 NORM_CALLS_PER_GRAPH = 20
+ROTATE_BYTES = 600 << 20      # distinct bytes per replay: > 2x the 256 MB MALL
+
+
+MAX_COPIES = 64
+
+
+def copies_for(nbytes):
+    """Copies of a call's buffers such that one replay of the graph touches
+    ROTATE_BYTES of distinct memory: the last-level cache (256 MB) then holds
+    none of a call's data when that call comes round again, so every figure
+    of a call of 10 MB or more is an HBM figure.  At most MAX_COPIES (calls
+    smaller than that, e.g. one decode token's row, are cache-resident in
+    use anyway)."""
+    return max(1, min(MAX_COPIES, -(-ROTATE_BYTES // nbytes)))
+
+
+def rotating(fns):
+    """One callable that runs fns[0], fns[1], ... in turn, one per call (so
+    the calls captured into a graph cycle through the buffer copies)."""
+    state = [0]
+
+    def f():
+        fns[state[0] % len(fns)]()
+        state[0] += 1
+    return f
+
+
+def time_graph(torch, fns, reps, nbytes):
+    """HIP-graph replays of max(NORM_CALLS_PER_GRAPH, len(fns)) calls cycling
+    over fns (one per set of buffer copies), events on the replay stream:
+    us and GB/s of `nbytes` algorithmic bytes per call."""
+    calls = max(NORM_CALLS_PER_GRAPH, len(fns))
+    gr = graph_of(torch, rotating(fns), calls)
+    for _ in range(max(10, reps // 10)):
+        gr.replay()
+    torch.cuda.synchronize()
+    t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
+    del gr
+    t /= calls
+    return {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
+            "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes": nbytes, "buffer_copies": len(fns),
+            "slice_gbs": spread([nbytes * calls / ts / 1e9 for ts in slices])}
 
 
 def bench_norm(torch, fq, reps, m=PREFILL_M, k=4096, eps=1e-6):
@@ -393,37 +444,29 @@ def bench_norm(torch, fq, reps, m=PREFILL_M, k=4096, eps=1e-6):
     bytes (x and gamma in; codes, scales and, when stored, the bf16 norm
     output out), with and without the bf16 output, and the unfused sequence
     (torch's bf16 rms_norm, then this library's quantizer) for comparison.
-    Each figure is a HIP-graph replay of NORM_CALLS_PER_GRAPH calls, timed
-    with events on the replay stream."""
+    Each figure is a HIP-graph replay whose calls cycle over copies of the
+    buffers (time_graph)."""
     from workloads import norm_inputs
     xb, gb = norm_inputs(m, k, seed=0)
-    x, g = to_dev(xb, torch), to_dev(gb, torch)
-    y = torch.empty_like(x)
+    x0, g = to_dev(xb, torch), to_dev(gb, torch)
     base = 2 * m * k + 2 * k + m * k + 4 * m
+    nc = copies_for(base)
+    xs = [x0] + [x0.clone() for _ in range(nc - 1)]
+    ys = [torch.empty_like(x0) for _ in range(nc)]
 
-    def unfused():
-        n = torch.nn.functional.rms_norm(x, (k,), weight=g, eps=eps)
+    def unfused(i):
+        n = torch.nn.functional.rms_norm(xs[i], (k,), weight=g, eps=eps)
         fq.quantize_act_per_token(n)
 
     res = {}
-    for name, fn, nbytes in (
-            ("fused", lambda: fq.rmsnorm_quantize(x, g, eps), base),
+    for name, mk, nbytes in (
+            ("fused", lambda i: lambda: fq.rmsnorm_quantize(xs[i], g, eps), base),
             ("fused_with_normed_output",
-             lambda: fq.rmsnorm_quantize(x, g, eps, out=y), base + 2 * m * k),
-            ("unfused_torch_rms_norm_then_quantize", unfused, base)):
-        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
-        for _ in range(max(10, reps // 10)):
-            gr.replay()
-        torch.cuda.synchronize()
-        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
-        t /= NORM_CALLS_PER_GRAPH
-        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
-                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes": nbytes,
-                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
-                                          for ts in slices])}
-        del gr
-    del x, g, y
+             lambda i: lambda: fq.rmsnorm_quantize(xs[i], g, eps, out=ys[i]),
+             base + 2 * m * k),
+            ("unfused_torch_rms_norm_then_quantize", lambda i: lambda: unfused(i), base)):
+        res[name] = time_graph(torch, [mk(i) for i in range(nc)], reps, nbytes)
+    del xs, ys, g
     torch.cuda.empty_cache()
     return res
 
@@ -434,51 +477,46 @@ def bench_swiglu(torch, fq, reps, m=PREFILL_M, n=12288):
     gate_up output [m, 2n]: GB/s of algorithmic bytes (gate and up in; codes
     and scales out; plus h when stored), beside the unfused sequence (torch's
     bf16 silu and multiply, then this library's quantizer).  HIP-graph
-    replays, as for the norm."""
+    replays over buffer copies, as for the norm."""
     from workloads import swiglu_inputs
     gb, ub = swiglu_inputs(m, n, seed=0)
-    gu = to_dev(np.concatenate([gb, ub], axis=1), torch)
-    g, u = gu[:, :n], gu[:, n:]
-    h = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    gu0 = to_dev(np.concatenate([gb, ub], axis=1), torch)
     base = 4 * m * n + m * n + 4 * m
+    nc = copies_for(base)
+    gus = [gu0] + [gu0.clone() for _ in range(nc - 1)]
+    hs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(nc)]
 
-    def unfused():
-        a = torch.nn.functional.silu(g) * u
+    def unfused(i):
+        a = torch.nn.functional.silu(gus[i][:, :n]) * gus[i][:, n:]
         fq.quantize_act_per_token(a)
 
     res = {}
-    for name, fn, nbytes in (
-            ("fused", lambda: fq.swiglu_quantize(g, u), base),
-            ("fused_with_h_output", lambda: fq.swiglu_quantize(g, u, out=h),
+    for name, mk, nbytes in (
+            ("fused", lambda i: lambda: fq.swiglu_quantize(gus[i][:, :n], gus[i][:, n:]),
+             base),
+            ("fused_with_h_output",
+             lambda i: lambda: fq.swiglu_quantize(gus[i][:, :n], gus[i][:, n:], out=hs[i]),
              base + 2 * m * n),
-            ("unfused_torch_silu_mul_then_quantize", unfused, base)):
-        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
-        for _ in range(max(10, reps // 10)):
-            gr.replay()
-        torch.cuda.synchronize()
-        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
-        t /= NORM_CALLS_PER_GRAPH
-        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
-                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes": nbytes,
-                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
-                                          for ts in slices])}
-        del gr
-    del gu, g, u, h
+            ("unfused_torch_silu_mul_then_quantize", lambda i: lambda: unfused(i), base)):
+        res[name] = time_graph(torch, [mk(i) for i in range(nc)], reps, nbytes)
+    del gus, hs
     torch.cuda.empty_cache()
     return res
 
 
 def bench_fused_layer(torch, fq, m, steps, copies=1, eps=1e-6):
     """One layer's Linear path with the adjacent fusions, HIP-graph replays:
-        rmsnorm_quantize(x1)       -> fp8_linear(q|k|v)        [6144 x 4096]
-        quant_linear(attention out)                            (o_proj)
-        rmsnorm_quantize(x2)       -> fp8_linear(gate|up)      [24576 x 4096]
-        swiglu_quantize(gate, up)  -> fp8_linear(down)         [4096 x 12288]
-    beside the same chain with torch's bf16 rms_norm and silu * up feeding
-    quant_linear.  Attention and the residual adds are not part of it (their
-    inputs are seeded data).  `copies` layers with distinct weights run per
-    replay so that decode-sized steps read their weights from HBM."""
+        rmsnorm_quant_linear(x1, q|k|v)         [6144 x 4096]
+        quant_linear(attention out)             (o_proj)
+        rmsnorm_quant_linear(x2, gate|up)       [24576 x 4096]
+        swiglu_quant_linear(gate, up, down)     [4096 x 12288]
+    (at decode sizes each of these is one kernel; otherwise the pre-step
+    kernel and then the Linear), beside the same chain as separate
+    rmsnorm_quantize / swiglu_quantize + fp8_linear calls and beside torch's
+    bf16 rms_norm and silu * up feeding quant_linear.  Attention and the
+    residual adds are not part of it (their inputs are seeded data).
+    `copies` layers with distinct weights run per replay so that
+    decode-sized steps read their weights from HBM."""
     from workloads import norm_inputs
     base = setup_layer(torch, fq, m, 3 if m == PREFILL_M else 2, packed=True)
     layers = [base]
@@ -490,13 +528,23 @@ def bench_fused_layer(torch, fq, m, steps, copies=1, eps=1e-6):
     g1, g2 = to_dev(g1, torch), to_dev(g2, torch)
     qkv, o, gu, down = base
     inter = gu["n"] // 2
-    wsb = max(fq.workspace_bytes(m, L["n"], L["k"], True) for L in base)
+    wsb = max(fq.workspace_bytes(m, L["n"], L["k"], mode) for L in base for mode in (1, 2, 3))
     ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
     flops = sum(2 * m * L["n"] * L["k"] for L in base)
     nbytes = (sum(L["n"] * L["k"] + 4 * L["n"] + 2 * m * L["k"] + 2 * m * L["n"] for L in base)
               + 2 * (2 * 4096) + 2 * 2 * m * inter)      # gammas, gate/up re-read
 
     def fused(layer):
+        qkv, o, gu, down = layer
+        fq.rmsnorm_quant_linear(qkv["x"], g1, eps, qkv["qw"], qkv["sw"], out=qkv["y"],
+                                workspace=ws)
+        fq.quant_linear(o["x"], o["qw"], o["sw"], out=o["y"], workspace=ws)
+        fq.rmsnorm_quant_linear(gu["x"], g2, eps, gu["qw"], gu["sw"], out=gu["y"],
+                                workspace=ws)
+        fq.swiglu_quant_linear(gu["y"][:, :inter], gu["y"][:, inter:], down["qw"],
+                               down["sw"], out=down["y"], workspace=ws)
+
+    def two_step(layer):
         qkv, o, gu, down = layer
         qx, sx = fq.rmsnorm_quantize(qkv["x"], g1, eps)
         fq.fp8_linear(qx, sx, qkv["qw"], qkv["sw"], out=qkv["y"], workspace=ws)
@@ -517,7 +565,8 @@ def bench_fused_layer(torch, fq, m, steps, copies=1, eps=1e-6):
         fq.quant_linear(a, down["qw"], down["sw"], out=down["y"], workspace=ws)
 
     res = {}
-    for name, fn in (("fused", fused), ("unfused_torch_norm_and_silu", unfused)):
+    for name, fn in (("fused", fused), ("two_step", two_step),
+                     ("unfused_torch_norm_and_silu", unfused)):
         gr = graph_of(torch, lambda: [fn(L) for L in layers], 1)
         for _ in range(max(5, steps // 4)):
             gr.replay()
@@ -540,34 +589,34 @@ def bench_kv(torch, fq, reps, t_write=PREFILL_M, t_read=32768, width=1024, group
     """The FP8 E4M3 KV-cache codec: quantizing one prefill chunk's K (or V)
     rows into the cache (t_write tokens x 8 KV heads x 128) and reading a
     t_read-token window back to bf16, one scale per head; GB/s of
-    algorithmic bytes (bf16 in/out, codes, scales), HIP-graph replays."""
+    algorithmic bytes (bf16 in/out, codes, scales), HIP-graph replays over
+    buffer copies (time_graph)."""
     from workloads import kv_inputs
-    x = to_dev(kv_inputs(t_write, width, seed=0), torch)
-    cache = torch.empty((t_read, width), dtype=torch.uint8, device="cuda")
-    cscale = torch.empty((t_read, width // group), dtype=torch.float32, device="cuda")
+    x0 = to_dev(kv_inputs(t_write, width, seed=0), torch)
     win = to_dev(kv_inputs(t_read, width, seed=1), torch)
-    fq.kv_quantize_fp8(win, group, cache, cscale)
-    out = torch.empty((t_read, width), dtype=torch.bfloat16, device="cuda")
+    cache0, cscale0 = fq.kv_quantize_fp8(win, group)
+    del win
+    qbytes = 3 * t_write * width + 4 * t_write * width // group
+    rbytes = 3 * t_read * width + 4 * t_read * width // group
     res = {}
-    for name, fn, nbytes in (
-            ("quantize", lambda: fq.kv_quantize_fp8(x, group, cache[:t_write],
-                                                    cscale[:t_write]),
-             3 * t_write * width + 4 * t_write * width // group),
-            ("dequantize", lambda: fq.kv_dequantize_fp8(cache, cscale, group, out=out),
-             3 * t_read * width + 4 * t_read * width // group)):
-        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
-        for _ in range(max(10, reps // 10)):
-            gr.replay()
-        torch.cuda.synchronize()
-        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
-        t /= NORM_CALLS_PER_GRAPH
-        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
-                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes": nbytes,
-                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
-                                          for ts in slices])}
-        del gr
-    del x, cache, cscale, win, out
+    nq = copies_for(qbytes)
+    xs = [x0] + [x0.clone() for _ in range(nq - 1)]
+    cq = [torch.empty((t_write, width), dtype=torch.uint8, device="cuda") for _ in range(nq)]
+    sq = [torch.empty((t_write, width // group), dtype=torch.float32, device="cuda")
+          for _ in range(nq)]
+    res["quantize"] = time_graph(
+        torch, [(lambda i: lambda: fq.kv_quantize_fp8(xs[i], group, cq[i], sq[i]))(i)
+                for i in range(nq)], reps, qbytes)
+    del xs, cq, sq
+    nr = copies_for(rbytes)
+    cs = [cache0] + [cache0.clone() for _ in range(nr - 1)]
+    ss = [cscale0] + [cscale0.clone() for _ in range(nr - 1)]
+    outs = [torch.empty((t_read, width), dtype=torch.bfloat16, device="cuda")
+            for _ in range(nr)]
+    res["dequantize"] = time_graph(
+        torch, [(lambda i: lambda: fq.kv_dequantize_fp8(cs[i], ss[i], group, out=outs[i]))(i)
+                for i in range(nr)], reps, rbytes)
+    del cs, ss, outs, x0, cache0, cscale0
     torch.cuda.empty_cache()
     return res
 
@@ -578,36 +627,37 @@ def bench_kv_int8(torch, fq, reps, t_write=PREFILL_M, t_read=32768, width=1024,
     64, newest 128 positions in bf16): quantizing t_write tokens into the
     INT8 store, and the cache read of a t_read-token window (t_read - 128
     dequantized history rows followed by the 128-row bf16 tail); GB/s of
-    algorithmic bytes, HIP-graph replays."""
+    algorithmic bytes, HIP-graph replays over buffer copies."""
     from workloads import kv_inputs
-    x = to_dev(kv_inputs(t_write, width, seed=0), torch)
+    x0 = to_dev(kv_inputs(t_write, width, seed=0), torch)
     hist = t_read - residual
     win = to_dev(kv_inputs(t_read, width, seed=1), torch)
-    codes, sc, mn = fq.kv_quantize_int8(win[:hist], group)
-    tail = win[hist:]
-    out = torch.empty((t_read, width), dtype=torch.bfloat16, device="cuda")
+    codes0, sc0, mn0 = fq.kv_quantize_int8(win[:hist], group)
+    tail0 = win[hist:].clone()
+    del win
     g = width // group
+    qbytes = 3 * t_write * width + 8 * t_write * g
+    rbytes = hist * width + 8 * hist * g + 2 * residual * width + 2 * t_read * width
     res = {}
-    for name, fn, nbytes in (
-            ("quantize", lambda: fq.kv_quantize_int8(x, group, codes[:t_write],
-                                                     sc[:t_write], mn[:t_write]),
-             3 * t_write * width + 8 * t_write * g),
-            ("read_history_and_tail",
-             lambda: fq.kv_read_int8(codes, sc, mn, tail=tail, group=group, out=out),
-             hist * width + 8 * hist * g + 2 * residual * width + 2 * t_read * width)):
-        gr = graph_of(torch, fn, NORM_CALLS_PER_GRAPH)
-        for _ in range(max(10, reps // 10)):
-            gr.replay()
-        torch.cuda.synchronize()
-        t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
-        t /= NORM_CALLS_PER_GRAPH
-        res[name] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1),
-                     "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes": nbytes,
-                     "slice_gbs": spread([nbytes * NORM_CALLS_PER_GRAPH / ts / 1e9
-                                          for ts in slices])}
-        del gr
-    del x, win, codes, sc, mn, tail, out
+    nq = copies_for(qbytes)
+    xs = [x0] + [x0.clone() for _ in range(nq - 1)]
+    cq = [torch.empty((t_write, width), dtype=torch.uint8, device="cuda") for _ in range(nq)]
+    sq = [torch.empty((t_write, g), dtype=torch.float32, device="cuda") for _ in range(nq)]
+    mq = [torch.empty((t_write, g), dtype=torch.float32, device="cuda") for _ in range(nq)]
+    res["quantize"] = time_graph(
+        torch, [(lambda i: lambda: fq.kv_quantize_int8(xs[i], group, cq[i], sq[i], mq[i]))(i)
+                for i in range(nq)], reps, qbytes)
+    del xs, cq, sq, mq
+    nr = copies_for(rbytes)
+    rc = [(codes0, sc0, mn0, tail0)] + [
+        (codes0.clone(), sc0.clone(), mn0.clone(), tail0.clone()) for _ in range(nr - 1)]
+    outs = [torch.empty((t_read, width), dtype=torch.bfloat16, device="cuda")
+            for _ in range(nr)]
+    res["read_history_and_tail"] = time_graph(
+        torch, [(lambda i: lambda: fq.kv_read_int8(*rc[i][:3], tail=rc[i][3], group=group,
+                                                   out=outs[i]))(i)
+                for i in range(nr)], reps, rbytes)
+    del rc, outs, x0, codes0, sc0, mn0, tail0
     torch.cuda.empty_cache()
     return res
 
@@ -652,6 +702,85 @@ def cpu_baseline(target_s=16.0):
                       f"fp64 matmul + epilogue; {secs:.1f} s"}
 
 
+def rocm_smi_clocks():
+    """rocm-smi's clock report (sclk, mclk, ...) for GPU 0, taken as a child
+    process before this process touches the GPU; None if unavailable."""
+    import subprocess
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                             text=True, timeout=60)
+        card = json.loads(res.stdout or "{}").get("card0", {})
+        return {k: v for k, v in card.items() if "clock" in k.lower()} or None
+    except Exception as e:                       # noqa: BLE001 - report only
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+
+
+def measured_peaks(torch, reps=10, wg=2048, iters=2048, read_bytes=2 << 30):
+    """The two roofs as this GPU sustains them (libfp8w8a8_peaks.so): an
+    MFMA-only loop of v_mfma_f32_32x32x64_f8f6f4 (TFLOP/s, and the shader
+    clock it ran at from the in-kernel cycle and 100 MHz counters), and a
+    streaming read of 2 GiB, 8x the last-level cache (GB/s).  HIP events on
+    the stream the kernels are launched on."""
+    import ctypes
+    from fp8_w8a8_dynamic_amd import build as fbuild
+    path = fbuild.PEAKS_LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the library first")
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.fp8w8a8_peaks_mfma_out_floats.restype = i64
+    lib.fp8w8a8_peaks_mfma_out_floats.argtypes = [i64]
+    lib.fp8w8a8_peaks_mfma_flops.restype = i64
+    lib.fp8w8a8_peaks_mfma_flops.argtypes = [i64, ctypes.c_int]
+    lib.fp8w8a8_peaks_read_workgroups.restype = i64
+    lib.fp8w8a8_peaks_read_workgroups.argtypes = [i64]
+    lib.fp8w8a8_peaks_mfma_loop.restype = ctypes.c_int
+    lib.fp8w8a8_peaks_mfma_loop.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    lib.fp8w8a8_peaks_read_stream.restype = ctypes.c_int
+    lib.fp8w8a8_peaks_read_stream.argtypes = [vp, i64, vp, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty(lib.fp8w8a8_peaks_mfma_out_floats(wg), dtype=torch.float32,
+                      device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+
+    def mfma():
+        st = lib.fp8w8a8_peaks_mfma_loop(out.data_ptr(), clk.data_ptr(), wg, iters, stream)
+        if st != 0:
+            raise RuntimeError(f"fp8w8a8_peaks_mfma_loop: status {st}")
+
+    for _ in range(3):
+        mfma()
+    torch.cuda.synchronize()
+    t = time_events(torch, mfma, reps)
+    cycles, ticks = (int(v) for v in clk.cpu())
+    mfma_tflops = lib.fp8w8a8_peaks_mfma_flops(wg, iters) / t / 1e12
+    del out, clk
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device="cuda")
+    rout = torch.empty(lib.fp8w8a8_peaks_read_workgroups(read_bytes) * 256,
+                       dtype=torch.int32, device="cuda")
+
+    def read():
+        st = lib.fp8w8a8_peaks_read_stream(buf.data_ptr(), read_bytes, rout.data_ptr(),
+                                           stream)
+        if st != 0:
+            raise RuntimeError(f"fp8w8a8_peaks_read_stream: status {st}")
+
+    for _ in range(3):
+        read()
+    torch.cuda.synchronize()
+    tr = time_events(torch, read, 2 * reps)
+    del buf, rout
+    torch.cuda.empty_cache()
+    return {"mfma_fp8_tflops": round(mfma_tflops, 1),
+            "mfma_loop_sclk_ghz": round(cycles / (ticks / 100e6) / 1e9, 3) if ticks else None,
+            "mfma_loop_us": round(t * 1e6, 1),
+            "hbm_read_gbs": round(read_bytes / tr / 1e9, 1),
+            "hbm_read_us": round(tr * 1e6, 1),
+            "what": "MFMA-only loop (2048 workgroups x 4 waves x 8 accumulators x 2048 "
+                    "v_mfma_f32_32x32x64_f8f6f4); a persistent read of 2 GiB (1024 workgroups, "
+                    "16-byte nontemporal loads, 8 in flight per thread)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -663,6 +792,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 36-layer stack leg")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA / HBM-read peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy "
                          "(reference for the HBM byte counters)")
@@ -671,6 +802,7 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only; "
                           "run with --gpus 1"}))
         return 2
+    smi = None if args.no_peaks else rocm_smi_clocks()
     import torch
     import fp8_w8a8_dynamic_amd as fq
     fq.load_library()
@@ -737,6 +869,12 @@ def main():
     if not args.no_decode:
         fl_dec = bench_fused_layer(torch, fq, DECODE_M, max(20, args.steps), DECODE_COPIES)
     log(f"fused layer M=4096 {fl}; M=1 {fl_dec}")
+    peaks = None
+    if not args.no_peaks:
+        log("measured peaks ...")
+        peaks = measured_peaks(torch)
+        peaks["rocm_smi_before_run"] = smi
+        log(f"measured peaks {peaks}")
     cpu = None
     if not args.no_cpu:
         log("cpu oracle ...")
@@ -821,7 +959,10 @@ def main():
                     "(token, head): quantize a 4096-token chunk into the cache, read a "
                     "32768-token window back to bf16",
         "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": d["frac_of_hbm"], "traffic": None,
+                     "unit": "GB/s", "frac": d["frac_of_hbm"],
+                     "traffic": kernel_traffic("kv_dequant"),
+                     "traffic_scope": "HBM bytes of one 32768-token read (rocprofv3 "
+                                      "FETCH_SIZE x2 + WRITE_SIZE); algorithmic 101,711,872",
                      "kernel": "kv_dequant_kernel"},
         "quantize": kv["quantize"], "dequantize": d}
     d = kv8["read_history_and_tail"]
@@ -830,15 +971,32 @@ def main():
                     "positions in bf16: quantize a 4096-token chunk into the INT8 store, "
                     "read a 32768-token window (32640 history + 128 tail) back to bf16",
         "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": d["frac_of_hbm"], "traffic": None,
+                     "unit": "GB/s", "frac": d["frac_of_hbm"],
+                     "traffic": kernel_traffic("kv_int8_read"),
+                     "traffic_scope": "HBM bytes of one 32768-token read (rocprofv3 "
+                                      "FETCH_SIZE x2 + WRITE_SIZE); algorithmic 104,972,288",
                      "kernel": "kv_int8_read_kernel"},
         "quantize": kv8["quantize"], "read": d}
     out["layer_with_fusions"] = {
-        "workload": "one layer's Linear path with the adjacent fusions: RMSNorm->quant "
-                    "-> q|k|v, o, RMSNorm->quant -> gate|up, SwiGLU->quant -> down "
-                    "(attention and residual adds excluded), beside the same chain with "
-                    "torch bf16 rms_norm / silu*up feeding quant_linear",
+        "workload": "one layer's Linear path with the adjacent fusions: "
+                    "rmsnorm_quant_linear(q|k|v), quant_linear(o), "
+                    "rmsnorm_quant_linear(gate|up), swiglu_quant_linear(down) "
+                    "(attention and residual adds excluded), beside the same chain as "
+                    "separate pre-step + fp8_linear calls (two_step) and with torch bf16 "
+                    "rms_norm / silu*up feeding quant_linear",
         "m4096": fl, "m1": fl_dec}
+    if peaks is not None:
+        out["measured_peaks"] = peaks
+        # Every roofline also against what this GPU sustained in the same run.
+        for key in ("roofline", "rmsnorm_quant", "swiglu_quant", "kv_cache_fp8",
+                    "kv_cache_int8"):
+            rf = out[key] if key == "roofline" else out[key]["roofline"]
+            meas = peaks["mfma_fp8_tflops"] if rf["bound"] == "mfma" else peaks["hbm_read_gbs"]
+            rf["measured_peak"] = meas
+            rf["frac_of_measured_peak"] = round(rf["achieved"] / meas, 4)
+        for d in (out.get("decode"), out["packed"].get("decode")):
+            if d:
+                d["frac_of_measured_hbm"] = round(d["value"] / peaks["hbm_read_gbs"], 4)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -23,6 +23,10 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "quant.hip", "norm.hip", "swiglu.hip", "kvcache.hip",
            "gemm.hip", "gemv.hip"]
 
+# The benchmark's measured-peak kernels, a library of their own.
+PEAKS_SOURCES = ["peaks.hip"]
+PEAKS_LIB_PATH = os.path.join(PKG_DIR, "libfp8w8a8_peaks.so")
+
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 # No fast-math and no denormal flushing: the quantizer must see IEEE float32
 # division and subnormal scales exactly as the format definition says.
@@ -53,20 +57,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; return its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
            "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link the library and the benchmark's peaks
+    library; return the library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+        print(f"built {PEAKS_LIB_PATH}")
     return LIB_PATH
 
 

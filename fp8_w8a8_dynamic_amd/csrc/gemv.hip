@@ -215,8 +215,7 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(
     // condition, which keeps their number, and the waits, static.
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      wa[s][h] = *reinterpret_cast<const uint4*>(
-          rp + min(chunk_off(st, h, g, c, C), K - 16));
+      wa[s][h] = load16_stream(rp + min(chunk_off(st, h, g, c, C), K - 16));
   };
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -557,7 +556,7 @@ __global__ __launch_bounds__(kTokWaves * 64) void gemv_tok_kernel(
       const int si = min(s + i, s1 - 1) * 128;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        wa[buf][i][h] = *reinterpret_cast<const uint4*>(wrow + si + h * 64);
+        wa[buf][i][h] = load16_stream(wrow + si + h * 64);
 #pragma unroll
         for (int t = 0; t < T; ++t)
           xb[buf][i][t][h] = *reinterpret_cast<const uint4*>(xrow[t] + si + h * 64);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(
   float* srow = scales + row * static_cast<int64_t>(groups);
   for (int base = 0; base < width; base += 512) {
     const int v = base / 8 + lane;                 // this lane's vector
-    const uint4 x = buf_load16(src, static_cast<uint32_t>(v) * 16u);
+    const uint4 x = buf_load16_stream(src, static_cast<uint32_t>(v) * 16u);
     uint32_t m = pk_max_u16(pk_max_u16(bf16x2_abs_bits(x.x), bf16x2_abs_bits(x.y)),
                             pk_max_u16(bf16x2_abs_bits(x.z), bf16x2_abs_bits(x.w)));
     m = group_max_u32<L>(max(m & 0xffffu, m >> 16));
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void kv_int8_quant_kernel(
   float* mrow = mins + row * static_cast<int64_t>(groups);
   for (int base = 0; base < width; base += 512) {
     const int v = base / 8 + lane;
-    const uint4 x = buf_load16(src, static_cast<uint32_t>(v) * 16u);
+    const uint4 x = buf_load16_stream(src, static_cast<uint32_t>(v) * 16u);
     const float e[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
                         bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
     float lo = e[0], hi = e[0];
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void kv_int8_read_kernel(
     const auto src = row_rsrc(tail + (row - hist) * ldt, static_cast<uint32_t>(width) * 2u);
     for (int base = 0; base < width; base += 512) {
       const uint32_t off = static_cast<uint32_t>(base / 8 + lane) * 16u;
-      buf_store16(buf_load16(src, off), dst, off);
+      buf_store16(buf_load16_stream(src, off), dst, off);
     }
     return;
   }

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   const uint32_t v0 = static_cast<uint32_t>(part * NV * 64 + lane);
   uint4 v[NV], g[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (v0 + i * 64) * 16u);
+  for (int i = 0; i < NV; ++i) v[i] = buf_load16_stream(src, (v0 + i * 64) * 16u);
 #pragma unroll
   for (int i = 0; i < NV; ++i) g[i] = buf_load16(gsrc, (v0 + i * 64) * 16u);
   float ss = row_sumsq<NV, S, false>(v, 1.0f, s_blk[rloc], part);

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const auto src = row_rsrc(x + row * ld, static_cast<uint32_t>(k) * 2u);
   uint4 v[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = buf_load16(src, (i * 64 + lane) * 16u);
+  for (int i = 0; i < NV; ++i) v[i] = buf_load16_stream(src, (i * 64 + lane) * 16u);
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {

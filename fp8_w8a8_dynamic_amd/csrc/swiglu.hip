@@ -53,9 +53,9 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
   const uint32_t v0 = static_cast<uint32_t>(part * NV * 64 + lane);
   uint4 g[NV], u[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) g[i] = buf_load16(gsrc, (v0 + i * 64) * 16u);
+  for (int i = 0; i < NV; ++i) g[i] = buf_load16_stream(gsrc, (v0 + i * 64) * 16u);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) u[i] = buf_load16(usrc, (v0 + i * 64) * 16u);
+  for (int i = 0; i < NV; ++i) u[i] = buf_load16_stream(usrc, (v0 + i * 64) * 16u);
   bool deep = false;
 #pragma unroll
   for (int i = 0; i < NV; ++i) deep |= any_deep8(g[i]);

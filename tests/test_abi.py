@@ -276,3 +276,30 @@ def test_workspace_sizes(lib):
     assert lib.fp8w8a8_workspace_init(A, 8, None) == ESHAPE
     assert lib.fp8w8a8_workspace_init(A + 8, 16, None) == EALIGN
     assert lib.fp8w8a8_workspace_init(A, 0, None) == OK
+
+
+def test_peaks_library_exports_and_validates():
+    """The benchmark's measured-peak library: every symbol its header
+    declares is exported, and bad arguments are refused before a launch."""
+    from fp8_w8a8_dynamic_amd import build as fbuild
+    text = open(os.path.join(ROOT, "include", "fp8w8a8_peaks.h")).read()
+    names = sorted(set(re.findall(r"\b(fp8w8a8_[a-z_0-9]+)\s*\(", text)))
+    assert len(names) == 5
+    plib = ctypes.CDLL(fbuild.PEAKS_LIB_PATH)
+    for name in names:
+        assert hasattr(plib, name), name
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    plib.fp8w8a8_peaks_mfma_flops.restype = i64
+    plib.fp8w8a8_peaks_mfma_flops.argtypes = [i64, ctypes.c_int]
+    assert plib.fp8w8a8_peaks_mfma_flops(2048, 2048) == 2048 * 4 * 8 * 2048 * 131072
+    plib.fp8w8a8_peaks_read_workgroups.restype = i64
+    plib.fp8w8a8_peaks_read_workgroups.argtypes = [i64]
+    assert plib.fp8w8a8_peaks_read_workgroups(2 << 30) == 1024
+    plib.fp8w8a8_peaks_mfma_loop.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    plib.fp8w8a8_peaks_read_stream.argtypes = [vp, i64, vp, vp]
+    assert plib.fp8w8a8_peaks_mfma_loop(None, A, 4, 4, None) == 1
+    assert plib.fp8w8a8_peaks_mfma_loop(A, A, 0, 4, None) == 2
+    assert plib.fp8w8a8_peaks_mfma_loop(A, A, 4, 0, None) == 2
+    assert plib.fp8w8a8_peaks_read_stream(None, 1024, A, None) == 1
+    assert plib.fp8w8a8_peaks_read_stream(A, 1000, A, None) == 2
+    assert plib.fp8w8a8_peaks_read_stream(A + 8, 1024, A, None) == 3
