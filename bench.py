@@ -63,8 +63,8 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # as null once that code differs.
 KERNEL_TRAFFIC = {
     "gemm": {"files": ("gemm.hip", "device_common.h"),
-             "sha1": "1ee7953892b20a2b7773e2512e426ed8c1c835f5",
-             "bytes": 1493114 * 1024},
+             "sha1": "cb7c6c10138bba7cfb20b5a932099fdbf2218fa8",
+             "bytes": 1493430 * 1024},
     "rmsnorm_quant": {"files": ("norm.hip", "row_ops.h", "device_common.h"),
                       "sha1": "b705eec0b08b238db4b13d64c022f7e387fd5c51",
                       "bytes": (16492 * 2 + 16416) * 1024},

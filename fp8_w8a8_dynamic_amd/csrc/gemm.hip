@@ -339,8 +339,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   for (int row = rr; row < S::WM && lane < RPW * CPR; row += RPW) {
     const uint4 v = *reinterpret_cast<const uint4*>(ep + row * S::EPI_ROW + cc * 16);
     const int gm = tok0 + row, gn = ch0 + cc * 8;
+    // The output is written once and not read back by this kernel: the
+    // nontemporal hint keeps the burst of a round of tiles finishing
+    // together from displacing operand panels in the caches (measured: the
+    // 7-Linear prefill step +1.6 %, the packed one +2.6 %).
     if (gm < M && gn < N)
-      *reinterpret_cast<uint4*>(y + static_cast<int64_t>(gm) * ldy + gn) = v;
+      __builtin_nontemporal_store(
+          v4u32_t{v.x, v.y, v.z, v.w},
+          reinterpret_cast<v4u32_t*>(y + static_cast<int64_t>(gm) * ldy + gn));
   }
 }
 
