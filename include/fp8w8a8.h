@@ -260,7 +260,11 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
 /*
  * The adjacent fusions followed by the Linear, in one call: exactly
  * fp8w8a8_rmsnorm_quantize(x, gamma, eps) (or fp8w8a8_swiglu_quantize(gate,
- * up)) followed by fp8w8a8_fp8_linear, with bit-identical output.  At decode
+ * up)) followed by fp8w8a8_fp8_linear, with bit-identical output.  The norm
+ * ahead of q/k/v and gate/up and the activation ahead of down stay BF16
+ * while the Linears after them are FP8_DYNAMIC (MOSS-VL-Realtime-FP8
+ * article, component / precision map; MOSS-VL quantization README,
+ * "FP8-Dynamic").  At decode
  * sizes (m <= 4 and m * k <= 16384; for the norm also k % 512 == 0) the
  * norm or activation runs inside the decode GEMV's activation staging, one
  * kernel in all; otherwise its codes go through the workspace.
@@ -270,7 +274,9 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
  *   qw, w_scale, y, ldy as for fp8w8a8_fp8_linear
  *   workspace    at least fp8w8a8_workspace_bytes(m, n, k, 2) (norm) or
  *                (m, n, k, 3) (activation) bytes
- * Rules as for fp8w8a8_fp8_linear and for the two fused steps.
+ * Rules as for fp8w8a8_fp8_linear and for the two fused steps (eps finite
+ * and >= 0; y may overlap none of the inputs, nor the workspace); errors
+ * are returned before anything is launched.
  */
 int fp8w8a8_rmsnorm_quant_linear(const uint16_t* x, int64_t ldx,
                                  const uint16_t* gamma, float eps,
