@@ -754,6 +754,164 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
   return GemvPlan{lg_mp, static_cast<int>(gpw), ni};
 }
 
+namespace detail {
+
+// One token (M = 1), its quantization fused, without LDS or barriers.  At
+// M = 1 the K-class layout above gives lane l of step s, half h the 16
+// bytes at 2048 s + 1024 h + 16 l of a weight row, and the same 16
+// positions of the activation codes.  Every wave owns R whole weight rows
+// and therefore needs the codes of the whole row; it loads its own 16-value
+// slices of x (the whole row across the wave, each value once), takes the
+// row amax with a wave reduction and quantizes in registers with the
+// quantizer's own device functions (bit-identical codes).  Per row, the CS
+// steps accumulate in order into one MFMA accumulator whose diagonal is
+// summed with the DPP tree, then the epilogue: the same order as the
+// LDS-staged kernel when it gives a wave whole rows.  The x loads are
+// issued before the weight loads, so waiting for them leaves the weights
+// in flight; out-of-range bytes (a ragged last step, rows past N) read as 0
+// through the buffer descriptors.
+template <int CS, int R>
+__global__ __launch_bounds__(256) void gemv_m1_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, int N, int K, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = (static_cast<int>(blockIdx.x) * 4 + wave) * R;
+  if (row0 >= N) return;
+  const auto xsrc = row_rsrc(x, static_cast<uint32_t>(K) * 2u);
+  uint4 xv[CS][2][2];
+#pragma unroll
+  for (int s = 0; s < CS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t off = static_cast<uint32_t>(s * 2048 + h * 1024 + lane * 16) * 2u;
+      xv[s][h][0] = buf_load16(xsrc, off);
+      xv[s][h][1] = buf_load16(xsrc, off + 16u);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  const int rows = min(R, N - row0);
+  const auto wsrc = row_rsrc(qw + static_cast<int64_t>(row0) * K,
+                             static_cast<uint32_t>(rows) * static_cast<uint32_t>(K));
+  uint4 wv[R][CS][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wv[r][s][h] = buf_load16_stream(
+            wsrc, static_cast<uint32_t>(r * K + s * 2048 + h * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t mm = 0;
+#pragma unroll
+  for (int s = 0; s < CS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].x));
+        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].y));
+        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].z));
+        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].w));
+      }
+  const float scale = row_scale(
+      __uint_as_float(wave_max_u32(max(mm & 0xffffu, mm >> 16)) << 16));
+  const RowDivisor d = make_divisor(scale);
+  v8i bq[CS];
+#pragma unroll
+  for (int s = 0; s < CS; ++s) {
+    uint4 half[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint2 lo = quantize8(xv[s][h][0], d), hi = quantize8(xv[s][h][1], d);
+      half[h] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    bq[s] = to_v8i(half[0], half[1]);
+  }
+  const int qd = (lane & 15) - 4 * (lane >> 4);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          to_v8i(wv[r][s][0], wv[r][s][1]), bq[s], acc, 0, 0, 0, 0, 0, 0);
+    float dg = qd == 0 ? acc[0] : qd == 1 ? acc[1] : qd == 2 ? acc[2]
+             : qd == 3 ? acc[3] : 0.0f;
+    dg = wave_sum_to_63(dg);
+    const int n = row0 + r;
+    if (lane == 63 && n < N) y[n] = f32_to_bf16_bits(dg * sw[n] * scale);
+  }
+}
+
+// Rows per wave for gemv_m1_kernel.  Every wave reads the whole activation
+// row (2 K bytes, from L2), so more rows per wave amortize it, fewer give
+// more waves: measured on MI355X at K = 4096, one row per wave up to
+// N = 2048 (k/v, 1024 x 4096: 3.0 us, against 4.9 us for the LDS-staged
+// kernel) and two above (q 5.0 against 5.9 us, gate 10.6 against 12.1,
+// packed qkv 6.4 against 7.4, packed gate_up 18.6 against 21.7); four or
+// more rows per wave were 2-20 % slower.  FP8W8A8_GEMV_M1_ROWS overrides
+// (a tuning aid; at most 8 items of 2 KB per wave).
+int m1_rows_per_wave(int64_t n, int cs) {
+  if (const char* e = std::getenv("FP8W8A8_GEMV_M1_ROWS")) {
+    const int v = std::atoi(e);
+    if ((v == 1 || v == 2 || v == 4 || v == 8) && cs * v <= 8) return v;
+  }
+  return (n <= 2048 || cs * 2 > 8) ? 1 : 2;
+}
+
+template <int CS, int R>
+hipError_t launch_m1(const uint16_t* x, const uint8_t* qw, const float* sw,
+                     int64_t n, int64_t k, uint16_t* y, hipStream_t stream) {
+  const int64_t waves = (n + R - 1) / R;
+  gemv_m1_kernel<CS, R><<<dim3(static_cast<uint32_t>((waves + 3) / 4)), dim3(256), 0,
+                          stream>>>(x, qw, sw, static_cast<int>(n), static_cast<int>(k), y);
+  return hipGetLastError();
+}
+
+template <int CS>
+hipError_t launch_m1_cs(const uint16_t* x, const uint8_t* qw, const float* sw,
+                        int64_t n, int64_t k, uint16_t* y, hipStream_t stream) {
+  switch (m1_rows_per_wave(n, CS)) {
+    case 8: if constexpr (CS * 8 <= 8) return launch_m1<CS, 8>(x, qw, sw, n, k, y, stream); break;
+    case 4: if constexpr (CS * 4 <= 8) return launch_m1<CS, 4>(x, qw, sw, n, k, y, stream); break;
+    case 2: if constexpr (CS * 2 <= 8) return launch_m1<CS, 2>(x, qw, sw, n, k, y, stream); break;
+    default: break;
+  }
+  return launch_m1<CS, 1>(x, qw, sw, n, k, y, stream);
+}
+
+}  // namespace detail
+
+// The barrier-free M = 1 kernel runs by default for K <= 4096 (two steps):
+// at K = 12288 (down) the activation row each wave re-reads is twice its
+// weight bytes, and it measured 14.4 us against 11.7 us for the LDS-staged
+// kernel.  FP8W8A8_GEMV_M1=0 switches it off, =1 takes it up to K = 16384
+// (comparison and test aids; where the LDS-staged kernel gives waves whole
+// rows the two give the same bits).
+bool gemv_m1_fits(int64_t m, int64_t k) {
+  if (m != 1 || k > 8 * 2048) return false;
+  const char* e = std::getenv("FP8W8A8_GEMV_M1");
+  if (e && e[0] == '0') return false;
+  if (e && e[0] == '1') return true;
+  return k <= 2 * 2048;
+}
+
+hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* qw, const float* sw,
+                          int64_t n, int64_t k, uint16_t* y, hipStream_t stream) {
+  switch ((k + 2047) / 2048) {
+    case 1: return launch_m1_cs<1>(x, qw, sw, n, k, y, stream);
+    case 2: return launch_m1_cs<2>(x, qw, sw, n, k, y, stream);
+    case 3: return launch_m1_cs<3>(x, qw, sw, n, k, y, stream);
+    case 4: return launch_m1_cs<4>(x, qw, sw, n, k, y, stream);
+    case 5: return launch_m1_cs<5>(x, qw, sw, n, k, y, stream);
+    case 6: return launch_m1_cs<6>(x, qw, sw, n, k, y, stream);
+    case 7: return launch_m1_cs<7>(x, qw, sw, n, k, y, stream);
+    case 8: return launch_m1_cs<8>(x, qw, sw, n, k, y, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                        const float* sx, const uint8_t* qw, const float* sw,
                        int64_t m, int64_t n, int64_t k, uint16_t* y,
@@ -763,6 +921,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
   const GemvPre none{nullptr, 0, 0.0f};
   if (x != nullptr) {
     if (!gemv_fused_fits(m, n, k)) return hipErrorInvalidValue;
+    if (gemv_m1_fits(m, k)) return launch_gemv_m1(x, qw, sw, n, k, y, stream);
     return launch_one<2, kFusedRegs>(x, ldx, qx, sx, qw, sw, m, pl.lg_mp, n, k,
                                      pl.gpw, pl.ni, y, ldy, none, stream);
   }

@@ -378,3 +378,30 @@ def test_packed_qkv_equals_separate_calls(m):
     check_close(yp, y64, f"packed qkv m={m}")
     if m != 4:
         assert np.array_equal(yp, np.concatenate(ys, axis=1))
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (1024, 4096), (12288, 4096), (4096, 12288),
+                                 (6144, 4096), (24576, 4096), (16, 128), (48, 4224),
+                                 (1040, 2176), (512, 16384), (8208, 6272)])
+@pytest.mark.parametrize("rows", [None, "1", "2", "4"])
+def test_m1_kernel_matches_lds_staged_kernel(n, k, rows, monkeypatch):
+    """The barrier-free M = 1 GEMV against the LDS-staged one: bitwise where
+    the latter gives every wave whole rows (all these shapes), and both
+    within the Linear's bound of the oracle."""
+    if rows is not None:
+        # ignored where steps x rows would exceed 8 items of 2 KB per wave
+        monkeypatch.setenv("FP8W8A8_GEMV_M1_ROWS", rows)
+    rng = np.random.default_rng(n * 7 + k)
+    x = bf16_from_f64(rng.standard_normal((1, k)) * np.where(rng.random(k) < 0.01, 20, 1))
+    w = bf16_from_f64(0.02 * rng.standard_normal((n, k)))
+    qw, sw = _quant_weights_gpu(w)
+    xd = to_dev_bf16(x)
+    monkeypatch.setenv("FP8W8A8_GEMV_M1", "1")        # also where K > 4096
+    y_new = host_bits(fq.quant_linear(xd, qw, sw))
+    monkeypatch.setenv("FP8W8A8_GEMV_M1", "0")
+    y_old = host_bits(fq.quant_linear(xd, qw, sw))
+    torch.cuda.synchronize()
+    check_bytes(y_new, y_old, f"m1 kernel vs LDS-staged, n={n} k={k}")
+    rqx, rsx = oracle.quant_act_ref(x)
+    rqw, rsw = oracle.quant_weight_ref(w)
+    check_close(y_new, oracle.linear_ref(rqx, rsx, rqw, rsw), f"m1 kernel vs oracle n={n} k={k}")
