@@ -756,7 +756,8 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
 
 namespace detail {
 
-// One token (M = 1), its quantization fused, without LDS or barriers.  At
+// One token (M = 1), its quantization fused (or its codes given), without
+// LDS or barriers.  At
 // M = 1 the K-class layout above gives lane l of step s, half h the 16
 // bytes at 2048 s + 1024 h + 16 l of a weight row, and the same 16
 // positions of the activation codes.  Every wave owns R whole weight rows
@@ -770,24 +771,37 @@ namespace detail {
 // issued before the weight loads, so waiting for them leaves the weights
 // in flight; out-of-range bytes (a ragged last step, rows past N) read as 0
 // through the buffer descriptors.
-template <int CS, int R>
+// CODES: the activation arrives already quantized (qx, one code per value,
+// and its scale sx[0]): the codes are loaded in the same slices instead.
+template <int CS, int R, bool CODES>
 __global__ __launch_bounds__(256) void gemv_m1_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qx,
+    const float* __restrict__ sx, const uint8_t* __restrict__ qw,
     const float* __restrict__ sw, int N, int K, uint16_t* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = (static_cast<int>(blockIdx.x) * 4 + wave) * R;
   if (row0 >= N) return;
-  const auto xsrc = row_rsrc(x, static_cast<uint32_t>(K) * 2u);
-  uint4 xv[CS][2][2];
+  uint4 xv[CODES ? 1 : CS][2][2];
+  uint4 cv[CODES ? CS : 1][2];
+  if constexpr (CODES) {
+    const auto csrc = row_rsrc(qx, static_cast<uint32_t>(K));
 #pragma unroll
-  for (int s = 0; s < CS; ++s)
+    for (int s = 0; s < CS; ++s)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t off = static_cast<uint32_t>(s * 2048 + h * 1024 + lane * 16) * 2u;
-      xv[s][h][0] = buf_load16(xsrc, off);
-      xv[s][h][1] = buf_load16(xsrc, off + 16u);
-    }
+      for (int h = 0; h < 2; ++h)
+        cv[s][h] = buf_load16(csrc, static_cast<uint32_t>(s * 2048 + h * 1024 + lane * 16));
+  } else {
+    const auto xsrc = row_rsrc(x, static_cast<uint32_t>(K) * 2u);
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = static_cast<uint32_t>(s * 2048 + h * 1024 + lane * 16) * 2u;
+        xv[s][h][0] = buf_load16(xsrc, off);
+        xv[s][h][1] = buf_load16(xsrc, off + 16u);
+      }
+  }
   __builtin_amdgcn_sched_barrier(0);
   const int rows = min(R, N - row0);
   const auto wsrc = row_rsrc(qw + static_cast<int64_t>(row0) * K,
@@ -802,31 +816,38 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(
         wv[r][s][h] = buf_load16_stream(
             wsrc, static_cast<uint32_t>(r * K + s * 2048 + h * 1024 + lane * 16));
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t mm = 0;
-#pragma unroll
-  for (int s = 0; s < CS; ++s)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].x));
-        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].y));
-        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].z));
-        mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].w));
-      }
-  const float scale = row_scale(
-      __uint_as_float(wave_max_u32(max(mm & 0xffffu, mm >> 16)) << 16));
-  const RowDivisor d = make_divisor(scale);
+  float scale;
   v8i bq[CS];
+  if constexpr (CODES) {
+    scale = sx[0];
 #pragma unroll
-  for (int s = 0; s < CS; ++s) {
-    uint4 half[2];
+    for (int s = 0; s < CS; ++s) bq[s] = to_v8i(cv[s][0], cv[s][1]);
+  } else {
+    uint32_t mm = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint2 lo = quantize8(xv[s][h][0], d), hi = quantize8(xv[s][h][1], d);
-      half[h] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].x));
+          mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].y));
+          mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].z));
+          mm = pk_max_u16(mm, bf16x2_abs_bits(xv[s][h][j].w));
+        }
+    scale = row_scale(
+        __uint_as_float(wave_max_u32(max(mm & 0xffffu, mm >> 16)) << 16));
+    const RowDivisor d = make_divisor(scale);
+#pragma unroll
+    for (int s = 0; s < CS; ++s) {
+      uint4 half[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint2 lo = quantize8(xv[s][h][0], d), hi = quantize8(xv[s][h][1], d);
+        half[h] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      bq[s] = to_v8i(half[0], half[1]);
     }
-    bq[s] = to_v8i(half[0], half[1]);
   }
   const int qd = (lane & 15) - 4 * (lane >> 4);
 #pragma unroll
@@ -860,25 +881,35 @@ int m1_rows_per_wave(int64_t n, int cs) {
   return (n <= 2048 || cs * 2 > 8) ? 1 : 2;
 }
 
-template <int CS, int R>
-hipError_t launch_m1(const uint16_t* x, const uint8_t* qw, const float* sw,
-                     int64_t n, int64_t k, uint16_t* y, hipStream_t stream) {
-  const int64_t waves = (n + R - 1) / R;
-  gemv_m1_kernel<CS, R><<<dim3(static_cast<uint32_t>((waves + 3) / 4)), dim3(256), 0,
-                          stream>>>(x, qw, sw, static_cast<int>(n), static_cast<int>(k), y);
+struct M1Args {
+  const uint16_t* x;
+  const uint8_t* qx;
+  const float* sx;
+  const uint8_t* qw;
+  const float* sw;
+  int64_t n, k;
+  uint16_t* y;
+};
+
+template <int CS, int R, bool CODES>
+hipError_t launch_m1(const M1Args& a, hipStream_t stream) {
+  const int64_t waves = (a.n + R - 1) / R;
+  gemv_m1_kernel<CS, R, CODES><<<dim3(static_cast<uint32_t>((waves + 3) / 4)), dim3(256),
+                                 0, stream>>>(a.x, a.qx, a.sx, a.qw, a.sw,
+                                              static_cast<int>(a.n),
+                                              static_cast<int>(a.k), a.y);
   return hipGetLastError();
 }
 
-template <int CS>
-hipError_t launch_m1_cs(const uint16_t* x, const uint8_t* qw, const float* sw,
-                        int64_t n, int64_t k, uint16_t* y, hipStream_t stream) {
-  switch (m1_rows_per_wave(n, CS)) {
-    case 8: if constexpr (CS * 8 <= 8) return launch_m1<CS, 8>(x, qw, sw, n, k, y, stream); break;
-    case 4: if constexpr (CS * 4 <= 8) return launch_m1<CS, 4>(x, qw, sw, n, k, y, stream); break;
-    case 2: if constexpr (CS * 2 <= 8) return launch_m1<CS, 2>(x, qw, sw, n, k, y, stream); break;
+template <int CS, bool CODES>
+hipError_t launch_m1_cs(const M1Args& a, hipStream_t stream) {
+  switch (m1_rows_per_wave(a.n, CS)) {
+    case 8: if constexpr (CS * 8 <= 8) return launch_m1<CS, 8, CODES>(a, stream); break;
+    case 4: if constexpr (CS * 4 <= 8) return launch_m1<CS, 4, CODES>(a, stream); break;
+    case 2: if constexpr (CS * 2 <= 8) return launch_m1<CS, 2, CODES>(a, stream); break;
     default: break;
   }
-  return launch_m1<CS, 1>(x, qw, sw, n, k, y, stream);
+  return launch_m1<CS, 1, CODES>(a, stream);
 }
 
 }  // namespace detail
@@ -897,17 +928,17 @@ bool gemv_m1_fits(int64_t m, int64_t k) {
   return k <= 2 * 2048;
 }
 
-hipError_t launch_gemv_m1(const uint16_t* x, const uint8_t* qw, const float* sw,
-                          int64_t n, int64_t k, uint16_t* y, hipStream_t stream) {
-  switch ((k + 2047) / 2048) {
-    case 1: return launch_m1_cs<1>(x, qw, sw, n, k, y, stream);
-    case 2: return launch_m1_cs<2>(x, qw, sw, n, k, y, stream);
-    case 3: return launch_m1_cs<3>(x, qw, sw, n, k, y, stream);
-    case 4: return launch_m1_cs<4>(x, qw, sw, n, k, y, stream);
-    case 5: return launch_m1_cs<5>(x, qw, sw, n, k, y, stream);
-    case 6: return launch_m1_cs<6>(x, qw, sw, n, k, y, stream);
-    case 7: return launch_m1_cs<7>(x, qw, sw, n, k, y, stream);
-    case 8: return launch_m1_cs<8>(x, qw, sw, n, k, y, stream);
+template <bool CODES>
+hipError_t launch_gemv_m1(const M1Args& a, hipStream_t stream) {
+  switch ((a.k + 2047) / 2048) {
+    case 1: return launch_m1_cs<1, CODES>(a, stream);
+    case 2: return launch_m1_cs<2, CODES>(a, stream);
+    case 3: return launch_m1_cs<3, CODES>(a, stream);
+    case 4: return launch_m1_cs<4, CODES>(a, stream);
+    case 5: return launch_m1_cs<5, CODES>(a, stream);
+    case 6: return launch_m1_cs<6, CODES>(a, stream);
+    case 7: return launch_m1_cs<7, CODES>(a, stream);
+    case 8: return launch_m1_cs<8, CODES>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -921,10 +952,13 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
   const GemvPre none{nullptr, 0, 0.0f};
   if (x != nullptr) {
     if (!gemv_fused_fits(m, n, k)) return hipErrorInvalidValue;
-    if (gemv_m1_fits(m, k)) return launch_gemv_m1(x, qw, sw, n, k, y, stream);
+    if (gemv_m1_fits(m, k))
+      return launch_gemv_m1<false>(M1Args{x, nullptr, nullptr, qw, sw, n, k, y}, stream);
     return launch_one<2, kFusedRegs>(x, ldx, qx, sx, qw, sw, m, pl.lg_mp, n, k,
                                      pl.gpw, pl.ni, y, ldy, none, stream);
   }
+  if (gemv_m1_fits(m, k))
+    return launch_gemv_m1<true>(M1Args{nullptr, qx, sx, qw, sw, n, k, y}, stream);
   if (m * ((k + 1023) / 1024 * 1024 + kLdsRowPad) <= kStageLds)
     return launch_one<1, 1>(x, ldx, qx, sx, qw, sw, m, pl.lg_mp, n, k, pl.gpw,
                             pl.ni, y, ldy, none, stream);

@@ -396,12 +396,17 @@ def test_m1_kernel_matches_lds_staged_kernel(n, k, rows, monkeypatch):
     w = bf16_from_f64(0.02 * rng.standard_normal((n, k)))
     qw, sw = _quant_weights_gpu(w)
     xd = to_dev_bf16(x)
+    qx, sx = fq.quantize_act_per_token(xd)
     monkeypatch.setenv("FP8W8A8_GEMV_M1", "1")        # also where K > 4096
     y_new = host_bits(fq.quant_linear(xd, qw, sw))
+    c_new = host_bits(fq.fp8_linear(qx, sx, qw, sw))   # codes given
     monkeypatch.setenv("FP8W8A8_GEMV_M1", "0")
     y_old = host_bits(fq.quant_linear(xd, qw, sw))
+    c_old = host_bits(fq.fp8_linear(qx, sx, qw, sw))
     torch.cuda.synchronize()
     check_bytes(y_new, y_old, f"m1 kernel vs LDS-staged, n={n} k={k}")
+    check_bytes(c_new, c_old, f"m1 kernel on codes vs LDS-staged, n={n} k={k}")
+    check_bytes(c_new, y_new, f"m1 kernel on codes vs fused, n={n} k={k}")
     rqx, rsx = oracle.quant_act_ref(x)
     rqw, rsw = oracle.quant_weight_ref(w)
     check_close(y_new, oracle.linear_ref(rqx, rsx, rqw, rsw), f"m1 kernel vs oracle n={n} k={k}")
