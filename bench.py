@@ -290,15 +290,18 @@ def library_gemm_tflops(torch, layer, flops, steps):
         return None
 
 
-def bench_decode(torch, fq, reps, packed=False):
-    base = setup_layer(torch, fq, DECODE_M, 2, packed)
+def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
+    """One layer's 7 fused calls (4 when packed) at m tokens, captured in a
+    HIP graph over DECODE_COPIES copies of the weights; GB/s of algorithmic
+    bytes."""
+    base = setup_layer(torch, fq, m, 2, packed)
     copies = [base]
     for _ in range(DECODE_COPIES - 1):
         copies.append([dict(L, qw=L["qw"].clone(), sw=L["sw"].clone(),
                             y=torch.empty_like(L["y"])) for L in base])
-    nbytes = sum(L["n"] * L["k"] + 4 * L["n"] + 2 * DECODE_M * L["k"]
-                 + 2 * DECODE_M * L["n"] for L in base)
-    wsb = max(fq.workspace_bytes(DECODE_M, L["n"], L["k"], True) for L in base)
+    nbytes = sum(L["n"] * L["k"] + 4 * L["n"] + 2 * m * L["k"]
+                 + 2 * m * L["n"] for L in base)
+    wsb = max(fq.workspace_bytes(m, L["n"], L["k"], True) for L in base)
     ws = fq.init_workspace(torch.empty(max(wsb, 1 << 20), dtype=torch.uint8, device="cuda"))
 
     def layer_pass(layer):
@@ -829,6 +832,10 @@ def main():
         log("decode ...")
         dec = bench_decode(torch, fq, max(20, args.steps))
         log(f"decode layer {dec['layer_us']:.2f} us  {dec['gbs']:.0f} GB/s")
+        dec_more = {mm: bench_decode(torch, fq, max(20, args.steps // 2), m=mm)
+                    for mm in (4, 8)}
+        log("decode M=4, 8: " + ", ".join(f"{v['layer_us']:.1f} us {v['gbs']:.0f} GB/s"
+                                          for v in dec_more.values()))
     log("packed layer ...")
     pre_p = bench_prefill(torch, fq, args.steps, args.warmup, packed=True)
     packed = {"linears": "qkv_proj (6144x4096), o_proj, gate_up_proj (24576x4096), "
@@ -920,7 +927,12 @@ def main():
                          "us_per_layer": round(dec["layer_us"], 3),
                          "frac_of_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                          "bytes_per_layer": dec["bytes"],
-                         "slice_gbs": spread(dec["slices"])}
+                         "slice_gbs": spread(dec["slices"]),
+                         "other_token_counts": {
+                             f"m{mm}": {"value": round(v["gbs"], 1), "unit": "GB/s",
+                                        "us_per_layer": round(v["layer_us"], 3),
+                                        "frac_of_hbm": round(v["gbs"] / HBM_PEAK_GBS, 4)}
+                             for mm, v in dec_more.items()}}
     out["packed"] = packed
     if stack is not None:
         out["stack_36_layers"] = {
