@@ -115,6 +115,28 @@ def to_dev(bits, torch):
         torch.bfloat16).to("cuda")
 
 
+# Every timed leg is first run for at least this long (besides any count of
+# warm-up calls): after an idle moment the GPU's clocks ramp up over several
+# milliseconds, and a fixed number of warm-up calls of a short leg would
+# leave its timed calls on the ramp.
+WARM_S = 0.25
+
+
+def warm_for(torch, fn, seconds=WARM_S):
+    """Call fn() (and synchronize) until at least `seconds` of wall time have
+    passed; returns the number of calls."""
+    t0 = time.perf_counter()
+    calls, batch = 0, 1
+    while True:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        calls += batch
+        if time.perf_counter() - t0 >= seconds:
+            return calls
+        batch = min(2 * batch, 64)
+
+
 def time_events(torch, fn, reps):
     """Average duration of fn() over reps calls, HIP events on the current
     stream (the stream the library launches on)."""
@@ -213,7 +235,7 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
     step = g.replay
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
+    warm_for(torch, step)
     t0 = time.perf_counter()
     step_time, slices = time_chunks(torch, step, steps)
     torch.cuda.synchronize()
@@ -233,9 +255,10 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
     s = torch.cuda.current_stream()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layer] for _ in range(steps)]
-    for L in layer:
-        fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
-    torch.cuda.synchronize()
+    def gemms():
+        for L in layer:
+            fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
+    warm_for(torch, gemms)
     for it in range(steps):
         for j, L in enumerate(layer):
             ev[it][j][0].record(s)
@@ -247,15 +270,13 @@ def bench_prefill(torch, fq, steps, warmup, packed=False):
     # The roofline figure: the same 7 launches back to back, two events
     # around the whole timed region (per-launch events add small gaps and
     # scatter; they give the per-Linear split only).
-    def gemms():
-        for L in layer:
-            fq.fp8_linear(L["qx"], L["sx"], L["qw"], L["sw"], out=L["y"])
+    warm_for(torch, gemms)
     gemm_region = time_events(torch, gemms, steps)
     lib_tflops = library_gemm_tflops(torch, layer, flops, steps)
     quant_t = []
     for L in layer:
         q = lambda L=L: fq.quantize_act_per_token(L["x"])
-        q()
+        warm_for(torch, q, 0.05)
         quant_t.append(time_events(torch, q, max(10, steps)))
     per = {L["name"]: {"gemm_us": round(t * 1e6, 2),
                        "gemm_tflops": round(2 * PREFILL_M * L["n"] * L["k"] / t / 1e12, 1),
@@ -282,8 +303,7 @@ def library_gemm_tflops(torch, layer, flops, steps):
         def seq():
             for a, b, sa, sb in ops:
                 torch._scaled_mm(a, b, scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
-        seq()
-        torch.cuda.synchronize()
+        warm_for(torch, seq)
         return round(flops / time_events(torch, seq, steps) / 1e12, 2)
     except Exception as e:                 # not offered by this torch build
         log(f"library comparison skipped: {type(e).__name__}: {e}")
@@ -323,12 +343,35 @@ def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
     torch.cuda.synchronize()
     for _ in range(max(3, reps // 2)):
         g.replay()
-    torch.cuda.synchronize()
+    warm_for(torch, g.replay)
     t, slices = time_chunks(torch, g.replay, reps)
     t /= DECODE_COPIES
-    del copies, base
+    del g
+    del copies
+    # Each Linear on its own: a graph of that Linear's call on copies of its
+    # weights in turn (at least ROTATE_BYTES of distinct weights per replay,
+    # so they come from HBM), replayed; GB/s of its own algorithmic bytes.
+    per = {}
+    for L in base:
+        lb = L["n"] * L["k"] + 4 * L["n"] + 2 * m * L["k"] + 2 * m * L["n"]
+        nc = max(2, -(-ROTATE_BYTES // lb))
+        ws_copies = [(L["qw"], L["sw"])] + [(L["qw"].clone(), L["sw"].clone())
+                                             for _ in range(nc - 1)]
+        gj = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gj, stream=cap):
+                for qw, sw in ws_copies:
+                    fq.quant_linear(L["x"], qw, sw, out=L["y"], workspace=ws)
+        torch.cuda.synchronize()
+        warm_for(torch, gj.replay, 0.05)
+        tj = time_events(torch, gj.replay, max(10, reps // 4)) / nc
+        per[L["name"]] = {"us": round(tj * 1e6, 3), "gbs": round(lb / tj / 1e9, 1),
+                          "frac_of_hbm": round(lb / tj / 1e9 / HBM_PEAK_GBS, 4),
+                          "weight_copies": nc}
+        del gj, ws_copies
+    del base
     torch.cuda.empty_cache()
-    return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes,
+    return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes, per_linear=per,
                 slices=[nbytes * DECODE_COPIES / ts / 1e9 for ts in slices])
 
 
@@ -366,7 +409,7 @@ def bench_stack(torch, fq, m, passes):
 
     for _ in range(3):
         one_pass()
-    torch.cuda.synchronize()
+    warm_for(torch, one_pass)
     t = time_events(torch, one_pass, passes)
     nbytes = 36 * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for _, n, k in LAYER_SHAPES)
     flops = 36 * sum(2 * m * n * k for _, n, k in LAYER_SHAPES)
@@ -431,7 +474,7 @@ def time_graph(torch, fns, reps, nbytes):
     gr = graph_of(torch, rotating(fns), calls)
     for _ in range(max(10, reps // 10)):
         gr.replay()
-    torch.cuda.synchronize()
+    warm_for(torch, gr.replay, 0.1)
     t, slices = time_chunks(torch, gr.replay, max(10, reps // 4))
     del gr
     t /= calls
@@ -573,7 +616,7 @@ def bench_fused_layer(torch, fq, m, steps, copies=1, eps=1e-6):
         gr = graph_of(torch, lambda: [fn(L) for L in layers], 1)
         for _ in range(max(5, steps // 4)):
             gr.replay()
-        torch.cuda.synchronize()
+        warm_for(torch, gr.replay)
         t, slices = time_chunks(torch, gr.replay, steps)
         t /= copies
         res[name] = {"us_per_layer": round(t * 1e6, 2),
@@ -665,44 +708,88 @@ def bench_kv_int8(torch, fq, reps, t_write=PREFILL_M, t_read=32768, width=1024,
     return res
 
 
-def cpu_baseline(target_s=16.0):
-    """The oracle as it stands, timed on a sample of the prefill workload:
-    all 7 Linears, a subset of tokens and of output channels (weights
-    quantized by the oracle beforehand, untimed, as the offline step)."""
+def host_info(threads):
+    """The host the CPU leg ran on: logical CPUs, lscpu's model name, the
+    BLAS thread count."""
+    import subprocess
+    model = None
+    try:
+        res = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=30)
+        for line in res.stdout.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:                            # noqa: BLE001 - report only
+        pass
+    return {"os_cpu_count": os.cpu_count(), "lscpu_model_name": model,
+            "blas_threads": int(threads)}
+
+
+def cpu_baseline(target_s=8.0, decode_frac=4):
+    """The oracle as it stands, timed on samples of the same workloads, with
+    the quantization and the matmul + epilogue timed separately:
+    * prefill: all 7 Linears of the M=4096 layer, a subset of tokens and of
+      output channels (weights quantized by the oracle beforehand, untimed,
+      as the offline step), grown until the timed part reaches ~target_s;
+    * decode: the M=1 layer's 7 Linears on 1/decode_frac of their output
+      channels, GB/s of the same algorithmic bytes as the GPU figure."""
     import oracle
     from workloads import LAYER_SHAPES
-    from workloads.generators import c3_x, weight_bf16
+    from workloads.generators import c3_x, outlier_act_bf16, rng_for, weight_bf16
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         threads = os.cpu_count() or 1
 
-    def run(m_s, n_frac):
-        flops, secs = 0, 0.0
+    def run(m_s, n_frac, decode=False):
+        r = dict(flops=0, quant_s=0.0, mm_s=0.0, quant_bytes=0, mm_bytes=0)
         for j, (_, n, k) in enumerate(LAYER_SHAPES):
             n_s = max(16, n // n_frac)
-            x = c3_x(PREFILL_M, k, j, rows=m_s)
-            w = weight_bf16(3, 0, j, n, k, rows=n_s)
+            x = (outlier_act_bf16(rng_for(2, m_s, j, 0), (m_s, k)) if decode
+                 else c3_x(PREFILL_M, k, j, rows=m_s))
+            w = weight_bf16(2 if decode else 3, 0, j, n, k, rows=n_s)
             qw, sw = oracle.quant_weight_ref(w)
             t0 = time.perf_counter()
-            oracle.quant_linear_ref(x, qw, sw)
-            secs += time.perf_counter() - t0
-            flops += 2 * m_s * n_s * k
-        return flops, secs
+            qx, sx = oracle.quant_act_ref(x)
+            t1 = time.perf_counter()
+            oracle.linear_ref(qx, sx, qw, sw)
+            t2 = time.perf_counter()
+            r["quant_s"] += t1 - t0
+            r["mm_s"] += t2 - t1
+            r["flops"] += 2 * m_s * n_s * k
+            r["quant_bytes"] += 3 * m_s * k + 4 * m_s
+            r["mm_bytes"] += n_s * k + 4 * n_s + m_s * k + 4 * m_s + 2 * m_s * n_s
+        return r
 
-    # Grow the sample until the timed oracle work reaches about target_s.
+    # Grow the prefill sample until the timed oracle work reaches target_s.
     sizes = [(64, 16), (256, 8), (512, 4), (1024, 4), (2048, 4), (4096, 4), (4096, 2),
              (4096, 1)]
     for m_s, n_frac in sizes:
-        flops, secs = run(m_s, n_frac)
-        if secs >= target_s / 2:
+        r = run(m_s, n_frac)
+        if r["quant_s"] + r["mm_s"] >= target_s:
             break
-    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s",
+    secs = r["quant_s"] + r["mm_s"]
+    d = run(1, decode_frac, decode=True)
+    dsecs = d["quant_s"] + d["mm_s"]
+    # Algorithmic bytes of the fused decode call, as on the GPU.
+    dbytes = sum(max(16, n // decode_frac) * k + 4 * max(16, n // decode_frac) + 2 * k
+                 + 2 * max(16, n // decode_frac) for _, n, k in LAYER_SHAPES)
+    return {"value": round(r["flops"] / secs / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
             "sample": f"prefill M=4096 layer, {m_s} tokens x 1/{n_frac} of the "
                       f"output channels of each of the 7 Linears; quantize + "
-                      f"fp64 matmul + epilogue; {secs:.1f} s"}
+                      f"fp64 matmul + epilogue; {secs:.1f} s",
+            "quant_gbs": round(r["quant_bytes"] / r["quant_s"] / 1e9, 3),
+            "matmul_gflops": round(r["flops"] / r["mm_s"] / 1e9, 2),
+            "matmul_gbs": round(r["mm_bytes"] / r["mm_s"] / 1e9, 3),
+            "quant_s": round(r["quant_s"], 3), "matmul_s": round(r["mm_s"], 3),
+            "decode": {"value": round(dbytes / dsecs / 1e9, 3), "unit": "GB/s",
+                       "sample": f"decode M=1 layer, 1/{decode_frac} of the output "
+                                 f"channels of each of the 7 Linears; quantize + fp64 "
+                                 f"matmul + epilogue; {dsecs:.2f} s",
+                       "quant_s": round(d["quant_s"], 4), "matmul_s": round(d["mm_s"], 3)},
+            "host": host_info(threads)}
 
 
 def rocm_smi_clocks():
@@ -850,7 +937,8 @@ def main():
         packed["decode"] = {"slice_gbs": spread(dec_p["slices"]),
                             "value": round(dec_p["gbs"], 1), "unit": "GB/s",
                             "us_per_layer": round(dec_p["layer_us"], 3),
-                            "frac_of_hbm": round(dec_p["gbs"] / HBM_PEAK_GBS, 4)}
+                            "frac_of_hbm": round(dec_p["gbs"] / HBM_PEAK_GBS, 4),
+                            "per_linear": dec_p["per_linear"]}
         log(f"packed decode {packed['decode']}")
     stack = None
     if not args.no_stack:
@@ -928,6 +1016,7 @@ def main():
                          "frac_of_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                          "bytes_per_layer": dec["bytes"],
                          "slice_gbs": spread(dec["slices"]),
+                         "per_linear": dec["per_linear"],
                          "other_token_counts": {
                              f"m{mm}": {"value": round(v["gbs"], 1), "unit": "GB/s",
                                         "us_per_layer": round(v["layer_us"], 3),

@@ -39,6 +39,17 @@ COMMON_FLAGS = [
 ]
 
 
+# Host-side sanitizer build (CPU tests of the argument validation): every
+# -fsanitize= applies to host code only (-Xarch_host); device code is built
+# as usual and never runs in those tests.
+SANITIZE_FLAGS = [f for opt in ("-fsanitize=address", "-fsanitize=undefined",
+                                "-fno-sanitize-recover=all",
+                                "-fno-omit-frame-pointer")
+                  for f in ("-Xarch_host", opt)]
+SANITIZED_DIR = os.path.join(BUILD_DIR, "sanitized")
+SANITIZED_LIB_PATH = os.path.join(SANITIZED_DIR, "libfp8w8a8_asan_ubsan.so")
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -46,9 +57,9 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", "-c",
+def _compile(src: str, out_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -57,9 +68,9 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, path):
+def _link(objs, path, extra=()):
     tmp = path + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs,
            "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -80,6 +91,32 @@ def build(verbose: bool = False) -> str:
         print(f"built {LIB_PATH}")
         print(f"built {PEAKS_LIB_PATH}")
     return LIB_PATH
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The library with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code (for CPU tests of the C ABI's validation; loaded with the
+    sanitizer runtime preloaded, see sanitizer_runtime()).  Returns its path."""
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    extra = ["-g", *SANITIZE_FLAGS]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, SANITIZED_DIR, extra), SOURCES))
+    _link(objs, SANITIZED_LIB_PATH, SANITIZE_FLAGS)
+    if verbose:
+        print(f"built {SANITIZED_LIB_PATH}")
+    return SANITIZED_LIB_PATH
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (which carries
+    the UndefinedBehaviorSanitizer handlers), to preload into a process
+    that loads the sanitized library."""
+    res = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the compiler's libclang_rt.asan-x86_64.so was not found")
+    return path
 
 
 if __name__ == "__main__":

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -57,12 +58,20 @@ struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
 
+// Byte range of a [rows, cols] matrix with row stride ld.  Computed in
+// 128-bit arithmetic and saturated at the top of the address space, so an
+// absurd size can only make the overlap tests below more conservative,
+// never wrap around and slip past them.
 Range span(const void* p, int64_t rows, int64_t cols, int64_t ld,
            size_t elem) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
   if (rows <= 0 || cols <= 0) return Range{lo, lo};
-  const size_t bytes = (static_cast<size_t>(rows - 1) * ld + cols) * elem;
-  return Range{lo, lo + bytes};
+  using u128 = unsigned __int128;
+  const u128 hi = static_cast<u128>(lo) +
+                  (static_cast<u128>(rows - 1) * static_cast<u128>(ld) +
+                   static_cast<u128>(cols)) * elem;
+  const u128 top = static_cast<u128>(UINTPTR_MAX);
+  return Range{lo, static_cast<uintptr_t>(hi > top ? top : hi)};
 }
 
 bool overlap(Range a, Range b) {
@@ -73,11 +82,18 @@ bool overlap(Range a, Range b) {
 // with 32-bit integers; element offsets use 64-bit arithmetic.
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 
+// A row stride (in elements) for rows of `cols` elements: at least cols, at
+// most kMaxDim (so that the byte ranges below cannot wrap), a multiple of 8
+// (16-byte aligned rows of 2-byte elements).
+bool ld_ok(int64_t ld, int64_t cols) {
+  return ld >= cols && ld <= kMaxDim && ld % 8 == 0;
+}
+
 int check_quant_args(const uint16_t* src, int64_t rows, int64_t k, int64_t ld,
                      const uint8_t* q, const float* scale) {
   if (!src || !q || !scale) return FP8W8A8_ERR_NULL;
   if (rows < 0 || rows > kMaxDim || k < 1 || k > kMaxDim || k % 8 != 0 ||
-      ld < k || ld % 8 != 0)
+      !ld_ok(ld, k))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(q) ||
       (reinterpret_cast<uintptr_t>(scale) & 3u) != 0)
@@ -96,7 +112,7 @@ constexpr int64_t kMaxLinearK = int64_t{1} << 22;
 
 int check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t ldy) {
   if (m < 0 || m > kMaxDim || n < 0 || n > kMaxDim || n % 16 != 0 ||
-      k < 128 || k > kMaxLinearK || k % 128 != 0 || ldy < n || ldy % 8 != 0)
+      k < 128 || k > kMaxLinearK || k % 128 != 0 || !ld_ok(ldy, n))
     return FP8W8A8_ERR_SHAPE;
   return FP8W8A8_OK;
 }
@@ -109,11 +125,11 @@ enum class Path { kGemv, kGemvTok, kGemm };
 // the layer's shapes: e.g. one layer at m = 16 in 108.6 us against 130.4;
 // beyond that each of its workgroups re-reading all activation codes costs
 // too much); everything else takes the tiled MFMA GEMM.
-// FP8W8A8_FORCE_PATH=gemm|gemv|tok overrides the choice (each only within
-// its range of m) so that the kernels can be cross-checked on identical
-// inputs.
+// With the test hooks on, FP8W8A8_FORCE_PATH=gemm|gemv|tok overrides the
+// choice (each only within its range of m) so that the kernels can be
+// cross-checked on identical inputs.
 Path choose_path(int64_t m, int64_t n, int64_t k) {
-  const char* force = std::getenv("FP8W8A8_FORCE_PATH");
+  const char* force = fp8w8a8::test_hook("FP8W8A8_FORCE_PATH");
   if (force && std::strcmp(force, "gemm") == 0) return Path::kGemm;
   if (force && std::strcmp(force, "gemv") == 0 && m <= kGemvMaxM)
     return Path::kGemv;
@@ -171,6 +187,20 @@ Layout layout_for(int64_t m, int64_t n, int64_t k, Pre pre, Path path,
 
 }  // namespace
 
+namespace fp8w8a8 {
+
+const char* test_hook(const char* name) {
+  static std::once_flag once;
+  static bool enabled = false;
+  std::call_once(once, [] {
+    const char* e = std::getenv("FP8W8A8_TEST_HOOKS");
+    enabled = e != nullptr && std::strcmp(e, "1") == 0;
+  });
+  return enabled ? std::getenv(name) : nullptr;
+}
+
+}  // namespace fp8w8a8
+
 extern "C" {
 
 const char* fp8w8a8_status_string(int status) {
@@ -218,8 +248,8 @@ int fp8w8a8_rmsnorm_quantize(const uint16_t* x, int64_t m, int64_t k,
                              uint8_t* qx, float* x_scale, uint16_t* y,
                              int64_t ldy, void* stream) {
   if (!x || !gamma || !qx || !x_scale) return FP8W8A8_ERR_NULL;
-  if (m < 0 || m > kMaxDim || k < 8 || k > kMaxDim || k % 8 != 0 || ldx < k ||
-      ldx % 8 != 0 || (y && (ldy < k || ldy % 8 != 0)) ||
+  if (m < 0 || m > kMaxDim || k < 8 || k > kMaxDim || k % 8 != 0 ||
+      !ld_ok(ldx, k) || (y && !ld_ok(ldy, k)) ||
       !(eps >= 0.0f && eps <= 3.4028235e38f))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(gamma) || !aligned16(qx) ||
@@ -250,8 +280,8 @@ int fp8w8a8_swiglu_quantize(const uint16_t* gate, int64_t ldg,
                             int64_t n, uint8_t* qh, float* h_scale,
                             uint16_t* h, int64_t ldh, void* stream) {
   if (!gate || !up || !qh || !h_scale) return FP8W8A8_ERR_NULL;
-  if (m < 0 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 || ldg < n ||
-      ldg % 8 != 0 || ldu < n || ldu % 8 != 0 || (h && (ldh < n || ldh % 8 != 0)))
+  if (m < 0 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 ||
+      !ld_ok(ldg, n) || !ld_ok(ldu, n) || (h && !ld_ok(ldh, n)))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(qh) || (h && !aligned16(h)) ||
       (reinterpret_cast<uintptr_t>(h_scale) & 3u) != 0)
@@ -284,7 +314,7 @@ int fp8w8a8_kv_quantize_fp8(const uint16_t* kv, int64_t rows, int64_t width,
                             float* scales, void* stream) {
   if (!kv || !codes || !scales) return FP8W8A8_ERR_NULL;
   if (rows < 0 || rows > kMaxDim || width < 8 || width > kMaxDim ||
-      width % 8 != 0 || !kv_group_ok(width, group) || ld < width || ld % 8 != 0)
+      width % 8 != 0 || !kv_group_ok(width, group) || !ld_ok(ld, width))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(kv) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
       (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
@@ -306,7 +336,7 @@ int fp8w8a8_kv_dequantize_fp8(const uint8_t* codes, const float* scales,
                               uint16_t* out, int64_t ldo, void* stream) {
   if (!codes || !scales || !out) return FP8W8A8_ERR_NULL;
   if (rows < 0 || rows > kMaxDim || width < 8 || width > kMaxDim ||
-      width % 8 != 0 || !kv_group_ok(width, group) || ldo < width || ldo % 8 != 0)
+      width % 8 != 0 || !kv_group_ok(width, group) || !ld_ok(ldo, width))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
       (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
@@ -328,7 +358,7 @@ int fp8w8a8_kv_quantize_int8(const uint16_t* kv, int64_t rows, int64_t width,
                              float* scales, float* mins, void* stream) {
   if (!kv || !codes || !scales || !mins) return FP8W8A8_ERR_NULL;
   if (rows < 0 || rows > kMaxDim || width < 8 || width > kMaxDim ||
-      width % 8 != 0 || !kv_group_ok(width, group) || ld < width || ld % 8 != 0)
+      width % 8 != 0 || !kv_group_ok(width, group) || !ld_ok(ld, width))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(kv) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
       (reinterpret_cast<uintptr_t>(scales) & 3u) != 0 ||
@@ -361,8 +391,8 @@ int fp8w8a8_kv_read_int8(const uint8_t* codes, const float* scales,
     return FP8W8A8_ERR_NULL;
   if (hist < 0 || tail_rows < 0 || hist > kMaxDim || tail_rows > kMaxDim ||
       hist + tail_rows > kMaxDim || width < 8 || width > kMaxDim || width % 8 != 0 ||
-      !kv_group_ok(width, group) || ldo < width || ldo % 8 != 0 ||
-      (tail_rows > 0 && (ldt < width || ldt % 8 != 0)))
+      !kv_group_ok(width, group) || !ld_ok(ldo, width) ||
+      (tail_rows > 0 && !ld_ok(ldt, width)))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(out) || (tail_rows > 0 && !aligned16(tail)) ||
       (hist > 0 && ((reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
@@ -446,7 +476,7 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
   if (!x || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
   int st = check_linear_shape(m, n, k, ldy);
   if (st != FP8W8A8_OK) return st;
-  if (ldx < k || ldx % 8 != 0) return FP8W8A8_ERR_SHAPE;
+  if (!ld_ok(ldx, k)) return FP8W8A8_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) ||
       !aligned16(y) || (workspace && !aligned16(workspace)))
     return FP8W8A8_ERR_ALIGN;
@@ -519,8 +549,8 @@ int pre_linear(Pre pre, const uint16_t* x, int64_t ldx, const uint16_t* x2,
   if (!x || !x2 || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
   int st = check_linear_shape(m, n, k, ldy);
   if (st != FP8W8A8_OK) return st;
-  if (ldx < k || ldx % 8 != 0) return FP8W8A8_ERR_SHAPE;
-  if (pre == Pre::kSwiGlu && (ld2 < k || ld2 % 8 != 0)) return FP8W8A8_ERR_SHAPE;
+  if (!ld_ok(ldx, k)) return FP8W8A8_ERR_SHAPE;
+  if (pre == Pre::kSwiGlu && !ld_ok(ld2, k)) return FP8W8A8_ERR_SHAPE;
   if (pre == Pre::kRmsNorm && !(eps >= 0.0f && eps <= 3.4028235e38f))
     return FP8W8A8_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(x2) || !aligned16(qw) || !aligned16(w_scale) ||

@@ -404,17 +404,18 @@ hipError_t launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
 }  // namespace detail
 using namespace detail;
 
-// Tile configuration and K splits.  FP8W8A8_GEMM_CONFIG=<index> overrides
-// the configuration, and with it FP8W8A8_GEMM_SPLITS=<n> the number of K
-// splits (1 if unset) -- tuning aids; every configuration computes the same
-// result, and the splits change only the float32 summation order.
+// Tile configuration and K splits.  With the test hooks on (launch.h),
+// FP8W8A8_GEMM_CONFIG=<index> overrides the configuration, and with it
+// FP8W8A8_GEMM_SPLITS=<n> the number of K splits (1 if unset) -- tuning
+// aids; every configuration computes the same result, and the splits
+// change only the float32 summation order.
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
   GemmPlan p{3, 1};
   if (m <= 0 || n <= 0 || k < kBK) return p;
-  if (const char* e = std::getenv("FP8W8A8_GEMM_CONFIG")) {
+  if (const char* e = test_hook("FP8W8A8_GEMM_CONFIG")) {
     p.cfg = std::atoi(e);
     if (p.cfg >= 0) {
-      if (const char* sp = std::getenv("FP8W8A8_GEMM_SPLITS")) {
+      if (const char* sp = test_hook("FP8W8A8_GEMM_SPLITS")) {
         int v = std::atoi(sp);
         const int kt = static_cast<int>(k / kBK);
         if (v > kt) v = kt;

@@ -741,9 +741,9 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k) {
     if (gpw > cap) gpw = best_fill(1, cap);
     if (gpw < 1) gpw = 1;
   }
-  // FP8W8A8_GEMV_GPW overrides (a tuning aid; every choice computes the
+  // With the test hooks on, FP8W8A8_GEMV_GPW overrides (a tuning aid; every choice computes the
   // same result up to float32 summation order).
-  if (const char* e = std::getenv("FP8W8A8_GEMV_GPW")) {
+  if (const char* e = test_hook("FP8W8A8_GEMV_GPW")) {
     const int64_t v = std::atoll(e);
     if (v >= 1 && v <= groups) gpw = v;
   }
@@ -871,10 +871,11 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(
 // N = 2048 (k/v, 1024 x 4096: 3.0 us, against 4.9 us for the LDS-staged
 // kernel) and two above (q 5.0 against 5.9 us, gate 10.6 against 12.1,
 // packed qkv 6.4 against 7.4, packed gate_up 18.6 against 21.7); four or
-// more rows per wave were 2-20 % slower.  FP8W8A8_GEMV_M1_ROWS overrides
-// (a tuning aid; at most 8 items of 2 KB per wave).
+// more rows per wave were 2-20 % slower.  With the test hooks on,
+// FP8W8A8_GEMV_M1_ROWS overrides (a tuning aid; at most 8 items of 2 KB per
+// wave).
 int m1_rows_per_wave(int64_t n, int cs) {
-  if (const char* e = std::getenv("FP8W8A8_GEMV_M1_ROWS")) {
+  if (const char* e = test_hook("FP8W8A8_GEMV_M1_ROWS")) {
     const int v = std::atoi(e);
     if ((v == 1 || v == 2 || v == 4 || v == 8) && cs * v <= 8) return v;
   }
@@ -917,12 +918,12 @@ hipError_t launch_m1_cs(const M1Args& a, hipStream_t stream) {
 // The barrier-free M = 1 kernel runs by default for K <= 4096 (two steps):
 // at K = 12288 (down) the activation row each wave re-reads is twice its
 // weight bytes, and it measured 14.4 us against 11.7 us for the LDS-staged
-// kernel.  FP8W8A8_GEMV_M1=0 switches it off, =1 takes it up to K = 16384
-// (comparison and test aids; where the LDS-staged kernel gives waves whole
+// kernel.  With the test hooks on, FP8W8A8_GEMV_M1=0 switches it off, =1
+// takes it up to K = 16384 (comparison and test aids; where the LDS-staged kernel gives waves whole
 // rows the two give the same bits).
 bool gemv_m1_fits(int64_t m, int64_t k) {
   if (m != 1 || k > 8 * 2048) return false;
-  const char* e = std::getenv("FP8W8A8_GEMV_M1");
+  const char* e = test_hook("FP8W8A8_GEMV_M1");
   if (e && e[0] == '0') return false;
   if (e && e[0] == '1') return true;
   return k <= 2 * 2048;

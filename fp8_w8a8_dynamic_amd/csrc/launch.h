@@ -9,6 +9,17 @@
 
 namespace fp8w8a8 {
 
+// Tuning and cross-check overrides (the kernel path, tile configuration,
+// K splits, GEMV grouping, norm split) exist for the test suite only.  They
+// are honoured only when the environment variable FP8W8A8_TEST_HOOKS is "1"
+// the first time the library looks (read once per process); otherwise
+// test_hook() returns nullptr for every name and no call ever reads the
+// environment, so a stray variable cannot change a production kernel
+// choice.  With the switch on, the named override is read at each call (the
+// tests vary it between calls; workspace sizes must then be queried under
+// the same overrides as the call).
+const char* test_hook(const char* name);
+
 // Per-row quantization of a bf16 matrix [rows, k] (row stride ld elements):
 // codes [rows, k] contiguous and one float32 scale per row.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t k,

@@ -231,10 +231,11 @@ hipError_t launch_norm_nv(const uint16_t* x, int64_t rows, int64_t k,
 }  // namespace detail
 using namespace detail;
 
-// Waves per row: FP8W8A8_NORM_SPLIT=1|2|4 overrides the choice (tuning and
-// tests); rows up to 4 x 12 vectors per lane take the register kernels.
+// Waves per row: with the test hooks on, FP8W8A8_NORM_SPLIT=1|2|4 overrides
+// the choice (tuning and tests); rows up to 4 x 12 vectors per lane take the
+// register kernels.
 int norm_split(int64_t rows, int64_t per_lane) {
-  if (const char* e = std::getenv("FP8W8A8_NORM_SPLIT")) {
+  if (const char* e = test_hook("FP8W8A8_NORM_SPLIT")) {
     const int v = std::atoi(e);
     if (v == 1 || v == 2 || v == 4) return v;
   }

@@ -43,8 +43,19 @@ def check_bytes(got: np.ndarray, want: np.ndarray, what: str = "bytes"):
         raise AssertionError(f"{what}: {len(bad)} mismatches; first {detail}")
 
 
+#: Every check_close call appends a summary here (what was compared, the
+#: largest error over the row RMS, the smallest floor that would still pass
+#: and the largest relative error); tests/conftest.py can write the list out
+#: so that the measured margins of a run are on record.
+REPORT_LOG = []
+
+
 def close_report(y_bf16_bits: np.ndarray, y64: np.ndarray) -> dict:
-    """Elementwise comparison data (no assertion)."""
+    """Elementwise comparison data (no assertion).
+
+    ``floor_needed`` is the smallest RMS floor (in units of the row RMS)
+    under which every element would pass: the largest ``err / (REL_TOL *
+    rms)`` over the elements whose error exceeds ``REL_TOL * |y64|``."""
     y = bf16_bits_to_f32(y_bf16_bits).astype(np.float64)
     y64 = np.asarray(y64, dtype=np.float64)
     if y.shape != y64.shape:
@@ -60,9 +71,13 @@ def close_report(y_bf16_bits: np.ndarray, y64: np.ndarray) -> dict:
     exact_bf16 = f64_to_bf16_bits(y64) == np.asarray(y_bf16_bits, np.uint16)
     err_rms = np.where(rms > 0, err / np.where(rms > 0, rms, 1.0),
                        np.where(err > 0, np.inf, 0.0)) if rel.size else rel
+    beyond = err > REL_TOL * np.abs(y64)
+    floor_needed = float(np.max(np.where(beyond, err_rms, 0.0))) / REL_TOL \
+        if rel.size else 0.0
     return {
         "max_rel": float(np.max(rel)) if rel.size else 0.0,
         "max_err_over_rms": float(np.max(err_rms)) if rel.size else 0.0,
+        "floor_needed": floor_needed,
         "worst_index": tuple(int(i) for i in np.unravel_index(
             np.argmax(rel), rel.shape)) if rel.size else (),
         "n_bad": int(np.sum((rel > REL_TOL) | ~finite)),
@@ -75,11 +90,17 @@ def close_report(y_bf16_bits: np.ndarray, y64: np.ndarray) -> dict:
 def check_close(y_bf16_bits: np.ndarray, y64: np.ndarray, what="output"):
     """Raise unless every element is within the elementwise tolerance."""
     r = close_report(y_bf16_bits, y64)
+    REPORT_LOG.append({"what": what, "max_err_over_rms": r["max_err_over_rms"],
+                       "floor_needed": r["floor_needed"], "max_rel": r["max_rel"],
+                       "frac_bf16_equal": r["frac_bf16_equal"], "n_bad": r["n_bad"],
+                       "elements": int(np.asarray(y64).size)})
     if r["n_bad"]:
         idx = r["worst_index"]
         y = bf16_bits_to_f32(np.asarray(y_bf16_bits, np.uint16))
         raise AssertionError(
             f"{what}: {r['n_bad']} elements out of tolerance; worst at {idx}: "
             f"got {float(y[idx])!r} want {float(np.asarray(y64)[idx])!r} "
-            f"rel {r['max_rel']:.3g}")
+            f"rel {r['max_rel']:.3g}; max error / row RMS "
+            f"{r['max_err_over_rms']:.3g} (floor {RMS_FLOOR:g} x RMS; this run "
+            f"needs {r['floor_needed']:.3g})")
     return r

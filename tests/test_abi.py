@@ -24,7 +24,10 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def lib():
-    return load_library()
+    # FP8W8A8_ABI_TEST_LIBRARY names another build of the same library (the
+    # host-sanitized one, tests/test_abi_sanitized.py); default: the product.
+    path = os.environ.get("FP8W8A8_ABI_TEST_LIBRARY")
+    return load_library(path) if path else load_library()
 
 
 def test_exports_every_declared_symbol(lib):
@@ -303,3 +306,62 @@ def test_peaks_library_exports_and_validates():
     assert plib.fp8w8a8_peaks_read_stream(None, 1024, A, None) == 1
     assert plib.fp8w8a8_peaks_read_stream(A, 1000, A, None) == 2
     assert plib.fp8w8a8_peaks_read_stream(A + 8, 1024, A, None) == 3
+
+
+BIG = 1 << 31        # one past the largest row stride (2^31 - 1 elements)
+
+
+def test_strides_are_bounded(lib):
+    """Every row stride is bounded by 2^31 - 1 elements, so the byte ranges
+    of the overlap checks cannot wrap around the address space."""
+    assert _q(lib, "fp8w8a8_quantize_act_per_token", A, 4, 64, BIG, 64 * A, 128 * A) == ESHAPE
+    assert _q(lib, "fp8w8a8_quantize_act_per_token", A, 4, 64, BIG - 8, 64 * A, 128 * A) \
+        in (EALIAS, EDEV)      # in range: x now spans the other buffers' addresses
+    assert _norm(lib, ldx=BIG) == ESHAPE
+    assert _norm(lib, ldy=BIG) == ESHAPE
+    assert _swi(lib, ldg=BIG) == ESHAPE and _swi(lib, ldu=BIG) == ESHAPE
+    assert _swi(lib, ldh=BIG) == ESHAPE
+    assert _kvq(lib, ld=BIG) == ESHAPE and _kvd(lib, ldo=BIG) == ESHAPE
+    assert _lin(lib, ldy=BIG) == ESHAPE
+    f = lib.fp8w8a8_quant_linear
+    assert f(A, BIG, 4 * A, 8 * A, 64, 64, 256, 16 * A, 64, 32 * A, 1 << 30, None) == ESHAPE
+    assert lib.fp8w8a8_rmsnorm_quant_linear(A, BIG, 2 * A, 1e-6, 4 * A, 8 * A, 32, 64, 256,
+                                            16 * A, 64, None, 0, None) == ESHAPE
+    assert lib.fp8w8a8_swiglu_quant_linear(A, 256, 2 * A, BIG, 4 * A, 8 * A, 32, 64, 256,
+                                           16 * A, 64, None, 0, None) == ESHAPE
+    # the largest valid stride and row count: the range saturates at the top
+    # of the address space instead of wrapping, so the overlap test still
+    # sees y reaching over the workspace placed after it
+    hi = (1 << 63) - (1 << 40)
+    assert f(A, 256, 4 * A, 8 * A, BIG - 1, 64, 256, hi, BIG - 8, hi + (1 << 30), 1 << 62,
+             None) == EALIAS
+
+
+def test_overrides_off_without_the_test_switch():
+    """The tuning overrides are honoured only with FP8W8A8_TEST_HOOKS=1 set
+    when the library first looks: a fresh process without the switch and
+    with an override that would change the workspace size gets the
+    production plan."""
+    import subprocess
+    import sys
+    code = (
+        "from fp8_w8a8_dynamic_amd import load_library\n"
+        "lib = load_library()\n"
+        "print(lib.fp8w8a8_workspace_bytes(1, 64, 4096, 0),"
+        " lib.fp8w8a8_workspace_bytes(64, 4096, 4096, 0))\n")
+    outs = {}
+    for hooks in ("0", "1"):
+        env = dict(os.environ, FP8W8A8_TEST_HOOKS=hooks, FP8W8A8_FORCE_PATH="gemm",
+                   FP8W8A8_GEMM_CONFIG="5", FP8W8A8_GEMM_SPLITS="2")
+        lib_env = os.environ.get("FP8W8A8_ABI_TEST_LIBRARY")
+        if lib_env:
+            code_run = code.replace("load_library()", f"load_library({lib_env!r})")
+        else:
+            code_run = code
+        res = subprocess.run([sys.executable, "-c", code_run], env=env, cwd=ROOT,
+                             capture_output=True, text=True, timeout=300)
+        assert res.returncode == 0, res.stderr[-2000:]
+        outs[hooks] = [int(v) for v in res.stdout.split()]
+    assert outs["0"][0] == 0                      # M = 1 stays on the GEMV: no scratch
+    assert outs["1"][0] == 2 * 1 * 64 * 4         # forced 2-way split-K GEMM
+    assert outs["0"][1] != outs["1"][1]

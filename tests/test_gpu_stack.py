@@ -1,27 +1,27 @@
 """The full quantized stack: 36 layers x 7 FP8_DYNAMIC Linears with distinct
 seeded weights (6.95 GB of E4M3), at M = 64 and M = 256 tokens; each layer's
 up-projection output feeds its down-projection and the down output, re-
-quantized per token, is the next layer's input.
+quantized per token, is the next layer's input (MOSS-VL quantization
+README, "FP8-Dynamic": the 252 Linears of the 36 self-attention layers,
+activations quantized per token at run time).
 
-The oracle runs the same chain on its own for the first two layers (its own
-bf16 outputs feed its next layer; nothing from the GPU enters it):
+Parity is teacher-forced per layer: the oracle for layer l takes the GPU's
+own bf16 input of that layer (X_l, and Y_up,l for down) as its test input,
+because a one-ulp difference in a bf16 input can legitimately re-draw a
+row's whole E4M3 rounding, so a free-running comparison cannot be held to
+the tolerance past the first re-quantization.  For every one of the 36
+layers, at both token counts:
 
-* where the GPU and the oracle see identical inputs (layer 0's q, k, v, o,
-  gate, up) every output is held to the elementwise tolerance of
-  oracle.check (q, k, v, o, gate on 128 sampled output channels);
-* once an output has been re-quantized (layer 0's down, all of layer 1) the
-  two chains' inputs differ by the GPU's accumulation error, and a 1-ulp
-  bf16 change of a row's amax element re-draws that row's whole E4M3
-  rounding.  There the outputs are held to a quantization-noise bound:
-  relative Frobenius error <= 3 % per Linear and RMS error <= 10 % of each
-  row's RMS.  (An oracle-only simulation with inputs perturbed by 1e-4 of
-  the row RMS gives <= 0.9 % and <= 2.4 %; the FP8 rounding of the
-  activations itself is ~2.6 %; a dropped K block of 128 or a wrong scale
-  exceeds both bounds.)
+* the per-token codes and scales of X_l and of Y_up,l (the GPU quantizer on
+  the GPU's own bf16 tensors) are bit-exact against the oracle's;
+* all 7 Linears' outputs on 128 seeded output channels each are within the
+  elementwise tolerance of oracle.check of the oracle's output on those
+  same inputs;
+* the seeded channels' weight codes and scales are bit-exact.
 
-Over all 36 layers the GPU chain is checked by properties: finite
-everywhere, and the per-layer growth of the activation RMS within the range
-the weight distribution implies (sqrt(4096)*0.02 * sqrt(12288)*0.02 ~ 2.8).
+The oracle's free-running chain (its own bf16 outputs feeding its next
+layer) over the first two layers is computed too and its relative
+Frobenius drift reported, not asserted.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -35,65 +35,57 @@ import oracle
 from oracle import bf16_bits_to_f32, check_bytes, check_close, f64_to_bf16_bits
 from tests.gpu_util import host_bits, to_dev_bf16
 from workloads import LAYER_SHAPES
-from workloads.generators import N_SELF_ATTN_LAYERS, c4_x0, weight_bf16
+from workloads.generators import N_SELF_ATTN_LAYERS, c4_x0, rng_for, weight_bf16
 
 pytestmark = pytest.mark.gpu
 
 LAYERS = N_SELF_ATTN_LAYERS
-ORACLE_LAYERS = 2
 Q, K_, V, O, GATE, UP, DOWN = range(7)
 POOL = 16
+CHANNELS = 128
+FREE_RUNNING_LAYERS = 2
+DRIFT = {}
+
+
+def _sample_channels(layer, j):
+    n = LAYER_SHAPES[j][1]
+    return np.sort(rng_for(4, layer, j, 3).choice(n, CHANNELS, replace=False))
 
 
 def _gen(args):
+    """One Linear's seeded bf16 weights, and the oracle's quantization of
+    its sampled output channels (each row is quantized on its own)."""
     layer, j = args
     _, n, k = LAYER_SHAPES[j]
-    return weight_bf16(4, layer, j, n, k)
+    w = weight_bf16(4, layer, j, n, k)
+    cols = _sample_channels(layer, j)
+    rqw, rsw = oracle.quant_weight_ref(w[cols])
+    return w, (cols, rqw, rsw)
 
 
 @pytest.fixture(scope="module")
-def stack_weights():
+def stack():
     """All 252 quantized weights on the GPU (quantized there from the seeded
-    bf16 draws, which are generated in parallel and dropped once used)."""
+    bf16 draws, generated in parallel and dropped once used) and the
+    oracle's codes of each Linear's sampled channels."""
     qws = [[None] * 7 for _ in range(LAYERS)]
+    ref = [[None] * 7 for _ in range(LAYERS)]
     jobs = [(layer, j) for layer in range(LAYERS) for j in range(7)]
     with ThreadPoolExecutor(POOL) as ex:
-        for (layer, j), w in zip(jobs, ex.map(_gen, jobs)):
+        for (layer, j), (w, r) in zip(jobs, ex.map(_gen, jobs)):
             qws[layer][j] = fq.quantize_weight_channelwise(to_dev_bf16(w))
+            ref[layer][j] = r
             del w
     torch.cuda.synchronize()
-    return qws
-
-
-def _oracle_quant_rows(w_bits):
-    """Oracle weight quantization of a large matrix, rows split over threads
-    (each row is quantized independently by definition)."""
-    chunks = np.array_split(np.arange(w_bits.shape[0]), POOL)
-    with ThreadPoolExecutor(POOL) as ex:
-        parts = list(ex.map(lambda r: oracle.quant_weight_ref(w_bits[r]), chunks))
-    return (np.concatenate([p[0] for p in parts]),
-            np.concatenate([p[1] for p in parts]))
-
-
-FRO_BOUND = 0.03
-ROW_BOUND = 0.10
-
-
-def _check_noise_bound(y_bits, y64, what):
-    y = bf16_bits_to_f32(y_bits).astype(np.float64)
-    d = y - y64
-    assert np.all(np.isfinite(y)), what
-    fro = np.linalg.norm(d) / np.linalg.norm(y64)
-    row = np.sqrt(np.mean(d * d, axis=1)) / np.sqrt(np.mean(y64 * y64, axis=1))
-    assert fro <= FRO_BOUND, f"{what}: relative Frobenius error {fro:.4f}"
-    assert row.max() <= ROW_BOUND, f"{what}: row RMS error {row.max():.4f}"
+    return qws, ref
 
 
 def _gpu_chain(qws, x0_bits):
-    """Run the stack on the GPU; keep every layer's input and the outputs of
-    the first ORACLE_LAYERS layers."""
+    """Run the stack on the GPU.  Per layer keep, on the host: its bf16 input
+    X_l, the up output Y_up,l, the GPU quantizer's codes and scales of both,
+    and every Linear's full output."""
     x = to_dev_bf16(x0_bits)
-    inputs, outs = [host_bits(x)], []
+    rec = []
     for layer in range(LAYERS):
         ys = {}
         for j in (Q, K_, V, O, GATE, UP):
@@ -101,63 +93,87 @@ def _gpu_chain(qws, x0_bits):
             ys[j] = fq.quant_linear(x, qw, sw)
         qw, sw = qws[layer][DOWN]
         ys[DOWN] = fq.quant_linear(ys[UP], qw, sw)
+        qx, sx = fq.quantize_act_per_token(x)
+        qu, su = fq.quantize_act_per_token(ys[UP])
+        rec.append({"x": host_bits(x), "qx": host_bits(qx), "sx": host_bits(sx),
+                    "qu": host_bits(qu), "su": host_bits(su),
+                    "y": {j: host_bits(t) for j, t in ys.items()}})
         x = ys[DOWN]
-        if layer < ORACLE_LAYERS:
-            outs.append({j: host_bits(t) for j, t in ys.items()})
-        inputs.append(host_bits(x))
     torch.cuda.synchronize()
-    return inputs, outs
+    return rec, host_bits(x)
 
 
-@pytest.mark.timeout(600)
+def _oracle_quant_rows(w_bits):
+    """Oracle weight quantization of a large matrix, rows split over threads."""
+    chunks = np.array_split(np.arange(w_bits.shape[0]), POOL)
+    with ThreadPoolExecutor(POOL) as ex:
+        parts = list(ex.map(lambda r: oracle.quant_weight_ref(w_bits[r]), chunks))
+    return (np.concatenate([p[0] for p in parts]),
+            np.concatenate([p[1] for p in parts]))
+
+
+def _free_running_drift(rec, x0, m):
+    """The oracle's own chain (its bf16 outputs feed its next layer) over the
+    first layers: relative Frobenius distance of the GPU's down output from
+    the oracle's, per layer.  Reported, not asserted."""
+    x_bits, drift = x0, []
+    for layer in range(FREE_RUNNING_LAYERS):
+        qx, sx = oracle.quant_act_ref(x_bits)
+        _, n, k = LAYER_SHAPES[UP]
+        rqw, rsw = _oracle_quant_rows(weight_bf16(4, layer, UP, n, k))
+        up_bits = f64_to_bf16_bits(oracle.linear_ref(qx, sx, rqw, rsw))
+        qu, su = oracle.quant_act_ref(up_bits)
+        _, n, k = LAYER_SHAPES[DOWN]
+        rqw, rsw = _oracle_quant_rows(weight_bf16(4, layer, DOWN, n, k))
+        y_dn = oracle.linear_ref(qu, su, rqw, rsw)
+        g = bf16_bits_to_f32(rec[layer]["y"][DOWN]).astype(np.float64)
+        drift.append(float(np.linalg.norm(g - y_dn) / np.linalg.norm(y_dn)))
+        x_bits = f64_to_bf16_bits(y_dn)
+    DRIFT[m] = drift
+    return drift
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("m", [64, 256])
-def test_stack_against_free_running_oracle(stack_weights, m):
+def test_stack_teacher_forced_every_layer(stack, m):
+    qws, ref = stack
     x0 = c4_x0(m)
-    inputs, outs = _gpu_chain(stack_weights, x0)
+    rec, x_out = _gpu_chain(qws, x0)
+    assert np.array_equal(rec[0]["x"], x0)
 
-    # Properties over the whole stack.
+    # Properties over the whole stack: finite, and the per-layer RMS growth
+    # within the range the weight distribution implies
+    # (sqrt(4096) * 0.02 * sqrt(12288) * 0.02 ~ 2.8).
     rms = []
-    for layer, xb in enumerate(inputs):
+    for layer, xb in enumerate([r["x"] for r in rec] + [x_out]):
         xf = bf16_bits_to_f32(xb).astype(np.float64)
         assert np.all(np.isfinite(xf)), f"non-finite input of layer {layer}"
         rms.append(float(np.sqrt(np.mean(xf * xf))))
     growth = np.array(rms[1:]) / np.array(rms[:-1])
     assert np.all((growth > 1.5) & (growth < 5.0)), growth
 
-    # The oracle's own chain for the first layers.
-    x_bits = x0
-    rng = np.random.default_rng(m)
-    for layer in range(ORACLE_LAYERS):
-        if layer == 0:
-            assert np.array_equal(inputs[0], x_bits)
-        qx, sx = oracle.quant_act_ref(x_bits)
-        for j in (Q, K_, V, O, GATE):
-            _, n, k = LAYER_SHAPES[j]
-            cols = np.sort(rng.choice(n, 128, replace=False))
-            w = weight_bf16(4, layer, j, n, k)[cols]
-            rqw, rsw = oracle.quant_weight_ref(w)
-            gq, gs = stack_weights[layer][j]
-            check_bytes(host_bits(gq)[cols], rqw, f"L{layer} {j} qw rows")
-            check_bytes(host_bits(gs)[cols].view(np.uint32), rsw.view(np.uint32),
-                        f"L{layer} {j} sw rows")
-            y64 = oracle.linear_ref(qx, sx, rqw, rsw)
-            if layer == 0:
-                check_close(outs[layer][j][:, cols], y64, f"L{layer} linear {j} m={m}")
-            else:
-                _check_noise_bound(outs[layer][j][:, cols], y64, f"L{layer} linear {j} m={m}")
-        w_up = weight_bf16(4, layer, UP, LAYER_SHAPES[UP][1], LAYER_SHAPES[UP][2])
-        rqw_up, rsw_up = _oracle_quant_rows(w_up)
-        del w_up
-        y_up64 = oracle.linear_ref(qx, sx, rqw_up, rsw_up)
-        if layer == 0:
-            check_close(outs[layer][UP], y_up64, f"L{layer} up m={m}")
-        else:
-            _check_noise_bound(outs[layer][UP], y_up64, f"L{layer} up m={m}")
-        up_bits = f64_to_bf16_bits(y_up64)               # the oracle's bf16 output
-        qu, su = oracle.quant_act_ref(up_bits)
-        w_dn = weight_bf16(4, layer, DOWN, LAYER_SHAPES[DOWN][1], LAYER_SHAPES[DOWN][2])
-        rqw_dn, rsw_dn = _oracle_quant_rows(w_dn)
-        del w_dn
-        y_dn64 = oracle.linear_ref(qu, su, rqw_dn, rsw_dn)
-        _check_noise_bound(outs[layer][DOWN], y_dn64, f"L{layer} down m={m}")
-        x_bits = f64_to_bf16_bits(y_dn64)                # next layer's input
+    for layer in range(LAYERS):
+        r = rec[layer]
+        # Layer input and down's input: per-token codes and scales of the
+        # GPU's own bf16 tensors, bit-exact.
+        qx, sx = oracle.quant_act_ref(r["x"])
+        check_bytes(r["sx"].view(np.uint32), sx.view(np.uint32), f"L{layer} m={m} X scales")
+        check_bytes(r["qx"], qx, f"L{layer} m={m} X codes")
+        qu, su = oracle.quant_act_ref(r["y"][UP])
+        check_bytes(r["su"].view(np.uint32), su.view(np.uint32), f"L{layer} m={m} Y_up scales")
+        check_bytes(r["qu"], qu, f"L{layer} m={m} Y_up codes")
+        for j in range(7):
+            cols, rqw, rsw = ref[layer][j]
+            gq, gs = qws[layer][j]
+            idx = torch.from_numpy(cols).to(gs.device)
+            check_bytes(host_bits(gq.view(torch.uint8)[idx]), rqw,
+                        f"L{layer} {LAYER_SHAPES[j][0]} qw rows")
+            check_bytes(host_bits(gs[idx]).view(np.uint32), rsw.view(np.uint32),
+                        f"L{layer} {LAYER_SHAPES[j][0]} sw rows")
+            a, s = (qu, su) if j == DOWN else (qx, sx)
+            check_close(r["y"][j][:, cols], oracle.linear_ref(a, s, rqw, rsw),
+                        f"stack m={m} L{layer} {LAYER_SHAPES[j][0]}")
+
+    drift = _free_running_drift(rec, x0, m)
+    print(f"free-running oracle chain, m={m}: relative Frobenius distance of "
+          f"down outputs per layer {[round(d, 4) for d in drift]}")
