@@ -6,16 +6,20 @@
   the float32 accumulation on the GPU, so they are compared with the
   oracle's float64 value elementwise, with a relative tolerance of 1e-2
   against the oracle's output magnitude.  Reading of "the output
-  magnitude": for element (m, n) it is ``max(|y64[m, n]|, rms(y64[m, :]))``,
-  the larger of the element itself and the root-mean-square of the token's
-  output row.  Elements at least as large as the row RMS are thus held to
-  1 % of their own value and smaller ones to 1 % of the row RMS.  The floor
-  comes from the arithmetic of FP8 matrix instructions: products inside one
-  instruction are summed in fixed point about 13 bits below the largest
+  magnitude": for element (m, n) it is
+  ``max(|y64[m, n]|, RMS_FLOOR * rms(y64[m, :]))`` with RMS_FLOOR = 2^-3:
+  an element at least an eighth of the token's output-row RMS is held to
+  1 % of its own value, a smaller one to 1.25e-3 of the row RMS.  The floor
+  comes from the arithmetic of FP8 matrix instructions: the products inside
+  one instruction are summed in fixed point about 13 bits below the largest
   product, so an output that cancels to near zero carries an absolute error
-  of order 1e-4 of the row RMS, which a per-element relative test cannot
-  absorb.  A row whose oracle output is all zero must be exactly +-0.
-  NaN or infinity in the GPU output is always a failure.
+  that is a small fraction of the row RMS, which a purely relative test
+  cannot absorb.  Measured over every output comparison of the GPU tests,
+  the largest such error is 7.8e-4 of the row RMS (random E4M3 codes, whose
+  products span 2^36) and 3.7e-4 on the model-shaped workloads, so 1.25e-3
+  leaves a margin of 1.6x and 3.4x; a wrong scale, index or dropped K block
+  moves elements by far more.  A row whose oracle output is all zero must
+  be exactly +-0.  NaN or infinity in the GPU output is always a failure.
 """
 
 import numpy as np
@@ -23,7 +27,7 @@ import numpy as np
 from .bf16 import bf16_bits_to_f32, f64_to_bf16_bits
 
 REL_TOL = 1e-2
-RMS_FLOOR = 1.0
+RMS_FLOOR = 2.0 ** -3
 
 
 def check_bytes(got: np.ndarray, want: np.ndarray, what: str = "bytes"):

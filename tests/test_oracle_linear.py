@@ -135,3 +135,20 @@ def test_check_close_plants():
     with pytest.raises(AssertionError):
         check_close(nan, y64)
     assert close_report(good, y64)["frac_bf16_equal"] == 1.0
+    # A small element (1 % of its row's RMS) off by 0.5 % of the row RMS,
+    # i.e. 50 % of itself: within 1e-2 x the row RMS (the floor of 1.0 it
+    # replaces), but not within 1e-2 x 2^-3 of it.
+    small = y64.copy()
+    rms1 = np.sqrt(np.mean(y64[1] ** 2))
+    small[1, 7] = 0.01 * rms1
+    off = f64_to_bf16_bits(small)
+    off[1, 7] = bf16_from_f64(np.array([small[1, 7] + 0.005 * rms1]))[0]
+    err = abs(float(bf16_bits_to_f32(off[1:2, 7:8])[0, 0]) - small[1, 7])
+    rms_small = np.sqrt(np.mean(small[1] ** 2))
+    assert 1e-2 * 2.0 ** -3 * rms_small < err < 1e-2 * rms_small
+    with pytest.raises(AssertionError):
+        check_close(off, small)
+    # ... while an error of 1e-3 of the row RMS on it passes.
+    ok = f64_to_bf16_bits(small)
+    ok[1, 7] = bf16_from_f64(np.array([small[1, 7] + 0.001 * rms1]))[0]
+    check_close(ok, small)
