@@ -47,6 +47,9 @@ SIGNATURES = {
     "fp8w8a8_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_quant_linear_noalloc":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                        _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_rmsnorm_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_i64,
                         _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -457,6 +460,30 @@ def quant_linear(x, qw, w_scale, out=None, workspace=None):
         y.data_ptr(), y.stride(0), ws.data_ptr() if ws is not None else None,
         ws.numel() if ws is not None else 0, _stream_ptr(x.device)),
         "quant_linear")
+    return y
+
+
+def quant_linear_noalloc(x, qw, w_scale, out=None):
+    """The fused forward without a workspace: the library stages what it
+    needs in its own per-GPU scratch array (no allocation by the library;
+    calls that overlap on one GPU race).  Same results as quant_linear."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    qw = _as_codes(qw)
+    m, k, ldx = _rows(x, "x")
+    n, k2, ldw = _rows(qw, "qw")
+    if k2 != k or ldw != k:
+        raise ValueError("qw must be contiguous [N, K] with the K of x")
+    if qw.device != x.device:
+        raise ValueError("x and qw must be on one device")
+    w_scale = _scales(w_scale, n, x.device, "w_scale")
+    y = _out(m, n, x.device, out)
+    if m == 0 or n == 0:
+        return y
+    _check(lib.fp8w8a8_quant_linear_noalloc(
+        x.data_ptr(), ldx, qw.data_ptr(), w_scale.data_ptr(), m, n, k,
+        y.data_ptr(), y.stride(0), _stream_ptr(x.device)), "quant_linear_noalloc")
     return y
 
 

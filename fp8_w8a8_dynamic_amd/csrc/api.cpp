@@ -201,6 +201,119 @@ const char* test_hook(const char* name) {
 
 }  // namespace fp8w8a8
 
+namespace {
+
+// ---- The allocation-free variant of the fused forward -----------------------
+//
+// fp8w8a8_quant_linear_noalloc takes no workspace: where the fused call
+// stages the quantized activations (and, for split-K plans, the float32
+// partial sums) it uses this file-scope device array instead.  Each GPU
+// holds its own copy (allocated when the code object is loaded on that GPU,
+// held until the process ends).  Host code never passes the array's name to
+// a kernel or a copy -- on the host that name is only a stand-in for the
+// symbol -- but the device address that hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in g_scratch_addr.
+// Nothing in it has to start at zero: every byte a call's kernels read was
+// written earlier in the same call (quantizer before matmul, every split
+// before the reduction).  Calls that overlap on one GPU share the array and
+// race.
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static_assert(kNoAllocScratchBytes == FP8W8A8_NOALLOC_SCRATCH_BYTES,
+              "header and library agree on the scratch size");
+__device__ __align__(256) static uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // guarded by g_scratch_mu
+
+// The current device's address of `scratch`, looked up on first use with
+// that device current.
+int scratch_address(uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = static_cast<int>(e);
+    return FP8W8A8_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e);
+    if (p == nullptr) return fail_hip(hipErrorInvalidSymbol);
+    g_scratch_addr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_addr[dev]);
+  return FP8W8A8_OK;
+}
+
+// The fused forward on a caller workspace (use_scratch == false) or on the
+// library's per-device scratch (use_scratch == true, workspace_bytes = its
+// size; the workspace pointer is ignored).
+int quant_linear_impl(const uint16_t* x, int64_t ldx, const uint8_t* qw,
+                      const float* w_scale, int64_t m, int64_t n, int64_t k,
+                      uint16_t* y, int64_t ldy, uint8_t* workspace,
+                      size_t workspace_bytes, bool use_scratch, void* stream) {
+  if (!x || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
+  int st = check_linear_shape(m, n, k, ldy);
+  if (st != FP8W8A8_OK) return st;
+  if (!ld_ok(ldx, k)) return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) ||
+      !aligned16(y) || (!use_scratch && workspace && !aligned16(workspace)))
+    return FP8W8A8_ERR_ALIGN;
+  const Range ry = span(y, m, n, ldy, 2);
+  const Range rx = span(x, m, k, ldx, 2);
+  if (overlap(ry, rx) || overlap(ry, span(qw, n, k, k, 1)) ||
+      overlap(ry, span(w_scale, n, 1, 1, 4)))
+    return FP8W8A8_ERR_ALIAS;
+  const Path path = choose_path(m, n, k);
+  const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
+  const Layout L = layout_for(m, n, k, Pre::kQuant, path, plan);
+  const size_t need = L.total;
+  if (need > 0) {
+    if (use_scratch) {
+      if (need > workspace_bytes) return FP8W8A8_ERR_WORKSPACE;
+    } else {
+      if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
+      const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                     reinterpret_cast<uintptr_t>(workspace) + need};
+      if (overlap(rw, ry) || overlap(rw, rx) || overlap(rw, span(qw, n, k, k, 1)) ||
+          overlap(rw, span(w_scale, n, 1, 1, 4)))
+        return FP8W8A8_ERR_ALIAS;
+    }
+  }
+  if (m == 0 || n == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  uint8_t* ws = workspace;
+  if (use_scratch) {
+    ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws)) != FP8W8A8_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k)) {
+    e = fp8w8a8::launch_gemv(x, ldx, nullptr, nullptr, qw, w_scale, m, n, k,
+                             y, ldy, s);
+  } else {
+    // Quantize into the workspace, then run the matching linear kernel.
+    uint8_t* qx = ws + L.qx;
+    float* sx = reinterpret_cast<float*>(ws + L.sx);
+    e = fp8w8a8::launch_quant_rows(x, m, k, ldx, qx, sx, s);
+    if (e == hipSuccess) {
+      if (path == Path::kGemv)
+        e = fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y,
+                                 ldy, s);
+      else if (path == Path::kGemvTok)
+        e = fp8w8a8::launch_gemv_tok(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
+      else
+        e = fp8w8a8::launch_gemm(plan, qx, sx, qw, w_scale, m, n, k, y, ldy,
+                                 reinterpret_cast<float*>(ws + L.part), s);
+    }
+  }
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fp8w8a8_status_string(int status) {
@@ -473,55 +586,17 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
                          const float* w_scale, int64_t m, int64_t n, int64_t k,
                          uint16_t* y, int64_t ldy, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (!x || !qw || !w_scale || !y) return FP8W8A8_ERR_NULL;
-  int st = check_linear_shape(m, n, k, ldy);
-  if (st != FP8W8A8_OK) return st;
-  if (!ld_ok(ldx, k)) return FP8W8A8_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(qw) || !aligned16(w_scale) ||
-      !aligned16(y) || (workspace && !aligned16(workspace)))
-    return FP8W8A8_ERR_ALIGN;
-  const Range ry = span(y, m, n, ldy, 2);
-  const Range rx = span(x, m, k, ldx, 2);
-  if (overlap(ry, rx) || overlap(ry, span(qw, n, k, k, 1)) ||
-      overlap(ry, span(w_scale, n, 1, 1, 4)))
-    return FP8W8A8_ERR_ALIAS;
-  const Path path = choose_path(m, n, k);
-  const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
-  const Layout L = layout_for(m, n, k, Pre::kQuant, path, plan);
-  const size_t need = L.total;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
-    const Range rw{reinterpret_cast<uintptr_t>(workspace),
-                   reinterpret_cast<uintptr_t>(workspace) + need};
-    if (overlap(rw, ry) || overlap(rw, rx) || overlap(rw, span(qw, n, k, k, 1)) ||
-        overlap(rw, span(w_scale, n, 1, 1, 4)))
-      return FP8W8A8_ERR_ALIAS;
-  }
-  if (m == 0 || n == 0) return FP8W8A8_OK;
-  if ((st = check_device()) != FP8W8A8_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipError_t e;
-  if (path == Path::kGemv && fp8w8a8::gemv_fused_fits(m, n, k)) {
-    e = fp8w8a8::launch_gemv(x, ldx, nullptr, nullptr, qw, w_scale, m, n, k,
-                             y, ldy, s);
-  } else {
-    // Quantize into the workspace, then run the matching linear kernel.
-    uint8_t* qx = ws + L.qx;
-    float* sx = reinterpret_cast<float*>(ws + L.sx);
-    e = fp8w8a8::launch_quant_rows(x, m, k, ldx, qx, sx, s);
-    if (e == hipSuccess) {
-      if (path == Path::kGemv)
-        e = fp8w8a8::launch_gemv(nullptr, 0, qx, sx, qw, w_scale, m, n, k, y,
-                                 ldy, s);
-      else if (path == Path::kGemvTok)
-        e = fp8w8a8::launch_gemv_tok(qx, sx, qw, w_scale, m, n, k, y, ldy, s);
-      else
-        e = fp8w8a8::launch_gemm(plan, qx, sx, qw, w_scale, m, n, k, y, ldy,
-                                 reinterpret_cast<float*>(ws + L.part), s);
-    }
-  }
-  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+  return quant_linear_impl(x, ldx, qw, w_scale, m, n, k, y, ldy,
+                           static_cast<uint8_t*>(workspace), workspace_bytes,
+                           false, stream);
+}
+
+int fp8w8a8_quant_linear_noalloc(const uint16_t* x, int64_t ldx,
+                                 const uint8_t* qw, const float* w_scale,
+                                 int64_t m, int64_t n, int64_t k, uint16_t* y,
+                                 int64_t ldy, void* stream) {
+  return quant_linear_impl(x, ldx, qw, w_scale, m, n, k, y, ldy, nullptr,
+                           kNoAllocScratchBytes, true, stream);
 }
 
 }  // extern "C"

@@ -258,6 +258,32 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
                          size_t workspace_bytes, void* stream);
 
 /*
+ * The fused forward above for callers that cannot allocate or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same kernels and bit-identical results as
+ * fp8w8a8_quant_linear; where that call would stage the quantized
+ * activations (and float32 split-K partial sums) in the caller's
+ * workspace, this one uses a device array of FP8W8A8_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on each GPU it runs on (from when the
+ * library's code is loaded on that GPU until the process ends).  It calls
+ * no allocating routine.
+ *   x, ldx, qw, w_scale, m, n, k, y, ldy  as for fp8w8a8_quant_linear
+ * Errors as for fp8w8a8_quant_linear, and FP8W8A8_ERR_WORKSPACE (nothing
+ * launched) when the call needs more scratch than the array holds, i.e.
+ * when fp8w8a8_workspace_bytes(m, n, k, 1) > FP8W8A8_NOALLOC_SCRATCH_BYTES
+ * (roughly m * k > 64 Mi codes).  Decode-sized calls need no scratch.
+ * All calls on one GPU share that GPU's array and it keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that may overlap
+ * on one GPU (other streams, other threads) race, and the caller must
+ * serialize them.
+ */
+#define FP8W8A8_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int fp8w8a8_quant_linear_noalloc(const uint16_t* x, int64_t ldx,
+                                 const uint8_t* qw, const float* w_scale,
+                                 int64_t m, int64_t n, int64_t k, uint16_t* y,
+                                 int64_t ldy, void* stream);
+
+/*
  * The adjacent fusions followed by the Linear, in one call: exactly
  * fp8w8a8_rmsnorm_quantize(x, gamma, eps) (or fp8w8a8_swiglu_quantize(gate,
  * up)) followed by fp8w8a8_fp8_linear, with bit-identical output.  The norm

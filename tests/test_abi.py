@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -365,3 +365,22 @@ def test_overrides_off_without_the_test_switch():
     assert outs["0"][0] == 0                      # M = 1 stays on the GEMV: no scratch
     assert outs["1"][0] == 2 * 1 * 64 * 4         # forced 2-way split-K GEMM
     assert outs["0"][1] != outs["1"][1]
+
+
+def test_quant_linear_noalloc_validation(lib):
+    """The allocation-free fused entry point validates like quant_linear and
+    refuses, before touching a device, a call whose staging would not fit
+    its fixed scratch array (64 MiB)."""
+    f = lib.fp8w8a8_quant_linear_noalloc
+    assert f(None, 256, 4 * A, 8 * A, 64, 64, 256, 16 * A, 64, None) == ENULL
+    assert f(A, 256, 4 * A, 8 * A, 64, 24, 256, 16 * A, 64, None) == ESHAPE
+    assert f(A, BIG, 4 * A, 8 * A, 64, 64, 256, 16 * A, 64, None) == ESHAPE
+    assert f(A + 8, 256, 4 * A, 8 * A, 64, 64, 256, 16 * A, 64, None) == EALIGN
+    assert f(A, 256, 4 * A, 8 * A, 64, 64, 256, A + 64, 64, None) == EALIAS
+    # 16384 x 4096 codes + scales: 64 MiB + 64 KiB of staging > 64 MiB
+    assert lib.fp8w8a8_workspace_bytes(16384, 4096, 4096, 1) > 64 << 20
+    assert f(A, 4096, 4 * A, 8 * A, 16384, 4096, 4096, 1 << 40, 4096, None) == EWS
+    # 16000 rows fit
+    assert lib.fp8w8a8_workspace_bytes(16000, 4096, 4096, 1) <= 64 << 20
+    assert f(A, 4096, 4 * A, 8 * A, 16000, 4096, 4096, 1 << 40, 4096, None) == EDEV
+    assert f(A, 256, 4 * A, 8 * A, 0, 64, 256, 16 * A, 64, None) == OK
