@@ -347,6 +347,29 @@ def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
     t, slices = time_chunks(torch, g.replay, reps)
     t /= DECODE_COPIES
     del g
+    single = None
+    if m == 1 and not packed:
+        # The same 7 Linears of each copy as one grouped call (one launch per
+        # layer copy: fp8w8a8_quant_linear_group_m1, outputs bit-identical
+        # to the 7 calls): the ceiling of one long weight stream.
+        def grouped(layer):
+            fq.quant_linear_group_m1([L["x"] for L in layer], [L["qw"] for L in layer],
+                                     [L["sw"] for L in layer], [L["y"] for L in layer])
+        gg = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            grouped(copies[0])
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gg, stream=cap):
+                for c in copies:
+                    grouped(c)
+        torch.cuda.synchronize()
+        warm_for(torch, gg.replay)
+        tg, gslices = time_chunks(torch, gg.replay, reps)
+        tg /= DECODE_COPIES
+        single = {"us_per_layer": round(tg * 1e6, 3), "value": round(nbytes / tg / 1e9, 1),
+                  "unit": "GB/s", "frac_of_hbm": round(nbytes / tg / 1e9 / HBM_PEAK_GBS, 4),
+                  "slice_gbs": spread([nbytes * DECODE_COPIES / ts / 1e9 for ts in gslices])}
+        del gg
     del copies
     # Each Linear on its own: a graph of that Linear's call on copies of its
     # weights in turn (at least ROTATE_BYTES of distinct weights per replay,
@@ -372,7 +395,47 @@ def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
     del base
     torch.cuda.empty_cache()
     return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes, per_linear=per,
+                single_launch=single,
                 slices=[nbytes * DECODE_COPIES / ts / 1e9 for ts in slices])
+
+
+def launch_floor(torch, sizes, reps=40):
+    """The bound that separate launches cannot pass: a HIP graph of one
+    plain streaming read (the measured-peak read kernel) per size in
+    `sizes`, back to back, over buffer copies past the last-level cache:
+    us per sequence and GB/s of the bytes read.  Compared with one read of
+    the summed size, it gives the fixed cost of each extra launch."""
+    import ctypes
+    from fp8_w8a8_dynamic_amd import build as fbuild
+    lib = ctypes.CDLL(fbuild.PEAKS_LIB_PATH)
+    lib.fp8w8a8_peaks_read_stream.restype = ctypes.c_int
+    lib.fp8w8a8_peaks_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+    total = sum(sizes)
+    copies = max(2, -(-ROTATE_BYTES // total))
+    bufs = [[torch.empty(sz, dtype=torch.uint8, device="cuda") for sz in sizes]
+            for _ in range(copies)]
+    one = [torch.empty(total, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    out = torch.empty(1024 * 256, dtype=torch.int32, device="cuda")
+
+    def seq(c, parts):
+        st = torch.cuda.current_stream().cuda_stream
+        for b in parts:
+            if lib.fp8w8a8_peaks_read_stream(b.data_ptr(), b.numel(), out.data_ptr(), st):
+                raise RuntimeError("read_stream failed")
+    res = {}
+    for name, sets in (("separate", bufs), ("one_read", [[o] for o in one])):
+        gr = graph_of(torch, rotating([lambda c=c: seq(0, c) for c in sets]), len(sets))
+        warm_for(torch, gr.replay, 0.1)
+        t = time_events(torch, gr.replay, reps) / len(sets)
+        res[name] = {"us": round(t * 1e6, 3), "gbs": round(total / t / 1e9, 1)}
+        del gr
+    res["launches"] = len(sizes)
+    res["fixed_cost_us_per_extra_launch"] = round(
+        (res["separate"]["us"] - res["one_read"]["us"]) / max(1, len(sizes) - 1), 3)
+    del bufs, one, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_stack(torch, fq, m, passes):
@@ -410,7 +473,14 @@ def bench_stack(torch, fq, m, passes):
     for _ in range(3):
         one_pass()
     warm_for(torch, one_pass)
-    t = time_events(torch, one_pass, passes)
+    # Eagerly launched from Python (each call's host-side cost included) ...
+    t_eager = time_events(torch, one_pass, passes)
+    # ... and the pass captured once in a HIP graph and replayed (as a
+    # serving loop would): the GPU-side figure.
+    gr = graph_of(torch, one_pass, 1)
+    warm_for(torch, gr.replay)
+    t = time_events(torch, gr.replay, passes)
+    del gr
     nbytes = 36 * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for _, n, k in LAYER_SHAPES)
     flops = 36 * sum(2 * m * n * k for _, n, k in LAYER_SHAPES)
     del layers, xs, ys
@@ -418,7 +488,9 @@ def bench_stack(torch, fq, m, passes):
     return {"m": m, "ms_per_pass": round(t * 1e3, 4), "gbs": round(nbytes / t / 1e9, 1),
             "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(flops / t / 1e12, 2),
-            "frac_of_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
+            "frac_of_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "us_per_layer": round(t * 1e6 / 36, 2),
+            "eager_ms_per_pass": round(t_eager * 1e3, 4)}
 
 
 def graph_of(torch, fn, calls):
@@ -918,7 +990,13 @@ def main():
     if not args.no_decode:
         log("decode ...")
         dec = bench_decode(torch, fq, max(20, args.steps))
-        log(f"decode layer {dec['layer_us']:.2f} us  {dec['gbs']:.0f} GB/s")
+        log(f"decode layer {dec['layer_us']:.2f} us  {dec['gbs']:.0f} GB/s; one launch "
+            f"{dec['single_launch']}")
+        from workloads import LAYER_SHAPES
+        dec_floor = launch_floor(torch, [n * k for _, n, k in LAYER_SHAPES])
+        dec_floor["what"] = ("plain streaming reads of the 7 weight matrices' bytes as 7 "
+                             "launches in a graph, against one read of their sum")
+        log(f"launch floor {dec_floor}")
         dec_more = {mm: bench_decode(torch, fq, max(20, args.steps // 2), m=mm)
                     for mm in (4, 8)}
         log("decode M=4, 8: " + ", ".join(f"{v['layer_us']:.1f} us {v['gbs']:.0f} GB/s"
@@ -1017,6 +1095,12 @@ def main():
                          "bytes_per_layer": dec["bytes"],
                          "slice_gbs": spread(dec["slices"]),
                          "per_linear": dec["per_linear"],
+                         "single_launch": dict(
+                             dec["single_launch"] or {},
+                             what="the same 7 Linears of the layer (independent inputs) "
+                                  "as ONE grouped call, fp8w8a8_quant_linear_group_m1 "
+                                  "(outputs bit-identical to the 7 calls)"),
+                         "launch_floor": dec_floor,
                          "other_token_counts": {
                              f"m{mm}": {"value": round(v["gbs"], 1), "unit": "GB/s",
                                         "us_per_layer": round(v["layer_us"], 3),
@@ -1026,8 +1110,9 @@ def main():
     if stack is not None:
         out["stack_36_layers"] = {
             "metric": "one pass of the 36-layer stack (252 fused calls, 6.946 GB of "
-                      "FP8 weights in HBM, layer outputs chained): GB/s of algorithmic "
-                      "bytes and TFLOP/s",
+                      "FP8 weights in HBM, layer outputs chained), captured in a HIP "
+                      "graph and replayed: GB/s of algorithmic bytes and TFLOP/s "
+                      "(eager_ms_per_pass: the same calls launched from Python)",
             "passes": stack}
     f = norm["fused"]
     out["rmsnorm_quant"] = {

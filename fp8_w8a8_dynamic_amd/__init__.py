@@ -14,7 +14,8 @@ marshalling only).
 from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
                       init_workspace, kv_dequantize_fp8, kv_quantize_fp8,
                       kv_quantize_int8, kv_read_int8, load_library,
-                      quant_linear, quant_linear_noalloc, quantize_act_per_token,
+                      quant_linear, quant_linear_group_m1, quant_linear_noalloc,
+                      quantize_act_per_token,
                       rmsnorm_quant_linear,
                       swiglu_quant_linear,
                       quantize_weight_channelwise, rmsnorm_quantize, swiglu_quantize,
@@ -23,7 +24,8 @@ from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
 __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
            "init_workspace", "kv_dequantize_fp8", "kv_quantize_fp8",
            "kv_quantize_int8", "kv_read_int8",
-           "load_library", "quant_linear", "quant_linear_noalloc",
+           "load_library", "quant_linear", "quant_linear_group_m1",
+           "quant_linear_noalloc",
            "quantize_act_per_token", "quantize_weight_channelwise",
            "rmsnorm_quantize", "rmsnorm_quant_linear", "swiglu_quantize",
            "swiglu_quant_linear", "workspace_bytes"]

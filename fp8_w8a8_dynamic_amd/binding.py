@@ -50,6 +50,8 @@ SIGNATURES = {
     "fp8w8a8_quant_linear_noalloc":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp]),
+    "fp8w8a8_quant_linear_group_m1":
+        (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp]),
     "fp8w8a8_rmsnorm_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_i64,
                         _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -485,6 +487,44 @@ def quant_linear_noalloc(x, qw, w_scale, out=None):
         x.data_ptr(), ldx, qw.data_ptr(), w_scale.data_ptr(), m, n, k,
         y.data_ptr(), y.stride(0), _stream_ptr(x.device)), "quant_linear_noalloc")
     return y
+
+
+class _GroupLinear(ctypes.Structure):
+    """Mirror of fp8w8a8_group_linear."""
+    _fields_ = [("x", _c_vp), ("qw", _c_vp), ("w_scale", _c_vp), ("y", _c_vp),
+                ("n", _c_i64), ("k", _c_i64)]
+
+
+def quant_linear_group_m1(xs, qws, w_scales, outs=None):
+    """Several independent one-token FP8_DYNAMIC forwards in one launch:
+    xs[i] bf16 [1, K_i] -> outs[i] bf16 [1, N_i], each bit-identical to
+    quant_linear(xs[i], qws[i], w_scales[i])."""
+    lib = load_library()
+    count = len(xs)
+    if not (len(qws) == len(w_scales) == count) or (outs is not None and len(outs) != count):
+        raise ValueError("one qw, w_scale (and out) per x")
+    items = (_GroupLinear * max(count, 1))()
+    ys = []
+    for i, (x, qw, sw) in enumerate(zip(xs, qws, w_scales)):
+        if x.dtype != torch.bfloat16:
+            raise TypeError("x must be bfloat16")
+        qw = _as_codes(qw)
+        m, k, _ = _rows(x, "x")
+        n, k2, ldw = _rows(qw, "qw")
+        if m != 1 or k2 != k or ldw != k or qw.device != x.device:
+            raise ValueError("each x must be [1, K] with qw [N, K] contiguous on its device")
+        sw = _scales(sw, n, x.device, "w_scale")
+        y = _out(1, n, x.device, None if outs is None else outs[i])
+        if not y.is_contiguous():
+            raise ValueError("each out must be contiguous")
+        items[i] = _GroupLinear(x.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                                n, k)
+        ys.append(y)
+    if count == 0:
+        return ys
+    _check(lib.fp8w8a8_quant_linear_group_m1(items, count, _stream_ptr(xs[0].device)),
+           "quant_linear_group_m1")
+    return ys
 
 
 def rmsnorm_quant_linear(x, gamma, eps, qw, w_scale, out=None, workspace=None):

@@ -591,6 +591,38 @@ int fp8w8a8_quant_linear(const uint16_t* x, int64_t ldx, const uint8_t* qw,
                            false, stream);
 }
 
+int fp8w8a8_quant_linear_group_m1(const fp8w8a8_group_linear* items, int count,
+                                  void* stream) {
+  if (!items) return FP8W8A8_ERR_NULL;
+  if (count < 1 || count > fp8w8a8::kGroupMax) return FP8W8A8_ERR_SHAPE;
+  fp8w8a8::GroupLinear g[fp8w8a8::kGroupMax];
+  for (int i = 0; i < count; ++i) {
+    const fp8w8a8_group_linear& L = items[i];
+    if (!L.x || !L.qw || !L.w_scale || !L.y) return FP8W8A8_ERR_NULL;
+    if (L.n < 16 || L.n > kMaxDim || L.n % 16 != 0 || L.k < 128 || L.k > 12288 ||
+        L.k % 128 != 0)
+      return FP8W8A8_ERR_SHAPE;
+    if (!aligned16(L.x) || !aligned16(L.qw) || !aligned16(L.w_scale) || !aligned16(L.y))
+      return FP8W8A8_ERR_ALIGN;
+    g[i] = fp8w8a8::GroupLinear{L.x, L.qw, L.w_scale, L.y, L.n, L.k};
+  }
+  for (int i = 0; i < count; ++i) {
+    const Range ry = span(items[i].y, 1, items[i].n, items[i].n, 2);
+    for (int j = 0; j < count; ++j) {
+      const fp8w8a8_group_linear& L = items[j];
+      if (overlap(ry, span(L.x, 1, L.k, L.k, 2)) ||
+          overlap(ry, span(L.qw, L.n, L.k, L.k, 1)) ||
+          overlap(ry, span(L.w_scale, L.n, 1, 1, 4)) ||
+          (j != i && overlap(ry, span(L.y, 1, L.n, L.n, 2))))
+        return FP8W8A8_ERR_ALIAS;
+    }
+  }
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_gemv_group_m1(g, count, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 int fp8w8a8_quant_linear_noalloc(const uint16_t* x, int64_t ldx,
                                  const uint8_t* qw, const float* w_scale,
                                  int64_t m, int64_t n, int64_t k, uint16_t* y,

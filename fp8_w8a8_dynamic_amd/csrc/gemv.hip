@@ -39,6 +39,7 @@
 // (x and gamma; the row sums in the block order of row_ops.h, through LDS)
 // and the SiLU-gated activation (gate and up), each with the arithmetic of
 // its stand-alone kernel, so the codes are those the two-step path makes.
+#include <algorithm>
 #include <cstdlib>
 
 #include "device_common.h"
@@ -773,15 +774,40 @@ namespace detail {
 // through the buffer descriptors.
 // CODES: the activation arrives already quantized (qx, one code per value,
 // and its scale sx[0]): the codes are loaded in the same slices instead.
+//
+// The per-row MFMA chain and its epilogue, shared with the grouped kernel
+// below: per row, the CS steps accumulate in order into one accumulator
+// whose diagonal (the K-class partial dot products) the DPP tree sums.
+template <int CS, int R>
+__device__ __forceinline__ void m1_rows_mfma(const uint4 (&wv)[R][CS][2],
+                                             const v8i (&bq)[CS], float scale,
+                                             const float* __restrict__ sw, int N,
+                                             int row0, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int qd = (lane & 15) - 4 * (lane >> 4);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          to_v8i(wv[r][s][0], wv[r][s][1]), bq[s], acc, 0, 0, 0, 0, 0, 0);
+    float dg = qd == 0 ? acc[0] : qd == 1 ? acc[1] : qd == 2 ? acc[2]
+             : qd == 3 ? acc[3] : 0.0f;
+    dg = wave_sum_to_63(dg);
+    const int n = row0 + r;
+    if (lane == 63 && n < N) y[n] = f32_to_bf16_bits(dg * sw[n] * scale);
+  }
+}
+
+// The whole body of gemv_m1_kernel for the wave whose first row is row0.
 template <int CS, int R, bool CODES>
-__global__ __launch_bounds__(256) void gemv_m1_kernel(
+__device__ __forceinline__ void m1_rows(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ qx,
     const float* __restrict__ sx, const uint8_t* __restrict__ qw,
-    const float* __restrict__ sw, int N, int K, uint16_t* __restrict__ y) {
+    const float* __restrict__ sw, int N, int K, uint16_t* __restrict__ y,
+    int row0) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = (static_cast<int>(blockIdx.x) * 4 + wave) * R;
-  if (row0 >= N) return;
   uint4 xv[CODES ? 1 : CS][2][2];
   uint4 cv[CODES ? CS : 1][2];
   if constexpr (CODES) {
@@ -849,19 +875,181 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(
       bq[s] = to_v8i(half[0], half[1]);
     }
   }
+  m1_rows_mfma<CS, R>(wv, bq, scale, sw, N, row0, y);
+}
+
+template <int CS, int R, bool CODES>
+__global__ __launch_bounds__(256) void gemv_m1_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qx,
+    const float* __restrict__ sx, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, int N, int K, uint16_t* __restrict__ y) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = (static_cast<int>(blockIdx.x) * 4 + wave) * R;
+  if (row0 >= N) return;
+  m1_rows<CS, R, CODES>(x, qx, sx, qw, sw, N, K, y, row0);
+}
+
+// One token, K above what a wave can hold as a whole bf16 row in registers
+// (K > 4096), for the grouped kernel: the workgroup's 4 waves share the
+// row through LDS.  Every thread loads CS 16-byte chunks of x (chunk c =
+// thread + 256 j), the waves' maxima meet in LDS, every thread quantizes its
+// chunks with the quantizer's device functions into the LDS code row, and
+// every wave then reads the codes of the whole row in the K-class layout and
+// runs m1_rows_mfma: the same codes, scale and MFMA order as m1_rows, so the
+// same bits.  Waves without rows (past N) still take part in the staging.
+// LDS use: CS * 2048 code bytes + 16 (K <= 12288 in the grouped kernel).
+constexpr int kGroupMaxSteps = 6;     // K <= 12288
+constexpr int kGroupLdsBytes = kGroupMaxSteps * 2048 + 16;
+
+template <int CS, int R>
+__device__ __forceinline__ void m1_rows_lds(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, int N, int K, uint16_t* __restrict__ y,
+    int row0, uint8_t* __restrict__ codes, uint32_t* __restrict__ wmax) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  // The workgroup may have staged another row in the same LDS just before
+  // (persistent grid): every wave is done reading it once all are here.
+  lds_barrier();
+  const auto xsrc = row_rsrc(x, static_cast<uint32_t>(K) * 2u);
+  uint4 xv[CS];
+#pragma unroll
+  for (int j = 0; j < CS; ++j)
+    xv[j] = buf_load16(xsrc, static_cast<uint32_t>(tid + 256 * j) * 16u);
+  __builtin_amdgcn_sched_barrier(0);
+  const int rows = max(0, min(R, N - row0));
+  const auto wsrc = row_rsrc(qw + static_cast<int64_t>(min(row0, N)) * K,
+                             static_cast<uint32_t>(rows) * static_cast<uint32_t>(K));
+  uint4 wv[R][CS][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wv[r][s][h] = buf_load16_stream(
+            wsrc, static_cast<uint32_t>(r * K + s * 2048 + h * 1024 + lane * 16));
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t mm = 0;
+#pragma unroll
+  for (int j = 0; j < CS; ++j) {
+    mm = pk_max_u16(mm, bf16x2_abs_bits(xv[j].x));
+    mm = pk_max_u16(mm, bf16x2_abs_bits(xv[j].y));
+    mm = pk_max_u16(mm, bf16x2_abs_bits(xv[j].z));
+    mm = pk_max_u16(mm, bf16x2_abs_bits(xv[j].w));
+  }
+  const uint32_t wm = wave_max_u32(max(mm & 0xffffu, mm >> 16));
+  if (lane == 0) wmax[wave] = wm;
+  lds_barrier();
+  const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float scale = row_scale(__uint_as_float(am << 16));
+  const RowDivisor d = make_divisor(scale);
+#pragma unroll
+  for (int j = 0; j < CS; ++j)
+    *reinterpret_cast<uint2*>(codes + (tid + 256 * j) * 8) = quantize8(xv[j], d);
+  lds_barrier();
+  if (rows <= 0) return;
+  // Step-major, so that one step's codes are live at a time; each row's
+  // accumulator still takes the steps in order (the bits of m1_rows_mfma).
+  v4f acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < CS; ++s) {
+    const v8i bq = to_v8i(*reinterpret_cast<const uint4*>(codes + s * 2048 + lane * 16),
+                          *reinterpret_cast<const uint4*>(codes + s * 2048 + 1024 + lane * 16));
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          to_v8i(wv[r][s][0], wv[r][s][1]), bq, acc[r], 0, 0, 0, 0, 0, 0);
+  }
   const int qd = (lane & 15) - 4 * (lane >> 4);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < CS; ++s)
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          to_v8i(wv[r][s][0], wv[r][s][1]), bq[s], acc, 0, 0, 0, 0, 0, 0);
-    float dg = qd == 0 ? acc[0] : qd == 1 ? acc[1] : qd == 2 ? acc[2]
-             : qd == 3 ? acc[3] : 0.0f;
+    float dg = qd == 0 ? acc[r][0] : qd == 1 ? acc[r][1] : qd == 2 ? acc[r][2]
+             : qd == 3 ? acc[r][3] : 0.0f;
     dg = wave_sum_to_63(dg);
     const int n = row0 + r;
     if (lane == 63 && n < N) y[n] = f32_to_bf16_bits(dg * sw[n] * scale);
+  }
+}
+
+// Grouped one-token Linears: up to kGroupMax independent FP8_DYNAMIC
+// Linears at M = 1, K <= 12288, in one launch (a whole decode layer's weight stream with
+// one ramp-up and one tail instead of one per Linear).  The grid is the
+// concatenation of the items' work units, each item a contiguous run of
+// units of 4 waves, R rows per wave; items with K <= 4096 run m1_rows
+// (barrier-free), longer ones m1_rows_lds.  Every item's output equals,
+// bit for bit, what gemv_m1_kernel gives for it alone.
+struct GroupItem {
+  const uint16_t* x;
+  const uint8_t* qw;
+  const float* sw;
+  uint16_t* y;
+  int n, k;
+  int wg0;    // first workgroup of the item
+  int rpw;    // rows per wave
+};
+struct GroupArgs {
+  GroupItem it[kGroupMax];
+  int count;
+  int units;  // workgroup-sized work units over all items
+};
+
+template <int CS, int R>
+__device__ __forceinline__ void group_item(const GroupItem& g, int row0,
+                                           uint8_t* codes, uint32_t* wmax) {
+  if constexpr (CS <= 2) {
+    if (row0 < g.n)
+      m1_rows<CS, R, false>(g.x, nullptr, nullptr, g.qw, g.sw, g.n, g.k, g.y, row0);
+  } else {
+    m1_rows_lds<CS, R>(g.x, g.qw, g.sw, g.n, g.k, g.y, row0, codes, wmax);
+  }
+}
+
+// Rows per wave in the grouped kernel: four for the register-held rows
+// (K <= 4096), one for the rows staged through LDS.  Measured on the decode
+// layer in one launch (7 Linears, 193 MB): the 6 K = 4096 Linears take
+// 27.9 us with four rows per wave against 31.2 with two (the one-Linear
+// launches prefer two: a grouped launch has work enough to fill the GPU
+// with fewer, longer waves).  Two rows per wave for down would take it
+// from 12.8 to 11.3 us alone, but its registers lower the whole kernel's
+// occupancy and the layer then takes 38.3 us against 34.9.  With the
+// kernel held to 128 VGPRs (4 waves per SIMD, no spills) the layer takes
+// 34.1 us.
+constexpr int kGroupRowsRegs = 4;
+constexpr int kGroupRowsLds = 1;
+
+template <int CS>
+__device__ __forceinline__ void group_cs(const GroupItem& g, int local_wg, int wave,
+                                         uint8_t* codes, uint32_t* wmax) {
+  constexpr int R = CS <= 2 ? kGroupRowsRegs : kGroupRowsLds;
+  group_item<CS, R>(g, (local_wg * 4 + wave) * R, codes, wmax);
+}
+
+// A workgroup takes work units blockIdx.x, blockIdx.x + gridDim.x, ...
+// (a persistent grid of at most a few workgroups per CU: dispatching
+// thousands of short workgroups costs more than looping).
+__global__ __launch_bounds__(256, 4) void gemv_group_kernel(const GroupArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[kGroupLdsBytes];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(codes + kGroupMaxSteps * 2048);
+  for (int unit = static_cast<int>(blockIdx.x); unit < a.units;
+       unit += static_cast<int>(gridDim.x)) {
+    int i = 0;
+    for (int j = 1; j < a.count; ++j)
+      if (unit >= a.it[j].wg0) i = j;
+    const GroupItem& g = a.it[i];
+    const int local = unit - g.wg0;
+    switch ((g.k + 2047) / 2048) {
+      case 1: group_cs<1>(g, local, wave, codes, wmax); break;
+      case 2: group_cs<2>(g, local, wave, codes, wmax); break;
+      case 3: group_cs<3>(g, local, wave, codes, wmax); break;
+      case 4: group_cs<4>(g, local, wave, codes, wmax); break;
+      case 5: group_cs<5>(g, local, wave, codes, wmax); break;
+      default: group_cs<6>(g, local, wave, codes, wmax); break;
+    }
   }
 }
 
@@ -967,8 +1155,48 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* qx,
                           pl.ni, y, ldy, none, stream);
 }
 
+// Whether the pre-step runs inside the LDS-staged GEMV's activation
+// staging.  Not at one token where the barrier-free M = 1 kernel takes the
+// shape: there the stand-alone pre-step kernel followed by that kernel on
+// the codes is faster (measured per decode layer with both fusions: 47.4 us
+// against 48.2 us with the norm in the staging), and gives the same bits.
+hipError_t launch_gemv_group_m1(const GroupLinear* items, int count,
+                                hipStream_t stream) {
+  if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+  GroupArgs a{};
+  a.count = count;
+  int64_t wgs = 0;
+  int order[kGroupMax];
+  for (int i = 0; i < count; ++i) order[i] = i;
+  if (const char* e = test_hook("FP8W8A8_GROUP_SORT")) {
+    if (e[0] == '1')  // longest rows first
+      std::stable_sort(order, order + count, [&](int p, int q) {
+        return items[p].k > items[q].k;
+      });
+  }
+  for (int i = 0; i < count; ++i) {
+    const GroupLinear& L = items[order[i]];
+    const int cs = static_cast<int>((L.k + 2047) / 2048);
+    if (cs > kGroupMaxSteps) return hipErrorInvalidValue;
+    const int rpw = cs <= 2 ? kGroupRowsRegs : kGroupRowsLds;
+    a.it[i] = GroupItem{L.x, L.qw, L.sw, L.y, static_cast<int>(L.n),
+                        static_cast<int>(L.k), static_cast<int>(wgs), rpw};
+    wgs += (L.n + 4 * rpw - 1) / (4 * rpw);
+  }
+  if (wgs <= 0 || wgs > (int64_t{1} << 31) - 1) return hipErrorInvalidValue;
+  a.units = static_cast<int>(wgs);
+  int64_t grid = wgs;
+  if (const char* e = test_hook("FP8W8A8_GROUP_GRID")) {
+    const int64_t v = std::atoll(e);
+    if (v >= 1) grid = std::min(grid, v);
+  }
+  gemv_group_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 bool gemv_pre_fits(int pre, int64_t m, int64_t n, int64_t k) {
   if (!gemv_fused_fits(m, n, k) || m > kGemvMaxM) return false;
+  if (gemv_m1_fits(m, k)) return false;
   if (pre == kPreRmsNorm) return k % 512 == 0 && k / 512 <= kMaxNormBlocksPerRow;
   return pre == kPreSwiGlu;
 }

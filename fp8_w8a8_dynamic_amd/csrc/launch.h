@@ -103,6 +103,20 @@ hipError_t launch_gemv_pre(int pre, const uint16_t* x, int64_t ldx,
                            int64_t n, int64_t k, uint16_t* y, int64_t ldy,
                            hipStream_t stream);
 
+// Grouped one-token Linears (bf16 x [1, k] -> bf16 y [1, n] each, their
+// quantization fused), up to kGroupMax of them in one launch; each item's
+// output is bit-identical to launch_gemv on it alone.  k <= 12288.
+constexpr int kGroupMax = 16;
+struct GroupLinear {
+  const uint16_t* x;
+  const uint8_t* qw;
+  const float* sw;
+  uint16_t* y;
+  int64_t n, k;
+};
+hipError_t launch_gemv_group_m1(const GroupLinear* items, int count,
+                                hipStream_t stream);
+
 // Token-group GEMV, kGemvMaxM < m <= kGemvTokMaxM, on quantized activations.
 constexpr int kGemvTokMaxM = 64;
 hipError_t launch_gemv_tok(const uint8_t* qx, const float* sx,

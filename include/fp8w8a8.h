@@ -284,6 +284,34 @@ int fp8w8a8_quant_linear_noalloc(const uint16_t* x, int64_t ldx,
                                  int64_t ldy, void* stream);
 
 /*
+ * Several one-token FP8_DYNAMIC forwards in one launch: count independent
+ * Linears at M = 1 (a decode step's projections: the README's
+ * "FP8-Dynamic" Linears, whose decode speed is set by the weight bytes per
+ * the MOSS-VL-Realtime-FP8 article, "why quantize"), each exactly
+ * fp8w8a8_quant_linear(x, qw, w_scale) on one token, with bit-identical
+ * output; one launch streams all their weights with one ramp-up and one
+ * tail instead of one per Linear.
+ *   items[i].x        bf16 [1, k] (one token), 16-byte aligned      (input)
+ *   items[i].qw       E4M3 [n, k] contiguous, w_scale float32 [n]    (input)
+ *   items[i].y        bf16 [1, n], 16-byte aligned                  (output)
+ *   items[i].n, .k    n >= 16, n % 16 == 0, n < 2^31;
+ *                     128 <= k <= 12288, k % 128 == 0
+ * Rules: 1 <= count <= 16; items is a HOST array (read during the call
+ * only); every y must overlap no input of any item and no other y.  No
+ * workspace.  Errors are returned before anything is launched.
+ */
+typedef struct fp8w8a8_group_linear {
+  const uint16_t* x;
+  const uint8_t* qw;
+  const float* w_scale;
+  uint16_t* y;
+  int64_t n;
+  int64_t k;
+} fp8w8a8_group_linear;
+int fp8w8a8_quant_linear_group_m1(const fp8w8a8_group_linear* items, int count,
+                                  void* stream);
+
+/*
  * The adjacent fusions followed by the Linear, in one call: exactly
  * fp8w8a8_rmsnorm_quantize(x, gamma, eps) (or fp8w8a8_swiglu_quantize(gate,
  * up)) followed by fp8w8a8_fp8_linear, with bit-identical output.  The norm
@@ -291,9 +319,11 @@ int fp8w8a8_quant_linear_noalloc(const uint16_t* x, int64_t ldx,
  * while the Linears after them are FP8_DYNAMIC (MOSS-VL-Realtime-FP8
  * article, component / precision map; MOSS-VL quantization README,
  * "FP8-Dynamic").  At decode
- * sizes (m <= 4 and m * k <= 16384; for the norm also k % 512 == 0) the
- * norm or activation runs inside the decode GEMV's activation staging, one
- * kernel in all; otherwise its codes go through the workspace.
+ * sizes (2 <= m <= 4 and m * k <= 16384, or m == 1 and k > 4096; for the
+ * norm also k % 512 == 0) the norm or activation runs inside the decode
+ * GEMV's activation staging, one kernel in all; otherwise (including one
+ * token with k <= 4096, where two kernels are faster) its codes go through
+ * the workspace.
  *   x / gate bf16 [m, k], row stride ldx / ldg >= k, % 8 == 0        (input)
  *   gamma    bf16 [k]                                                (input)
  *   up       bf16 [m, k], row stride ldu >= k, ldu % 8 == 0          (input)

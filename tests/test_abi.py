@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -214,7 +214,9 @@ def test_pre_linear_validation(lib):
     assert swi() == EWS
     ws_norm = lib.fp8w8a8_workspace_bytes(32, 64, 256, 2)
     assert ws_norm == lib.fp8w8a8_workspace_bytes(32, 64, 256, 1) > 0
-    assert lib.fp8w8a8_workspace_bytes(1, 4096, 4096, 2) == 0   # fused into the GEMV
+    assert lib.fp8w8a8_workspace_bytes(2, 4096, 4096, 2) == 0   # fused into the GEMV
+    # one token: norm kernel, then the barrier-free M = 1 GEMV on its codes
+    assert lib.fp8w8a8_workspace_bytes(1, 4096, 4096, 2) >= 4096 + 4
     assert lib.fp8w8a8_workspace_bytes(1, 4096, 4224, 2) > 0    # k % 512 != 0
     assert lib.fp8w8a8_workspace_bytes(1, 4096, 4224, 3) == 0
     assert lib.fp8w8a8_workspace_bytes(2, 4096, 12288, 3) > 0   # m * k too large
@@ -384,3 +386,28 @@ def test_quant_linear_noalloc_validation(lib):
     assert lib.fp8w8a8_workspace_bytes(16000, 4096, 4096, 1) <= 64 << 20
     assert f(A, 4096, 4 * A, 8 * A, 16000, 4096, 4096, 1 << 40, 4096, None) == EDEV
     assert f(A, 256, 4 * A, 8 * A, 0, 64, 256, 16 * A, 64, None) == OK
+
+
+def test_group_m1_validation(lib):
+    """The grouped one-token call validates every item before a launch."""
+    from fp8_w8a8_dynamic_amd.binding import _GroupLinear
+
+    def run(items):
+        arr = (_GroupLinear * max(1, len(items)))(*items)
+        return lib.fp8w8a8_quant_linear_group_m1(arr, len(items), None)
+
+    def item(x=A, qw=4 * A, sw=8 * A, y=16 * A, n=64, k=256):
+        return _GroupLinear(x, qw, sw, y, n, k)
+
+    assert lib.fp8w8a8_quant_linear_group_m1(None, 1, None) == ENULL
+    assert run([]) == ESHAPE                                    # count 0
+    assert run([item()] * 17) == ESHAPE                         # count > 16
+    assert run([item(x=None)]) == ENULL
+    assert run([item(n=24)]) == ESHAPE and run([item(n=0)]) == ESHAPE
+    assert run([item(k=192)]) == ESHAPE
+    assert run([item(k=12288 + 128)]) == ESHAPE                 # K <= 12288
+    assert run([item(y=16 * A + 8)]) == EALIGN
+    assert run([item(y=A + 64)]) == EALIAS                      # y over its x
+    assert run([item(), item(x=32 * A, y=16 * A + 64)]) == EALIAS   # ys overlap
+    assert run([item(), item(x=16 * A, y=64 * A)]) == EALIAS    # y over another x
+    assert run([item(), item(x=32 * A, y=64 * A)]) == EDEV      # valid: no device here
