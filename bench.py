@@ -470,6 +470,28 @@ def bench_stack(torch, fq, m, passes):
                 fq.quant_linear(x, lw[j][0], lw[j][1], out=ys[j], workspace=ws)
             fq.quant_linear(ys[5], lw[6][0], lw[6][1], out=xs[li + 1], workspace=ws)
 
+    # The same stack as the checkpoint's packed modules run it: q|k|v and
+    # gate|up concatenated along the output channels, and each distinct
+    # input quantized once (X_l for qkv, o, gate_up; up's output for down):
+    # 2 quantizations and 4 matmuls per layer instead of 7 fused calls.
+    packed = [(torch.cat([lw[0][0], lw[1][0], lw[2][0]]), torch.cat([lw[0][1], lw[1][1], lw[2][1]]),
+               lw[3], torch.cat([lw[4][0], lw[5][0]]), torch.cat([lw[4][1], lw[5][1]]), lw[6])
+              for lw in layers]
+    y_qkv = torch.empty(m, 6144, dtype=torch.bfloat16, device="cuda")
+    y_gu = torch.empty(m, 24576, dtype=torch.bfloat16, device="cuda")
+    wsp = max(fq.workspace_bytes(m, n, k, False) for n, k in
+              ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)))
+    ws2 = fq.init_workspace(torch.empty(max(wsp, 1 << 20), dtype=torch.uint8, device="cuda"))
+
+    def packed_pass():
+        for li, (wqkv, sqkv, (wo, so), wgu, sgu, (wd, sd)) in enumerate(packed):
+            qx, sx = fq.quantize_act_per_token(xs[li])
+            fq.fp8_linear(qx, sx, wqkv, sqkv, out=y_qkv, workspace=ws2)
+            fq.fp8_linear(qx, sx, wo, so, out=ys[3], workspace=ws2)
+            fq.fp8_linear(qx, sx, wgu, sgu, out=y_gu, workspace=ws2)
+            qu, su = fq.quantize_act_per_token(y_gu[:, 12288:])
+            fq.fp8_linear(qu, su, wd, sd, out=xs[li + 1], workspace=ws2)
+
     for _ in range(3):
         one_pass()
     warm_for(torch, one_pass)
@@ -481,6 +503,10 @@ def bench_stack(torch, fq, m, passes):
     warm_for(torch, gr.replay)
     t = time_events(torch, gr.replay, passes)
     del gr
+    gp = graph_of(torch, packed_pass, 1)
+    warm_for(torch, gp.replay)
+    t_packed = time_events(torch, gp.replay, passes)
+    del gp, packed
     nbytes = 36 * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for _, n, k in LAYER_SHAPES)
     flops = 36 * sum(2 * m * n * k for _, n, k in LAYER_SHAPES)
     del layers, xs, ys
@@ -490,7 +516,13 @@ def bench_stack(torch, fq, m, passes):
             "tflops": round(flops / t / 1e12, 2),
             "frac_of_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4),
             "us_per_layer": round(t * 1e6 / 36, 2),
-            "eager_ms_per_pass": round(t_eager * 1e3, 4)}
+            "eager_ms_per_pass": round(t_eager * 1e3, 4),
+            "packed": {"ms_per_pass": round(t_packed * 1e3, 4),
+                       "gbs": round(nbytes / t_packed / 1e9, 1),
+                       "frac_of_hbm": round(nbytes / t_packed / 1e9 / HBM_PEAK_GBS, 4),
+                       "us_per_layer": round(t_packed * 1e6 / 36, 2),
+                       "what": "q|k|v and gate|up packed, each distinct input quantized "
+                               "once: 2 quantizations + 4 matmuls per layer"}}
 
 
 def graph_of(torch, fn, calls):

@@ -11,6 +11,8 @@
 // with round-to-nearest-even by v_cvt_pk_fp8_f32; codes leave as 8-byte
 // stores that are contiguous across the wave.  HBM traffic is the algorithmic
 // 2 bytes in + 1 byte out per element + 4 bytes of scale per row.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -47,6 +49,52 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     buf_store8(c, dst, (i * 64 + lane) * 8u);
   });
   if (lane == 0) scale[row] = s;
+}
+
+// Few rows (a decode or mid-size chunk of tokens): one wave per row gives
+// too few waves to keep the memory system busy, so S waves share a row
+// (a 4-wave workgroup holds 4 / S rows).  Wave w of a row holds the
+// 16-byte vectors i * 64 S + 64 w + lane, i < NV; the waves' maxima meet in
+// LDS; each element is then quantized with the same device functions as
+// above, so codes and scale are those of quant_rows_kernel.
+template <int NV, int S>
+__global__ __launch_bounds__(256) void quant_rows_split_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int k, int64_t ld,
+    uint8_t* __restrict__ q, float* __restrict__ scale) {
+  static_assert(S == 2 || S == 4, "2 or 4 waves per row");
+  __shared__ uint32_t wmax[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave % S;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (4 / S) + wave / S;
+  const bool live = row < rows;
+  const int64_t r = live ? row : 0;
+  const auto src = row_rsrc(x + r * ld, live ? static_cast<uint32_t>(k) * 2u : 0u);
+  uint4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    v[i] = buf_load16_stream(src, ((i * S + part) * 64 + lane) * 16u);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    m = pk_max_u16(m, bf16x2_abs_bits(v[i].x));
+    m = pk_max_u16(m, bf16x2_abs_bits(v[i].y));
+    m = pk_max_u16(m, bf16x2_abs_bits(v[i].z));
+    m = pk_max_u16(m, bf16x2_abs_bits(v[i].w));
+  }
+  const uint32_t mw = wave_max_u32(max(m & 0xffffu, m >> 16));
+  if (lane == 0) wmax[wave] = mw;
+  __syncthreads();
+  uint32_t mrow = 0;
+#pragma unroll
+  for (int j = 0; j < S; ++j) mrow = max(mrow, wmax[wave - part + j]);
+  if (!live) return;
+  const float s = row_scale(__uint_as_float(mrow << 16));
+  const auto dst = row_rsrc(q + r * static_cast<int64_t>(k), static_cast<uint32_t>(k));
+  quantize_row<NV>(v, make_divisor(s), [&](int i, uint2 c) {
+    buf_store8(c, dst, ((i * S + part) * 64 + lane) * 8u);
+  });
+  if (lane == 0 && part == 0) scale[r] = s;
 }
 
 // Rows longer than the register-resident variants: two passes, the second
@@ -92,6 +140,27 @@ hipError_t launch_nv(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
   return hipGetLastError();
 }
 
+template <int NV, int S>
+hipError_t launch_split(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
+                        uint8_t* q, float* scale, hipStream_t stream) {
+  const int64_t blocks = (rows + (4 / S) - 1) / (4 / S);
+  quant_rows_split_kernel<NV, S><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                                   stream>>>(x, rows, static_cast<int>(k), ld, q, scale);
+  return hipGetLastError();
+}
+
+// Waves per row for few rows.  With the test hooks on,
+// FP8W8A8_QUANT_SPLIT=1|2|4 overrides (tuning and tests).
+int quant_split(int64_t rows, int64_t per_lane) {
+  int sp = rows < 512 ? 4 : rows < 2048 ? 2 : 1;
+  if (const char* e = test_hook("FP8W8A8_QUANT_SPLIT")) {
+    const int v = std::atoi(e);
+    if (v == 1 || v == 2 || v == 4) sp = v;
+  }
+  if (per_lane < 2) sp = 1;
+  return sp;
+}
+
 }  // namespace detail
 using namespace detail;
 
@@ -101,6 +170,21 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t k,
   if (rows == 0) return hipSuccess;
   const int64_t nvec = k / 8;
   const int64_t per_lane = (nvec + 63) / 64;
+  const int sp = per_lane <= 24 ? quant_split(rows, per_lane) : 1;
+  if (sp > 1) {
+    const int64_t pl = (per_lane + sp - 1) / sp;   // vectors per lane
+#define FP8W8A8_SPLIT(S)                                                  \
+    if (pl <= 1) return launch_split<1, S>(x, rows, k, ld, q, scale, stream); \
+    if (pl <= 2) return launch_split<2, S>(x, rows, k, ld, q, scale, stream); \
+    if (pl <= 3) return launch_split<3, S>(x, rows, k, ld, q, scale, stream); \
+    if (pl <= 4) return launch_split<4, S>(x, rows, k, ld, q, scale, stream); \
+    if (pl <= 6) return launch_split<6, S>(x, rows, k, ld, q, scale, stream); \
+    if (pl <= 8) return launch_split<8, S>(x, rows, k, ld, q, scale, stream); \
+    return launch_split<12, S>(x, rows, k, ld, q, scale, stream);
+    if (sp == 2) { FP8W8A8_SPLIT(2) }
+    FP8W8A8_SPLIT(4)
+#undef FP8W8A8_SPLIT
+  }
   if (per_lane <= 1) return launch_nv<1>(x, rows, k, ld, q, scale, stream);
   if (per_lane <= 2) return launch_nv<2>(x, rows, k, ld, q, scale, stream);
   if (per_lane <= 4) return launch_nv<4>(x, rows, k, ld, q, scale, stream);

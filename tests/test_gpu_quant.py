@@ -146,3 +146,22 @@ def test_deterministic():
     a = _gpu_quant(x)
     b = _gpu_quant(x)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("split", ["1", "2", "4"])
+@pytest.mark.parametrize("m,k,ld", [(1, 8, 8), (3, 520, 528), (7, 4104, 4104),
+                                    (64, 4096, 4096), (5, 12288, 12296), (33, 1032, 1040),
+                                    (130, 16392, 16400)])
+def test_rows_split_over_waves(split, m, k, ld, monkeypatch):
+    """Rows shared by 2 or 4 waves (the few-row variant): the waves' maxima
+    meet in LDS, each wave quantizes its interleaved vectors; codes and
+    scales bit-exact against the oracle for ragged and strided rows, a zero
+    row and rows of very different magnitudes."""
+    monkeypatch.setenv("FP8W8A8_QUANT_SPLIT", split)
+    rng = np.random.default_rng(m * 13 + k)
+    full = bf16_from_f64(rng.standard_normal((m, ld)) * 10.0 ** rng.uniform(-30, 30, (m, 1)))
+    full[m // 2, :] = 0
+    x = to_dev_bf16(full)[:, :k]
+    q, s = fq.quantize_act_per_token(x)
+    torch.cuda.synchronize()
+    _check_rows(full[:, :k], host_bits(q), host_bits(s), what=f"split {split} {m}x{k}")
