@@ -70,7 +70,11 @@ struct GemmShape {
   // Epilogue staging: each wave's WM x WN bf16 tile, rows padded by 16 B.
   static constexpr int EPI_ROW = WN * 2 + 16;
   static constexpr int EPI = WAVES * WM * EPI_ROW;
-  static constexpr int SMEM = LDS > EPI ? LDS : EPI;
+  // The tile's token scales (1 KB) and channel scales (1 KB), copied into
+  // LDS at the start so that the epilogue does not wait on global loads.
+  static constexpr int SC_OFF = ((LDS > EPI ? LDS : EPI) + 15) / 16 * 16;
+  static constexpr int SMEM = SC_OFF + 2048;
+  static_assert(BM <= 256 && BN <= 256, "one 1 KB copy per scale vector");
   static_assert(SMEM <= 160 * 1024, "LDS budget of one CU");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 &&
                 A_LOADS * 1024 * WAVES == A_STAGE &&
@@ -187,6 +191,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   const int kt0 = static_cast<int>(blockIdx.y) * KT_all / static_cast<int>(gridDim.y);
   const int KT = (static_cast<int>(blockIdx.y) + 1) * KT_all / static_cast<int>(gridDim.y) - kt0;
   const uint32_t kbase = static_cast<uint32_t>(kt0 * kBK);
+  // Wave 0 copies the scales first (so the prologue's wait below, which
+  // leaves only later stages outstanding, covers them); rows past M or N
+  // read as 0.  The split-K partial sums need no scales.
+  if (part == nullptr && wave == 0) {
+    lds_copy16(make_rsrc(reinterpret_cast<const uint8_t*>(sx + m0),
+                         static_cast<uint32_t>(min(M - m0, BM)) * 4u),
+               static_cast<uint32_t>(lane) * 16u, 0u, lds0 + S::SC_OFF);
+    lds_copy16(make_rsrc(reinterpret_cast<const uint8_t*>(sw + n0),
+                         static_cast<uint32_t>(min(N - n0, BN)) * 4u),
+               static_cast<uint32_t>(lane) * 16u, 0u, lds0 + S::SC_OFF + 1024);
+  }
 #pragma unroll
   for (int st = 0; st < NB; ++st)
     if (st < KT) {
@@ -302,20 +317,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   }
   __syncthreads();  // every wave is done with the stage buffers
   uint8_t* ep = smem + wave * (S::WM * S::EPI_ROW);
+  const float* sc_tok = reinterpret_cast<const float*>(smem + S::SC_OFF) + wm * S::WM;
+  const float* sc_ch = reinterpret_cast<const float*>(smem + S::SC_OFF + 1024) + wn * S::WN;
   // Channel scales of this lane: 4 consecutive channels per (u, q).
   float4 ws[S::TN][4];
 #pragma unroll
   for (int u = 0; u < S::TN; ++u)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = ch0 + 32 * u + 8 * q + 4 * fhalf;
-      ws[u][q] = c < N ? *reinterpret_cast<const float4*>(sw + c)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int q = 0; q < 4; ++q)
+      ws[u][q] = *reinterpret_cast<const float4*>(sc_ch + 32 * u + 8 * q + 4 * fhalf);
 #pragma unroll
   for (int t = 0; t < S::TM; ++t) {
     const int tl = 32 * t + frow;                    // token inside the wave tile
-    const float xs = tok0 + tl < M ? sx[tok0 + tl] : 0.0f;
+    const float xs = sc_tok[tl];
 #pragma unroll
     for (int u = 0; u < S::TN; ++u) {
 #pragma unroll
