@@ -63,8 +63,11 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # as null once that code differs.
 KERNEL_TRAFFIC = {
     "gemm": {"files": ("gemm.hip", "device_common.h"),
-             "sha1": "cb7c6c10138bba7cfb20b5a932099fdbf2218fa8",
-             "bytes": 1493430 * 1024},
+             "sha1": "28705f3e3ef3fef8958126aa3f19fd23d8adecad",
+             "bytes": 1493435 * 1024},
+    "gemv_group": {"files": ("gemv.hip", "row_ops.h", "device_common.h"),
+                   "sha1": "3a03b37f980147340cfe1bf8c5ab1fecf7d3aabd",
+                   "bytes": (94860 * 2 + 101) * 1024},
     "rmsnorm_quant": {"files": ("norm.hip", "row_ops.h", "device_common.h"),
                       "sha1": "b705eec0b08b238db4b13d64c022f7e387fd5c51",
                       "bytes": (16492 * 2 + 16416) * 1024},
@@ -1114,6 +1117,15 @@ def main():
                                       "(rocprofv3 FETCH_SIZE x2 + WRITE_SIZE); "
                                       "algorithmic 663 MB",
                      "kernel": "gemm_fp8_kernel",
+                     "mfma_busy": {
+                         "counted_equals_algorithmic":
+                             True if code_sha1(KERNEL_TRAFFIC["gemm"]["files"])
+                             == KERNEL_TRAFFIC["gemm"]["sha1"] else None,
+                         "frac_of_gemm_time_at_2p4ghz": round(
+                             pre["gemm_tflops"] * 1e12 * 64 / (131072 * 1024) / 2.4e9, 4),
+                         "source": "profiles/gemm_fp8_kernel_mfma_busy_lds_conflicts_"
+                                   "prefill_layer.txt (SQ_VALU_MFMA_BUSY_CYCLES / 1024 "
+                                   "SIMDs = the algorithmic 64 cycles per MFMA)"},
                      "library_same_operands_tflops": pre.get("lib_tflops"),
                      "library": "hipBLASLt via torch._scaled_mm, row-wise scales (comparison only)",
                      "per_linear": pre["per_linear"]},
@@ -1131,7 +1143,12 @@ def main():
                              dec["single_launch"] or {},
                              what="the same 7 Linears of the layer (independent inputs) "
                                   "as ONE grouped call, fp8w8a8_quant_linear_group_m1 "
-                                  "(outputs bit-identical to the 7 calls)"),
+                                  "(outputs bit-identical to the 7 calls)",
+                             kernel="gemv_group_kernel",
+                             traffic=kernel_traffic("gemv_group"),
+                             traffic_scope="HBM bytes of one launch (one layer; rocprofv3 "
+                                           "FETCH_SIZE x2 + WRITE_SIZE); algorithmic "
+                                           "193,245,184"),
                          "launch_floor": dec_floor,
                          "other_token_counts": {
                              f"m{mm}": {"value": round(v["gbs"], 1), "unit": "GB/s",
