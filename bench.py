@@ -991,6 +991,9 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 36-layer stack leg")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured MFMA / HBM-read peaks")
+    ap.add_argument("--only-stack", action="store_true",
+                    help="run only the 36-layer stack leg (M = 64 and 256) and print "
+                         "its figures (for profiling that leg on its own)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy "
                          "(reference for the HBM byte counters)")
@@ -1006,6 +1009,10 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.only_stack:
+        passes = [bench_stack(torch, fq, m, max(3, args.steps // 20)) for m in (64, 256)]
+        print(json.dumps({"stack_36_layers": {"passes": passes}}), flush=True)
+        return 0
     if args.calibrate_copy:
         # A plain elementwise kernel of known traffic: reads 256 MiB, writes
         # 256 MiB (torch's vectorized add on uint8).
