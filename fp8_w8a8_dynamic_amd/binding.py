@@ -52,6 +52,10 @@ SIGNATURES = {
                         _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_quant_linear_group_m1":
         (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp]),
+    "fp8w8a8_tile_weights":
+        (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "fp8w8a8_fp8_linear_group":
+        (ctypes.c_int, [_c_vp, ctypes.c_int, _c_i64, _c_vp]),
     "fp8w8a8_rmsnorm_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_i64,
                         _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -524,6 +528,72 @@ def quant_linear_group_m1(xs, qws, w_scales, outs=None):
         return ys
     _check(lib.fp8w8a8_quant_linear_group_m1(items, count, _stream_ptr(xs[0].device)),
            "quant_linear_group_m1")
+    return ys
+
+
+def tile_weights(qw, out=None):
+    """E4M3 weight codes [N, K] (row-major, as quantized) -> the same bytes
+    in MFMA-tile order (uint8, N * K), the weight layout of
+    fp8_linear_group."""
+    lib = load_library()
+    qw = _as_codes(qw)
+    n, k, ldw = _rows(qw, "qw")
+    if ldw != k:
+        raise ValueError("qw must be contiguous [N, K]")
+    if out is None:
+        out = torch.empty((n * k,), dtype=torch.uint8, device=qw.device)
+    elif (out.dtype != torch.uint8 or out.numel() != n * k or not out.is_contiguous()
+          or out.device != qw.device):
+        raise ValueError(f"out must be a contiguous uint8 tensor of {n * k} bytes on {qw.device}")
+    _check(lib.fp8w8a8_tile_weights(qw.data_ptr(), n, k, out.data_ptr(),
+                                    _stream_ptr(qw.device)), "tile_weights")
+    return out
+
+
+class _GroupFp8Linear(ctypes.Structure):
+    """Mirror of fp8w8a8_group_fp8_linear."""
+    _fields_ = [("qx", _c_vp), ("x_scale", _c_vp), ("qw_tiled", _c_vp), ("w_scale", _c_vp),
+                ("y", _c_vp), ("n", _c_i64), ("k", _c_i64)]
+
+
+def fp8_linear_group(qxs, x_scales, qws_tiled, w_scales, ns, outs=None):
+    """Several Linears on given codes at one token count M (1..64) in one
+    launch: outs[i] bf16 [M, ns[i]] = fp8_linear(qxs[i], x_scales[i], W_i,
+    w_scales[i]) up to float32 summation order, with qws_tiled[i] =
+    tile_weights(W_i).  Items may share qx and x_scale (pass the same
+    tensors)."""
+    lib = load_library()
+    count = len(qxs)
+    if (not (len(x_scales) == len(qws_tiled) == len(w_scales) == len(ns) == count)
+            or (outs is not None and len(outs) != count)):
+        raise ValueError("one x_scale, tiled qw, w_scale, n (and out) per qx")
+    items = (_GroupFp8Linear * max(count, 1))()
+    ys, m0 = [], None
+    for i, (qx, sx, qt, sw, n) in enumerate(zip(qxs, x_scales, qws_tiled, w_scales, ns)):
+        qx = _as_codes(qx)
+        m, k, ldq = _rows(qx, "qx")
+        if ldq != k:
+            raise ValueError("each qx must be contiguous [M, K]")
+        if m0 is None:
+            m0 = m
+        elif m != m0 or qx.device != qxs[0].device:
+            raise ValueError("every qx must have the same M, on one device")
+        if (qt.dtype != torch.uint8 or qt.numel() != n * k or not qt.is_contiguous()
+                or qt.device != qx.device):
+            raise ValueError(f"tiled weights must be contiguous uint8, {n} x {k} bytes, "
+                             "on the codes' device")
+        sx = _scales(sx, m, qx.device, "x_scale")
+        sw = _scales(sw, n, qx.device, "w_scale")
+        y = _out(m, n, qx.device, None if outs is None else outs[i])
+        if not y.is_contiguous():
+            raise ValueError("each out must be contiguous")
+        items[i] = _GroupFp8Linear(qx.data_ptr(), sx.data_ptr(), qt.data_ptr(),
+                                   sw.data_ptr(), y.data_ptr(), n, k)
+        ys.append(y)
+    if count == 0:
+        return ys
+    _check(lib.fp8w8a8_fp8_linear_group(items, count, m0, _stream_ptr(qxs[0].device)),
+           "fp8_linear_group")
     return ys
 
 

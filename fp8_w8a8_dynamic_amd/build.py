@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "quant.hip", "norm.hip", "swiglu.hip", "kvcache.hip",
-           "gemm.hip", "gemv.hip"]
+           "gemm.hip", "gemv.hip", "tokgroup.hip"]
 
 # The benchmark's measured-peak kernels, a library of their own.
 PEAKS_SOURCES = ["peaks.hip"]

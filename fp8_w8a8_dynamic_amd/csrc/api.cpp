@@ -623,6 +623,56 @@ int fp8w8a8_quant_linear_group_m1(const fp8w8a8_group_linear* items, int count,
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
+int fp8w8a8_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* tiled,
+                         void* stream) {
+  if (!qw || !tiled) return FP8W8A8_ERR_NULL;
+  if (n < 0 || n > kMaxDim || n % 16 != 0 || k < 128 || k > fp8w8a8::kTokGroupMaxK ||
+      k % 128 != 0)
+    return FP8W8A8_ERR_SHAPE;
+  if (!aligned16(qw) || !aligned16(tiled)) return FP8W8A8_ERR_ALIGN;
+  if (overlap(span(qw, n, k, k, 1), span(tiled, n, k, k, 1))) return FP8W8A8_ERR_ALIAS;
+  if (n == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_tile_weights(qw, n, k, tiled, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_fp8_linear_group(const fp8w8a8_group_fp8_linear* items, int count,
+                             int64_t m, void* stream) {
+  if (!items) return FP8W8A8_ERR_NULL;
+  if (count < 1 || count > fp8w8a8::kGroupMax || m < 1 || m > fp8w8a8::kTokGroupMaxM)
+    return FP8W8A8_ERR_SHAPE;
+  fp8w8a8::TokLinear g[fp8w8a8::kGroupMax];
+  for (int i = 0; i < count; ++i) {
+    const fp8w8a8_group_fp8_linear& L = items[i];
+    if (!L.qx || !L.x_scale || !L.qw_tiled || !L.w_scale || !L.y) return FP8W8A8_ERR_NULL;
+    if (L.n < 64 || L.n > (int64_t{1} << 24) || L.n % 64 != 0 || L.k < 128 ||
+        L.k > fp8w8a8::kTokGroupMaxK || L.k % 128 != 0)
+      return FP8W8A8_ERR_SHAPE;
+    if (!aligned16(L.qx) || !aligned16(L.x_scale) || !aligned16(L.qw_tiled) ||
+        !aligned16(L.w_scale) || !aligned16(L.y))
+      return FP8W8A8_ERR_ALIGN;
+    g[i] = fp8w8a8::TokLinear{L.qx, L.x_scale, L.qw_tiled, L.w_scale, L.y, L.n, L.k};
+  }
+  for (int i = 0; i < count; ++i) {
+    const Range ry = span(items[i].y, m, items[i].n, items[i].n, 2);
+    for (int j = 0; j < count; ++j) {
+      const fp8w8a8_group_fp8_linear& L = items[j];
+      if (overlap(ry, span(L.qx, m, L.k, L.k, 1)) ||
+          overlap(ry, span(L.x_scale, m, 1, 1, 4)) ||
+          overlap(ry, span(L.qw_tiled, L.n, L.k, L.k, 1)) ||
+          overlap(ry, span(L.w_scale, L.n, 1, 1, 4)) ||
+          (j != i && overlap(ry, span(L.y, m, L.n, L.n, 2))))
+        return FP8W8A8_ERR_ALIAS;
+    }
+  }
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_tok_group(g, count, m, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 int fp8w8a8_quant_linear_noalloc(const uint16_t* x, int64_t ldx,
                                  const uint8_t* qw, const float* w_scale,
                                  int64_t m, int64_t n, int64_t k, uint16_t* y,

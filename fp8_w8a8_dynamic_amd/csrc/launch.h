@@ -117,6 +117,27 @@ struct GroupLinear {
 hipError_t launch_gemv_group_m1(const GroupLinear* items, int count,
                                 hipStream_t stream);
 
+// Grouped Linears on given codes (qx [m, k] E4M3 + sx [m] -> bf16 y [m, n]
+// each, all items at the same m), 1 <= m <= kTokGroupMaxM, up to kGroupMax
+// of them in one launch; qw in the MFMA-tile order of launch_tile_weights.
+// n % 64 == 0, k % 128 == 0, k <= kTokGroupMaxK.
+constexpr int kTokGroupMaxM = 64;
+constexpr int kTokGroupMaxK = 16384;
+struct TokLinear {
+  const uint8_t* qx;
+  const float* sx;
+  const uint8_t* qw;
+  const float* sw;
+  uint16_t* y;
+  int64_t n, k;
+};
+hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
+                            hipStream_t stream);
+// The MFMA-tile permutation of a row-major [n, k] E4M3 matrix (n % 16 == 0,
+// k % 128 == 0) into out (n * k bytes).
+hipError_t launch_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* out,
+                               hipStream_t stream);
+
 // Token-group GEMV, kGemvMaxM < m <= kGemvTokMaxM, on quantized activations.
 constexpr int kGemvTokMaxM = 64;
 hipError_t launch_gemv_tok(const uint8_t* qx, const float* sx,

@@ -1,0 +1,409 @@
+// Grouped FP8_DYNAMIC Linears on given codes for a few tokens (1 <= M <= 64),
+// up to kGroupMax of them in one persistent launch: per-token E4M3 codes and
+// scales times channel-wise E4M3 weights, float32 accumulation, bf16 output
+// through the token-scale x channel-scale epilogue (MOSS-VL quantization
+// README, "FP8-Dynamic").  At these token counts every Linear is bound by
+// its weight bytes (MOSS-VL-Realtime-FP8 article, on why the model is
+// quantized), and a run of small launches pays a ramp-up and a tail per
+// launch; Linears that read the same activations can share one code buffer
+// and go out as one stream.
+//
+// Weights in MFMA tiles.  Offline, next to the quantization, a Linear's
+// [N, K] codes are permuted (tile_weights_kernel) so that each MFMA item --
+// 16 weight rows x 128 K bytes -- is one contiguous 2 KB tile laid out in
+// the order the lanes take it: tile byte h * 1024 + 16 l + e holds row
+// 16 rb + (l & 15), K byte 128 i + 64 h + 16 (l >> 4) + e of item i of row
+// block rb, and the tiles of a row block follow each other in K order.  A
+// wave then fetches an item with two fully contiguous 1 KB loads, and four
+// items (a stage) are 8 KB of consecutive memory.  (Row-major rows fetched
+// 64 bytes at a time from 16 rows per load instruction measured ~25 %
+// slower for the same bytes.)
+//
+// Work decomposition.  A work unit is 64 consecutive weight rows (four row
+// blocks) of one item over the item's whole K; each of the four waves of a
+// workgroup owns one row block.  K is walked in stages of 512 bytes (four
+// MFMA items).  A stage's weights are requested into registers D stages
+// ahead (a ring of D + 1 slots); its codes (16 T token rows x 512 bytes,
+// T = ceil(M / 16), each thread a 16-byte share) one stage ahead, into
+// registers, and written to LDS one step before their use, where the four
+// waves read them.  A weight fragment feeds T MFMAs, one per block of 16
+// tokens, so the codes cross L2 once per 64 weight rows.  A workgroup walks
+// its units (blockIdx.x, + gridDim.x, ...) as one stream of stages: the next
+// unit's first stages are in flight while the current unit finishes.  No
+// workgroup waits on another and no partial sums leave the wave: each
+// output is one lane's accumulator, items in K order.
+//
+// MFMA layout (v_mfma_f32_16x16x128_f8f6f4): lane (r, g) = (l & 15, l >> 4)
+// holds, of each 128-byte item, bytes 16 g .. 16 g + 15 and 64 + 16 g .. +15
+// of weight row r (A) and of token r of the block (B), the same K order on
+// both operands; accumulator entry q of lane l is (weight row 4 g + q, token
+// r).  LDS rows are 512 bytes per token with the 16-byte chunks XOR-swizzled
+// by the token's low four bits, so the 16 lanes of one chunk column read 16
+// distinct bank groups.
+//
+// Out-of-range bytes read as 0 through buffer descriptors: tokens past M
+// (the codes' descriptor covers M * K bytes), the K tail of a last stage
+// (offsets moved past the descriptor), outputs of tokens past M (dropped by
+// the output's descriptor, M * N values).
+#include <algorithm>
+#include <cstdlib>
+#include <utility>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8w8a8 {
+
+namespace tokgroup {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kItemsPerStage = 4;
+constexpr int kStageBytes = kItemsPerStage * 128;
+constexpr uint32_t kPastEnd = 0x80000000u;  // an offset past every descriptor
+constexpr int kDepth = 2;                   // stages of weights requested ahead
+
+struct Item {
+  const uint8_t* qx;
+  const float* sx;
+  const uint8_t* qw;  // tiled
+  const float* sw;
+  uint16_t* y;
+  int n, k;
+  int u0;  // first work unit of the item
+};
+struct Args {
+  Item it[kGroupMax];
+  int count;
+  int units;
+  int m;
+};
+
+__device__ __forceinline__ v8i to_v8i(uint4 lo, uint4 hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wave-uniform position in a workgroup's stream of stages.
+struct Cursor {
+  int unit, stage, item, stages;
+};
+
+__device__ __forceinline__ void cursor_at(Cursor& c, const Args& a, int unit) {
+  c.unit = unit;
+  c.stage = 0;
+  c.item = 0;
+  for (int j = 1; j < a.count; ++j)
+    if (unit >= a.it[j].u0) c.item = j;
+  c.stages = (a.it[c.item].k + kStageBytes - 1) / kStageBytes;
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const Args& a) {
+  if (++c.stage == c.stages) cursor_at(c, a, c.unit + static_cast<int>(gridDim.x));
+}
+
+// The epilogue's scales for a unit: sw of rows 4 g .. 4 g + 3 of the wave's
+// row block, sx of token r of each token block.
+template <int T>
+struct Scales {
+  float4 w;
+  float x[T];
+};
+
+// A stage's weight fragments in one wave's registers.
+struct Weights {
+  uint4 w[kItemsPerStage][2];
+};
+// This thread's share of a stage's codes (LDS slots j * 256 + tid).
+template <int T>
+struct Codes {
+  uint4 x[2 * T];
+};
+
+// Requests for stage c.  When `live` is false the same instructions go out
+// with offsets past the descriptors' ends (nothing is read), so the
+// instruction stream -- and with it every wait count -- is the same on
+// every path.
+template <int T>
+__device__ __forceinline__ void load_codes(Codes<T>& xc, const Args& a, const Cursor& c,
+                                           bool live, int M, int tid) {
+  const Item& it = a.it[c.item];
+  const int K = it.k;
+  const int k0 = c.stage * kStageBytes;
+  const auto xr = row_rsrc(it.qx, static_cast<uint32_t>(M * K));
+#pragma unroll
+  for (int j = 0; j < 2 * T; ++j) {
+    // LDS slot p (16 bytes) = token p / 32, chunk (p % 32) ^ (token % 16).
+    const int p = j * 256 + tid;
+    const int tok = p >> 5;
+    const int ch = (p & 31) ^ (tok & 15);
+    const bool ok = live && k0 + (ch >> 3) * 128 < K;
+    xc.x[j] = buf_load16(xr, ok ? static_cast<uint32_t>(tok * K + k0 + ch * 16) : kPastEnd);
+  }
+}
+
+__device__ __forceinline__ void load_weights(Weights& s, const Args& a, const Cursor& c,
+                                             bool live, int wave, int lane) {
+  const Item& it = a.it[c.item];
+  const int K = it.k;
+  const int k0 = c.stage * kStageBytes;
+  // The wave's row block: K / 128 consecutive 2 KB tiles.
+  const int rb = (c.unit - it.u0) * 4 + wave;
+  const auto wr = row_rsrc(it.qw + static_cast<int64_t>(rb) * 16 * K,
+                           static_cast<uint32_t>(16 * K));
+#pragma unroll
+  for (int i = 0; i < kItemsPerStage; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = live && k0 + i * 128 < K;
+      s.w[i][h] = buf_load16_stream(
+          wr, ok ? static_cast<uint32_t>((k0 / 128 + i) * 2048 + h * 1024 + lane * 16)
+                 : kPastEnd);
+    }
+}
+
+template <int T>
+__device__ __forceinline__ void load_scales(Scales<T>& sc, const Args& a, const Cursor& c,
+                                            int M, int wave, int lane) {
+  const Item& it = a.it[c.item];
+  const int r = lane & 15, g = lane >> 4;
+  sc.w = *reinterpret_cast<const float4*>(it.sw + (c.unit - it.u0) * 64 + wave * 16 + 4 * g);
+#pragma unroll
+  for (int t = 0; t < T; ++t) sc.x[t] = it.sx[min(16 * t + r, M - 1)];
+}
+
+template <int T>
+__device__ __forceinline__ void store_codes(const Codes<T>& xc, uint8_t* xs, int tid) {
+#pragma unroll
+  for (int j = 0; j < 2 * T; ++j)
+    *reinterpret_cast<uint4*>(xs + (j * 256 + tid) * 16) = xc.x[j];
+}
+
+template <int T>
+__device__ __forceinline__ void compute_stage(v4f (&acc)[T], const Weights& s,
+                                              const uint8_t* xs, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < kItemsPerStage; ++i) {
+    const v8i a = to_v8i(s.w[i][0], s.w[i][1]);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint8_t* row = xs + (16 * t + r) * kStageBytes;
+      const uint4 lo = *reinterpret_cast<const uint4*>(row + (((i * 8 + g) ^ r) * 16));
+      const uint4 hi = *reinterpret_cast<const uint4*>(row + (((i * 8 + 4 + g) ^ r) * 16));
+      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          a, to_v8i(lo, hi), acc[t], 0, 0, 0, 0, 0, 0);
+    }
+    // One item's fragments at a time (hoisting every LDS read of the stage
+    // would hold 4 x 8 T registers).
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
+                                         const Args& a, const Cursor& c, int M,
+                                         int wave, int lane) {
+  const Item& it = a.it[c.item];
+  const int N = it.n;
+  const int r = lane & 15, g = lane >> 4;
+  const int n = (c.unit - it.u0) * 64 + wave * 16 + 4 * g;
+  const auto yr = row_rsrc(it.y, static_cast<uint32_t>(M * N) * 2u);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const v4f v = acc[t];
+    const float xs = sc.x[t];
+    uint2 pk;
+    pk.x = pack_bf16x2(v[0] * sc.w.x * xs, v[1] * sc.w.y * xs);
+    pk.y = pack_bf16x2(v[2] * sc.w.z * xs, v[3] * sc.w.w * xs);
+    buf_store8(pk, yr, static_cast<uint32_t>(((16 * t + r) * N + n) * 2));
+    acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+
+// Step I of the stream (I counts modulo lcm(D + 1, 2)), computing stage C.
+// Vector-memory requests complete in order, so the issue order carries the
+// pipeline: the codes of stage C + 1 go out first, then the weights of
+// stage C + D (ring slot (I + D) % (D + 1)).  Stage C is computed from
+// weight slot I % (D + 1) and LDS buffer I % 2; then the codes of C + 1 are
+// written to LDS buffer (I + 1) % 2 (nobody reads it since the previous
+// step's barrier) -- the wait for them also completes the weights
+// requested before them, up to stage C + D - 1, and leaves C + D's in
+// flight.  Every request is one the compiler tracks, so the waits it places
+// are exact.  Returns false once C was the workgroup's last stage.
+template <int I, int T, int D>
+__device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T>& X,
+                                     uint8_t (*xs)[16 * T * kStageBytes], Cursor (&Q)[D + 1],
+                                     const Args& a, int M, int wave, int tid) {
+  // Q[0] = C, Q[j] = C + j (a unit past the end once the units run out).
+  const int lane = tid & 63;
+  const bool more1 = Q[1].unit < a.units, moreD = Q[D].unit < a.units;
+  const bool last = Q[0].stage == Q[0].stages - 1;
+  // The epilogue's scales first: waiting for them completes nothing issued
+  // after them.
+  Scales<T> sc;
+  if (last) load_scales(sc, a, Q[0], M, wave, lane);
+  load_codes(X, a, more1 ? Q[1] : Q[0], more1, M, tid);
+  load_weights(S[(I + D) % (D + 1)], a, moreD ? Q[D] : Q[0], moreD, wave, lane);
+  // Keep the requests ahead of the MFMAs (the scheduler would otherwise
+  // sink them below).
+  __builtin_amdgcn_sched_barrier(0);
+  compute_stage(acc, S[I % (D + 1)], xs[I % 2], lane);
+  if (last) epilogue(acc, sc, a, Q[0], M, wave, lane);
+  if (!more1) return false;
+  store_codes(X, xs[(I + 1) % 2], tid);
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < D; ++j) Q[j] = Q[j + 1];
+  if (moreD) cursor_next(Q[D], a);
+  return true;
+}
+
+template <int T, int D, int... Is>
+__device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&acc)[T],
+                                      Weights (&S)[D + 1], Codes<T>& X,
+                                      uint8_t (*xs)[16 * T * kStageBytes],
+                                      Cursor (&Q)[D + 1], const Args& a, int M, int wave,
+                                      int tid) {
+  return (step<Is, T, D>(acc, S, X, xs, Q, a, M, wave, tid) && ...);
+}
+
+template <int T, int D>
+__global__ __launch_bounds__(256, 2) void tok_group_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * kStageBytes];
+  const int tid = static_cast<int>(threadIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int M = a.m;
+  if (static_cast<int>(blockIdx.x) >= a.units) return;
+  // Q[0]: the stage computed; Q[1..D]: the next D (a unit past the end once
+  // the workgroup's units run out).
+  Cursor Q[D + 1];
+  cursor_at(Q[0], a, static_cast<int>(blockIdx.x));
+#pragma unroll
+  for (int j = 1; j <= D; ++j) {
+    Q[j] = Q[j - 1];
+    if (Q[j].unit < a.units) cursor_next(Q[j], a);
+  }
+  Weights S[D + 1];
+  Codes<T> X;
+  v4f acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // Codes of stage 0 (into LDS buffer 0) and weights of stages 0 .. D - 1
+  // in flight.
+  load_codes(X, a, Q[0], true, M, tid);
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const bool live = Q[j].unit < a.units;
+    load_weights(S[j], a, live ? Q[j] : Q[0], live, wave, lane);
+  }
+  store_codes(X, xs[0], tid);
+  lds_barrier();
+  constexpr int kPeriod = (D + 1) % 2 == 0 ? D + 1 : 2 * (D + 1);
+  while (steps<T, D>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, Q, a, M,
+                     wave, tid)) {
+  }
+  // Nothing in flight when the workgroup leaves (the last requests read
+  // nothing, but their registers go with the workgroup).
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+template <int T, int D>
+hipError_t launch_d(const Args& a, hipStream_t stream) {
+  // Two workgroups per CU (LDS: 16 KB per token block; registers: two
+  // waves per SIMD), 256 CUs.
+  int64_t grid = std::min<int64_t>(a.units, 2 * 256);
+  if (const char* e = test_hook("FP8W8A8_TOKG_GRID")) {
+    const int64_t v = std::atoll(e);
+    if (v >= 1) grid = std::min<int64_t>(a.units, v);
+  }
+  tok_group_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int T>
+hipError_t launch_t(const Args& a, hipStream_t stream) {
+  const char* e = test_hook("FP8W8A8_TOKG_DEPTH");
+  const int d = e ? std::atoi(e) : kDepth;
+  return d == 3 ? launch_d<T, 3>(a, stream) : launch_d<T, 2>(a, stream);
+}
+
+// The MFMA-tile permutation of a row-major [n, k] code matrix: one thread
+// per 16 bytes of the output (tile byte h * 1024 + 16 l of tile (rb, i)
+// takes row 16 rb + (l & 15), bytes 128 i + 64 h + 16 (l >> 4) .. + 15).
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t* __restrict__ qw,
+                                                           int64_t chunks, int k,
+                                                           uint8_t* __restrict__ out) {
+  const int ki = k / 128;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+       c += stride) {
+    const int l = static_cast<int>(c & 63);
+    const int h = static_cast<int>((c >> 6) & 1);
+    const int64_t tile = c >> 7;
+    const int64_t rb = tile / ki;
+    const int i = static_cast<int>(tile - rb * ki);
+    const int64_t row = rb * 16 + (l & 15);
+    const int64_t src = row * k + i * 128 + h * 64 + (l >> 4) * 16;
+    *reinterpret_cast<uint4*>(out + c * 16) = *reinterpret_cast<const uint4*>(qw + src);
+  }
+}
+
+}  // namespace tokgroup
+
+hipError_t launch_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* out,
+                               hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  if (n % 16 != 0 || k % 128 != 0) return hipErrorInvalidValue;
+  const int64_t chunks = n * k / 16;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  tokgroup::tile_weights_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                                  stream>>>(qw, chunks, static_cast<int>(k), out);
+  return hipGetLastError();
+}
+
+hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
+                            hipStream_t stream) {
+  using namespace tokgroup;
+  if (count < 1 || count > kGroupMax || m < 1 || m > kTokGroupMaxM)
+    return hipErrorInvalidValue;
+  for (int i = 0; i < count; ++i)
+    if (items[i].n % 64 != 0 || items[i].k % 128 != 0 || items[i].k > kTokGroupMaxK)
+      return hipErrorInvalidValue;
+  // Longest rows first, so that the workgroups' strided unit lists even out.
+  int order[kGroupMax];
+  for (int i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order, order + count,
+                   [&](int p, int q) { return items[p].k > items[q].k; });
+  Args a{};
+  a.count = count;
+  a.m = static_cast<int>(m);
+  int64_t units = 0;
+  for (int i = 0; i < count; ++i) {
+    const TokLinear& L = items[order[i]];
+    a.it[i] = Item{L.qx, L.sx, L.qw, L.sw, L.y, static_cast<int>(L.n),
+                   static_cast<int>(L.k), static_cast<int>(units)};
+    units += L.n / 64;
+  }
+  if (units <= 0 || units > (int64_t{1} << 30)) return hipErrorInvalidValue;
+  a.units = static_cast<int>(units);
+  switch ((m + 15) / 16) {
+    case 1: return launch_t<1>(a, stream);
+    case 2: return launch_t<2>(a, stream);
+    case 3: return launch_t<3>(a, stream);
+    default: return launch_t<4>(a, stream);
+  }
+}
+
+}  // namespace fp8w8a8

@@ -312,6 +312,62 @@ int fp8w8a8_quant_linear_group_m1(const fp8w8a8_group_linear* items, int count,
                                   void* stream);
 
 /*
+ * E4M3 weight codes in MFMA-tile order, the weight layout of
+ * fp8w8a8_fp8_linear_group.  An offline step next to the channel-wise
+ * quantization (README "FP8-Dynamic": the weights are quantized once,
+ * statically); a pure byte permutation, its codes and scales unchanged.
+ *   qw      E4M3 [n, k], contiguous (row-major, as quantized)     (input)
+ *   tiled   n * k bytes                                          (output)
+ * Layout: for row block rb (16 rows), K block i (128 bytes), h in {0, 1},
+ * l in [0, 64), e in [0, 16):
+ *   tiled[(rb * (k / 128) + i) * 2048 + h * 1024 + 16 * l + e]
+ *     = qw[16 * rb + (l % 16), 128 * i + 64 * h + 16 * (l / 16) + e]
+ * i.e. each 16 x 128-byte block is one contiguous 2 KB tile, and the tiles
+ * of a row block follow each other in K order.
+ * Rules: n >= 0, n % 16 == 0; 128 <= k <= 16384, k % 128 == 0; both pointers
+ * 16-byte aligned; the two ranges must not overlap.
+ */
+int fp8w8a8_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* tiled,
+                         void* stream);
+
+/*
+ * Several Linears on already-quantized operands at a few tokens, in one
+ * launch: count independent fp8w8a8_fp8_linear calls (README "FP8-Dynamic":
+ * per-token dynamic E4M3 activations, channel-wise E4M3 weights) at one
+ * token count m, each
+ *   y[m,n] = bf16_rne( (sum_k dec(qx[m,k]) * dec(qw[n,k])) * x_scale[m]
+ *                      * w_scale[n] )
+ * with float32 accumulation (summation order unspecified; each output is
+ * one thread's sum over K in ascending order of 128-byte blocks, the same
+ * whatever the grouping).  At a few tokens the Linears are bound by their
+ * weight bytes (MOSS-VL-Realtime-FP8 article, "why quantize"); one launch
+ * streams every item's weights with one ramp-up and one tail, and items may
+ * share their codes (e.g. the Linears of a layer that read the same input,
+ * quantized once).
+ *   items[i].qx       E4M3 [m, k] contiguous, x_scale float32 [m]     (input)
+ *   items[i].qw_tiled the item's [n, k] weight codes in the order of
+ *                     fp8w8a8_tile_weights, w_scale float32 [n]      (input)
+ *   items[i].y        bf16 [m, n] contiguous                         (output)
+ *   items[i].n, .k    64 <= n <= 2^24, n % 64 == 0;
+ *                     128 <= k <= 16384, k % 128 == 0
+ * Rules: 1 <= m <= 64; 1 <= count <= 16; items is a HOST array (read during
+ * the call only); all pointers 16-byte aligned; every y must overlap no
+ * input of any item and no other y.  No workspace.  Errors are returned
+ * before anything is launched.
+ */
+typedef struct fp8w8a8_group_fp8_linear {
+  const uint8_t* qx;
+  const float* x_scale;
+  const uint8_t* qw_tiled;
+  const float* w_scale;
+  uint16_t* y;
+  int64_t n;
+  int64_t k;
+} fp8w8a8_group_fp8_linear;
+int fp8w8a8_fp8_linear_group(const fp8w8a8_group_fp8_linear* items, int count,
+                             int64_t m, void* stream);
+
+/*
  * The adjacent fusions followed by the Linear, in one call: exactly
  * fp8w8a8_rmsnorm_quantize(x, gamma, eps) (or fp8w8a8_swiglu_quantize(gate,
  * up)) followed by fp8w8a8_fp8_linear, with bit-identical output.  The norm

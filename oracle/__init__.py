@@ -28,6 +28,8 @@ swiglu  the SiLU-gated activation between gate/up and down and the
 kvcache the FP8 E4M3 key/value-cache codec (group-wise dynamic scales,
         float32 read-back rounded to bf16) and the INT8 group-wise cache
         with a BF16 residual window (asymmetric min-max reading of HQQ).
+tiles   the MFMA-tile order of weight codes read by the grouped few-token
+        call (a byte permutation of the library's own).
 check   the pass criteria (bit-exact bytes, elementwise output tolerance).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
@@ -42,11 +44,12 @@ from .e4m3 import (DECODE_TABLE, FINITE_MAX, decode, encode, encode_exact,
 from .bf16 import bf16_bits_to_f32, f64_to_bf16_bits
 from .quant import quant_act_ref, quant_weight_ref, quant_rows_ref
 from .linear import linear_ref, quant_linear_ref
+from .tiles import tile_weights_ref
 from .check import check_bytes, check_close, close_report
 
 __all__ = [
     "DECODE_TABLE", "FINITE_MAX", "POSITIVE_VALUES", "decode", "encode",
     "encode_exact", "bf16_bits_to_f32", "f64_to_bf16_bits", "quant_act_ref",
     "quant_weight_ref", "quant_rows_ref", "linear_ref", "quant_linear_ref",
-    "check_bytes", "check_close", "close_report",
+    "tile_weights_ref", "check_bytes", "check_close", "close_report",
 ]

@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 20
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -411,3 +411,49 @@ def test_group_m1_validation(lib):
     assert run([item(), item(x=32 * A, y=16 * A + 64)]) == EALIAS   # ys overlap
     assert run([item(), item(x=16 * A, y=64 * A)]) == EALIAS    # y over another x
     assert run([item(), item(x=32 * A, y=64 * A)]) == EDEV      # valid: no device here
+
+
+def test_tile_weights_validation(lib):
+    f = lib.fp8w8a8_tile_weights
+    assert f(None, 16, 128, A, None) == ENULL and f(A, 16, 128, None, None) == ENULL
+    assert f(A, 24, 128, 4 * A, None) == ESHAPE                 # n % 16
+    assert f(A, 16, 192, 4 * A, None) == ESHAPE                 # k % 128
+    assert f(A, 16, 16384 + 128, 4 * A, None) == ESHAPE         # k <= 16384
+    assert f(A, -16, 128, 4 * A, None) == ESHAPE
+    assert f(A + 8, 16, 128, 4 * A, None) == EALIGN
+    assert f(A, 16, 128, A + 1024, None) == EALIAS              # ranges overlap
+    assert f(A, 0, 128, 4 * A, None) == OK                      # empty
+    assert f(A, 16, 128, 4 * A, None) == EDEV                   # valid: no device here
+
+
+def test_fp8_linear_group_validation(lib):
+    """The grouped call on given codes validates m and every item before a
+    launch."""
+    from fp8_w8a8_dynamic_amd.binding import _GroupFp8Linear
+
+    def run(items, m=64):
+        arr = (_GroupFp8Linear * max(1, len(items)))(*items)
+        return lib.fp8w8a8_fp8_linear_group(arr, len(items), m, None)
+
+    def item(qx=A, sx=2 * A, qw=4 * A, sw=8 * A, y=16 * A, n=128, k=256):
+        return _GroupFp8Linear(qx, sx, qw, sw, y, n, k)
+
+    assert lib.fp8w8a8_fp8_linear_group(None, 1, 64, None) == ENULL
+    assert run([]) == ESHAPE                                    # count 0
+    assert run([item()] * 17) == ESHAPE                         # count > 16
+    assert run([item()], m=0) == ESHAPE and run([item()], m=65) == ESHAPE
+    assert run([item(sx=None)]) == ENULL and run([item(qw=None)]) == ENULL
+    assert run([item(n=96)]) == ESHAPE and run([item(n=0)]) == ESHAPE
+    assert run([item(n=(1 << 24) + 64)]) == ESHAPE              # n <= 2^24
+    assert run([item(k=192)]) == ESHAPE and run([item(k=64)]) == ESHAPE
+    assert run([item(k=16384 + 128)]) == ESHAPE                 # k <= 16384
+    assert run([item(sx=2 * A + 4)]) == EALIGN
+    assert run([item(y=A + 64)]) == EALIAS                      # y over its codes
+    assert run([item(y=2 * A)]) == EALIAS                       # y over its scales
+    assert run([item(y=4 * A + 64)]) == EALIAS                  # y over its weights
+    # ys of 64 x 128 bf16 (16 KB): overlapping, and over another item's codes.
+    assert run([item(), item(y=16 * A + 8192)]) == EALIAS
+    assert run([item(), item(qx=16 * A, y=64 * A)]) == EALIAS
+    # Valid, with the codes shared by both items: no device here.
+    assert run([item(), item(qw=32 * A, sw=48 * A, y=64 * A)]) == EDEV
+    assert run([item(n=64, k=128)], m=1) == EDEV

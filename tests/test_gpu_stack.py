@@ -22,6 +22,11 @@ layers, at both token counts:
 The oracle's free-running chain (its own bf16 outputs feeding its next
 layer) over the first two layers is computed too and its relative
 Frobenius drift reported, not asserted.
+
+At M = 64 the stack also runs as the grouped few-token path would serve it
+(the layer input quantized once, q, k, v, o, gate and up in one grouped
+launch on MFMA-tiled weights, up's output quantized, then down), held to
+the same teacher-forced checks on all 36 layers.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -103,6 +108,46 @@ def _gpu_chain(qws, x0_bits):
     return rec, host_bits(x)
 
 
+def _gpu_chain_grouped(qws, tiled, x0_bits):
+    """The stack through the grouped call: per layer one quantization of
+    X_l, one launch for the six Linears that read it, then down.  Same
+    record per layer as _gpu_chain."""
+    ns = [LAYER_SHAPES[j][1] for j in range(6)]
+    x = to_dev_bf16(x0_bits)
+    rec = []
+    for layer in range(LAYERS):
+        qx, sx = fq.quantize_act_per_token(x)
+        outs = fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[layer],
+                                   [qws[layer][j][1] for j in range(6)], ns)
+        ys = dict(enumerate(outs))
+        qu, su = fq.quantize_act_per_token(ys[UP])
+        qw, sw = qws[layer][DOWN]
+        ys[DOWN] = fq.fp8_linear(qu, su, qw, sw)
+        rec.append({"x": host_bits(x), "qx": host_bits(qx), "sx": host_bits(sx),
+                    "qu": host_bits(qu), "su": host_bits(su),
+                    "y": {j: host_bits(t) for j, t in ys.items()}})
+        x = ys[DOWN]
+    torch.cuda.synchronize()
+    return rec, host_bits(x)
+
+
+def _check_layers(rec, ref, m, what):
+    """Teacher-forced checks of every layer of a recorded chain."""
+    for layer in range(LAYERS):
+        r = rec[layer]
+        qx, sx = oracle.quant_act_ref(r["x"])
+        check_bytes(r["sx"].view(np.uint32), sx.view(np.uint32), f"{what} L{layer} X scales")
+        check_bytes(r["qx"], qx, f"{what} L{layer} X codes")
+        qu, su = oracle.quant_act_ref(r["y"][UP])
+        check_bytes(r["su"].view(np.uint32), su.view(np.uint32), f"{what} L{layer} Y_up scales")
+        check_bytes(r["qu"], qu, f"{what} L{layer} Y_up codes")
+        for j in range(7):
+            cols, rqw, rsw = ref[layer][j]
+            a, sc = (qu, su) if j == DOWN else (qx, sx)
+            check_close(r["y"][j][:, cols], oracle.linear_ref(a, sc, rqw, rsw),
+                        f"{what} m={m} L{layer} {LAYER_SHAPES[j][0]}")
+
+
 def _oracle_quant_rows(w_bits):
     """Oracle weight quantization of a large matrix, rows split over threads."""
     chunks = np.array_split(np.arange(w_bits.shape[0]), POOL)
@@ -177,3 +222,16 @@ def test_stack_teacher_forced_every_layer(stack, m):
     drift = _free_running_drift(rec, x0, m)
     print(f"free-running oracle chain, m={m}: relative Frobenius distance of "
           f"down outputs per layer {[round(d, 4) for d in drift]}")
+
+
+@pytest.mark.timeout(900)
+def test_stack_grouped_teacher_forced_every_layer_m64(stack):
+    qws, ref = stack
+    m = 64
+    tiled = [[fq.tile_weights(qws[layer][j][0]) for j in range(6)] for layer in range(LAYERS)]
+    x0 = c4_x0(m)
+    rec, _ = _gpu_chain_grouped(qws, tiled, x0)
+    del tiled
+    torch.cuda.empty_cache()
+    assert np.array_equal(rec[0]["x"], x0)
+    _check_layers(rec, ref, m, "grouped stack")

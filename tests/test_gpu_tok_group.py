@@ -1,0 +1,171 @@
+"""The grouped call on given codes at a few tokens (fp8w8a8_fp8_linear_group,
+1 <= M <= 64 tokens, up to 16 Linears in one launch) and the weight tiling
+it reads (fp8w8a8_tile_weights).
+
+The tiling is bit-exact against oracle.tile_weights_ref.  Every item's
+output is held to the elementwise tolerance of oracle.check against the
+oracle's Linear on the same codes, computed on the row-major weights: the
+activations are the oracle's own per-token quantization of seeded bf16 rows
+(uploaded), the weights the GPU quantizer's codes (bit-exact against the
+oracle in the weight tests), read back, and tiled on the GPU for the call.  The outputs are also bit-identical between two
+runs and between persistent grids of different sizes: each output is one
+thread's sum over K in ascending 128-value blocks whichever workgroup takes
+its unit.
+
+Cases: layer 0 of the 36-layer stack at M = 64 (q, k, v, o, gate, up on
+one shared code buffer in one launch; down on the oracle's codes of the
+GPU's up output), ragged shapes at M = 1 .. 64 (N = 64, K with a partial
+last 512-byte stage, tokens past the last full block of 16, zero and large
+rows), 16 items at the largest K, and the tiling alone on its edge shapes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_dynamic_amd as fq
+import oracle
+from oracle import check_bytes, check_close
+from tests.gpu_util import host_bits, to_dev_bf16, to_dev_f32, to_dev_u8
+from workloads import LAYER_SHAPES, bf16_from_f64
+from workloads.generators import c4_weight, c4_x0, outlier_act_bf16
+
+pytestmark = pytest.mark.gpu
+
+UP = 5
+
+
+def _codes(x_bits):
+    """The oracle's per-token codes and scales of x, on the host and the GPU."""
+    qx, sx = oracle.quant_act_ref(x_bits)
+    return (qx, sx), (to_dev_u8(qx), to_dev_f32(sx))
+
+
+def _weights(w_bits):
+    """GPU-quantized weights (tiled for the call) and their host copies
+    (row-major); the tiling checked bit-exact against the oracle's."""
+    qw, sw = fq.quantize_weight_channelwise(to_dev_bf16(w_bits))
+    tiled = fq.tile_weights(qw)
+    hq = host_bits(qw)
+    check_bytes(host_bits(tiled), oracle.tile_weights_ref(hq), "tiled weights")
+    return (tiled, sw, qw.shape[0]), (hq, host_bits(sw))
+
+
+def _group(acts, weights, outs=None):
+    return fq.fp8_linear_group([a[1][0] for a in acts], [a[1][1] for a in acts],
+                               [w[0][0] for w in weights], [w[0][1] for w in weights],
+                               [w[0][2] for w in weights], outs=outs)
+
+
+def _run_and_check(acts, weights, what):
+    """acts[i] = ((qx, sx) host, (qx, sx) device); weights[i] likewise
+    (device first).  Runs the group, checks every item against the oracle,
+    returns the outputs' bits."""
+    ys = _group(acts, weights)
+    torch.cuda.synchronize()
+    out = []
+    for i, (a, w) in enumerate(zip(acts, weights)):
+        y = host_bits(ys[i])
+        check_close(y, oracle.linear_ref(a[0][0], a[0][1], w[1][0], w[1][1]),
+                    f"{what} item {i}")
+        out.append(y)
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_stack_layer0_m64():
+    """Layer 0 of the 36-layer stack at M = 64: the six Linears that read
+    the layer input in one launch on one shared code buffer, then down."""
+    m = 64
+    x = c4_x0(m)
+    a = _codes(x)
+    ws = [_weights(c4_weight(0, j)) for j in range(6)]
+    ys = _run_and_check([a] * 6, ws, "stack layer 0, M = 64")
+    up_bits = ys[UP]
+    wd = _weights(c4_weight(0, 6))
+    _run_and_check([_codes(up_bits)], [wd], "stack layer 0 down, M = 64")
+    assert [y.shape for y in ys] == [(m, s[1]) for s in LAYER_SHAPES[:6]]
+
+
+WIDE = [(128, 640), (256, 640), (1024, 1152), (128, 4224), (384, 12288),
+        (4096, 512), (128, 128)]
+NARROW = [(64, 640), (192, 640), (320, 4224), (64, 128), (1024, 12288)]
+
+
+def _ragged_inputs(m, seed, shapes):
+    """Items of assorted shapes; items 0 and 1 share one code buffer."""
+    rng = np.random.default_rng(700 + seed)
+    acts, weights = [], []
+    shared = None
+    for i, (n, k) in enumerate(shapes):
+        if i == 1:
+            acts.append(shared)
+        else:
+            xf = rng.standard_normal((m, k)) * (10.0 ** rng.uniform(-3, 3, size=(m, 1)))
+            xf *= np.where(rng.random((m, k)) < 0.01, 20.0, 1.0)
+            if m >= 5:
+                xf[1] = 0.0          # a zero row: scale 0, codes 0, output 0
+                xf[3] *= 1e4         # a large row
+            a = _codes(bf16_from_f64(xf))
+            acts.append(a)
+            if i == 0:
+                shared = a
+        weights.append(_weights(bf16_from_f64(rng.standard_normal((n, k)) * 0.02)))
+    return acts, weights
+
+
+@pytest.mark.parametrize("m,shapes", [(m, "wide") for m in (1, 5, 16, 17, 33, 63, 64)]
+                         + [(m, "narrow") for m in (3, 40, 64)])
+def test_ragged_shapes(m, shapes, monkeypatch):
+    acts, weights = _ragged_inputs(m, m, WIDE if shapes == "wide" else NARROW)
+    base = _run_and_check(acts, weights, f"ragged {shapes} M = {m}")
+    # The same bits on a persistent grid of 1, 2 and 7 workgroups (hundreds
+    # of units each, the pipeline running across unit boundaries) and with
+    # the weights requested three stages ahead instead of two.
+    for key, val in (("FP8W8A8_TOKG_GRID", "1"), ("FP8W8A8_TOKG_GRID", "2"),
+                     ("FP8W8A8_TOKG_GRID", "7"), ("FP8W8A8_TOKG_DEPTH", "3")):
+        monkeypatch.setenv(key, val)
+        ys = _group(acts, weights)
+        torch.cuda.synchronize()
+        monkeypatch.delenv(key)
+        for i, y in enumerate(ys):
+            check_bytes(host_bits(y), base[i],
+                        f"ragged {shapes} M = {m} {key}={val} item {i}")
+
+
+def test_sixteen_items_largest_k():
+    """16 items of N = 64 (one 64-row unit each) at K = 16384, M = 64, each
+    with its own codes; run twice, same bits."""
+    m = 64
+    rng = np.random.default_rng(77)
+    acts = [_codes(outlier_act_bf16(rng, (m, 16384))) for _ in range(16)]
+    weights = [_weights(bf16_from_f64(rng.standard_normal((64, 16384)) * 0.02))
+               for _ in range(16)]
+    first = _run_and_check(acts, weights, "16 items K = 16384")
+    again = _run_and_check(acts, weights, "16 items K = 16384, again")
+    for i in range(16):
+        check_bytes(again[i], first[i], f"16 items run twice item {i}")
+
+
+def test_outputs_into_given_buffers():
+    """outs= given: results land in the caller's tensors, others untouched."""
+    m, rng = 24, np.random.default_rng(9)
+    a = _codes(outlier_act_bf16(rng, (m, 1024)))
+    w = _weights(bf16_from_f64(rng.standard_normal((256, 1024)) * 0.02))
+    big = torch.full((m + 2, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[1:m + 1]
+    _group([a], [w], outs=[out])
+    torch.cuda.synchronize()
+    check_close(host_bits(out), oracle.linear_ref(a[0][0], a[0][1], w[1][0], w[1][1]),
+                "outs given")
+    assert torch.all(big[0] == 7.0) and torch.all(big[m + 1] == 7.0)
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (4096, 4096), (1024, 12288),
+                                 (80, 16384)])
+def test_tile_weights_bit_exact(n, k):
+    qw = torch.from_numpy(np.random.default_rng(n + k).integers(
+        0, 256, size=(n, k), dtype=np.uint8)).to("cuda")
+    t = fq.tile_weights(qw)
+    torch.cuda.synchronize()
+    check_bytes(host_bits(t), oracle.tile_weights_ref(host_bits(qw)), f"tile {n}x{k}")
