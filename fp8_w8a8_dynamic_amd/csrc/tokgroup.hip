@@ -44,7 +44,8 @@
 // Out-of-range bytes read as 0 through buffer descriptors: tokens past M
 // (the codes' descriptor covers M * K bytes), the K tail of a last stage
 // (offsets moved past the descriptor), outputs of tokens past M (dropped by
-// the output's descriptor, M * N values).
+// the output's descriptor, M * N values).  A unit's outputs leave through
+// LDS as whole 128-byte row segments.
 #include <algorithm>
 #include <cstdlib>
 #include <utility>
@@ -209,15 +210,23 @@ __device__ __forceinline__ void compute_stage(v4f (&acc)[T], const Weights& s,
   }
 }
 
+// One token's 64 outputs of a unit in LDS (bf16), padded so that the 16
+// tokens of a write land in 16 distinct bank groups.
+constexpr int kOutRow = 64 * 2 + 16;
+
+// The unit's 16 T x 64 outputs: scaled, rounded to bf16 and staged in LDS by
+// the four waves (token 16 t + r, channels 16 wave + 4 g .. + 3 per lane),
+// then written out as whole 128-byte row segments, 16 bytes per thread
+// (tokens past M dropped by the output's descriptor).  Every wave is at its
+// unit's last stage here, so the barrier is met by all four; the next write
+// to `ob` is a later unit's, after at least one more step's barrier.
 template <int T>
 __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
                                          const Args& a, const Cursor& c, int M,
-                                         int wave, int lane) {
+                                         int wave, int tid, uint8_t* ob) {
   const Item& it = a.it[c.item];
   const int N = it.n;
-  const int r = lane & 15, g = lane >> 4;
-  const int n = (c.unit - it.u0) * 64 + wave * 16 + 4 * g;
-  const auto yr = row_rsrc(it.y, static_cast<uint32_t>(M * N) * 2u);
+  const int lane = tid & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const v4f v = acc[t];
@@ -225,8 +234,20 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
     uint2 pk;
     pk.x = pack_bf16x2(v[0] * sc.w.x * xs, v[1] * sc.w.y * xs);
     pk.y = pack_bf16x2(v[2] * sc.w.z * xs, v[3] * sc.w.w * xs);
-    buf_store8(pk, yr, static_cast<uint32_t>(((16 * t + r) * N + n) * 2));
+    *reinterpret_cast<uint2*>(ob + (16 * t + r) * kOutRow + (16 * wave + 4 * g) * 2) = pk;
     acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  lds_barrier();
+  const int n0 = (c.unit - it.u0) * 64;
+  const auto yr = row_rsrc(it.y, static_cast<uint32_t>(M * N) * 2u);
+#pragma unroll
+  for (int j = 0; j < (T + 1) / 2; ++j) {
+    const int p = j * 256 + tid;
+    const int tok = p >> 3, ch = p & 7;
+    if (tok < 16 * T) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ob + tok * kOutRow + ch * 16);
+      buf_store16(v, yr, static_cast<uint32_t>((tok * N + n0 + ch * 8) * 2));
+    }
   }
 }
 
@@ -242,8 +263,9 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
 // are exact.  Returns false once C was the workgroup's last stage.
 template <int I, int T, int D>
 __device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T>& X,
-                                     uint8_t (*xs)[16 * T * kStageBytes], Cursor (&Q)[D + 1],
-                                     const Args& a, int M, int wave, int tid) {
+                                     uint8_t (*xs)[16 * T * kStageBytes], uint8_t* ob,
+                                     Cursor (&Q)[D + 1], const Args& a, int M, int wave,
+                                     int tid) {
   // Q[0] = C, Q[j] = C + j (a unit past the end once the units run out).
   const int lane = tid & 63;
   const bool more1 = Q[1].unit < a.units, moreD = Q[D].unit < a.units;
@@ -258,7 +280,7 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T
   // sink them below).
   __builtin_amdgcn_sched_barrier(0);
   compute_stage(acc, S[I % (D + 1)], xs[I % 2], lane);
-  if (last) epilogue(acc, sc, a, Q[0], M, wave, lane);
+  if (last) epilogue(acc, sc, a, Q[0], M, wave, tid, ob);
   if (!more1) return false;
   store_codes(X, xs[(I + 1) % 2], tid);
   lds_barrier();
@@ -271,15 +293,16 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T
 template <int T, int D, int... Is>
 __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&acc)[T],
                                       Weights (&S)[D + 1], Codes<T>& X,
-                                      uint8_t (*xs)[16 * T * kStageBytes],
+                                      uint8_t (*xs)[16 * T * kStageBytes], uint8_t* ob,
                                       Cursor (&Q)[D + 1], const Args& a, int M, int wave,
                                       int tid) {
-  return (step<Is, T, D>(acc, S, X, xs, Q, a, M, wave, tid) && ...);
+  return (step<Is, T, D>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
 }
 
 template <int T, int D>
 __global__ __launch_bounds__(256, 2) void tok_group_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ob[16 * T * kOutRow];
   const int tid = static_cast<int>(threadIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -310,8 +333,8 @@ __global__ __launch_bounds__(256, 2) void tok_group_kernel(const Args a) {
   store_codes(X, xs[0], tid);
   lds_barrier();
   constexpr int kPeriod = (D + 1) % 2 == 0 ? D + 1 : 2 * (D + 1);
-  while (steps<T, D>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, Q, a, M,
-                     wave, tid)) {
+  while (steps<T, D>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, ob, Q, a,
+                     M, wave, tid)) {
   }
   // Nothing in flight when the workgroup leaves (the last requests read
   // nothing, but their registers go with the workgroup).
