@@ -373,6 +373,41 @@ def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
                   "unit": "GB/s", "frac_of_hbm": round(nbytes / tg / 1e9 / HBM_PEAK_GBS, 4),
                   "slice_gbs": spread([nbytes * DECODE_COPIES / ts / 1e9 for ts in gslices])}
         del gg
+    grouped = None
+    if 1 < m <= 64 and not packed:
+        # The same 7 Linears of each copy as two launches: their 7 inputs
+        # quantized in one (fp8w8a8_quantize_act_group), then one grouped
+        # call on the codes (fp8w8a8_fp8_linear_group; weights tiled
+        # beforehand, as an offline step next to their quantization).
+        for c in copies:
+            for L in c:
+                L["qt"] = fq.tile_weights(L["qw"])
+
+        def grouped_pass(layer):
+            qs = fq.quantize_act_group([L["x"] for L in layer])
+            fq.fp8_linear_group([q for q, _ in qs], [sc for _, sc in qs],
+                                [L["qt"] for L in layer], [L["sw"] for L in layer],
+                                [L["n"] for L in layer], outs=[L["y"] for L in layer])
+        gt = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            grouped_pass(copies[0])
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gt, stream=cap):
+                for c in copies:
+                    grouped_pass(c)
+        torch.cuda.synchronize()
+        warm_for(torch, gt.replay)
+        tt, tslices = time_chunks(torch, gt.replay, reps)
+        tt /= DECODE_COPIES
+        grouped = {"us_per_layer": round(tt * 1e6, 3), "value": round(nbytes / tt / 1e9, 1),
+                   "unit": "GB/s", "frac_of_hbm": round(nbytes / tt / 1e9 / HBM_PEAK_GBS, 4),
+                   "slice_gbs": spread([nbytes * DECODE_COPIES / ts / 1e9 for ts in tslices]),
+                   "what": "the 7 inputs quantized in one launch, then the 7 Linears in "
+                           "one grouped launch on MFMA-tiled weights"}
+        del gt
+        for c in copies:
+            for L in c:
+                L.pop("qt", None)
     del copies
     # Each Linear on its own: a graph of that Linear's call on copies of its
     # weights in turn (at least ROTATE_BYTES of distinct weights per replay,
@@ -398,7 +433,7 @@ def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
     del base
     torch.cuda.empty_cache()
     return dict(layer_us=t * 1e6, gbs=nbytes / t / 1e9, bytes=nbytes, per_linear=per,
-                single_launch=single,
+                single_launch=single, grouped=grouped,
                 slices=[nbytes * DECODE_COPIES / ts / 1e9 for ts in slices])
 
 
@@ -1072,7 +1107,8 @@ def main():
         log(f"launch floor {dec_floor}")
         dec_more = {mm: bench_decode(torch, fq, max(20, args.steps // 2), m=mm)
                     for mm in (4, 8)}
-        log("decode M=4, 8: " + ", ".join(f"{v['layer_us']:.1f} us {v['gbs']:.0f} GB/s"
+        log("decode M=4, 8: " + ", ".join(f"{v['layer_us']:.1f} us {v['gbs']:.0f} GB/s "
+                                          f"(grouped {v['grouped']['us_per_layer']} us)"
                                           for v in dec_more.values()))
     log("packed layer ...")
     pre_p = bench_prefill(torch, fq, args.steps, args.warmup, packed=True)
@@ -1191,7 +1227,8 @@ def main():
                          "other_token_counts": {
                              f"m{mm}": {"value": round(v["gbs"], 1), "unit": "GB/s",
                                         "us_per_layer": round(v["layer_us"], 3),
-                                        "frac_of_hbm": round(v["gbs"] / HBM_PEAK_GBS, 4)}
+                                        "frac_of_hbm": round(v["gbs"] / HBM_PEAK_GBS, 4),
+                                        "grouped": v["grouped"]}
                              for mm, v in dec_more.items()}}
     out["packed"] = packed
     if stack is not None:

@@ -16,7 +16,7 @@ from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
                       fp8_linear_group, init_workspace, kv_dequantize_fp8, kv_quantize_fp8,
                       kv_quantize_int8, kv_read_int8, load_library,
                       quant_linear, quant_linear_group_m1, quant_linear_noalloc,
-                      quantize_act_per_token,
+                      quantize_act_group, quantize_act_per_token,
                       rmsnorm_quant_linear,
                       swiglu_quant_linear, tile_weights,
                       quantize_weight_channelwise, rmsnorm_quantize, swiglu_quantize,
@@ -28,6 +28,6 @@ __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
            "kv_quantize_int8", "kv_read_int8",
            "load_library", "quant_linear", "quant_linear_group_m1",
            "quant_linear_noalloc",
-           "quantize_act_per_token", "quantize_weight_channelwise",
+           "quantize_act_group", "quantize_act_per_token", "quantize_weight_channelwise",
            "rmsnorm_quantize", "rmsnorm_quant_linear", "swiglu_quantize",
            "swiglu_quant_linear", "workspace_bytes"]

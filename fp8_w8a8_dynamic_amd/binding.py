@@ -52,6 +52,8 @@ SIGNATURES = {
                         _c_vp, _c_i64, _c_vp]),
     "fp8w8a8_quant_linear_group_m1":
         (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp]),
+    "fp8w8a8_quantize_act_group":
+        (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp]),
     "fp8w8a8_tile_weights":
         (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "fp8w8a8_fp8_linear_group":
@@ -529,6 +531,37 @@ def quant_linear_group_m1(xs, qws, w_scales, outs=None):
     _check(lib.fp8w8a8_quant_linear_group_m1(items, count, _stream_ptr(xs[0].device)),
            "quant_linear_group_m1")
     return ys
+
+
+class _GroupQuant(ctypes.Structure):
+    """Mirror of fp8w8a8_group_quant."""
+    _fields_ = [("x", _c_vp), ("m", _c_i64), ("k", _c_i64), ("ldx", _c_i64),
+                ("qx", _c_vp), ("x_scale", _c_vp)]
+
+
+def quantize_act_group(xs):
+    """Per-token quantization of several bf16 matrices in one launch:
+    [(qX float8_e4m3fn [M_i, K_i], x_scale float32 [M_i]) for each X_i],
+    each bit-identical to quantize_act_per_token(X_i)."""
+    lib = load_library()
+    count = len(xs)
+    items = (_GroupQuant * max(count, 1))()
+    outs = []
+    for i, x in enumerate(xs):
+        if x.dtype != torch.bfloat16:
+            raise TypeError("each x must be bfloat16")
+        m, k, ld = _rows(x, "x")
+        if x.device != xs[0].device:
+            raise ValueError("every x must be on one device")
+        qx = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+        sx = torch.empty((m,), dtype=torch.float32, device=x.device)
+        items[i] = _GroupQuant(x.data_ptr(), m, k, ld, qx.data_ptr(), sx.data_ptr())
+        outs.append((qx.view(torch.float8_e4m3fn), sx))
+    if count == 0:
+        return outs
+    _check(lib.fp8w8a8_quantize_act_group(items, count, _stream_ptr(xs[0].device)),
+           "quantize_act_group")
+    return outs
 
 
 def tile_weights(qw, out=None):

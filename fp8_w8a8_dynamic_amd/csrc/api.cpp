@@ -623,6 +623,49 @@ int fp8w8a8_quant_linear_group_m1(const fp8w8a8_group_linear* items, int count,
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 
+int fp8w8a8_quantize_act_group(const fp8w8a8_group_quant* items, int count,
+                               void* stream) {
+  if (!items) return FP8W8A8_ERR_NULL;
+  if (count < 1 || count > fp8w8a8::kGroupMax) return FP8W8A8_ERR_SHAPE;
+  fp8w8a8::QuantItem g[fp8w8a8::kGroupMax];
+  int live = 0;
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) {
+    const fp8w8a8_group_quant& L = items[i];
+    if (L.m == 0) {  // nothing to read or write: only the shape is checked
+      if (L.k < 8 || L.k > fp8w8a8::kQuantGroupMaxK || L.k % 8 != 0 || !ld_ok(L.ldx, L.k))
+        return FP8W8A8_ERR_SHAPE;
+      continue;
+    }
+    const int st = check_quant_args(L.x, L.m, L.k, L.ldx, L.qx, L.x_scale);
+    if (st != FP8W8A8_OK) return st;
+    if (L.k > fp8w8a8::kQuantGroupMaxK) return FP8W8A8_ERR_SHAPE;
+    rows += L.m;
+    if (rows > kMaxDim) return FP8W8A8_ERR_SHAPE;
+    g[live++] = fp8w8a8::QuantItem{L.x, L.m, L.k, L.ldx, L.qx, L.x_scale, 0};
+  }
+  // No output may overlap any item's input or another output.
+  for (int i = 0; i < count; ++i) {
+    const Range oq = span(items[i].qx, items[i].m, items[i].k, items[i].k, 1);
+    const Range os = span(items[i].x_scale, items[i].m, 1, 1, 4);
+    for (int j = 0; j < count; ++j) {
+      const Range in = span(items[j].x, items[j].m, items[j].k, items[j].ldx, 2);
+      if (overlap(oq, in) || overlap(os, in)) return FP8W8A8_ERR_ALIAS;
+      if (j != i &&
+          (overlap(oq, span(items[j].qx, items[j].m, items[j].k, items[j].k, 1)) ||
+           overlap(oq, span(items[j].x_scale, items[j].m, 1, 1, 4)) ||
+           overlap(os, span(items[j].qx, items[j].m, items[j].k, items[j].k, 1)) ||
+           overlap(os, span(items[j].x_scale, items[j].m, 1, 1, 4))))
+        return FP8W8A8_ERR_ALIAS;
+    }
+  }
+  if (rows == 0) return FP8W8A8_OK;
+  int st = check_device();
+  if (st != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_quant_group(g, live, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
 int fp8w8a8_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* tiled,
                          void* stream) {
   if (!qw || !tiled) return FP8W8A8_ERR_NULL;

@@ -26,6 +26,19 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t k,
                              int64_t ld, uint8_t* q, float* scale,
                              hipStream_t stream);
 
+// Per-row quantization of up to kGroupMax bf16 matrices in one launch
+// (codes and scales as launch_quant_rows gives for each); k <= kQuantGroupMaxK.
+constexpr int kGroupMax = 16;
+constexpr int64_t kQuantGroupMaxK = 16384;
+struct QuantItem {
+  const uint16_t* x;
+  int64_t rows, k, ld;
+  uint8_t* q;
+  float* scale;
+  int64_t row0;  // first row of the item in the launch (set by the launcher)
+};
+hipError_t launch_quant_group(const QuantItem* items, int count, hipStream_t stream);
+
 // RMSNorm of each row of x [rows, k] with weight gamma [k], then the
 // per-row quantization of the bf16 result: codes [rows, k] contiguous, one
 // float32 scale per row, and the bf16 result itself into y (row stride ldy)
@@ -106,7 +119,6 @@ hipError_t launch_gemv_pre(int pre, const uint16_t* x, int64_t ldx,
 // Grouped one-token Linears (bf16 x [1, k] -> bf16 y [1, n] each, their
 // quantization fused), up to kGroupMax of them in one launch; each item's
 // output is bit-identical to launch_gemv on it alone.  k <= 12288.
-constexpr int kGroupMax = 16;
 struct GroupLinear {
   const uint16_t* x;
   const uint8_t* qw;

@@ -11,6 +11,7 @@
 // with round-to-nearest-even by v_cvt_pk_fp8_f32; codes leave as 8-byte
 // stores that are contiguous across the wave.  HBM traffic is the algorithmic
 // 2 bytes in + 1 byte out per element + 4 bytes of scale per row.
+#include <algorithm>
 #include <cstdlib>
 
 #include "device_common.h"
@@ -95,6 +96,54 @@ __global__ __launch_bounds__(256) void quant_rows_split_kernel(
     buf_store8(c, dst, ((i * S + part) * 64 + lane) * 8u);
   });
   if (lane == 0 && part == 0) scale[r] = s;
+}
+
+// Several matrices' rows in one launch (fp8w8a8_quantize_act_group): one
+// row per workgroup, its four waves sharing it as in quant_rows_split_kernel
+// (wave w holds the 16-byte vectors i * 256 + 64 w + lane, i < NV, NV sized
+// for the longest row; vectors past a shorter row read as 0 through the
+// descriptor and are never stored).  The workgroup finds its item by
+// comparing its index with the items' first rows.  Codes and scales are
+// those of quant_rows_kernel for every row.
+struct QuantGroupArgs {
+  QuantItem it[kGroupMax];
+  int count;
+};
+
+template <int NV>
+__global__ __launch_bounds__(256) void quant_group_kernel(const QuantGroupArgs a) {
+  __shared__ uint32_t wmax[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = blockIdx.x;
+  int i = 0;
+  for (int j = 1; j < a.count; ++j)
+    if (b >= a.it[j].row0) i = j;
+  const QuantItem& it = a.it[i];
+  const int64_t row = b - it.row0;
+  const int k = static_cast<int>(it.k);
+  const auto src = row_rsrc(it.x + row * it.ld, static_cast<uint32_t>(k) * 2u);
+  uint4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = buf_load16_stream(src, ((j * 4 + wave) * 64 + lane) * 16u);
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    m = pk_max_u16(m, bf16x2_abs_bits(v[j].x));
+    m = pk_max_u16(m, bf16x2_abs_bits(v[j].y));
+    m = pk_max_u16(m, bf16x2_abs_bits(v[j].z));
+    m = pk_max_u16(m, bf16x2_abs_bits(v[j].w));
+  }
+  const uint32_t mw = wave_max_u32(max(m & 0xffffu, m >> 16));
+  if (lane == 0) wmax[wave] = mw;
+  __syncthreads();
+  const uint32_t mrow = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s = row_scale(__uint_as_float(mrow << 16));
+  const auto dst = row_rsrc(it.q + row * it.k, static_cast<uint32_t>(k));
+  quantize_row<NV>(v, make_divisor(s), [&](int j, uint2 c) {
+    buf_store8(c, dst, ((j * 4 + wave) * 64 + lane) * 8u);
+  });
+  if (lane == 0 && wave == 0) it.scale[row] = s;
 }
 
 // Rows longer than the register-resident variants: two passes, the second
@@ -195,6 +244,31 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t k,
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   quant_rows_long_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream>>>(
         x, rows, k, ld, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_group(const QuantItem* items, int count, hipStream_t stream) {
+  if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+  QuantGroupArgs a{};
+  a.count = count;
+  int64_t rows = 0, kmax = 0;
+  for (int i = 0; i < count; ++i) {
+    a.it[i] = items[i];
+    a.it[i].row0 = rows;
+    rows += items[i].rows;
+    kmax = std::max(kmax, items[i].k);
+  }
+  if (rows == 0) return hipSuccess;
+  if (rows > (int64_t{1} << 31) - 1 || kmax > kQuantGroupMaxK) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(rows)), block(256);
+  switch ((kmax + 2047) / 2048) {
+    case 1: quant_group_kernel<1><<<grid, block, 0, stream>>>(a); break;
+    case 2: quant_group_kernel<2><<<grid, block, 0, stream>>>(a); break;
+    case 3: quant_group_kernel<3><<<grid, block, 0, stream>>>(a); break;
+    case 4: quant_group_kernel<4><<<grid, block, 0, stream>>>(a); break;
+    case 5: case 6: quant_group_kernel<6><<<grid, block, 0, stream>>>(a); break;
+    default: quant_group_kernel<8><<<grid, block, 0, stream>>>(a); break;
+  }
   return hipGetLastError();
 }
 

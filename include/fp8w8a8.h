@@ -312,6 +312,32 @@ int fp8w8a8_quant_linear_group_m1(const fp8w8a8_group_linear* items, int count,
                                   void* stream);
 
 /*
+ * Per-token dynamic quantization of several activation matrices in one
+ * launch: count independent fp8w8a8_quantize_act_per_token calls (README
+ * "FP8-Dynamic": activations FP8 per token, dynamic), each item's codes and
+ * scales bit-identical to that call -- e.g. the inputs of a decode step's
+ * Linears ahead of one fp8w8a8_fp8_linear_group.
+ *   items[i].x        bf16 [m, k], row stride ldx >= k, ldx % 8 == 0  (input)
+ *   items[i].qx       E4M3 [m, k], contiguous                         (output)
+ *   items[i].x_scale  float32 [m]                                     (output)
+ * Rules: 1 <= count <= 16; items is a HOST array (read during the call
+ * only); per item m >= 0, 8 <= k <= 16384, k % 8 == 0, x and qx 16-byte
+ * aligned, x_scale 4-byte aligned; no output may overlap any item's input
+ * or another output.  An item with m == 0 is skipped (its pointers may be
+ * NULL).  Errors are returned before anything is launched.
+ */
+typedef struct fp8w8a8_group_quant {
+  const uint16_t* x;
+  int64_t m;
+  int64_t k;
+  int64_t ldx;
+  uint8_t* qx;
+  float* x_scale;
+} fp8w8a8_group_quant;
+int fp8w8a8_quantize_act_group(const fp8w8a8_group_quant* items, int count,
+                               void* stream);
+
+/*
  * E4M3 weight codes in MFMA-tile order, the weight layout of
  * fp8w8a8_fp8_linear_group.  An offline step next to the channel-wise
  * quantization (README "FP8-Dynamic": the weights are quantized once,

@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -411,6 +411,37 @@ def test_group_m1_validation(lib):
     assert run([item(), item(x=32 * A, y=16 * A + 64)]) == EALIAS   # ys overlap
     assert run([item(), item(x=16 * A, y=64 * A)]) == EALIAS    # y over another x
     assert run([item(), item(x=32 * A, y=64 * A)]) == EDEV      # valid: no device here
+
+
+def test_quantize_act_group_validation(lib):
+    """The grouped quantizer validates every item and the cross-item
+    overlaps before a launch."""
+    from fp8_w8a8_dynamic_amd.binding import _GroupQuant
+
+    def run(items):
+        arr = (_GroupQuant * max(1, len(items)))(*items)
+        return lib.fp8w8a8_quantize_act_group(arr, len(items), None)
+
+    def item(x=A, m=4, k=256, ldx=256, qx=8 * A, sx=16 * A):
+        return _GroupQuant(x, m, k, ldx, qx, sx)
+
+    assert lib.fp8w8a8_quantize_act_group(None, 1, None) == ENULL
+    assert run([]) == ESHAPE and run([item()] * 17) == ESHAPE
+    assert run([item(x=None)]) == ENULL and run([item(sx=None)]) == ENULL
+    assert run([item(k=12)]) == ESHAPE                          # k % 8
+    assert run([item(k=16384 + 8, ldx=16392)]) == ESHAPE        # k <= 16384
+    assert run([item(ldx=128)]) == ESHAPE                       # ldx < k
+    assert run([item(m=-1)]) == ESHAPE
+    assert run([item(qx=8 * A + 8)]) == EALIGN
+    assert run([item(qx=A + 512)]) == EALIAS                    # codes over its x
+    # Codes of one item over another item's input, or over its codes.
+    assert run([item(), item(x=32 * A, qx=32 * A + 256, sx=48 * A)]) == EALIAS
+    assert run([item(), item(x=32 * A, qx=8 * A + 512, sx=48 * A)]) == EALIAS
+    assert run([item(), item(x=32 * A, qx=A + 256, sx=48 * A)]) == EALIAS  # over item 0's x
+    assert run([item(m=0), item(m=0, x=32 * A, qx=40 * A, sx=48 * A)]) == OK   # empty
+    assert run([item(m=0, x=None, qx=None, sx=None)]) == OK     # empty: no pointers needed
+    assert run([item(m=0, k=12, x=None, qx=None, sx=None)]) == ESHAPE
+    assert run([item(), item(x=32 * A, qx=40 * A, sx=48 * A)]) == EDEV          # valid
 
 
 def test_tile_weights_validation(lib):

@@ -165,3 +165,40 @@ def test_rows_split_over_waves(split, m, k, ld, monkeypatch):
     q, s = fq.quantize_act_per_token(x)
     torch.cuda.synchronize()
     _check_rows(full[:, :k], host_bits(q), host_bits(s), what=f"split {split} {m}x{k}")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_quantize_act_group_matches_oracle_and_single_calls(seed):
+    """Several matrices in one launch (fp8w8a8_quantize_act_group): every
+    item's codes and scales bit-exact against the oracle and against
+    quantize_act_per_token on it alone; rows of K = 8 .. 16384 (ragged tails
+    of a 16-byte step), 0 .. 300 rows, zero and large rows, a strided x."""
+    rng = np.random.default_rng(900 + seed)
+    shapes = [(1, 4096), (4, 12288), (3, 16384), (64, 4104), (0, 256), (300, 8),
+              (17, 1024), (8, 2056)]
+    xs_bits, xs = [], []
+    for m, k in shapes:
+        xf = rng.standard_normal((m, k)) * (10.0 ** rng.uniform(-3, 3, size=(m, 1)))
+        if m >= 3:
+            xf[1] = 0.0
+            xf[2] *= 1e4
+        bits = bf16_from_f64(xf)
+        xs_bits.append(bits)
+        xs.append(to_dev_bf16(bits) if m > 0 else
+                  torch.empty((0, k), dtype=torch.bfloat16, device="cuda"))
+    # One item read through a row stride larger than its row.
+    wide = to_dev_bf16(bf16_from_f64(rng.standard_normal((5, 1024 + 64))))
+    xs.append(wide[:, :1024])
+    xs_bits.append(host_bits(wide)[:, :1024])
+    outs = fq.quantize_act_group(xs)
+    torch.cuda.synchronize()
+    for i, (bits, x, (q, s)) in enumerate(zip(xs_bits, xs, outs)):
+        rq, rs = oracle.quant_act_ref(bits)
+        check_bytes(host_bits(s).view(np.uint32), rs.view(np.uint32), f"group quant {i} scales")
+        check_bytes(host_bits(q), rq, f"group quant {i} codes")
+        if x.shape[0] > 0:
+            q1, s1 = fq.quantize_act_per_token(x)
+            torch.cuda.synchronize()
+            check_bytes(host_bits(q), host_bits(q1), f"group quant {i} vs single")
+            check_bytes(host_bits(s).view(np.uint32), host_bits(s1).view(np.uint32),
+                        f"group quant {i} scales vs single")
