@@ -28,8 +28,15 @@
 // registers, and written to LDS one step before their use, where the four
 // waves read them.  A weight fragment feeds T MFMAs, one per block of 16
 // tokens, so the codes cross L2 once per 64 weight rows.  A workgroup walks
-// its units (blockIdx.x, + gridDim.x, ...) as one stream of stages: the next
-// unit's first stages are in flight while the current unit finishes.  No
+// its units as one stream of stages: the next unit's first stages are in
+// flight while the current unit finishes.  Units are numbered longest K
+// first and dealt out in rounds of gridDim.x.  Workgroups start in index
+// order, so among equal units the low indices finish first; round r + 1
+// starts at the first workgroup that held a unit of round 0's shortest
+// length (a shift of that many workgroups per round; 0 when all units
+// are equal).  In a decoder layer at a few tokens, down's 64 units at
+// K = 12288 (24 stages) go to workgroups 0-63 and the units past the
+// first round to workgroups 64, 65, ..., which hold 8-stage units.  No
 // workgroup waits on another and no partial sums leave the wave: each
 // output is one lane's accumulator, items in K order.
 //
@@ -79,6 +86,7 @@ struct Args {
   int count;
   int units;
   int m;
+  int shift;  // workgroups by which each round's deal turns (0 <= shift < grid)
 };
 
 __device__ __forceinline__ v8i to_v8i(uint4 lo, uint4 hi) {
@@ -108,8 +116,16 @@ __device__ __forceinline__ void cursor_at(Cursor& c, const Args& a, int unit) {
   c.stages = (a.it[c.item].k + kStageBytes - 1) / kStageBytes;
 }
 
+// The workgroup's unit after u: round r holds units r G .. r G + G - 1, and
+// workgroup b takes unit r G + ((b - r shift) mod G) of it.
+__device__ __forceinline__ int next_unit(int u, int shift) {
+  const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  const int r = u / G + 1;
+  return r * G + (b + G - (r % G) * shift % G) % G;
+}
+
 __device__ __forceinline__ void cursor_next(Cursor& c, const Args& a) {
-  if (++c.stage == c.stages) cursor_at(c, a, c.unit + static_cast<int>(gridDim.x));
+  if (++c.stage == c.stages) cursor_at(c, a, next_unit(c.unit, a.shift));
 }
 
 // The epilogue's scales for a unit: sw of rows 4 g .. 4 g + 3 of the wave's
@@ -342,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void tok_group_kernel(const Args a) {
 }
 
 template <int T, int D>
-hipError_t launch_d(const Args& a, hipStream_t stream) {
+hipError_t launch_d(Args a, hipStream_t stream) {
   // Two workgroups per CU (LDS: 16 KB per token block; registers: two
   // waves per SIMD), 256 CUs.
   int64_t grid = std::min<int64_t>(a.units, 2 * 256);
@@ -350,6 +366,21 @@ hipError_t launch_d(const Args& a, hipStream_t stream) {
     const int64_t v = std::atoll(e);
     if (v >= 1) grid = std::min<int64_t>(a.units, v);
   }
+  // The deal's shift: how many of round 0's units (0 .. grid - 1, longest K
+  // first) are longer than its last.
+  const auto stages_of = [&](int unit) {
+    int i = 0;
+    for (int j = 1; j < a.count; ++j)
+      if (unit >= a.it[j].u0) i = j;
+    return (a.it[i].k + kStageBytes - 1) / kStageBytes;
+  };
+  const int shortest = stages_of(static_cast<int>(grid) - 1);
+  a.shift = 0;
+  for (int i = 0; i < a.count && a.it[i].u0 < grid; ++i)
+    if ((a.it[i].k + kStageBytes - 1) / kStageBytes > shortest) {
+      const int end = i + 1 < a.count ? a.it[i + 1].u0 : a.units;
+      a.shift += std::min<int>(end, static_cast<int>(grid)) - a.it[i].u0;
+    }
   tok_group_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -404,7 +435,7 @@ hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
   for (int i = 0; i < count; ++i)
     if (items[i].n % 64 != 0 || items[i].k % 128 != 0 || items[i].k > kTokGroupMaxK)
       return hipErrorInvalidValue;
-  // Longest rows first, so that the workgroups' strided unit lists even out.
+  // Longest rows first (the deal in rounds, below, relies on it).
   int order[kGroupMax];
   for (int i = 0; i < count; ++i) order[i] = i;
   std::stable_sort(order, order + count,

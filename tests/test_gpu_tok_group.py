@@ -14,7 +14,8 @@ its unit.
 
 Cases: layer 0 of the 36-layer stack at M = 64 (q, k, v, o, gate, up on
 one shared code buffer in one launch; down on the oracle's codes of the
-GPU's up output), ragged shapes at M = 1 .. 64 (N = 64, K with a partial
+GPU's up output), the decode layer's seven Linears at M = 4 and 8 in one
+launch after one grouped quantization, ragged shapes at M = 1 .. 64 (N = 64, K with a partial
 last 512-byte stage, tokens past the last full block of 16, zero and large
 rows), 16 items at the largest K, and the tiling alone on its edge shapes.
 """
@@ -28,7 +29,7 @@ import oracle
 from oracle import check_bytes, check_close
 from tests.gpu_util import host_bits, to_dev_bf16, to_dev_f32, to_dev_u8
 from workloads import LAYER_SHAPES, bf16_from_f64
-from workloads.generators import c4_weight, c4_x0, outlier_act_bf16
+from workloads.generators import c2_inputs, c4_weight, c4_x0, outlier_act_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +86,40 @@ def test_stack_layer0_m64():
     wd = _weights(c4_weight(0, 6))
     _run_and_check([_codes(up_bits)], [wd], "stack layer 0 down, M = 64")
     assert [y.shape for y in ys] == [(m, s[1]) for s in LAYER_SHAPES[:6]]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("m", [4, 8])
+def test_decode_layer_grouped(m):
+    """The decode layer at a few tokens in two launches: the seven Linears'
+    inputs quantized by one quantize_act_group call, then the seven Linears
+    on their codes in one grouped launch.  The 608 units of 64 rows exceed
+    the 512-workgroup grid, so a second round is dealt (shifted past the 64
+    workgroups that hold down's longer units).  Codes and scales bit-exact
+    against the oracle's, outputs within its tolerance, and every output
+    bit-identical to the same Linear alone in a one-item group (one round)."""
+    xs, ws = [], []
+    for j in range(7):
+        x, w = c2_inputs(m, j)
+        xs.append(x)
+        ws.append(_weights(w))
+    qs = fq.quantize_act_group([to_dev_bf16(x) for x in xs])
+    refs = [oracle.quant_act_ref(x) for x in xs]
+    for j, ((q, sc), (rq, rs)) in enumerate(zip(qs, refs)):
+        check_bytes(host_bits(q), rq, f"decode M = {m} codes {j}")
+        check_bytes(host_bits(sc).view(np.uint32), rs.view(np.uint32),
+                    f"decode M = {m} scales {j}")
+    ys = fq.fp8_linear_group([q for q, _ in qs], [sc for _, sc in qs],
+                             [w[0][0] for w in ws], [w[0][1] for w in ws],
+                             [w[0][2] for w in ws])
+    torch.cuda.synchronize()
+    for j, (y, w, r) in enumerate(zip(ys, ws, refs)):
+        name = f"decode M = {m} {LAYER_SHAPES[j][0]}"
+        yb = host_bits(y)
+        check_close(yb, oracle.linear_ref(r[0], r[1], w[1][0], w[1][1]), name)
+        alone = fq.fp8_linear_group([qs[j][0]], [qs[j][1]], [w[0][0]], [w[0][1]], [w[0][2]])
+        torch.cuda.synchronize()
+        check_bytes(host_bits(alone[0]), yb, f"{name}: grouped against alone")
 
 
 WIDE = [(128, 640), (256, 640), (1024, 1152), (128, 4224), (384, 12288),
