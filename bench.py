@@ -511,7 +511,10 @@ def bench_stack(torch, fq, m, passes):
     # The same stack as the checkpoint's packed modules run it: q|k|v and
     # gate|up concatenated along the output channels, and each distinct
     # input quantized once (X_l for qkv, o, gate_up; up's output for down):
-    # 2 quantizations and 4 matmuls per layer instead of 7 fused calls.
+    # 4 matmuls per layer instead of 7 fused calls, with up's output
+    # quantized on its own and down's output re-quantized for the next
+    # layer by down's own call (fp8_linear_requant; the last layer's output
+    # is not).
     packed = [(torch.cat([lw[0][0], lw[1][0], lw[2][0]]), torch.cat([lw[0][1], lw[1][1], lw[2][1]]),
                lw[3], torch.cat([lw[4][0], lw[5][0]]), torch.cat([lw[4][1], lw[5][1]]), lw[6])
               for lw in layers]
@@ -521,14 +524,22 @@ def bench_stack(torch, fq, m, passes):
               ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)))
     ws2 = fq.init_workspace(torch.empty(max(wsp, 1 << 20), dtype=torch.uint8, device="cuda"))
 
+    def down_of(li, qu, su, wd, sd, ws):
+        """Down; its output re-quantized for the next layer unless last."""
+        if li + 1 < 36:
+            _, qn, sn = fq.fp8_linear_requant(qu, su, wd, sd, out=xs[li + 1], workspace=ws)
+            return qn, sn
+        fq.fp8_linear(qu, su, wd, sd, out=xs[li + 1], workspace=ws)
+        return None, None
+
     def packed_pass():
+        qx, sx = fq.quantize_act_per_token(xs[0])
         for li, (wqkv, sqkv, (wo, so), wgu, sgu, (wd, sd)) in enumerate(packed):
-            qx, sx = fq.quantize_act_per_token(xs[li])
             fq.fp8_linear(qx, sx, wqkv, sqkv, out=y_qkv, workspace=ws2)
             fq.fp8_linear(qx, sx, wo, so, out=ys[3], workspace=ws2)
             fq.fp8_linear(qx, sx, wgu, sgu, out=y_gu, workspace=ws2)
             qu, su = fq.quantize_act_per_token(y_gu[:, 12288:])
-            fq.fp8_linear(qu, su, wd, sd, out=xs[li + 1], workspace=ws2)
+            qx, sx = down_of(li, qu, su, wd, sd, ws2)
 
     for _ in range(3):
         one_pass()
@@ -545,21 +556,21 @@ def bench_stack(torch, fq, m, passes):
     warm_for(torch, gp.replay)
     t_packed = time_events(torch, gp.replay, passes)
     del gp, packed
-    # At up to 64 tokens: the layer input quantized once and the six
-    # Linears that read it in one grouped launch (weights tiled offline),
-    # then down's input quantized and down.
+    # At up to 64 tokens: the six Linears that read the layer input in one
+    # grouped launch (weights tiled offline), then down's input quantized
+    # and down, which re-quantizes its output as the next layer's input.
     grouped = None
     if m <= 64:
         tiled = [[fq.tile_weights(lw[j][0]) for j in range(6)] for lw in layers]
         ns = [n for _, n, _ in LAYER_SHAPES[:6]]
 
         def grouped_pass():
+            qx, sx = fq.quantize_act_per_token(xs[0])
             for li, lw in enumerate(layers):
-                qx, sx = fq.quantize_act_per_token(xs[li])
                 fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[li], [lw[j][1] for j in range(6)],
                                     ns, outs=ys[:6])
                 qu, su = fq.quantize_act_per_token(ys[5])
-                fq.fp8_linear(qu, su, lw[6][0], lw[6][1], out=xs[li + 1], workspace=ws2)
+                qx, sx = down_of(li, qu, su, lw[6][0], lw[6][1], ws2)
 
         for _ in range(2):
             grouped_pass()
@@ -570,8 +581,9 @@ def bench_stack(torch, fq, m, passes):
         grouped = {"ms_per_pass": round(t_grouped * 1e3, 4),
                    "gbs": None, "frac_of_hbm": None,
                    "us_per_layer": round(t_grouped * 1e6 / 36, 2),
-                   "what": "each distinct input quantized once; q, k, v, o, gate, up "
-                           "in one grouped launch on MFMA-tiled weights, then down"}
+                   "what": "q, k, v, o, gate, up in one grouped launch on MFMA-tiled "
+                           "weights, up's output quantized, then down, which re-quantizes "
+                           "its output as the next layer's input"}
     nbytes = 36 * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for _, n, k in LAYER_SHAPES)
     flops = 36 * sum(2 * m * n * k for _, n, k in LAYER_SHAPES)
     if grouped is not None:
@@ -590,7 +602,8 @@ def bench_stack(torch, fq, m, passes):
                        "frac_of_hbm": round(nbytes / t_packed / 1e9 / HBM_PEAK_GBS, 4),
                        "us_per_layer": round(t_packed * 1e6 / 36, 2),
                        "what": "q|k|v and gate|up packed, each distinct input quantized "
-                               "once: 2 quantizations + 4 matmuls per layer"},
+                               "once (down re-quantizes its output as the next layer's "
+                               "input): 4 matmuls + 1 quantization per layer"},
             "grouped": grouped}
 
 

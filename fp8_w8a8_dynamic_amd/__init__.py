@@ -12,7 +12,7 @@ of ``include/fp8w8a8.h``; this package is its Python binding (argument
 marshalling only).
 """
 
-from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
+from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear, fp8_linear_requant,
                       fp8_linear_group, init_workspace, kv_dequantize_fp8, kv_quantize_fp8,
                       kv_quantize_int8, kv_read_int8, load_library,
                       quant_linear, quant_linear_group_m1, quant_linear_noalloc,
@@ -23,7 +23,7 @@ from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear,
                       workspace_bytes)
 
 __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
-           "fp8_linear_group", "tile_weights",
+           "fp8_linear_group", "tile_weights", "fp8_linear_requant",
            "init_workspace", "kv_dequantize_fp8", "kv_quantize_fp8",
            "kv_quantize_int8", "kv_read_int8",
            "load_library", "quant_linear", "quant_linear_group_m1",

@@ -44,6 +44,9 @@ SIGNATURES = {
     "fp8w8a8_fp8_linear":
         (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fp8w8a8_fp8_linear_requant":
+        (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                        _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "fp8w8a8_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                         _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -443,6 +446,39 @@ def fp8_linear(qx, x_scale, qw, w_scale, out=None, workspace=None):
         ws.numel() if ws is not None else 0, _stream_ptr(qx.device)),
         "fp8_linear")
     return y
+
+
+def fp8_linear_requant(qx, x_scale, qw, w_scale, out=None, workspace=None):
+    """:func:`fp8_linear` whose output is also quantized per token for the
+    Linear that reads it next.
+
+    Returns ``(y bf16 [M, N], qy float8_e4m3fn [M, N], y_scale float32 [M])``:
+    y as :func:`fp8_linear` gives it and ``(qy, y_scale)`` as
+    :func:`quantize_act_per_token` gives them for y."""
+    lib = load_library()
+    qx, qw = _as_codes(qx), _as_codes(qw)
+    m, k, ldq = _rows(qx, "qx")
+    n, k2, ldw = _rows(qw, "qw")
+    if k2 != k or ldq != k or ldw != k:
+        raise ValueError("qx [M, K] and qw [N, K] must be contiguous with one K")
+    if qw.device != qx.device:
+        raise ValueError("qx and qw must be on one device")
+    x_scale = _scales(x_scale, m, qx.device, "x_scale")
+    w_scale = _scales(w_scale, n, qx.device, "w_scale")
+    y = _out(m, n, qx.device, out)
+    qy = torch.empty((m, n), dtype=torch.uint8, device=qx.device)
+    sy = torch.empty((m,), dtype=torch.float32, device=qx.device)
+    if m == 0 or n == 0:
+        return y, qy.view(torch.float8_e4m3fn), sy
+    need = workspace_bytes(m, n, k, False)
+    ws = _pick_workspace(qx.device, need, workspace)
+    _check(lib.fp8w8a8_fp8_linear_requant(
+        qx.data_ptr(), x_scale.data_ptr(), qw.data_ptr(), w_scale.data_ptr(),
+        m, n, k, y.data_ptr(), y.stride(0), qy.data_ptr(), sy.data_ptr(),
+        ws.data_ptr() if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream_ptr(qx.device)),
+        "fp8_linear_requant")
+    return y, qy.view(torch.float8_e4m3fn), sy
 
 
 def quant_linear(x, qw, w_scale, out=None, workspace=None):

@@ -166,6 +166,12 @@ bool pre_in_gemv(Pre pre, int64_t m, int64_t n, int64_t k) {
   }
 }
 
+// The linear kernel for `path` on staged codes (defined below).
+hipError_t linear_on_codes(Path path, const fp8w8a8::GemmPlan& plan,
+                           const uint8_t* qx, const float* sx, const uint8_t* qw,
+                           const float* w_scale, int64_t m, int64_t n, int64_t k,
+                           uint16_t* y, int64_t ldy, float* part, hipStream_t s);
+
 Layout layout_for(int64_t m, int64_t n, int64_t k, Pre pre, Path path,
                   const fp8w8a8::GemmPlan& plan) {
   Layout L;
@@ -579,6 +585,58 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
                              reinterpret_cast<float*>(
                                  static_cast<uint8_t*>(workspace) + L.part),
                              s);
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+int fp8w8a8_fp8_linear_requant(const uint8_t* qx, const float* x_scale,
+                               const uint8_t* qw, const float* w_scale, int64_t m,
+                               int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                               uint8_t* qy, float* y_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!qx || !x_scale || !qw || !w_scale || !y || !qy || !y_scale) return FP8W8A8_ERR_NULL;
+  int st = check_linear_shape(m, n, k, ldy);
+  if (st != FP8W8A8_OK) return st;
+  if (!aligned16(qx) || !aligned16(x_scale) || !aligned16(qw) ||
+      !aligned16(w_scale) || !aligned16(y) || !aligned16(qy) ||
+      (reinterpret_cast<uintptr_t>(y_scale) & 3u) != 0 ||
+      (workspace && !aligned16(workspace)))
+    return FP8W8A8_ERR_ALIGN;
+  // Outputs: y, its codes and its scales; none may overlap an input or
+  // another output.
+  const Range outs[3] = {span(y, m, n, ldy, 2), span(qy, m, n, n, 1),
+                         span(y_scale, m, 1, 1, 4)};
+  const Range ins[4] = {span(qx, m, k, k, 1), span(x_scale, m, 1, 1, 4),
+                        span(qw, n, k, k, 1), span(w_scale, n, 1, 1, 4)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return FP8W8A8_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FP8W8A8_ERR_ALIAS;
+  }
+  const Path path = choose_path(m, n, k);
+  const fp8w8a8::GemmPlan plan = fp8w8a8::plan_gemm(m, n, k);
+  const Layout L = layout_for(m, n, k, Pre::kNone, path, plan);
+  if (L.total > 0) {
+    if (!workspace || workspace_bytes < L.total) return FP8W8A8_ERR_WORKSPACE;
+    const Range rw{reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + L.total};
+    for (const Range& r : outs)
+      if (overlap(rw, r)) return FP8W8A8_ERR_ALIAS;
+    for (const Range& r : ins)
+      if (overlap(rw, r)) return FP8W8A8_ERR_ALIAS;
+  }
+  if (m == 0 || n == 0) return FP8W8A8_OK;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + L.part);
+  hipError_t e;
+  if (path == Path::kGemm) {
+    e = fp8w8a8::launch_gemm_requant(plan, qx, x_scale, qw, w_scale, m, n, k, y, ldy,
+                                     qy, y_scale, part, s);
+  } else {
+    e = linear_on_codes(path, plan, qx, x_scale, qw, w_scale, m, n, k, y, ldy, part, s);
+    if (e == hipSuccess) e = fp8w8a8::launch_quant_rows(y, m, n, ldy, qy, y_scale, s);
+  }
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 

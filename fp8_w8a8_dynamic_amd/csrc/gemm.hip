@@ -393,11 +393,93 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   }
 }
 
+// The same sum and epilogue for one output row per workgroup, followed by
+// the per-token quantization of the bf16 row it produced (the next
+// Linear's input).  The row is spread over kRqWaves waves so that a row of
+// 4096 channels is one 16-byte vector (8 channels) per thread: wave w forms
+// the vectors (j * kRqWaves + w) * 64 + lane, j < NV, in registers -- the
+// splits added in split order and scaled as above -- and stores them as y;
+// then the row's magnitude maximum over those bf16 values (waves meeting
+// in LDS) and the quantizer's own device functions.  So y, codes and scale
+// are bit for bit those of splitk_reduce_kernel followed by the per-token
+// quantizer on y, with one launch and one read of the row fewer.
+constexpr int kRqWaves = 8;
+
+template <int NV>
+__global__ __launch_bounds__(64 * kRqWaves) void splitk_reduce_quant_kernel(
+    const float* __restrict__ part, int splits, const float* __restrict__ sx,
+    const float* __restrict__ sw, int M, int N, uint16_t* __restrict__ y,
+    int64_t ldy, uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ uint32_t wmax[kRqWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
+  const int64_t plane = static_cast<int64_t>(M) * N;
+  const float* p = part + row * N;
+  const float xs = sx[row];
+  const auto yr = row_rsrc(y + row * ldy, static_cast<uint32_t>(N) * 2u);
+  uint4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = ((j * kRqWaves + wave) * 64 + lane) * 8;
+    v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < N) {
+      float4 a = *reinterpret_cast<const float4*>(p + c);
+      float4 b = *reinterpret_cast<const float4*>(p + c + 4);
+      for (int sp = 1; sp < splits; ++sp) {
+        const float4 u = *reinterpret_cast<const float4*>(p + sp * plane + c);
+        const float4 t = *reinterpret_cast<const float4*>(p + sp * plane + c + 4);
+        a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+        b.x += t.x; b.y += t.y; b.z += t.z; b.w += t.w;
+      }
+      const float4 wa = *reinterpret_cast<const float4*>(sw + c);
+      const float4 wb = *reinterpret_cast<const float4*>(sw + c + 4);
+      v[j].x = pack_bf16x2(a.x * wa.x * xs, a.y * wa.y * xs);
+      v[j].y = pack_bf16x2(a.z * wa.z * xs, a.w * wa.w * xs);
+      v[j].z = pack_bf16x2(b.x * wb.x * xs, b.y * wb.y * xs);
+      v[j].w = pack_bf16x2(b.z * wb.z * xs, b.w * wb.w * xs);
+      buf_store16(v[j], yr, static_cast<uint32_t>(c) * 2u);
+    }
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    mx = pk_max_u16(mx, bf16x2_abs_bits(v[j].x));
+    mx = pk_max_u16(mx, bf16x2_abs_bits(v[j].y));
+    mx = pk_max_u16(mx, bf16x2_abs_bits(v[j].z));
+    mx = pk_max_u16(mx, bf16x2_abs_bits(v[j].w));
+  }
+  const uint32_t mw = wave_max_u32(max(mx & 0xffffu, mx >> 16));
+  if (lane == 0) wmax[wave] = mw;
+  __syncthreads();
+  uint32_t mrow = wmax[0];
+#pragma unroll
+  for (int i = 1; i < kRqWaves; ++i) mrow = max(mrow, wmax[i]);
+  const float s = row_scale(__uint_as_float(mrow << 16));
+  const auto dst = row_rsrc(q + row * N, static_cast<uint32_t>(N));
+  quantize_row<NV>(v, make_divisor(s), [&](int j, uint2 cd) {
+    buf_store8(cd, dst, ((j * kRqWaves + wave) * 64 + lane) * 8u);
+  });
+  if (lane == 0 && wave == 0) scale[row] = s;
+}
+
+template <int NV>
+hipError_t launch_reduce_quant(const float* part, int splits, const float* sx,
+                               const float* sw, int64_t m, int64_t n, uint16_t* y,
+                               int64_t ldy, uint8_t* q, float* scale, hipStream_t stream) {
+  splitk_reduce_quant_kernel<NV>
+      <<<dim3(static_cast<uint32_t>(m)), dim3(64 * kRqWaves), 0, stream>>>(
+          part, splits, sx, sw, static_cast<int>(m), static_cast<int>(n), y, ldy, q, scale);
+  return hipGetLastError();
+}
+
+// With splits > 1 the GEMM stores float32 partial sums to `part`; `reduce`
+// then launches splitk_reduce_kernel (otherwise the caller reduces them).
 template <int BM, int BN, int WGM, int WGN, int NB, int MINB>
 hipError_t launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
                       const float* sw, int64_t m, int64_t n, int64_t k,
                       uint16_t* y, int64_t ldy, int splits, float* part,
-                      hipStream_t stream) {
+                      bool reduce, hipStream_t stream) {
   const int tiles_m = static_cast<int>((m + BM - 1) / BM);
   const int tiles_n = static_cast<int>((n + BN - 1) / BN);
   gemm_fp8_kernel<BM, BN, WGM, WGN, NB, MINB>
@@ -407,7 +489,7 @@ hipError_t launch_cfg(const uint8_t* qx, const float* sx, const uint8_t* qw,
           static_cast<int>(k), y, ldy, tiles_m, tiles_n,
           splits > 1 ? part : nullptr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || splits == 1 || !reduce) return e;
   int64_t blocks = (m * (n / 4) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   splitk_reduce_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream>>>(
@@ -478,23 +560,55 @@ size_t gemm_partial_bytes(const GemmPlan& p, int64_t m, int64_t n) {
   return p.splits > 1 ? static_cast<size_t>(p.splits) * m * n * sizeof(float) : 0;
 }
 
+namespace {
+
+hipError_t gemm_cfg(const GemmPlan& p, const uint8_t* qx, const float* sx,
+                    const uint8_t* qw, const float* sw, int64_t m, int64_t n,
+                    int64_t k, uint16_t* y, int64_t ldy, float* part, bool reduce,
+                    hipStream_t stream) {
+  const int sp = p.splits;
+  switch (p.cfg) {
+    case 0: return launch_cfg<256, 256, 2, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 1: return launch_cfg<256, 256, 2, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 2: return launch_cfg<128, 128, 2, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 3: return launch_cfg<256, 256, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 4: return launch_cfg<128, 128, 2, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 6: return launch_cfg<64, 128, 2, 2, 2, 3>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 7: return launch_cfg<64, 64, 2, 1, 2, 4>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 8: return launch_cfg<256, 192, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const GemmPlan& p, const uint8_t* qx, const float* sx,
                        const uint8_t* qw, const float* sw, int64_t m, int64_t n,
                        int64_t k, uint16_t* y, int64_t ldy, float* part,
                        hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
   if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
-  const int sp = p.splits;
-  switch (p.cfg) {
-    case 0: return launch_cfg<256, 256, 2, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 1: return launch_cfg<256, 256, 2, 4, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 2: return launch_cfg<128, 128, 2, 2, 2, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 3: return launch_cfg<256, 256, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 4: return launch_cfg<128, 128, 2, 2, 4, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 6: return launch_cfg<64, 128, 2, 2, 2, 3>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 7: return launch_cfg<64, 64, 2, 1, 2, 4>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    case 8: return launch_cfg<256, 192, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
-    default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, stream);
+  return gemm_cfg(p, qx, sx, qw, sw, m, n, k, y, ldy, part, true, stream);
+}
+
+hipError_t launch_gemm_requant(const GemmPlan& p, const uint8_t* qx, const float* sx,
+                               const uint8_t* qw, const float* sw, int64_t m, int64_t n,
+                               int64_t k, uint16_t* y, int64_t ldy, uint8_t* q,
+                               float* scale, float* part, hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+  if (p.splits == 1 || n > kRequantMaxN || n % 8 != 0) {
+    hipError_t e = gemm_cfg(p, qx, sx, qw, sw, m, n, k, y, ldy, part, true, stream);
+    return e == hipSuccess ? launch_quant_rows(y, m, n, ldy, q, scale, stream) : e;
+  }
+  hipError_t e = gemm_cfg(p, qx, sx, qw, sw, m, n, k, y, ldy, part, false, stream);
+  if (e != hipSuccess) return e;
+  // 512 vectors of 8 channels per j: NV = ceil(n / 4096) <= 4.
+  switch ((n + 4095) / 4096) {
+    case 1: return launch_reduce_quant<1>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    case 2: return launch_reduce_quant<2>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    case 3: return launch_reduce_quant<3>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    default: return launch_reduce_quant<4>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
   }
 }
 

@@ -92,6 +92,16 @@ hipError_t launch_gemm(const GemmPlan& p, const uint8_t* qx, const float* sx,
                        const uint8_t* qw, const float* sw, int64_t m, int64_t n,
                        int64_t k, uint16_t* y, int64_t ldy, float* part,
                        hipStream_t stream);
+// The GEMM with its bf16 output also quantized per token (codes q [m, n]
+// contiguous, one float32 scale per row): the same y, q and scale as
+// launch_gemm followed by launch_quant_rows on y.  Where the plan splits K
+// and n <= kRequantMaxN, one kernel adds the splits, writes y and quantizes
+// it (one launch and one read of y fewer).
+constexpr int64_t kRequantMaxN = 16384;
+hipError_t launch_gemm_requant(const GemmPlan& p, const uint8_t* qx, const float* sx,
+                               const uint8_t* qw, const float* sw, int64_t m, int64_t n,
+                               int64_t k, uint16_t* y, int64_t ldy, uint8_t* q,
+                               float* scale, float* part, hipStream_t stream);
 
 // Decode GEMV (m <= kGemvMaxM).  If x != nullptr the activations are
 // quantized inside the kernel (fused; only where gemv_fused_fits), otherwise

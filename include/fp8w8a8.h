@@ -243,6 +243,29 @@ int fp8w8a8_fp8_linear(const uint8_t* qx, const float* x_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same Linear with its output also quantized per token for the Linear
+ * that reads it next (the dynamic per-token activation quantization of
+ * README "FP8-Dynamic", applied to a layer's output where it is the next
+ * layer's input): y exactly as fp8w8a8_fp8_linear gives it, and qy, y_scale
+ * exactly as fp8w8a8_quantize_act_per_token(y) gives them.
+ *   qx, x_scale, qw, w_scale, y, ldy, workspace  as for fp8w8a8_fp8_linear
+ *                (the same workspace size)
+ *   qy           uint8 [m, n] E4M3 codes of y, contiguous          (output)
+ *   y_scale      float32 [m], amax of y's row / 448                (output)
+ * Where the matmul splits K (a few hundred tokens or less on the tiled
+ * GEMM) and n <= 16384, one kernel adds the splits, writes y and quantizes
+ * it; otherwise the Linear's kernel, then the quantizer on y.
+ * Rules as for fp8w8a8_fp8_linear; qy 16-byte and y_scale 4-byte aligned;
+ * y, qy and y_scale overlap neither one another, nor an input, nor the
+ * workspace.  Errors are returned before anything is launched.
+ */
+int fp8w8a8_fp8_linear_requant(const uint8_t* qx, const float* x_scale,
+                               const uint8_t* qw, const float* w_scale, int64_t m,
+                               int64_t n, int64_t k, uint16_t* y, int64_t ldy,
+                               uint8_t* qy, float* y_scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Fused FP8_DYNAMIC forward, bf16 in -> bf16 out: per-token quantization of
  * x (exactly as fp8w8a8_quantize_act_per_token) followed by
  * fp8w8a8_fp8_linear.  This is what a quantized Linear's forward is to its

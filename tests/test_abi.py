@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -247,6 +247,37 @@ def test_linear_validation(lib):
     assert lib.fp8w8a8_workspace_bytes(16, 4096, 4096, 0) == 0
     assert lib.fp8w8a8_workspace_bytes(4096, 4096, 4096, 0) == 0
     assert lib.fp8w8a8_workspace_bytes(64, 4096, 4096, 0) >= 2 * 64 * 4096 * 4
+
+
+def _req(lib, qx=A, sx=2 * A, qw=4 * A, sw=24 * A, m=64, n=4096, k=4096, y=32 * A,
+         ldy=4096, qy=40 * A, sy=44 * A, ws=48 * A, wsb=1 << 24):
+    # qw spans 16 MiB from 4 A; every other buffer fits in its 1-8 MiB slot
+    return lib.fp8w8a8_fp8_linear_requant(qx, sx, qw, sw, m, n, k, y, ldy, qy, sy, ws,
+                                          wsb, None)
+
+
+def test_linear_requant_validation(lib):
+    assert _req(lib, qy=None) == ENULL
+    assert _req(lib, sy=None) == ENULL
+    assert _req(lib, y=None) == ENULL
+    assert _req(lib, n=24) == ESHAPE            # n % 16
+    assert _req(lib, k=192) == ESHAPE           # k % 128
+    assert _req(lib, ldy=4088) == ESHAPE        # ldy < n
+    assert _req(lib, qy=40 * A + 8) == EALIGN
+    assert _req(lib, sy=44 * A + 2) == EALIGN
+    assert _req(lib, qy=32 * A + 64) == EALIAS  # codes inside y
+    assert _req(lib, sy=40 * A + 64) == EALIAS  # scales inside the codes
+    assert _req(lib, sy=32 * A) == EALIAS       # scales inside y
+    assert _req(lib, qy=A) == EALIAS            # codes over the input codes
+    assert _req(lib, sy=24 * A) == EALIAS       # scales over the weight scales
+    assert _req(lib, y=8 * A) == EALIAS         # y inside the weight codes
+    # m = 64: the GEMM splits K, so the partial sums need the workspace,
+    # which must not overlap any output
+    assert _req(lib, ws=None, wsb=0) == EWS
+    assert _req(lib, wsb=1024) == EWS
+    assert _req(lib, ws=40 * A) == EALIAS
+    assert _req(lib, m=0) == OK
+    assert _req(lib, n=0) == OK
 
 
 def test_quant_linear_validation(lib):

@@ -438,3 +438,47 @@ def test_m1_kernel_matches_lds_staged_kernel(n, k, rows, monkeypatch):
     rqx, rsx = oracle.quant_act_ref(x)
     rqw, rsw = oracle.quant_weight_ref(w)
     check_close(y_new, oracle.linear_ref(rqx, rsx, rqw, rsw), f"m1 kernel vs oracle n={n} k={k}")
+
+
+# fp8w8a8_fp8_linear_requant: K-split shapes, where one kernel adds the
+# splits, writes y and quantizes it (n up to 16384), and shapes on the other
+# paths (GEMV, token-group GEMV, unsplit GEMM: the Linear, then the
+# quantizer).  Each has a zero row (scale 0, codes 0).
+REQUANT = [(64, 4096, 12288), (256, 4096, 12288), (64, 1024, 4096), (100, 1040, 1152),
+           (1, 1024, 4096), (17, 640, 1024), (4096, 512, 256)]
+
+
+def _check_requant(m, n, k, seed, what):
+    qx, sx, qw, sw = _rand_operands(m, n, k, seed)
+    if m > 3:
+        qx[3] = 0
+    dev = (to_dev_u8(qx), to_dev_f32(sx), to_dev_u8(qw), to_dev_f32(sw))
+    y, qy, sy = fq.fp8_linear_requant(*dev)
+    y2 = fq.fp8_linear(*dev)
+    q2, s2 = fq.quantize_act_per_token(y2)
+    torch.cuda.synchronize()
+    yb = host_bits(y)
+    check_bytes(yb, host_bits(y2), f"{what}: y against fp8_linear")
+    check_bytes(host_bits(qy), host_bits(q2), f"{what}: codes against the quantizer on y")
+    check_bytes(host_bits(sy).view(np.uint32), host_bits(s2).view(np.uint32),
+                f"{what}: scales against the quantizer on y")
+    rq, rs = oracle.quant_act_ref(yb)
+    check_bytes(host_bits(qy), rq, f"{what}: codes against the oracle")
+    check_bytes(host_bits(sy).view(np.uint32), rs.view(np.uint32),
+                f"{what}: scales against the oracle")
+    check_close(yb, oracle.linear_ref(qx, sx, qw, sw), f"{what}: y against the oracle")
+
+
+@pytest.mark.parametrize("m,n,k", REQUANT)
+def test_fp8_linear_requant(m, n, k):
+    _check_requant(m, n, k, 5 * m + n + k, f"requant {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k,splits", [(64, 2048, 4096, 8), (33, 16384, 1024, 3),
+                                          (130, 656, 2048, 5)])
+def test_fp8_linear_requant_forced_splits(m, n, k, splits, monkeypatch):
+    """More K splits than the planner picks (the 128x64 configuration),
+    the longest row the fused kernel takes (n = 16384) and a ragged one."""
+    monkeypatch.setenv("FP8W8A8_GEMM_CONFIG", "5")
+    monkeypatch.setenv("FP8W8A8_GEMM_SPLITS", str(splits))
+    _check_requant(m, n, k, 11 * m + n + splits, f"requant {m}x{n}x{k} {splits} splits")

@@ -109,24 +109,27 @@ def _gpu_chain(qws, x0_bits):
 
 
 def _gpu_chain_grouped(qws, tiled, x0_bits):
-    """The stack through the grouped call: per layer one quantization of
-    X_l, one launch for the six Linears that read it, then down.  Same
-    record per layer as _gpu_chain."""
+    """The stack through the grouped call: per layer one launch for the six
+    Linears that read X_l, one quantization of up's output, then down,
+    which re-quantizes its output for the next layer in the same call
+    (fp8_linear_requant: at M = 64 its K splits are added, written and
+    quantized by one kernel).  Same record per layer as _gpu_chain; the
+    codes and scales of X_l past layer 0 are down's."""
     ns = [LAYER_SHAPES[j][1] for j in range(6)]
     x = to_dev_bf16(x0_bits)
+    qx, sx = fq.quantize_act_per_token(x)
     rec = []
     for layer in range(LAYERS):
-        qx, sx = fq.quantize_act_per_token(x)
         outs = fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[layer],
                                    [qws[layer][j][1] for j in range(6)], ns)
         ys = dict(enumerate(outs))
         qu, su = fq.quantize_act_per_token(ys[UP])
         qw, sw = qws[layer][DOWN]
-        ys[DOWN] = fq.fp8_linear(qu, su, qw, sw)
+        ys[DOWN], qn, sn = fq.fp8_linear_requant(qu, su, qw, sw)
         rec.append({"x": host_bits(x), "qx": host_bits(qx), "sx": host_bits(sx),
                     "qu": host_bits(qu), "su": host_bits(su),
                     "y": {j: host_bits(t) for j, t in ys.items()}})
-        x = ys[DOWN]
+        x, qx, sx = ys[DOWN], qn, sn
     torch.cuda.synchronize()
     return rec, host_bits(x)
 
