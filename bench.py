@@ -556,34 +556,62 @@ def bench_stack(torch, fq, m, passes):
     warm_for(torch, gp.replay)
     t_packed = time_events(torch, gp.replay, passes)
     del gp, packed
-    # At up to 64 tokens: the six Linears that read the layer input in one
-    # grouped launch (weights tiled offline), then down's input quantized
-    # and down, which re-quantizes its output as the next layer's input.
+    # At up to 64 tokens, on weights tiled offline: per layer q, o, gate and
+    # up in one grouped launch (one round of 64-row units), up's output
+    # quantized, then down -- its K summed in ranges that are units of
+    # their own -- beside k and v in a second grouped launch, whose ranges
+    # one kernel adds, writes and re-quantizes as the next layer's input.
+    # Also timed: the six Linears that read the layer input in one launch,
+    # then down through fp8_linear_requant (the previous arrangement).
     grouped = None
     if m <= 64:
-        tiled = [[fq.tile_weights(lw[j][0]) for j in range(6)] for lw in layers]
-        ns = [n for _, n, _ in LAYER_SHAPES[:6]]
+        tiled = [[fq.tile_weights(lw[j][0]) for j in range(7)] for lw in layers]
+        ns = [n for _, n, _ in LAYER_SHAPES]
+        first, second = (0, 3, 4, 5), (6, 1, 2)
+        ws3 = torch.empty(8 * m * 4096 * 4, dtype=torch.uint8, device="cuda")
 
         def grouped_pass():
             qx, sx = fq.quantize_act_per_token(xs[0])
             for li, lw in enumerate(layers):
-                fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[li], [lw[j][1] for j in range(6)],
-                                    ns, outs=ys[:6])
+                fq.fp8_linear_group([qx] * 4, [sx] * 4, [tiled[li][j] for j in first],
+                                    [lw[j][1] for j in first], [ns[j] for j in first],
+                                    outs=[ys[j] for j in first])
+                qu, su = fq.quantize_act_per_token(ys[5])
+                # (The last layer's output is re-quantized too: a few KB.)
+                _, qx, sx = fq.fp8_linear_group_requant(
+                    [qu, qx, qx], [su, sx, sx], [tiled[li][j] for j in second],
+                    [lw[j][1] for j in second], [ns[j] for j in second], 0,
+                    outs=[xs[li + 1], ys[1], ys[2]], workspace=ws3)
+
+        def grouped_six_pass():
+            qx, sx = fq.quantize_act_per_token(xs[0])
+            for li, lw in enumerate(layers):
+                fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[li][:6],
+                                    [lw[j][1] for j in range(6)], ns[:6], outs=ys[:6])
                 qu, su = fq.quantize_act_per_token(ys[5])
                 qx, sx = down_of(li, qu, su, lw[6][0], lw[6][1], ws2)
 
-        for _ in range(2):
-            grouped_pass()
-        gg = graph_of(torch, grouped_pass, 1)
-        warm_for(torch, gg.replay)
-        t_grouped = time_events(torch, gg.replay, passes)
-        del gg, tiled
+        timed = {}
+        for name, fn in (("grouped", grouped_pass), ("six", grouped_six_pass)):
+            for _ in range(2):
+                fn()
+            gg = graph_of(torch, fn, 1)
+            warm_for(torch, gg.replay)
+            timed[name] = time_events(torch, gg.replay, passes)
+            del gg
+        del tiled
+        t_grouped = timed["grouped"]
         grouped = {"ms_per_pass": round(t_grouped * 1e3, 4),
                    "gbs": None, "frac_of_hbm": None,
                    "us_per_layer": round(t_grouped * 1e6 / 36, 2),
-                   "what": "q, k, v, o, gate, up in one grouped launch on MFMA-tiled "
-                           "weights, up's output quantized, then down, which re-quantizes "
-                           "its output as the next layer's input"}
+                   "what": "per layer q, o, gate, up in one grouped launch on MFMA-tiled "
+                           "weights, up's output quantized, then down (K summed in ranges "
+                           "spread over the launch) beside k and v in a second grouped "
+                           "launch, down's output re-quantized as the next layer's input",
+                   "six_in_one_launch": {
+                       "ms_per_pass": round(timed["six"] * 1e3, 4),
+                       "what": "q, k, v, o, gate, up in one grouped launch, up's output "
+                               "quantized, then down through fp8_linear_requant"}}
     nbytes = 36 * sum(n * k + 4 * n + 2 * m * k + 2 * m * n for _, n, k in LAYER_SHAPES)
     flops = 36 * sum(2 * m * n * k for _, n, k in LAYER_SHAPES)
     if grouped is not None:

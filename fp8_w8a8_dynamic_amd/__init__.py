@@ -13,8 +13,9 @@ marshalling only).
 """
 
 from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear, fp8_linear_requant,
-                      fp8_linear_group, init_workspace, kv_dequantize_fp8, kv_quantize_fp8,
-                      kv_quantize_int8, kv_read_int8, load_library,
+                      fp8_linear_group, fp8_linear_group_requant, init_workspace,
+                      kv_dequantize_fp8, kv_quantize_fp8, kv_quantize_int8, kv_read_int8,
+                      load_library,
                       quant_linear, quant_linear_group_m1, quant_linear_noalloc,
                       quantize_act_group, quantize_act_per_token,
                       rmsnorm_quant_linear,
@@ -23,7 +24,8 @@ from .binding import (LIBRARY_PATH, SIGNATURES, Fp8W8A8Error, fp8_linear, fp8_li
                       workspace_bytes)
 
 __all__ = ["LIBRARY_PATH", "SIGNATURES", "Fp8W8A8Error", "fp8_linear",
-           "fp8_linear_group", "tile_weights", "fp8_linear_requant",
+           "fp8_linear_group", "fp8_linear_group_requant", "tile_weights",
+           "fp8_linear_requant",
            "init_workspace", "kv_dequantize_fp8", "kv_quantize_fp8",
            "kv_quantize_int8", "kv_read_int8",
            "load_library", "quant_linear", "quant_linear_group_m1",

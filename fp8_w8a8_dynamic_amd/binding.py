@@ -61,6 +61,11 @@ SIGNATURES = {
         (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "fp8w8a8_fp8_linear_group":
         (ctypes.c_int, [_c_vp, ctypes.c_int, _c_i64, _c_vp]),
+    "fp8w8a8_group_requant_workspace_bytes":
+        (_c_sz, [_c_vp, ctypes.c_int, _c_i64, ctypes.c_int]),
+    "fp8w8a8_fp8_linear_group_requant":
+        (ctypes.c_int, [_c_vp, ctypes.c_int, _c_i64, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                        _c_sz, _c_vp]),
     "fp8w8a8_rmsnorm_quant_linear":
         (ctypes.c_int, [_c_vp, _c_i64, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_i64,
                         _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
@@ -625,13 +630,8 @@ class _GroupFp8Linear(ctypes.Structure):
                 ("y", _c_vp), ("n", _c_i64), ("k", _c_i64)]
 
 
-def fp8_linear_group(qxs, x_scales, qws_tiled, w_scales, ns, outs=None):
-    """Several Linears on given codes at one token count M (1..64) in one
-    launch: outs[i] bf16 [M, ns[i]] = fp8_linear(qxs[i], x_scales[i], W_i,
-    w_scales[i]) up to float32 summation order, with qws_tiled[i] =
-    tile_weights(W_i).  Items may share qx and x_scale (pass the same
-    tensors)."""
-    lib = load_library()
+def _group_items(qxs, x_scales, qws_tiled, w_scales, ns, outs):
+    """The items array of a grouped call on given codes, with the outputs."""
     count = len(qxs)
     if (not (len(x_scales) == len(qws_tiled) == len(w_scales) == len(ns) == count)
             or (outs is not None and len(outs) != count)):
@@ -659,11 +659,47 @@ def fp8_linear_group(qxs, x_scales, qws_tiled, w_scales, ns, outs=None):
         items[i] = _GroupFp8Linear(qx.data_ptr(), sx.data_ptr(), qt.data_ptr(),
                                    sw.data_ptr(), y.data_ptr(), n, k)
         ys.append(y)
-    if count == 0:
+    return items, ys, m0
+
+
+def fp8_linear_group(qxs, x_scales, qws_tiled, w_scales, ns, outs=None):
+    """Several Linears on given codes at one token count M (1..64) in one
+    launch: outs[i] bf16 [M, ns[i]] = fp8_linear(qxs[i], x_scales[i], W_i,
+    w_scales[i]) up to float32 summation order, with qws_tiled[i] =
+    tile_weights(W_i).  Items may share qx and x_scale (pass the same
+    tensors)."""
+    lib = load_library()
+    items, ys, m0 = _group_items(qxs, x_scales, qws_tiled, w_scales, ns, outs)
+    if not ys:
         return ys
-    _check(lib.fp8w8a8_fp8_linear_group(items, count, m0, _stream_ptr(qxs[0].device)),
+    _check(lib.fp8w8a8_fp8_linear_group(items, len(ys), m0, _stream_ptr(qxs[0].device)),
            "fp8_linear_group")
     return ys
+
+
+def fp8_linear_group_requant(qxs, x_scales, qws_tiled, w_scales, ns, rq, outs=None,
+                             workspace=None):
+    """fp8_linear_group whose item rq also has its output quantized per
+    token (its K summed in ranges spread over the launch, then added in
+    order): returns (ys, qy float8_e4m3fn [M, ns[rq]], y_scale float32 [M]),
+    with (qy, y_scale) = quantize_act_per_token(ys[rq])."""
+    lib = load_library()
+    items, ys, m0 = _group_items(qxs, x_scales, qws_tiled, w_scales, ns, outs)
+    if not ys:
+        raise ValueError("at least one item")
+    count = len(ys)
+    if not 0 <= rq < count:
+        raise ValueError(f"rq must index one of the {count} items")
+    dev = ys[0].device
+    qy = torch.empty((m0, ns[rq]), dtype=torch.uint8, device=dev)
+    sy = torch.empty((m0,), dtype=torch.float32, device=dev)
+    need = int(lib.fp8w8a8_group_requant_workspace_bytes(items, count, m0, rq))
+    ws = _pick_workspace(dev, need, workspace)
+    _check(lib.fp8w8a8_fp8_linear_group_requant(
+        items, count, m0, rq, qy.data_ptr(), sy.data_ptr(),
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream_ptr(dev)), "fp8_linear_group_requant")
+    return ys, qy.view(torch.float8_e4m3fn), sy
 
 
 def rmsnorm_quant_linear(x, gamma, eps, qw, w_scale, out=None, workspace=None):

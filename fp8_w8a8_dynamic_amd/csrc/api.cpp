@@ -320,6 +320,65 @@ int quant_linear_impl(const uint16_t* x, int64_t ldx, const uint8_t* qw,
 
 }  // namespace
 
+namespace {
+
+// Shared validation of fp8w8a8_fp8_linear_group's items (also the items of
+// the re-quantizing variant): shapes, alignment and the overlap of every
+// output with every input and with the other outputs.
+int check_group_items(const fp8w8a8_group_fp8_linear* items, int count, int64_t m,
+                      fp8w8a8::TokLinear* g) {
+  if (!items) return FP8W8A8_ERR_NULL;
+  if (count < 1 || count > fp8w8a8::kGroupMax || m < 1 || m > fp8w8a8::kTokGroupMaxM)
+    return FP8W8A8_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    const fp8w8a8_group_fp8_linear& L = items[i];
+    if (!L.qx || !L.x_scale || !L.qw_tiled || !L.w_scale || !L.y) return FP8W8A8_ERR_NULL;
+    if (L.n < 64 || L.n > (int64_t{1} << 24) || L.n % 64 != 0 || L.k < 128 ||
+        L.k > fp8w8a8::kTokGroupMaxK || L.k % 128 != 0)
+      return FP8W8A8_ERR_SHAPE;
+    if (!aligned16(L.qx) || !aligned16(L.x_scale) || !aligned16(L.qw_tiled) ||
+        !aligned16(L.w_scale) || !aligned16(L.y))
+      return FP8W8A8_ERR_ALIGN;
+    g[i] = fp8w8a8::TokLinear{L.qx, L.x_scale, L.qw_tiled, L.w_scale, L.y, L.n, L.k};
+  }
+  for (int i = 0; i < count; ++i) {
+    const Range ry = span(items[i].y, m, items[i].n, items[i].n, 2);
+    for (int j = 0; j < count; ++j) {
+      const fp8w8a8_group_fp8_linear& L = items[j];
+      if (overlap(ry, span(L.qx, m, L.k, L.k, 1)) ||
+          overlap(ry, span(L.x_scale, m, 1, 1, 4)) ||
+          overlap(ry, span(L.qw_tiled, L.n, L.k, L.k, 1)) ||
+          overlap(ry, span(L.w_scale, L.n, 1, 1, 4)) ||
+          (j != i && overlap(ry, span(L.y, m, L.n, L.n, 2))))
+        return FP8W8A8_ERR_ALIAS;
+    }
+  }
+  return FP8W8A8_OK;
+}
+
+// Shape rules of the re-quantized item; its split count and workspace.
+int group_requant_plan(const fp8w8a8_group_fp8_linear* items, int count, int64_t m,
+                       int rq, fp8w8a8::TokLinear* g, int* splits, size_t* bytes) {
+  int st = check_group_items(items, count, m, g);
+  if (st != FP8W8A8_OK) return st;
+  if (rq < 0 || rq >= count || items[rq].n > fp8w8a8::kRequantMaxN) return FP8W8A8_ERR_SHAPE;
+  *splits = fp8w8a8::tok_group_splits(g, count, m, rq);
+  *bytes = static_cast<size_t>(*splits) * static_cast<size_t>(m) *
+           static_cast<size_t>(items[rq].n) * sizeof(float);
+  return FP8W8A8_OK;
+}
+
+}  // namespace
+
+namespace {
+
+bool kv_group_ok(int64_t width, int64_t group) {
+  return group >= 8 && group <= 512 && (group & (group - 1)) == 0 &&
+         width % group == 0;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fp8w8a8_status_string(int status) {
@@ -421,11 +480,6 @@ int fp8w8a8_swiglu_quantize(const uint16_t* gate, int64_t ldg,
                                               h_scale, h, ldh,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
-}
-
-bool kv_group_ok(int64_t width, int64_t group) {
-  return group >= 8 && group <= 512 && (group & (group - 1)) == 0 &&
-         width % group == 0;
 }
 
 int fp8w8a8_kv_quantize_fp8(const uint16_t* kv, int64_t rows, int64_t width,
@@ -741,36 +795,59 @@ int fp8w8a8_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* tiled
 
 int fp8w8a8_fp8_linear_group(const fp8w8a8_group_fp8_linear* items, int count,
                              int64_t m, void* stream) {
-  if (!items) return FP8W8A8_ERR_NULL;
-  if (count < 1 || count > fp8w8a8::kGroupMax || m < 1 || m > fp8w8a8::kTokGroupMaxM)
-    return FP8W8A8_ERR_SHAPE;
   fp8w8a8::TokLinear g[fp8w8a8::kGroupMax];
-  for (int i = 0; i < count; ++i) {
-    const fp8w8a8_group_fp8_linear& L = items[i];
-    if (!L.qx || !L.x_scale || !L.qw_tiled || !L.w_scale || !L.y) return FP8W8A8_ERR_NULL;
-    if (L.n < 64 || L.n > (int64_t{1} << 24) || L.n % 64 != 0 || L.k < 128 ||
-        L.k > fp8w8a8::kTokGroupMaxK || L.k % 128 != 0)
-      return FP8W8A8_ERR_SHAPE;
-    if (!aligned16(L.qx) || !aligned16(L.x_scale) || !aligned16(L.qw_tiled) ||
-        !aligned16(L.w_scale) || !aligned16(L.y))
-      return FP8W8A8_ERR_ALIGN;
-    g[i] = fp8w8a8::TokLinear{L.qx, L.x_scale, L.qw_tiled, L.w_scale, L.y, L.n, L.k};
-  }
-  for (int i = 0; i < count; ++i) {
-    const Range ry = span(items[i].y, m, items[i].n, items[i].n, 2);
+  int st = check_group_items(items, count, m, g);
+  if (st != FP8W8A8_OK) return st;
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_tok_group(g, count, m, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
+}
+
+size_t fp8w8a8_group_requant_workspace_bytes(const fp8w8a8_group_fp8_linear* items,
+                                             int count, int64_t m, int rq) {
+  fp8w8a8::TokLinear g[fp8w8a8::kGroupMax];
+  int splits = 0;
+  size_t bytes = 0;
+  return group_requant_plan(items, count, m, rq, g, &splits, &bytes) == FP8W8A8_OK ? bytes
+                                                                                  : 0;
+}
+
+int fp8w8a8_fp8_linear_group_requant(const fp8w8a8_group_fp8_linear* items, int count,
+                                     int64_t m, int rq, uint8_t* qy, float* y_scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  fp8w8a8::TokLinear g[fp8w8a8::kGroupMax];
+  int splits = 0;
+  size_t need = 0;
+  int st = group_requant_plan(items, count, m, rq, g, &splits, &need);
+  if (st != FP8W8A8_OK) return st;
+  if (!qy || !y_scale || !workspace) return FP8W8A8_ERR_NULL;
+  if (!aligned16(qy) || (reinterpret_cast<uintptr_t>(y_scale) & 3u) != 0 ||
+      !aligned16(workspace))
+    return FP8W8A8_ERR_ALIGN;
+  if (workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
+  // qy, y_scale and the workspace overlap no input, no y and one another.
+  const Range extra[3] = {span(qy, m, items[rq].n, items[rq].n, 1),
+                          span(y_scale, m, 1, 1, 4),
+                          Range{reinterpret_cast<uintptr_t>(workspace),
+                                reinterpret_cast<uintptr_t>(workspace) + need}};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(extra[a], extra[b])) return FP8W8A8_ERR_ALIAS;
     for (int j = 0; j < count; ++j) {
       const fp8w8a8_group_fp8_linear& L = items[j];
-      if (overlap(ry, span(L.qx, m, L.k, L.k, 1)) ||
-          overlap(ry, span(L.x_scale, m, 1, 1, 4)) ||
-          overlap(ry, span(L.qw_tiled, L.n, L.k, L.k, 1)) ||
-          overlap(ry, span(L.w_scale, L.n, 1, 1, 4)) ||
-          (j != i && overlap(ry, span(L.y, m, L.n, L.n, 2))))
+      if (overlap(extra[a], span(L.qx, m, L.k, L.k, 1)) ||
+          overlap(extra[a], span(L.x_scale, m, 1, 1, 4)) ||
+          overlap(extra[a], span(L.qw_tiled, L.n, L.k, L.k, 1)) ||
+          overlap(extra[a], span(L.w_scale, L.n, 1, 1, 4)) ||
+          overlap(extra[a], span(L.y, m, L.n, L.n, 2)))
         return FP8W8A8_ERR_ALIAS;
     }
   }
-  int st = check_device();
-  if (st != FP8W8A8_OK) return st;
-  hipError_t e = fp8w8a8::launch_tok_group(g, count, m, static_cast<hipStream_t>(stream));
+  if ((st = check_device()) != FP8W8A8_OK) return st;
+  hipError_t e = fp8w8a8::launch_tok_group_requant(
+      g, count, m, rq, splits, static_cast<float*>(workspace), qy, y_scale,
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8W8A8_OK : fail_hip(e);
 }
 

@@ -36,6 +36,7 @@
 // Rows beyond M or N read as zero (buffer descriptors bounded to the tile's
 // valid rows) and are never stored.  K must be a multiple of 128.
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -140,18 +141,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
 
   // Global -> LDS assignment.  One wave copy fills 1 KB of LDS = RPI rows of
   // 128 bytes; lane j lands at byte 16*j: row j / CH, physical chunk j % CH,
-  // which holds logical chunk (j % CH) ^ swz(row).
-  uint32_t a_off[S::A_LOADS], b_off[S::B_LOADS];
+  // which holds logical chunk (j % CH) ^ swz(row).  Copy number q (of the
+  // operand's q = wave * LOADS + i) covers rows 8q .. 8q + 7, so its row is
+  // 8q + lane / 8 and swz(row) = (4 (q & 1) + lane / 16) & 7: the offset is
+  // a lane part that depends only on the parity of q (two registers) plus
+  // the wave-uniform 8 q K, which goes with the stage's K into the copy's
+  // scalar offset.
+  static_assert(S::RPI == 8 && S::CH == 8, "128-byte stage rows");
+  uint32_t lane_off[2];
 #pragma unroll
-  for (int i = 0; i < S::A_LOADS; ++i) {
-    const int r = (wave * S::A_LOADS + i) * S::RPI + lane / S::CH;
-    a_off[i] = static_cast<uint32_t>(r * K + (((lane % S::CH) ^ swz(r)) * 16));
-  }
-#pragma unroll
-  for (int i = 0; i < S::B_LOADS; ++i) {
-    const int r = (wave * S::B_LOADS + i) * S::RPI + lane / S::CH;
-    b_off[i] = static_cast<uint32_t>(r * K + (((lane % S::CH) ^ swz(r)) * 16));
-  }
+  for (int par = 0; par < 2; ++par)
+    lane_off[par] = static_cast<uint32_t>((lane / S::CH) * K +
+                                          (((lane % S::CH) ^ ((4 * par + (lane >> 4)) & 7)) * 16));
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const uint32_t a_lds = lds0 + wave * S::A_LOADS * 1024;
   const uint32_t b_lds = lds0 + S::A_STAGE + wave * S::B_LOADS * 1024;
@@ -178,11 +179,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   // Copy c (0 <= c < COPIES) of the stage starting at K byte k0 into buffer
   // buf.
   auto copy = [&](int c, int buf, uint32_t k0) {
-    if (c < S::A_LOADS)
-      lds_copy16(a_rsrc, a_off[c], k0, a_lds + buf * S::STAGE + c * 1024);
-    else
-      lds_copy16(b_rsrc, b_off[c - S::A_LOADS], k0,
+    if (c < S::A_LOADS) {
+      const int q = wave * S::A_LOADS + c;
+      lds_copy16(a_rsrc, lane_off[q & 1], k0 + static_cast<uint32_t>(8 * q * K),
+                 a_lds + buf * S::STAGE + c * 1024);
+    } else {
+      const int q = wave * S::B_LOADS + (c - S::A_LOADS);
+      lds_copy16(b_rsrc, lane_off[q & 1], k0 + static_cast<uint32_t>(8 * q * K),
                  b_lds + buf * S::STAGE + (c - S::A_LOADS) * 1024);
+    }
   };
 
   // K split blockIdx.y of gridDim.y takes stages [kt0, kt0 + KT) (all of
@@ -247,18 +252,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   read_step(af0, bf0, smem, p0);
-  for (int kt = 0; kt < KT; ++kt) {
+  // One stage.  Whether it refills its buffer (stage kt + NB exists) and
+  // whether a next stage follows are compile-time flags: the steady-state
+  // loop below has neither branch, so the compiler's wait counts before
+  // the step-1 MFMAs only cover the fragments those MFMAs read (behind a
+  // branch its count merge was conservative and made them wait for the
+  // next stage's fragment reads as well).
+  auto stage = [&](int kt, auto refill_c, auto more_c) {
+    constexpr bool refill = decltype(refill_c)::value;
+    constexpr bool more = decltype(more_c)::value;
     const int buf = kt & (NB - 1);
+    // This stage's step-0 fragments (read under the previous stage's last
+    // MFMAs) have landed before its step-1 reads go out, so the step-0
+    // MFMAs below wait for nothing.
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     read_step(af1, bf1, smem + buf * S::STAGE, p1);
-    const bool refill = kt + NB < KT;
-    const bool more = kt + 1 < KT;
     const uint32_t next_k = kbase + static_cast<uint32_t>((kt + NB) * kBK);
+    // Source order is the schedule (reads, MFMAs and copies interleaved as
+    // described above): nothing moves across these points.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
       // Every wave holds this stage's fragments: the buffer takes stage
       // kt+NB.
-      if (i == kRel && refill) __syncthreads();
-      if (i == kNext && more) {
+      if (refill && i == kRel) __syncthreads();
+      if (more && i == kNext) {
         // Stage kt+1 has landed once only stages kt+2 .. kt+NB-1 and the
         // first kBefore copies of stage kt+NB are outstanding.
         if (refill)
@@ -267,6 +285,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         read_step(af0, bf0, smem + ((kt + 1) & (NB - 1)) * S::STAGE, p0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const int t = (i / S::TN) % S::TM, u = i % S::TN;
       if (i < T)
@@ -282,8 +301,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_kernel(
           if (c < S::COPIES) copy(c, buf, next_k);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  int kt = 0;
+  for (; kt + NB < KT; ++kt) stage(kt, yes{}, yes{});
+  for (; kt + 1 < KT; ++kt) stage(kt, no{}, yes{});
+  stage(kt, no{}, no{});
 
   // Epilogue.  The MFMAs ran with the weight fragment as the A operand, so
   // in the 32x32 accumulator layout a lane holds one token, (lane & 31) of
@@ -603,12 +629,21 @@ hipError_t launch_gemm_requant(const GemmPlan& p, const uint8_t* qx, const float
   }
   hipError_t e = gemm_cfg(p, qx, sx, qw, sw, m, n, k, y, ldy, part, false, stream);
   if (e != hipSuccess) return e;
+  return launch_splitk_reduce_quant(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
+}
+
+hipError_t launch_splitk_reduce_quant(const float* part, int splits, const float* sx,
+                                      const float* sw, int64_t m, int64_t n, uint16_t* y,
+                                      int64_t ldy, uint8_t* q, float* scale,
+                                      hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (n > kRequantMaxN || n % 8 != 0 || splits < 1) return hipErrorInvalidValue;
   // 512 vectors of 8 channels per j: NV = ceil(n / 4096) <= 4.
   switch ((n + 4095) / 4096) {
-    case 1: return launch_reduce_quant<1>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
-    case 2: return launch_reduce_quant<2>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
-    case 3: return launch_reduce_quant<3>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
-    default: return launch_reduce_quant<4>(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    case 1: return launch_reduce_quant<1>(part, splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    case 2: return launch_reduce_quant<2>(part, splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    case 3: return launch_reduce_quant<3>(part, splits, sx, sw, m, n, y, ldy, q, scale, stream);
+    default: return launch_reduce_quant<4>(part, splits, sx, sw, m, n, y, ldy, q, scale, stream);
   }
 }
 

@@ -73,13 +73,16 @@ constexpr uint32_t kPastEnd = 0x80000000u;  // an offset past every descriptor
 constexpr int kDepth = 2;                   // stages of weights requested ahead
 
 struct Item {
-  const uint8_t* qx;
+  const uint8_t* qx;  // codes of the item's first K byte (row stride ldx)
   const float* sx;
-  const uint8_t* qw;  // tiled
+  const uint8_t* qw;  // tiled: tiles of the item's K range, row blocks wrb bytes apart
   const float* sw;
   uint16_t* y;
-  int n, k;
-  int u0;  // first work unit of the item
+  float* part;  // non-null: raw float32 sums [M, n] here instead of y
+  int n, k;     // k: the K range the item sums over
+  int ldx;      // bytes between token rows of the codes (>= k)
+  int wrb;      // bytes between row blocks of the tiled weights (>= 16 k)
+  int u0;       // first work unit of the item
 };
 struct Args {
   Item it[kGroupMax];
@@ -156,15 +159,18 @@ __device__ __forceinline__ void load_codes(Codes<T>& xc, const Args& a, const Cu
   const Item& it = a.it[c.item];
   const int K = it.k;
   const int k0 = c.stage * kStageBytes;
-  const auto xr = row_rsrc(it.qx, static_cast<uint32_t>(M * K));
+  // The descriptor ends with token M - 1's last byte of the K range, so
+  // tokens past M read as zero.
+  const auto xr = row_rsrc(it.qx, static_cast<uint32_t>((M - 1) * it.ldx + K));
 #pragma unroll
   for (int j = 0; j < 2 * T; ++j) {
     // LDS slot p (16 bytes) = token p / 32, chunk (p % 32) ^ (token % 16).
     const int p = j * 256 + tid;
     const int tok = p >> 5;
     const int ch = (p & 31) ^ (tok & 15);
-    const bool ok = live && k0 + (ch >> 3) * 128 < K;
-    xc.x[j] = buf_load16(xr, ok ? static_cast<uint32_t>(tok * K + k0 + ch * 16) : kPastEnd);
+    const bool ok = live && k0 + (ch >> 3) * 128 < K && tok < M;
+    xc.x[j] = buf_load16(xr, ok ? static_cast<uint32_t>(tok * it.ldx + k0 + ch * 16)
+                                : kPastEnd);
   }
 }
 
@@ -175,7 +181,7 @@ __device__ __forceinline__ void load_weights(Weights& s, const Args& a, const Cu
   const int k0 = c.stage * kStageBytes;
   // The wave's row block: K / 128 consecutive 2 KB tiles.
   const int rb = (c.unit - it.u0) * 4 + wave;
-  const auto wr = row_rsrc(it.qw + static_cast<int64_t>(rb) * 16 * K,
+  const auto wr = row_rsrc(it.qw + static_cast<int64_t>(rb) * it.wrb,
                            static_cast<uint32_t>(16 * K));
 #pragma unroll
   for (int i = 0; i < kItemsPerStage; ++i)
@@ -243,6 +249,24 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
   const Item& it = a.it[c.item];
   const int N = it.n;
   const int lane = tid & 63, r = lane & 15, g = lane >> 4;
+  if (it.part != nullptr) {
+    // A K range of a split Linear: the raw sums, 4 consecutive channels of
+    // a token per lane (tokens past M dropped by the descriptor).  The
+    // branch is uniform over the workgroup and takes no barrier.
+    const int n0 = (c.unit - it.u0) * 64 + 16 * wave + 4 * g;
+    const auto pr = row_rsrc(it.part, static_cast<uint32_t>(M * N) * 4u);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const v4f v = acc[t];
+      // Default cache policy: the reduction reads them back right away.
+      __builtin_amdgcn_raw_buffer_store_b128(
+          v4u32_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                  __float_as_uint(v[3])},
+          pr, static_cast<int>(((16 * t + r) * N + n0) * 4), 0, 0);
+      acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const v4f v = acc[t];
@@ -427,28 +451,22 @@ hipError_t launch_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t*
   return hipGetLastError();
 }
 
-hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
-                            hipStream_t stream) {
+namespace {
+
+// Items sorted longest K first (the deal in rounds relies on it), their
+// units numbered in that order, and the launch at the token count's T.
+hipError_t launch_items(tokgroup::Item* list, int count, int64_t m, hipStream_t stream) {
   using namespace tokgroup;
-  if (count < 1 || count > kGroupMax || m < 1 || m > kTokGroupMaxM)
-    return hipErrorInvalidValue;
-  for (int i = 0; i < count; ++i)
-    if (items[i].n % 64 != 0 || items[i].k % 128 != 0 || items[i].k > kTokGroupMaxK)
-      return hipErrorInvalidValue;
-  // Longest rows first (the deal in rounds, below, relies on it).
-  int order[kGroupMax];
-  for (int i = 0; i < count; ++i) order[i] = i;
-  std::stable_sort(order, order + count,
-                   [&](int p, int q) { return items[p].k > items[q].k; });
+  std::stable_sort(list, list + count,
+                   [](const Item& p, const Item& q) { return p.k > q.k; });
   Args a{};
   a.count = count;
   a.m = static_cast<int>(m);
   int64_t units = 0;
   for (int i = 0; i < count; ++i) {
-    const TokLinear& L = items[order[i]];
-    a.it[i] = Item{L.qx, L.sx, L.qw, L.sw, L.y, static_cast<int>(L.n),
-                   static_cast<int>(L.k), static_cast<int>(units)};
-    units += L.n / 64;
+    a.it[i] = list[i];
+    a.it[i].u0 = static_cast<int>(units);
+    units += list[i].n / 64;
   }
   if (units <= 0 || units > (int64_t{1} << 30)) return hipErrorInvalidValue;
   a.units = static_cast<int>(units);
@@ -458,6 +476,86 @@ hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
     case 3: return launch_t<3>(a, stream);
     default: return launch_t<4>(a, stream);
   }
+}
+
+tokgroup::Item whole_item(const TokLinear& L) {
+  return tokgroup::Item{L.qx, L.sx, L.qw, L.sw, L.y, nullptr, static_cast<int>(L.n),
+                        static_cast<int>(L.k), static_cast<int>(L.k),
+                        static_cast<int>(16 * L.k), 0};
+}
+
+bool item_ok(const TokLinear& L) {
+  return L.n % 64 == 0 && L.n > 0 && L.k % 128 == 0 && L.k > 0 && L.k <= kTokGroupMaxK;
+}
+
+}  // namespace
+
+hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
+                            hipStream_t stream) {
+  using namespace tokgroup;
+  if (count < 1 || count > kGroupMax || m < 1 || m > kTokGroupMaxM)
+    return hipErrorInvalidValue;
+  Item list[kGroupMax];
+  for (int i = 0; i < count; ++i) {
+    if (!item_ok(items[i])) return hipErrorInvalidValue;
+    list[i] = whole_item(items[i]);
+  }
+  return launch_items(list, count, m, stream);
+}
+
+int tok_group_splits(const TokLinear* items, int count, int64_t m, int rq) {
+  (void)m;
+  if (count < 1 || count > kGroupMax || rq < 0 || rq >= count) return 1;
+  int64_t others = 0;
+  for (int i = 0; i < count; ++i)
+    if (i != rq) others += items[i].n / 64;
+  const int64_t ur = items[rq].n / 64;
+  const int kt = static_cast<int>(items[rq].k / 128);
+  const int room = count - 1;  // items left for the K ranges
+  int best = 1;
+  // The most K ranges (whole 512-byte stages each) that keep the launch at
+  // one workgroup per CU (256 CUs): measured on the 36-layer stack at 64
+  // tokens (down, K = 12288, beside k and v), 3 ranges (224 units) took
+  // 55.9 us per layer, 4 or 6 ranges (288 / 416 units, some CUs running two
+  // workgroups and so finishing last) 60.1 / 60.6 us, 2 ranges 60.1 us.
+  for (int s = 2; s <= kTokGroupMaxSplits && s <= kGroupMax - room; ++s)
+    if (kt % (4 * s) == 0 && others + s * ur <= 256) best = s;
+  if (const char* e = test_hook("FP8W8A8_TOKG_SPLITS")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= kTokGroupMaxSplits && v <= kGroupMax - room && kt % v == 0) best = v;
+  }
+  return best;
+}
+
+hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m, int rq,
+                                    int splits, float* part, uint8_t* qy, float* y_scale,
+                                    hipStream_t stream) {
+  using namespace tokgroup;
+  if (count < 1 || count > kGroupMax || m < 1 || m > kTokGroupMaxM || rq < 0 ||
+      rq >= count || splits < 1 || count - 1 + splits > kGroupMax)
+    return hipErrorInvalidValue;
+  const TokLinear& R = items[rq];
+  if (!item_ok(R) || R.n > kRequantMaxN || R.k % (128 * splits) != 0)
+    return hipErrorInvalidValue;
+  Item list[kGroupMax];
+  int c = 0;
+  for (int i = 0; i < count; ++i) {
+    if (i == rq) continue;
+    if (!item_ok(items[i])) return hipErrorInvalidValue;
+    list[c++] = whole_item(items[i]);
+  }
+  // K range j of the re-quantized Linear: codes from byte j * ks of each
+  // token row, the tiles from tile j * ks / 128 of each row block, raw
+  // sums into part[j].
+  const int64_t ks = R.k / splits;
+  for (int j = 0; j < splits; ++j)
+    list[c++] = Item{R.qx + j * ks, R.sx, R.qw + (j * ks / 128) * 2048, R.sw, R.y,
+                     part + j * m * R.n, static_cast<int>(R.n), static_cast<int>(ks),
+                     static_cast<int>(R.k), static_cast<int>(16 * R.k), 0};
+  hipError_t e = launch_items(list, c, m, stream);
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce_quant(part, splits, R.sx, R.sw, m, R.n, R.y, R.n, qy,
+                                    y_scale, stream);
 }
 
 }  // namespace fp8w8a8

@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 24
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(SIGNATURES) == names
@@ -519,3 +519,67 @@ def test_fp8_linear_group_validation(lib):
     # Valid, with the codes shared by both items: no device here.
     assert run([item(), item(qw=32 * A, sw=48 * A, y=64 * A)]) == EDEV
     assert run([item(n=64, k=128)], m=1) == EDEV
+
+
+def test_fp8_linear_group_requant_validation(lib):
+    """The grouped call with one item re-quantized: the items' rules, rq in
+    range with n <= 16384, the extra outputs' alignment and overlaps, and
+    the workspace, all checked before a launch; the workspace query gives
+    ranges x m x n x 4 bytes, 0 for invalid arguments."""
+    from fp8_w8a8_dynamic_amd.binding import _GroupFp8Linear
+
+    def arr(items):
+        return (_GroupFp8Linear * max(1, len(items)))(*items)
+
+    def ws_bytes(items, m=64, rq=0):
+        return lib.fp8w8a8_group_requant_workspace_bytes(arr(items), len(items), m, rq)
+
+    def run(items, m=64, rq=0, qy=80 * A, sy=96 * A, ws=112 * A, wsb=1 << 24):
+        return lib.fp8w8a8_fp8_linear_group_requant(arr(items), len(items), m, rq, qy, sy,
+                                                    ws, wsb, None)
+
+    # A is 1 MiB: down's weights (48 MiB) at 1024 A, k's and v's (4 MiB
+    # each) at 1100 A and 1110 A.
+    def item(qx=A, sx=2 * A, qw=1024 * A, sw=8 * A, y=16 * A, n=4096, k=12288):
+        return _GroupFp8Linear(qx, sx, qw, sw, y, n, k)
+
+    down = item()
+    kv = [item(qx=128 * A, sx=130 * A, qw=1100 * A, sw=134 * A, y=136 * A, n=1024, k=4096),
+          item(qx=128 * A, sx=130 * A, qw=1110 * A, sw=142 * A, y=144 * A, n=1024, k=4096)]
+    # Down alone (64 units): the most 512-byte-stage ranges that keep the
+    # launch at one workgroup per CU (256) is 4; beside k and v (32 units),
+    # 3 (3 x 64 + 32 <= 256).
+    assert ws_bytes([down]) == 4 * 64 * 4096 * 4
+    assert ws_bytes([down] + kv) == 3 * 64 * 4096 * 4
+    assert ws_bytes(kv + [down], rq=2) == 3 * 64 * 4096 * 4
+    assert ws_bytes([down], m=3) == 4 * 3 * 4096 * 4
+    assert ws_bytes([down], rq=1) == 0 and ws_bytes([down], rq=-1) == 0
+    assert ws_bytes([item(n=16384 + 64)]) == 0                  # n <= 16384
+    assert ws_bytes([item(n=96)]) == 0
+    assert lib.fp8w8a8_group_requant_workspace_bytes(None, 1, 64, 0) == 0
+    # K = 640: 5 tiles, no split into whole stages (one range).
+    assert ws_bytes([item(k=640)]) == 64 * 4096 * 4
+
+    assert lib.fp8w8a8_fp8_linear_group_requant(None, 1, 64, 0, 80 * A, 96 * A, 112 * A,
+                                                1 << 24, None) == ENULL
+    assert run([]) == ESHAPE and run([down] * 17) == ESHAPE
+    assert run([down], m=0) == ESHAPE and run([down], m=65) == ESHAPE
+    assert run([down], rq=1) == ESHAPE and run([down], rq=-1) == ESHAPE
+    assert run([item(n=16384 + 64)]) == ESHAPE
+    assert run([item(sx=None)]) == ENULL
+    assert run([down], qy=None) == ENULL and run([down], sy=None) == ENULL
+    assert run([down], ws=None) == ENULL
+    assert run([down], qy=80 * A + 8) == EALIGN and run([down], sy=96 * A + 2) == EALIGN
+    assert run([down], ws=112 * A + 8) == EALIGN
+    assert run([down], wsb=4 * 64 * 4096 * 4 - 1) == EWS
+    assert run([down], qy=A + 64) == EALIAS                     # qy over the codes
+    assert run([down], sy=16 * A + 4) == EALIAS                 # scales over y
+    assert run([down], ws=1030 * A) == EALIAS                   # workspace over weights
+    assert run([down], qy=112 * A + 4096) == EALIAS             # qy in the workspace
+    assert run([down] + kv, qy=136 * A) == EALIAS               # qy over k's y
+    # Item rules are the grouped call's (y over another item's codes).
+    assert run([down, item(qx=16 * A, qw=1200 * A, sw=202 * A, y=204 * A, n=64, k=128)]) \
+        == EALIAS
+    # Valid: no device here.
+    assert run([down]) == EDEV and run([down] + kv) == EDEV
+    assert run(kv + [down], rq=2) == EDEV

@@ -26,7 +26,10 @@ Frobenius drift reported, not asserted.
 At M = 64 the stack also runs as the grouped few-token path would serve it
 (the layer input quantized once, q, k, v, o, gate and up in one grouped
 launch on MFMA-tiled weights, up's output quantized, then down), held to
-the same teacher-forced checks on all 36 layers.
+the same teacher-forced checks on all 36 layers; and as the bench's grouped
+leg serves it (q, o, gate and up in one launch, up's output quantized, then
+down with its K split in ranges beside k and v in one launch, down's output
+re-quantized for the next layer), held to the same checks.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -120,12 +123,43 @@ def _gpu_chain_grouped(qws, tiled, x0_bits):
     qx, sx = fq.quantize_act_per_token(x)
     rec = []
     for layer in range(LAYERS):
-        outs = fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[layer],
+        outs = fq.fp8_linear_group([qx] * 6, [sx] * 6, tiled[layer][:6],
                                    [qws[layer][j][1] for j in range(6)], ns)
         ys = dict(enumerate(outs))
         qu, su = fq.quantize_act_per_token(ys[UP])
         qw, sw = qws[layer][DOWN]
         ys[DOWN], qn, sn = fq.fp8_linear_requant(qu, su, qw, sw)
+        rec.append({"x": host_bits(x), "qx": host_bits(qx), "sx": host_bits(sx),
+                    "qu": host_bits(qu), "su": host_bits(su),
+                    "y": {j: host_bits(t) for j, t in ys.items()}})
+        x, qx, sx = ys[DOWN], qn, sn
+    torch.cuda.synchronize()
+    return rec, host_bits(x)
+
+
+def _gpu_chain_grouped_split(qws, tiled, x0_bits):
+    """The stack as the bench's grouped leg serves it: per layer one launch
+    for q, o, gate and up (one round of 64-row units), one quantization of
+    up's output, then one launch for down -- its K summed in ranges that
+    are units of their own -- beside k and v, whose ranges one kernel adds,
+    writes and re-quantizes for the next layer (fp8_linear_group_requant).
+    Same record per layer as _gpu_chain."""
+    first = (Q, O, GATE, UP)
+    second = (DOWN, K_, V)
+    ns = [LAYER_SHAPES[j][1] for j in range(7)]
+    x = to_dev_bf16(x0_bits)
+    qx, sx = fq.quantize_act_per_token(x)
+    rec = []
+    for layer in range(LAYERS):
+        sws = [qws[layer][j][1] for j in range(7)]
+        outs = fq.fp8_linear_group([qx] * 4, [sx] * 4, [tiled[layer][j] for j in first],
+                                   [sws[j] for j in first], [ns[j] for j in first])
+        ys = dict(zip(first, outs))
+        qu, su = fq.quantize_act_per_token(ys[UP])
+        outs, qn, sn = fq.fp8_linear_group_requant(
+            [qu, qx, qx], [su, sx, sx], [tiled[layer][j] for j in second],
+            [sws[j] for j in second], [ns[j] for j in second], 0)
+        ys.update(zip(second, outs))
         rec.append({"x": host_bits(x), "qx": host_bits(qx), "sx": host_bits(sx),
                     "qu": host_bits(qu), "su": host_bits(su),
                     "y": {j: host_bits(t) for j, t in ys.items()}})
@@ -228,13 +262,15 @@ def test_stack_teacher_forced_every_layer(stack, m):
 
 
 @pytest.mark.timeout(900)
-def test_stack_grouped_teacher_forced_every_layer_m64(stack):
+@pytest.mark.parametrize("chain", ["grouped", "grouped_split"])
+def test_stack_grouped_teacher_forced_every_layer_m64(stack, chain):
     qws, ref = stack
     m = 64
-    tiled = [[fq.tile_weights(qws[layer][j][0]) for j in range(6)] for layer in range(LAYERS)]
+    tiled = [[fq.tile_weights(qws[layer][j][0]) for j in range(7)] for layer in range(LAYERS)]
     x0 = c4_x0(m)
-    rec, _ = _gpu_chain_grouped(qws, tiled, x0)
+    run = _gpu_chain_grouped if chain == "grouped" else _gpu_chain_grouped_split
+    rec, _ = run(qws, tiled, x0)
     del tiled
     torch.cuda.empty_cache()
     assert np.array_equal(rec[0]["x"], x0)
-    _check_layers(rec, ref, m, "grouped stack")
+    _check_layers(rec, ref, m, f"{chain} stack")

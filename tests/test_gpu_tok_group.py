@@ -18,6 +18,13 @@ GPU's up output), the decode layer's seven Linears at M = 4 and 8 in one
 launch after one grouped quantization, ragged shapes at M = 1 .. 64 (N = 64, K with a partial
 last 512-byte stage, tokens past the last full block of 16, zero and large
 rows), 16 items at the largest K, and the tiling alone on its edge shapes.
+
+fp8w8a8_fp8_linear_group_requant (one item's K summed in ranges, its output
+re-quantized): that item's output within the oracle's tolerance and its
+codes and scales bit-exact against the oracle's quantization of the GPU's
+output, the other items bit-identical to the grouped call without it; on
+layer 0 of the stack at M = 64 (down beside k and v, 1 to 8 ranges) and on
+ragged items.
 """
 
 import numpy as np
@@ -204,3 +211,95 @@ def test_tile_weights_bit_exact(n, k):
     t = fq.tile_weights(qw)
     torch.cuda.synchronize()
     check_bytes(host_bits(t), oracle.tile_weights_ref(host_bits(qw)), f"tile {n}x{k}")
+
+
+def _requant_check(ys, qy, sy, acts, weights, rq, what):
+    """Item rq's y within the oracle's tolerance and its codes and scales
+    bit-exact against the oracle's quantization of that y; returns every
+    item's output bits."""
+    out = []
+    for i, (y, a, w) in enumerate(zip(ys, acts, weights)):
+        yb = host_bits(y)
+        check_close(yb, oracle.linear_ref(a[0][0], a[0][1], w[1][0], w[1][1]),
+                    f"{what} item {i}")
+        out.append(yb)
+    rq_codes, rq_scales = oracle.quant_act_ref(out[rq])
+    check_bytes(host_bits(qy), rq_codes, f"{what} codes of item {rq}")
+    check_bytes(host_bits(sy).view(np.uint32), rq_scales.view(np.uint32),
+                f"{what} scales of item {rq}")
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_group_requant_stack_layer0_m64(monkeypatch):
+    """Layer 0 of the stack at M = 64 as the bench's grouped leg runs its
+    second launch: down (K = 12288, its K summed in ranges that are units
+    of their own) beside k and v, down's output re-quantized.  down within
+    tolerance of the oracle, its codes and scales bit-exact against the
+    oracle's quantization of the GPU's down output; k and v bit-identical
+    to the grouped call without down (each output one thread's sum over K).
+    The same for every range count from 1 to 8 (test hook), and bit-equal
+    on a second run."""
+    m = 64
+    x = c4_x0(m)
+    a = _codes(x)
+    wk, wv = _weights(c4_weight(0, 1)), _weights(c4_weight(0, 2))
+    ref_kv = _group([a, a], [wk, wv])
+    torch.cuda.synchronize()
+    ref_kv = [host_bits(t) for t in ref_kv]
+    wu = _weights(c4_weight(0, UP))
+    up = _group([a], [wu])[0]
+    torch.cuda.synchronize()
+    au = _codes(host_bits(up))
+    wd = _weights(c4_weight(0, 6))
+    acts, weights = [au, a, a], [wd, wk, wv]
+
+    def run():
+        ys, qy, sy = fq.fp8_linear_group_requant(
+            [t[1][0] for t in acts], [t[1][1] for t in acts], [w[0][0] for w in weights],
+            [w[0][1] for w in weights], [w[0][2] for w in weights], 0)
+        torch.cuda.synchronize()
+        return ys, qy, sy
+
+    base = _requant_check(*run(), acts, weights, 0, "group requant M = 64")
+    for i in (1, 2):
+        check_bytes(base[i], ref_kv[i - 1], f"group requant M = 64 item {i} against alone")
+    again = _requant_check(*run(), acts, weights, 0, "group requant M = 64, again")
+    check_bytes(again[0], base[0], "group requant M = 64 run twice")
+    for s in (1, 2, 3, 4, 6, 8):
+        monkeypatch.setenv("FP8W8A8_TOKG_SPLITS", str(s))
+        got = _requant_check(*run(), acts, weights, 0, f"group requant M = 64, {s} ranges")
+        monkeypatch.delenv("FP8W8A8_TOKG_SPLITS")
+        for i in (1, 2):
+            check_bytes(got[i], ref_kv[i - 1], f"{s} ranges item {i} against alone")
+
+
+@pytest.mark.parametrize("m", [1, 5, 17, 33, 64])
+@pytest.mark.parametrize("rq", [0, 2])
+def test_group_requant_ragged(m, rq, monkeypatch):
+    """Ragged items (zero and large token rows, K with a partial last
+    512-byte stage, N = 64) with the re-quantized item first or last; the
+    ranges checked on a persistent grid of 1 and 7 workgroups too."""
+    # (Items 0 and 1 share one code buffer, so they share K.)
+    shapes = ([(320, 1536), (64, 1536), (1024, 1152)] if rq == 0
+              else [(64, 640), (192, 640), (384, 1536)])
+    acts, weights = _ragged_inputs(m, 40 + m + rq, shapes)
+    def run():
+        ys, qy, sy = fq.fp8_linear_group_requant(
+            [t[1][0] for t in acts], [t[1][1] for t in acts], [w[0][0] for w in weights],
+            [w[0][1] for w in weights], [w[0][2] for w in weights], rq)
+        torch.cuda.synchronize()
+        return ys, qy, sy
+    base = _requant_check(*run(), acts, weights, rq, f"ragged requant M = {m}")
+    alone = _group([a for i, a in enumerate(acts) if i != rq],
+                   [w for i, w in enumerate(weights) if i != rq])
+    torch.cuda.synchronize()
+    others = [i for i in range(3) if i != rq]
+    for i, y in zip(others, alone):
+        check_bytes(base[i], host_bits(y), f"ragged requant M = {m} item {i} against alone")
+    for g in ("1", "7"):
+        monkeypatch.setenv("FP8W8A8_TOKG_GRID", g)
+        got = _requant_check(*run(), acts, weights, rq, f"ragged requant M = {m} grid {g}")
+        monkeypatch.delenv("FP8W8A8_TOKG_GRID")
+        for i in range(3):
+            check_bytes(got[i], base[i], f"ragged requant M = {m} grid {g} item {i}")
