@@ -230,9 +230,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int vmcnt_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
-// s_waitcnt immediate that waits until at most n LDS (and scalar memory)
-// operations are outstanding (vmcnt and expcnt left at their maxima).
-constexpr int lgkmcnt_imm(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
 
 // Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0).  Loads
 // at offsets >= bytes return zero.

@@ -50,6 +50,11 @@ typedef v4i_t v4i;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kGroupM = 4;
+
+// s_waitcnt immediate that waits until at most n LDS (and scalar memory)
+// operations are outstanding (gfx9 encoding; vmcnt and expcnt left at their
+// maxima).
+constexpr int lgkmcnt_imm(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
 constexpr int kBK = 128;     // K bytes per stage
 
 // Tile configuration: BM x BN output tile per workgroup of WGM x WGN waves,

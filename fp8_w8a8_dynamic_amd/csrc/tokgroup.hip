@@ -291,30 +291,33 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
   }
 }
 
-// Step I of the stream (I counts modulo lcm(D + 1, 2)), computing stage C.
+// Step I of the stream (I counts modulo lcm(D + 1, 2)), computing stage C,
+// with the codes requested DC stages ahead (ring slot (stage) % DC of X).
 // Vector-memory requests complete in order, so the issue order carries the
-// pipeline: the codes of stage C + 1 go out first, then the weights of
+// pipeline: the codes of stage C + DC go out first, then the weights of
 // stage C + D (ring slot (I + D) % (D + 1)).  Stage C is computed from
 // weight slot I % (D + 1) and LDS buffer I % 2; then the codes of C + 1 are
 // written to LDS buffer (I + 1) % 2 (nobody reads it since the previous
 // step's barrier) -- the wait for them also completes the weights
-// requested before them, up to stage C + D - 1, and leaves C + D's in
-// flight.  Every request is one the compiler tracks, so the waits it places
-// are exact.  Returns false once C was the workgroup's last stage.
-template <int I, int T, int D>
-__device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T>& X,
+// requested before them and leaves the later requests in flight.  Every
+// request is one the compiler tracks, so the waits it places are exact.
+// Returns false once C was the workgroup's last stage.
+template <int I, int T, int D, int DC>
+__device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T> (&X)[DC],
                                      uint8_t (*xs)[16 * T * kStageBytes], uint8_t* ob,
                                      Cursor (&Q)[D + 1], const Args& a, int M, int wave,
                                      int tid) {
+  static_assert(DC >= 1 && DC <= D, "codes at most as far ahead as the weights");
   // Q[0] = C, Q[j] = C + j (a unit past the end once the units run out).
   const int lane = tid & 63;
-  const bool more1 = Q[1].unit < a.units, moreD = Q[D].unit < a.units;
+  const bool more1 = Q[1].unit < a.units, moreC = Q[DC].unit < a.units,
+             moreD = Q[D].unit < a.units;
   const bool last = Q[0].stage == Q[0].stages - 1;
   // The epilogue's scales first: waiting for them completes nothing issued
   // after them.
   Scales<T> sc;
   if (last) load_scales(sc, a, Q[0], M, wave, lane);
-  load_codes(X, a, more1 ? Q[1] : Q[0], more1, M, tid);
+  load_codes(X[I % DC], a, moreC ? Q[DC] : Q[0], moreC, M, tid);
   load_weights(S[(I + D) % (D + 1)], a, moreD ? Q[D] : Q[0], moreD, wave, lane);
   // Keep the requests ahead of the MFMAs (the scheduler would otherwise
   // sink them below).
@@ -322,7 +325,7 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T
   compute_stage(acc, S[I % (D + 1)], xs[I % 2], lane);
   if (last) epilogue(acc, sc, a, Q[0], M, wave, tid, ob);
   if (!more1) return false;
-  store_codes(X, xs[(I + 1) % 2], tid);
+  store_codes(X[(I + 1) % DC], xs[(I + 1) % 2], tid);
   lds_barrier();
 #pragma unroll
   for (int j = 0; j < D; ++j) Q[j] = Q[j + 1];
@@ -330,17 +333,21 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T
   return true;
 }
 
-template <int T, int D, int... Is>
+template <int T, int D, int DC, int... Is>
 __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&acc)[T],
-                                      Weights (&S)[D + 1], Codes<T>& X,
+                                      Weights (&S)[D + 1], Codes<T> (&X)[DC],
                                       uint8_t (*xs)[16 * T * kStageBytes], uint8_t* ob,
                                       Cursor (&Q)[D + 1], const Args& a, int M, int wave,
                                       int tid) {
-  return (step<Is, T, D>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
+  return (step<Is, T, D, DC>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
 }
 
-template <int T, int D>
-__global__ __launch_bounds__(256, 2) void tok_group_kernel(const Args a) {
+// DC = 1: two workgroups per CU (two waves per SIMD, 256 registers each).
+// DC = 2: the codes two stages ahead as well, which takes one workgroup per
+// CU (a wave's registers beyond 256), for launches of at most one unit per
+// CU, where a workgroup's stage time is the codes' latency.
+template <int T, int D, int DC>
+__global__ __launch_bounds__(256, DC == 1 ? 2 : 1) void tok_group_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ob[16 * T * kOutRow];
   const int tid = static_cast<int>(threadIdx.x);
@@ -358,34 +365,40 @@ __global__ __launch_bounds__(256, 2) void tok_group_kernel(const Args a) {
     if (Q[j].unit < a.units) cursor_next(Q[j], a);
   }
   Weights S[D + 1];
-  Codes<T> X;
+  Codes<T> X[DC];
   v4f acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // Codes of stage 0 (into LDS buffer 0) and weights of stages 0 .. D - 1
-  // in flight.
-  load_codes(X, a, Q[0], true, M, tid);
+  // Codes of stage 0 (into LDS buffer 0), weights of stages 0 .. D - 1 and
+  // codes of stages 1 .. DC - 1 in flight.
+  load_codes(X[0], a, Q[0], true, M, tid);
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const bool live = Q[j].unit < a.units;
     load_weights(S[j], a, live ? Q[j] : Q[0], live, wave, lane);
   }
-  store_codes(X, xs[0], tid);
+#pragma unroll
+  for (int j = 1; j < DC; ++j) {
+    const bool live = Q[j].unit < a.units;
+    load_codes(X[j], a, live ? Q[j] : Q[0], live, M, tid);
+  }
+  store_codes(X[0], xs[0], tid);
   lds_barrier();
   constexpr int kPeriod = (D + 1) % 2 == 0 ? D + 1 : 2 * (D + 1);
-  while (steps<T, D>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, ob, Q, a,
-                     M, wave, tid)) {
+  static_assert(kPeriod % DC == 0, "code ring period");
+  while (steps<T, D, DC>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, ob, Q,
+                         a, M, wave, tid)) {
   }
   // Nothing in flight when the workgroup leaves (the last requests read
   // nothing, but their registers go with the workgroup).
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-template <int T, int D>
+template <int T, int D, int DC>
 hipError_t launch_d(Args a, hipStream_t stream) {
-  // Two workgroups per CU (LDS: 16 KB per token block; registers: two
-  // waves per SIMD), 256 CUs.
-  int64_t grid = std::min<int64_t>(a.units, 2 * 256);
+  // DC = 1: two workgroups per CU (LDS: 16 KB per token block; registers:
+  // two waves per SIMD); DC = 2: one.  256 CUs.
+  int64_t grid = std::min<int64_t>(a.units, (DC == 1 ? 2 : 1) * 256);
   if (const char* e = test_hook("FP8W8A8_TOKG_GRID")) {
     const int64_t v = std::atoll(e);
     if (v >= 1) grid = std::min<int64_t>(a.units, v);
@@ -405,15 +418,22 @@ hipError_t launch_d(Args a, hipStream_t stream) {
       const int end = i + 1 < a.count ? a.it[i + 1].u0 : a.units;
       a.shift += std::min<int>(end, static_cast<int>(grid)) - a.it[i].u0;
     }
-  tok_group_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
+  tok_group_kernel<T, D, DC><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
+// Codes two stages ahead (one workgroup per CU) when the launch has at most
+// one unit per CU, else one stage ahead (two workgroups per CU); test hooks
+// FP8W8A8_TOKG_CODES (1 or 2) and FP8W8A8_TOKG_DEPTH (2 or 3) override.
 template <int T>
 hipError_t launch_t(const Args& a, hipStream_t stream) {
   const char* e = test_hook("FP8W8A8_TOKG_DEPTH");
   const int d = e ? std::atoi(e) : kDepth;
-  return d == 3 ? launch_d<T, 3>(a, stream) : launch_d<T, 2>(a, stream);
+  const char* c = test_hook("FP8W8A8_TOKG_CODES");
+  const int dc = c ? std::atoi(c) : (a.units <= 256 ? 2 : 1);
+  if (dc == 2)
+    return d == 3 ? launch_d<T, 3, 2>(a, stream) : launch_d<T, 2, 2>(a, stream);
+  return d == 3 ? launch_d<T, 3, 1>(a, stream) : launch_d<T, 2, 1>(a, stream);
 }
 
 // The MFMA-tile permutation of a row-major [n, k] code matrix: one thread

@@ -162,10 +162,12 @@ def test_ragged_shapes(m, shapes, monkeypatch):
     acts, weights = _ragged_inputs(m, m, WIDE if shapes == "wide" else NARROW)
     base = _run_and_check(acts, weights, f"ragged {shapes} M = {m}")
     # The same bits on a persistent grid of 1, 2 and 7 workgroups (hundreds
-    # of units each, the pipeline running across unit boundaries) and with
-    # the weights requested three stages ahead instead of two.
+    # of units each, the pipeline running across unit boundaries), with
+    # the weights requested three stages ahead instead of two, and with the
+    # codes one and two stages ahead.
     for key, val in (("FP8W8A8_TOKG_GRID", "1"), ("FP8W8A8_TOKG_GRID", "2"),
-                     ("FP8W8A8_TOKG_GRID", "7"), ("FP8W8A8_TOKG_DEPTH", "3")):
+                     ("FP8W8A8_TOKG_GRID", "7"), ("FP8W8A8_TOKG_DEPTH", "3"),
+                     ("FP8W8A8_TOKG_CODES", "1"), ("FP8W8A8_TOKG_CODES", "2")):
         monkeypatch.setenv(key, val)
         ys = _group(acts, weights)
         torch.cuda.synchronize()
@@ -279,7 +281,8 @@ def test_group_requant_stack_layer0_m64(monkeypatch):
 def test_group_requant_ragged(m, rq, monkeypatch):
     """Ragged items (zero and large token rows, K with a partial last
     512-byte stage, N = 64) with the re-quantized item first or last; the
-    ranges checked on a persistent grid of 1 and 7 workgroups too."""
+    same bits on a persistent grid of 1 and 7 workgroups and with the codes
+    one and two stages ahead."""
     # (Items 0 and 1 share one code buffer, so they share K.)
     shapes = ([(320, 1536), (64, 1536), (1024, 1152)] if rq == 0
               else [(64, 640), (192, 640), (384, 1536)])
@@ -297,9 +300,10 @@ def test_group_requant_ragged(m, rq, monkeypatch):
     others = [i for i in range(3) if i != rq]
     for i, y in zip(others, alone):
         check_bytes(base[i], host_bits(y), f"ragged requant M = {m} item {i} against alone")
-    for g in ("1", "7"):
-        monkeypatch.setenv("FP8W8A8_TOKG_GRID", g)
-        got = _requant_check(*run(), acts, weights, rq, f"ragged requant M = {m} grid {g}")
-        monkeypatch.delenv("FP8W8A8_TOKG_GRID")
+    for key, val in (("FP8W8A8_TOKG_GRID", "1"), ("FP8W8A8_TOKG_GRID", "7"),
+                     ("FP8W8A8_TOKG_CODES", "1"), ("FP8W8A8_TOKG_CODES", "2")):
+        monkeypatch.setenv(key, val)
+        got = _requant_check(*run(), acts, weights, rq, f"ragged requant M = {m} {key}={val}")
+        monkeypatch.delenv(key)
         for i in range(3):
-            check_bytes(got[i], base[i], f"ragged requant M = {m} grid {g} item {i}")
+            check_bytes(got[i], base[i], f"ragged requant M = {m} {key}={val} item {i}")
