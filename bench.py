@@ -383,28 +383,50 @@ def bench_decode(torch, fq, reps, packed=False, m=DECODE_M):
             for L in c:
                 L["qt"] = fq.tile_weights(L["qw"])
 
+        # Down (K = 12288, three times the stages of the others) has its K
+        # summed in ranges that are units of their own in the launch, then
+        # added in order by one more kernel (fp8w8a8_fp8_linear_group_requant
+        # without re-quantization); also timed: the one launch unsplit.
+        wsd = torch.empty(8 * m * 4096 * 4, dtype=torch.uint8, device="cuda")
+
         def grouped_pass(layer):
+            qs = fq.quantize_act_group([L["x"] for L in layer])
+            fq.fp8_linear_group_requant(
+                [q for q, _ in qs], [sc for _, sc in qs], [L["qt"] for L in layer],
+                [L["sw"] for L in layer], [L["n"] for L in layer], 6,
+                outs=[L["y"] for L in layer], workspace=wsd, requant=False)
+
+        def unsplit_pass(layer):
             qs = fq.quantize_act_group([L["x"] for L in layer])
             fq.fp8_linear_group([q for q, _ in qs], [sc for _, sc in qs],
                                 [L["qt"] for L in layer], [L["sw"] for L in layer],
                                 [L["n"] for L in layer], outs=[L["y"] for L in layer])
-        gt = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            grouped_pass(copies[0])
+        timed = {}
+        for name, fn in (("split", grouped_pass), ("unsplit", unsplit_pass)):
+            gt = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                fn(copies[0])
+                torch.cuda.synchronize()
+                with torch.cuda.graph(gt, stream=cap):
+                    for c in copies:
+                        fn(c)
             torch.cuda.synchronize()
-            with torch.cuda.graph(gt, stream=cap):
-                for c in copies:
-                    grouped_pass(c)
-        torch.cuda.synchronize()
-        warm_for(torch, gt.replay)
-        tt, tslices = time_chunks(torch, gt.replay, reps)
-        tt /= DECODE_COPIES
+            warm_for(torch, gt.replay)
+            tt, tslices = time_chunks(torch, gt.replay, reps)
+            timed[name] = (tt / DECODE_COPIES, tslices)
+            del gt
+        tt, tslices = timed["split"]
+        tu = timed["unsplit"][0]
         grouped = {"us_per_layer": round(tt * 1e6, 3), "value": round(nbytes / tt / 1e9, 1),
                    "unit": "GB/s", "frac_of_hbm": round(nbytes / tt / 1e9 / HBM_PEAK_GBS, 4),
                    "slice_gbs": spread([nbytes * DECODE_COPIES / ts / 1e9 for ts in tslices]),
                    "what": "the 7 inputs quantized in one launch, then the 7 Linears in "
-                           "one grouped launch on MFMA-tiled weights"}
-        del gt
+                           "one grouped launch on MFMA-tiled weights, down's K summed in "
+                           "ranges spread over the launch and added by one more kernel",
+                   "unsplit": {"us_per_layer": round(tu * 1e6, 3),
+                               "value": round(nbytes / tu / 1e9, 1),
+                               "what": "the same with down's units unsplit (one launch "
+                                       "after the quantization)"}}
         for c in copies:
             for L in c:
                 L.pop("qt", None)

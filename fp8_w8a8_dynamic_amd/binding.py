@@ -678,11 +678,12 @@ def fp8_linear_group(qxs, x_scales, qws_tiled, w_scales, ns, outs=None):
 
 
 def fp8_linear_group_requant(qxs, x_scales, qws_tiled, w_scales, ns, rq, outs=None,
-                             workspace=None):
-    """fp8_linear_group whose item rq also has its output quantized per
-    token (its K summed in ranges spread over the launch, then added in
-    order): returns (ys, qy float8_e4m3fn [M, ns[rq]], y_scale float32 [M]),
-    with (qy, y_scale) = quantize_act_per_token(ys[rq])."""
+                             workspace=None, requant=True):
+    """fp8_linear_group whose item rq has its K summed in ranges spread over
+    the launch, then added in order, and (requant=True) its output quantized
+    per token: returns (ys, qy float8_e4m3fn [M, ns[rq]], y_scale float32
+    [M]) with (qy, y_scale) = quantize_act_per_token(ys[rq]), or (ys, None,
+    None) with requant=False."""
     lib = load_library()
     items, ys, m0 = _group_items(qxs, x_scales, qws_tiled, w_scales, ns, outs)
     if not ys:
@@ -691,14 +692,17 @@ def fp8_linear_group_requant(qxs, x_scales, qws_tiled, w_scales, ns, rq, outs=No
     if not 0 <= rq < count:
         raise ValueError(f"rq must index one of the {count} items")
     dev = ys[0].device
-    qy = torch.empty((m0, ns[rq]), dtype=torch.uint8, device=dev)
-    sy = torch.empty((m0,), dtype=torch.float32, device=dev)
+    qy = torch.empty((m0, ns[rq]), dtype=torch.uint8, device=dev) if requant else None
+    sy = torch.empty((m0,), dtype=torch.float32, device=dev) if requant else None
     need = int(lib.fp8w8a8_group_requant_workspace_bytes(items, count, m0, rq))
     ws = _pick_workspace(dev, need, workspace)
     _check(lib.fp8w8a8_fp8_linear_group_requant(
-        items, count, m0, rq, qy.data_ptr(), sy.data_ptr(),
+        items, count, m0, rq, qy.data_ptr() if requant else None,
+        sy.data_ptr() if requant else None,
         ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
         _stream_ptr(dev)), "fp8_linear_group_requant")
+    if not requant:
+        return ys, None, None
     return ys, qy.view(torch.float8_e4m3fn), sy
 
 

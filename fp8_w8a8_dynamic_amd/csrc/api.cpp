@@ -356,12 +356,15 @@ int check_group_items(const fp8w8a8_group_fp8_linear* items, int count, int64_t 
   return FP8W8A8_OK;
 }
 
-// Shape rules of the re-quantized item; its split count and workspace.
+// Shape rules of the split item (n <= kRequantMaxN when its output is
+// re-quantized); its split count and workspace.
 int group_requant_plan(const fp8w8a8_group_fp8_linear* items, int count, int64_t m,
-                       int rq, fp8w8a8::TokLinear* g, int* splits, size_t* bytes) {
+                       int rq, bool requant, fp8w8a8::TokLinear* g, int* splits,
+                       size_t* bytes) {
   int st = check_group_items(items, count, m, g);
   if (st != FP8W8A8_OK) return st;
-  if (rq < 0 || rq >= count || items[rq].n > fp8w8a8::kRequantMaxN) return FP8W8A8_ERR_SHAPE;
+  if (rq < 0 || rq >= count || (requant && items[rq].n > fp8w8a8::kRequantMaxN))
+    return FP8W8A8_ERR_SHAPE;
   *splits = fp8w8a8::tok_group_splits(g, count, m, rq);
   *bytes = static_cast<size_t>(*splits) * static_cast<size_t>(m) *
            static_cast<size_t>(items[rq].n) * sizeof(float);
@@ -808,8 +811,9 @@ size_t fp8w8a8_group_requant_workspace_bytes(const fp8w8a8_group_fp8_linear* ite
   fp8w8a8::TokLinear g[fp8w8a8::kGroupMax];
   int splits = 0;
   size_t bytes = 0;
-  return group_requant_plan(items, count, m, rq, g, &splits, &bytes) == FP8W8A8_OK ? bytes
-                                                                                  : 0;
+  return group_requant_plan(items, count, m, rq, false, g, &splits, &bytes) == FP8W8A8_OK
+             ? bytes
+             : 0;
 }
 
 int fp8w8a8_fp8_linear_group_requant(const fp8w8a8_group_fp8_linear* items, int count,
@@ -819,16 +823,19 @@ int fp8w8a8_fp8_linear_group_requant(const fp8w8a8_group_fp8_linear* items, int 
   fp8w8a8::TokLinear g[fp8w8a8::kGroupMax];
   int splits = 0;
   size_t need = 0;
-  int st = group_requant_plan(items, count, m, rq, g, &splits, &need);
+  // qy and y_scale: both given (re-quantize) or both null (split only).
+  const bool requant = qy != nullptr || y_scale != nullptr;
+  int st = group_requant_plan(items, count, m, rq, requant, g, &splits, &need);
   if (st != FP8W8A8_OK) return st;
-  if (!qy || !y_scale || !workspace) return FP8W8A8_ERR_NULL;
-  if (!aligned16(qy) || (reinterpret_cast<uintptr_t>(y_scale) & 3u) != 0 ||
+  if ((requant && (!qy || !y_scale)) || !workspace) return FP8W8A8_ERR_NULL;
+  if ((requant && (!aligned16(qy) || (reinterpret_cast<uintptr_t>(y_scale) & 3u) != 0)) ||
       !aligned16(workspace))
     return FP8W8A8_ERR_ALIGN;
   if (workspace_bytes < need) return FP8W8A8_ERR_WORKSPACE;
-  // qy, y_scale and the workspace overlap no input, no y and one another.
-  const Range extra[3] = {span(qy, m, items[rq].n, items[rq].n, 1),
-                          span(y_scale, m, 1, 1, 4),
+  // qy, y_scale and the workspace overlap no input, no y and one another
+  // (a null output's range is empty).
+  const Range extra[3] = {span(qy, requant ? m : 0, items[rq].n, items[rq].n, 1),
+                          span(y_scale, requant ? m : 0, 1, 1, 4),
                           Range{reinterpret_cast<uintptr_t>(workspace),
                                 reinterpret_cast<uintptr_t>(workspace) + need}};
   for (int a = 0; a < 3; ++a) {

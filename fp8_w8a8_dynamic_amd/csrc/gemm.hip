@@ -637,6 +637,18 @@ hipError_t launch_gemm_requant(const GemmPlan& p, const uint8_t* qx, const float
   return launch_splitk_reduce_quant(part, p.splits, sx, sw, m, n, y, ldy, q, scale, stream);
 }
 
+hipError_t launch_splitk_reduce(const float* part, int splits, const float* sx,
+                                const float* sw, int64_t m, int64_t n, uint16_t* y,
+                                int64_t ldy, hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (n % 4 != 0 || splits < 1) return hipErrorInvalidValue;
+  int64_t blocks = (m * (n / 4) + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  splitk_reduce_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream>>>(
+      part, splits, sx, sw, static_cast<int>(m), static_cast<int>(n), y, ldy);
+  return hipGetLastError();
+}
+
 hipError_t launch_splitk_reduce_quant(const float* part, int splits, const float* sx,
                                       const float* sw, int64_t m, int64_t n, uint16_t* y,
                                       int64_t ldy, uint8_t* q, float* scale,

@@ -155,18 +155,24 @@ struct TokLinear {
 };
 hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
                             hipStream_t stream);
-// The same launch with item rq's output also quantized per token: its K is
-// summed in `splits` ranges of whole 512-byte stages (units of their own in
-// the launch; raw float32 sums [splits, m, n] to `part`), then one kernel
-// adds the ranges in order, writes y and its codes qy [m, n] and scales
-// y_scale [m] (n <= kRequantMaxN).  tok_group_splits is the number of ranges
-// a call takes (test hook FP8W8A8_TOKG_SPLITS), at most kTokGroupMaxSplits
+// The same launch with item rq's K summed in `splits` ranges (units of
+// their own in the launch; raw float32 sums [splits, m, n] to `part`), then
+// one kernel adds the ranges in order and writes y -- and, when qy is not
+// null, quantizes it per token into codes qy [m, n] and scales y_scale [m]
+// (then n <= kRequantMaxN).  tok_group_splits is the number of ranges a
+// call takes (test hook FP8W8A8_TOKG_SPLITS), at most kTokGroupMaxSplits
 // and at most kGroupMax - count + 1.
 constexpr int kTokGroupMaxSplits = 8;
 int tok_group_splits(const TokLinear* items, int count, int64_t m, int rq);
 hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m, int rq,
                                     int splits, float* part, uint8_t* qy, float* y_scale,
                                     hipStream_t stream);
+// Split sums part [splits, m, n] added in split order and scaled as the
+// GEMM's epilogue does, y = bf16(sum * sw[n] * sx[m]) (row stride ldy);
+// n % 4 == 0.
+hipError_t launch_splitk_reduce(const float* part, int splits, const float* sx,
+                                const float* sw, int64_t m, int64_t n, uint16_t* y,
+                                int64_t ldy, hipStream_t stream);
 // Split sums part [splits, m, n] added in split order, scaled as the GEMM's
 // epilogue does (y = bf16(sum * sw[n] * sx[m])), written to y (row stride
 // ldy) and quantized per token into q [m, n] and scale [m];

@@ -527,19 +527,28 @@ int tok_group_splits(const TokLinear* items, int count, int64_t m, int rq) {
   (void)m;
   if (count < 1 || count > kGroupMax || rq < 0 || rq >= count) return 1;
   int64_t others = 0;
+  int64_t k_other = 0;  // the longest K among the other items
   for (int i = 0; i < count; ++i)
-    if (i != rq) others += items[i].n / 64;
+    if (i != rq) {
+      others += items[i].n / 64;
+      k_other = std::max<int64_t>(k_other, items[i].k);
+    }
   const int64_t ur = items[rq].n / 64;
   const int kt = static_cast<int>(items[rq].k / 128);
   const int room = count - 1;  // items left for the K ranges
   int best = 1;
-  // The most K ranges (whole 512-byte stages each) that keep the launch at
-  // one workgroup per CU (256 CUs): measured on the 36-layer stack at 64
-  // tokens (down, K = 12288, beside k and v), 3 ranges (224 units) took
-  // 55.9 us per layer, 4 or 6 ranges (288 / 416 units, some CUs running two
-  // workgroups and so finishing last) 60.1 / 60.6 us, 2 ranges 60.1 us.
-  for (int s = 2; s <= kTokGroupMaxSplits && s <= kGroupMax - room; ++s)
-    if (kt % (4 * s) == 0 && others + s * ur <= 256) best = s;
+  // K ranges of whole 512-byte stages.  Beside other items: the most ranges
+  // that are no shorter than the longest other item, so that the item's
+  // units are not the launch's long pole (measured on the 36-layer stack at
+  // 64 tokens, down with K = 12288 beside k and v, K = 4096: 3 ranges took
+  // 55.2 us per layer, 2 / 4 / 6 ranges 58.9 / 60.0 / 60.4 us; and on the
+  // decode layer at a few tokens, down beside the six other Linears).  On
+  // its own: the most ranges that keep the launch at one workgroup per CU
+  // (256 CUs).
+  for (int s = 2; s <= kTokGroupMaxSplits && s <= kGroupMax - room; ++s) {
+    if (kt % (4 * s) != 0) continue;
+    if (count > 1 ? items[rq].k / s >= k_other : others + s * ur <= 256) best = s;
+  }
   if (const char* e = test_hook("FP8W8A8_TOKG_SPLITS")) {
     const int v = std::atoi(e);
     if (v >= 1 && v <= kTokGroupMaxSplits && v <= kGroupMax - room && kt % v == 0) best = v;
@@ -555,7 +564,7 @@ hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m
       rq >= count || splits < 1 || count - 1 + splits > kGroupMax)
     return hipErrorInvalidValue;
   const TokLinear& R = items[rq];
-  if (!item_ok(R) || R.n > kRequantMaxN || R.k % (128 * splits) != 0)
+  if (!item_ok(R) || (qy != nullptr && R.n > kRequantMaxN) || R.k % (128 * splits) != 0)
     return hipErrorInvalidValue;
   Item list[kGroupMax];
   int c = 0;
@@ -574,6 +583,7 @@ hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m
                      static_cast<int>(R.k), static_cast<int>(16 * R.k), 0};
   hipError_t e = launch_items(list, c, m, stream);
   if (e != hipSuccess) return e;
+  if (qy == nullptr) return launch_splitk_reduce(part, splits, R.sx, R.sw, m, R.n, R.y, R.n, stream);
   return launch_splitk_reduce_quant(part, splits, R.sx, R.sw, m, R.n, R.y, R.n, qy,
                                     y_scale, stream);
 }

@@ -417,31 +417,36 @@ int fp8w8a8_fp8_linear_group(const fp8w8a8_group_fp8_linear* items, int count,
                              int64_t m, void* stream);
 
 /*
- * fp8w8a8_fp8_linear_group with the output of one item, items[rq], also
- * quantized per token for the Linear that reads it next (README
- * "FP8-Dynamic": dynamic per-token activation scales, here for a layer's
- * output that is the next layer's input, as fp8w8a8_fp8_linear_requant
- * does for one Linear).  At a few tokens a layer's last Linear (e.g. down,
- * K = 12288) has too few 64-row units to fill the GPU; here its K is
- * summed in several ranges, each range its own units of the one launch
- * beside the other items (e.g. k and v), and one more kernel adds the
- * ranges in order, writes y and quantizes it:
+ * fp8w8a8_fp8_linear_group with one item, items[rq], summed over K in
+ * several ranges, and optionally its output also quantized per token for
+ * the Linear that reads it next (README "FP8-Dynamic": dynamic per-token
+ * activation scales, here for a layer's output that is the next layer's
+ * input, as fp8w8a8_fp8_linear_requant does for one Linear).  At a few
+ * tokens a long-K Linear (e.g. down, K = 12288) has few 64-row units, each
+ * three times as long as those of the K = 4096 Linears, and becomes the
+ * launch's long pole or leaves the GPU half idle (MOSS-VL-Realtime-FP8
+ * article, "why quantize": these Linears are bound by their weight bytes);
+ * here its K is summed in several ranges, each range its own units of the
+ * one launch beside the other items, and one more kernel adds the ranges
+ * in order, writes y and, if asked, quantizes it:
  *   items[rq].y   exactly what the raw float32 sum of the ranges, added in
  *                 range order, gives through the epilogue
  *                 bf16_rne(sum * x_scale[m] * w_scale[n]) (summation order
  *                 unspecified, so within the tolerance of any float32 sum)
  *   qy            uint8 [m, items[rq].n] E4M3 codes of that y, contiguous,
  *                 and y_scale float32 [m]: exactly
- *                 fp8w8a8_quantize_act_per_token(y)                (output)
+ *                 fp8w8a8_quantize_act_per_token(y); both NULL: y only
+ *                 (output)
  *   every other item exactly as fp8w8a8_fp8_linear_group gives it
  *   workspace     device scratch of at least
  *                 fp8w8a8_group_requant_workspace_bytes(items, count, m, rq)
  *                 bytes (float32 sums [ranges, m, n]; no state survives a
  *                 call; calls that may run concurrently need distinct ones)
- * Rules: those of fp8w8a8_fp8_linear_group; 0 <= rq < count;
- * items[rq].n <= 16384; qy and the workspace 16-byte, y_scale 4-byte
- * aligned; qy, y_scale and the workspace overlap no input, no y and one
- * another.  Errors are returned before anything is launched.
+ * Rules: those of fp8w8a8_fp8_linear_group; 0 <= rq < count; qy and
+ * y_scale both given or both NULL; with them items[rq].n <= 16384, qy
+ * 16-byte and y_scale 4-byte aligned; the workspace 16-byte aligned; qy,
+ * y_scale and the workspace overlap no input, no y and one another.  Errors
+ * are returned before anything is launched.
  * fp8w8a8_group_requant_workspace_bytes returns 0 for invalid arguments.
  */
 size_t fp8w8a8_group_requant_workspace_bytes(const fp8w8a8_group_fp8_linear* items,

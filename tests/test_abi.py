@@ -554,7 +554,12 @@ def test_fp8_linear_group_requant_validation(lib):
     assert ws_bytes(kv + [down], rq=2) == 3 * 64 * 4096 * 4
     assert ws_bytes([down], m=3) == 4 * 3 * 4096 * 4
     assert ws_bytes([down], rq=1) == 0 and ws_bytes([down], rq=-1) == 0
-    assert ws_bytes([item(n=16384 + 64)]) == 0                  # n <= 16384
+    # n > 16384 is allowed without re-quantization (checked at the call);
+    # its 257 units alone exceed one per CU, so one range.
+    assert ws_bytes([item(n=16384 + 64)]) == 64 * (16384 + 64) * 4
+    # Beside items of K = 4096: ranges no shorter than 4096 (decode layer).
+    assert ws_bytes([down, item(qx=300 * A, sx=302 * A, qw=1300 * A, sw=304 * A,
+                                y=306 * A, n=12288, k=4096)], m=4) == 3 * 4 * 4096 * 4
     assert ws_bytes([item(n=96)]) == 0
     assert lib.fp8w8a8_group_requant_workspace_bytes(None, 1, 64, 0) == 0
     # K = 640: 5 tiles, no split into whole stages (one range).
@@ -568,6 +573,12 @@ def test_fp8_linear_group_requant_validation(lib):
     assert run([item(n=16384 + 64)]) == ESHAPE
     assert run([item(sx=None)]) == ENULL
     assert run([down], qy=None) == ENULL and run([down], sy=None) == ENULL
+    # Both null: the ranges added without re-quantization (no n limit).
+    assert run([down], qy=None, sy=None) == EDEV
+    assert run([item(n=16384 + 64)], qy=None, sy=None) == EDEV
+    assert run([down], qy=None, sy=None, ws=None) == ENULL
+    assert run([down], qy=None, sy=None, wsb=4 * 64 * 4096 * 4 - 1) == EWS
+    assert run([down], qy=None, sy=None, ws=1030 * A) == EALIAS
     assert run([down], ws=None) == ENULL
     assert run([down], qy=80 * A + 8) == EALIGN and run([down], sy=96 * A + 2) == EALIGN
     assert run([down], ws=112 * A + 8) == EALIGN

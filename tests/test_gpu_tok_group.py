@@ -129,6 +129,36 @@ def test_decode_layer_grouped(m):
         check_bytes(host_bits(alone[0]), yb, f"{name}: grouped against alone")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("m", [4, 8])
+def test_decode_layer_grouped_down_split(m):
+    """The decode layer at a few tokens as the bench's grouped leg runs it:
+    the seven Linears in one launch with down's K summed in ranges (units of
+    their own beside the other six, then added in order by one more
+    kernel, no re-quantization).  Every output within the oracle's
+    tolerance; the six others bit-identical to the unsplit grouped call."""
+    xs, ws = [], []
+    for j in range(7):
+        x, w = c2_inputs(m, j)
+        xs.append(x)
+        ws.append(_weights(w))
+    refs = [oracle.quant_act_ref(x) for x in xs]
+    acts = [(r, (to_dev_u8(r[0]), to_dev_f32(r[1]))) for r in refs]
+    ys, qy, sy = fq.fp8_linear_group_requant(
+        [a[1][0] for a in acts], [a[1][1] for a in acts], [w[0][0] for w in ws],
+        [w[0][1] for w in ws], [w[0][2] for w in ws], 6, requant=False)
+    torch.cuda.synchronize()
+    assert qy is None and sy is None
+    base = _group(acts, ws)
+    torch.cuda.synchronize()
+    for j, (y, w, r) in enumerate(zip(ys, ws, refs)):
+        name = f"decode M = {m} {LAYER_SHAPES[j][0]}, down split"
+        yb = host_bits(y)
+        check_close(yb, oracle.linear_ref(r[0], r[1], w[1][0], w[1][1]), name)
+        if j != 6:
+            check_bytes(yb, host_bits(base[j]), f"{name}: against the unsplit call")
+
+
 WIDE = [(128, 640), (256, 640), (1024, 1152), (128, 4224), (384, 12288),
         (4096, 512), (128, 128)]
 NARROW = [(64, 640), (192, 640), (320, 4224), (64, 128), (1024, 12288)]
@@ -307,3 +337,12 @@ def test_group_requant_ragged(m, rq, monkeypatch):
         monkeypatch.delenv(key)
         for i in range(3):
             check_bytes(got[i], base[i], f"ragged requant M = {m} {key}={val} item {i}")
+    # Without re-quantization: the same y (the ranges added in the same
+    # order by the plain reduction), no codes.
+    ys, qy, sy = fq.fp8_linear_group_requant(
+        [t[1][0] for t in acts], [t[1][1] for t in acts], [w[0][0] for w in weights],
+        [w[0][1] for w in weights], [w[0][2] for w in weights], rq, requant=False)
+    torch.cuda.synchronize()
+    assert qy is None and sy is None
+    for i in range(3):
+        check_bytes(host_bits(ys[i]), base[i], f"ragged split-only M = {m} item {i}")
