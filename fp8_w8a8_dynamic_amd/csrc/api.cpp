@@ -363,7 +363,8 @@ int group_requant_plan(const fp8w8a8_group_fp8_linear* items, int count, int64_t
                        size_t* bytes) {
   int st = check_group_items(items, count, m, g);
   if (st != FP8W8A8_OK) return st;
-  if (rq < 0 || rq >= count || (requant && items[rq].n > fp8w8a8::kRequantMaxN))
+  if (rq < 0 || rq >= count ||
+      items[rq].n > (requant ? fp8w8a8::kRequantMaxN : fp8w8a8::kTokSplitMaxN))
     return FP8W8A8_ERR_SHAPE;
   *splits = fp8w8a8::tok_group_splits(g, count, m, rq);
   *bytes = static_cast<size_t>(*splits) * static_cast<size_t>(m) *

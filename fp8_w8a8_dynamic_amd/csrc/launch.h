@@ -163,6 +163,9 @@ hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
 // call takes (test hook FP8W8A8_TOKG_SPLITS), at most kTokGroupMaxSplits
 // and at most kGroupMax - count + 1.
 constexpr int kTokGroupMaxSplits = 8;
+// The split item's raw sums are addressed with 32-bit offsets per range
+// (m * n * 4 bytes, m <= 64): n is bounded accordingly.
+constexpr int64_t kTokSplitMaxN = int64_t{1} << 20;
 int tok_group_splits(const TokLinear* items, int count, int64_t m, int rq);
 hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m, int rq,
                                     int splits, float* part, uint8_t* qy, float* y_scale,

@@ -564,7 +564,8 @@ hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m
       rq >= count || splits < 1 || count - 1 + splits > kGroupMax)
     return hipErrorInvalidValue;
   const TokLinear& R = items[rq];
-  if (!item_ok(R) || (qy != nullptr && R.n > kRequantMaxN) || R.k % (128 * splits) != 0)
+  if (!item_ok(R) || R.n > (qy != nullptr ? kRequantMaxN : kTokSplitMaxN) ||
+      R.k % (128 * splits) != 0)
     return hipErrorInvalidValue;
   Item list[kGroupMax];
   int c = 0;

@@ -443,7 +443,8 @@ int fp8w8a8_fp8_linear_group(const fp8w8a8_group_fp8_linear* items, int count,
  *                 bytes (float32 sums [ranges, m, n]; no state survives a
  *                 call; calls that may run concurrently need distinct ones)
  * Rules: those of fp8w8a8_fp8_linear_group; 0 <= rq < count; qy and
- * y_scale both given or both NULL; with them items[rq].n <= 16384, qy
+ * y_scale both given or both NULL; items[rq].n <= 2^20, and with them
+ * items[rq].n <= 16384, qy
  * 16-byte and y_scale 4-byte aligned; the workspace 16-byte aligned; qy,
  * y_scale and the workspace overlap no input, no y and one another.  Errors
  * are returned before anything is launched.

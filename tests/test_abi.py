@@ -576,6 +576,10 @@ def test_fp8_linear_group_requant_validation(lib):
     # Both null: the ranges added without re-quantization (no n limit).
     assert run([down], qy=None, sy=None) == EDEV
     assert run([item(n=16384 + 64)], qy=None, sy=None) == EDEV
+    # The split item's sums are addressed in 32 bits: n <= 2^20.
+    big = item(qw=4096 * A, y=64 * A, n=(1 << 20) + 64, k=128)
+    assert ws_bytes([big]) == 0
+    assert run([big], qy=None, sy=None, ws=8192 * A) == ESHAPE
     assert run([down], qy=None, sy=None, ws=None) == ENULL
     assert run([down], qy=None, sy=None, wsb=4 * 64 * 4096 * 4 - 1) == EWS
     assert run([down], qy=None, sy=None, ws=1030 * A) == EALIAS
