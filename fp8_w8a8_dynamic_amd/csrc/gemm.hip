@@ -569,13 +569,25 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k) {
     if (t8 < t3) p.cfg = 8;
   }
   const int64_t tiles4 = ((m + 127) / 128) * ((n + 127) / 128);
+  if (p.cfg == 4 && tiles4 > 256) {
+    // More than one round of 128x128 tiles (one workgroup per CU) where
+    // 256x128 tiles fit in one: e.g. a packed gate|up projection (N = 24576)
+    // at 256 tokens, 384 tiles of 128x128 against 192 of 256x128 (measured
+    // 48.3 -> 35.5 us).
+    const int64_t tiles10 = ((m + 255) / 256) * ((n + 127) / 128);
+    if (tiles10 <= 256) p.cfg = 10;
+  }
   if (big_tiles < 128 && tiles4 < 128) {
     // Few tokens (m up to a few hundred): too few output tiles to keep the
     // CUs streaming the weights.  128x64 tiles (one workgroup per CU), and
     // K split so that about one workgroup per CU results, at most 8 ways
     // (measured at m = 64 and 256 on the layer's shapes: more splits cost
     // more in partial-sum traffic than they gain); the splits' float32
-    // partial sums go through the workspace to a reduction kernel.
+    // partial sums go through the workspace to a reduction kernel.  (Leaving
+    // K = 4096 unsplit looked 20-30 % faster in eager back-to-back calls,
+    // where the extra reduction launch costs host time, but made the
+    // 36-layer stack replayed as a graph slower: 4.16 -> 4.52 ms per pass at
+    // m = 64.)
     p.cfg = 5;
     const int64_t tiles5 = ((m + 127) / 128) * ((n + 63) / 64);
     const int64_t kt = k / kBK;
@@ -607,6 +619,7 @@ hipError_t gemm_cfg(const GemmPlan& p, const uint8_t* qx, const float* sx,
     case 6: return launch_cfg<64, 128, 2, 2, 2, 3>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
     case 7: return launch_cfg<64, 64, 2, 1, 2, 4>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
     case 8: return launch_cfg<256, 192, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
+    case 10: return launch_cfg<256, 128, 4, 2, 2, 1>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
     default: return launch_cfg<128, 64, 2, 2, 4, 2>(qx, sx, qw, sw, m, n, k, y, ldy, sp, part, reduce, stream);
   }
 }

@@ -247,6 +247,7 @@ def test_linear_validation(lib):
     assert lib.fp8w8a8_workspace_bytes(16, 4096, 4096, 0) == 0
     assert lib.fp8w8a8_workspace_bytes(4096, 4096, 4096, 0) == 0
     assert lib.fp8w8a8_workspace_bytes(64, 4096, 4096, 0) >= 2 * 64 * 4096 * 4
+    assert lib.fp8w8a8_workspace_bytes(64, 4096, 12288, 0) >= 2 * 64 * 4096 * 4
 
 
 def _req(lib, qx=A, sx=2 * A, qw=4 * A, sw=24 * A, m=64, n=4096, k=4096, y=32 * A,
@@ -271,11 +272,13 @@ def test_linear_requant_validation(lib):
     assert _req(lib, qy=A) == EALIAS            # codes over the input codes
     assert _req(lib, sy=24 * A) == EALIAS       # scales over the weight scales
     assert _req(lib, y=8 * A) == EALIAS         # y inside the weight codes
-    # m = 64: the GEMM splits K, so the partial sums need the workspace,
-    # which must not overlap any output
-    assert _req(lib, ws=None, wsb=0) == EWS
-    assert _req(lib, wsb=1024) == EWS
-    assert _req(lib, ws=40 * A) == EALIAS
+    # m = 64, k = 12288: the GEMM splits K, so the partial sums need the
+    # workspace, which must not overlap any output (qw: 12 MiB from 4 A)
+    long_k = dict(n=1024, k=12288, ldy=1024)
+    assert _req(lib, **long_k) == EDEV
+    assert _req(lib, ws=None, wsb=0, **long_k) == EWS
+    assert _req(lib, wsb=1024, **long_k) == EWS
+    assert _req(lib, ws=40 * A, **long_k) == EALIAS
     assert _req(lib, m=0) == OK
     assert _req(lib, n=0) == OK
 

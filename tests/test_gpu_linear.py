@@ -211,18 +211,24 @@ def test_deterministic_outputs():
         assert np.array_equal(a, b)
 
 
-SPLIT_SHAPES = [(17, 4096, 4096), (64, 1024, 4096), (64, 4112, 12288),
-                (100, 272, 384), (129, 2048, 1152), (256, 4096, 4096),
-                (100, 6144, 4096)]
+# (m, n, k, splits): None = the plan's own split (long K), else the 128x64
+# configuration forced to that many splits (the plan leaves K <= 4096
+# unsplit).
+SPLIT_SHAPES = [(17, 4096, 4096, 4), (64, 1024, 4096, 8), (64, 4112, 12288, None),
+                (100, 272, 384, 3), (129, 2048, 1152, 5), (256, 4096, 4096, 2),
+                (100, 6144, 4096, 2), (48, 4096, 12288, None), (256, 4096, 12288, None)]
 
 
-@pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
-def test_split_k_gemm(m, n, k, monkeypatch):
+@pytest.mark.parametrize("m,n,k,splits", SPLIT_SHAPES)
+def test_split_k_gemm(m, n, k, splits, monkeypatch):
     """Token counts with few output tiles split K over workgroups (float32
     partial sums in the workspace, added in split order by a second
     kernel): against the oracle, ragged m and n, uneven splits of K, and
     bit-identical on a second run."""
     monkeypatch.setenv("FP8W8A8_FORCE_PATH", "gemm")
+    if splits is not None:
+        monkeypatch.setenv("FP8W8A8_GEMM_CONFIG", "5")
+        monkeypatch.setenv("FP8W8A8_GEMM_SPLITS", str(splits))
     assert fq.workspace_bytes(m, n, k, False) >= m * n * 4 * 2, "plan does not split K"
     qx, sx, qw, sw = _rand_operands(m, n, k, 7 * m + n + k)
     y = _run_linear(qx, sx, qw, sw)
@@ -299,7 +305,8 @@ def _check_pairs(qx, sx, qw, sw, what):
 
 
 @pytest.mark.parametrize("path,cfg", [("gemm", "3"), ("gemm", "4"), ("gemm", "8"),
-                                      ("gemm", "-1"), ("tok", None)])
+                                      ("gemm", "10"), ("gemm", "-1"),
+                                      ("tok", None)])
 def test_all_code_pairs_exact_tiles(path, cfg, monkeypatch):
     """All 254 x 254 finite code pairs through the MFMA tiles (the GEMM's
     configurations, its split-K plan, the token-group GEMV), at K positions
@@ -362,7 +369,7 @@ def test_empty_calls():
     assert y.shape == (0, 16)
 
 
-GEMM_CONFIGS = ["0", "1", "2", "3", "4", "5", "6", "7", "8"]
+GEMM_CONFIGS = ["0", "1", "2", "3", "4", "5", "6", "7", "8", "10"]
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 1040, 384), (513, 528, 640), (4096, 272, 256),
