@@ -663,7 +663,7 @@ def _group_items(qxs, x_scales, qws_tiled, w_scales, ns, outs):
 
 
 def fp8_linear_group(qxs, x_scales, qws_tiled, w_scales, ns, outs=None):
-    """Several Linears on given codes at one token count M (1..64) in one
+    """Several Linears on given codes at one token count M (1..256) in one
     launch: outs[i] bf16 [M, ns[i]] = fp8_linear(qxs[i], x_scales[i], W_i,
     w_scales[i]) up to float32 summation order, with qws_tiled[i] =
     tile_weights(W_i).  Items may share qx and x_scale (pass the same

@@ -333,8 +333,10 @@ int check_group_items(const fp8w8a8_group_fp8_linear* items, int count, int64_t 
   for (int i = 0; i < count; ++i) {
     const fp8w8a8_group_fp8_linear& L = items[i];
     if (!L.qx || !L.x_scale || !L.qw_tiled || !L.w_scale || !L.y) return FP8W8A8_ERR_NULL;
+    // (m * n <= 2^30: the kernel addresses an item's bf16 outputs with
+    // 32-bit byte offsets.)
     if (L.n < 64 || L.n > (int64_t{1} << 24) || L.n % 64 != 0 || L.k < 128 ||
-        L.k > fp8w8a8::kTokGroupMaxK || L.k % 128 != 0)
+        L.k > fp8w8a8::kTokGroupMaxK || L.k % 128 != 0 || L.n * m > (int64_t{1} << 30))
       return FP8W8A8_ERR_SHAPE;
     if (!aligned16(L.qx) || !aligned16(L.x_scale) || !aligned16(L.qw_tiled) ||
         !aligned16(L.w_scale) || !aligned16(L.y))

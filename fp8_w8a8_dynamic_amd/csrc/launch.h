@@ -143,7 +143,7 @@ hipError_t launch_gemv_group_m1(const GroupLinear* items, int count,
 // each, all items at the same m), 1 <= m <= kTokGroupMaxM, up to kGroupMax
 // of them in one launch; qw in the MFMA-tile order of launch_tile_weights.
 // n % 64 == 0, k % 128 == 0, k <= kTokGroupMaxK.
-constexpr int kTokGroupMaxM = 64;
+constexpr int kTokGroupMaxM = 256;
 constexpr int kTokGroupMaxK = 16384;
 struct TokLinear {
   const uint8_t* qx;
@@ -164,7 +164,7 @@ hipError_t launch_tok_group(const TokLinear* items, int count, int64_t m,
 // and at most kGroupMax - count + 1.
 constexpr int kTokGroupMaxSplits = 8;
 // The split item's raw sums are addressed with 32-bit offsets per range
-// (m * n * 4 bytes, m <= 64): n is bounded accordingly.
+// (m * n * 4 bytes, m <= 256): n is bounded accordingly.
 constexpr int64_t kTokSplitMaxN = int64_t{1} << 20;
 int tok_group_splits(const TokLinear* items, int count, int64_t m, int rq);
 hipError_t launch_tok_group_requant(const TokLinear* items, int count, int64_t m, int rq,

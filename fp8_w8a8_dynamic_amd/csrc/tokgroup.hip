@@ -1,4 +1,4 @@
-// Grouped FP8_DYNAMIC Linears on given codes for a few tokens (1 <= M <= 64),
+// Grouped FP8_DYNAMIC Linears on given codes for a few tokens (1 <= M <= 256),
 // up to kGroupMax of them in one persistent launch: per-token E4M3 codes and
 // scales times channel-wise E4M3 weights, float32 accumulation, bf16 output
 // through the token-scale x channel-scale epilogue (MOSS-VL quantization
@@ -67,10 +67,26 @@ namespace tokgroup {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kItemsPerStage = 4;
-constexpr int kStageBytes = kItemsPerStage * 128;
 constexpr uint32_t kPastEnd = 0x80000000u;  // an offset past every descriptor
-constexpr int kDepth = 2;                   // stages of weights requested ahead
+constexpr int kDepth = 2;                   // stages of weights requested ahead (T <= 4)
+
+// Stage geometry per token-block count T (16 T token rows): a stage is IPS
+// MFMA items of 128 K bytes, so that two stages of codes (16 T x 128 IPS
+// bytes each) fit LDS: 4 items up to 64 tokens, 2 up to 128, 1 up to 256.
+constexpr int ips_of(int T) { return T <= 4 ? 4 : (T <= 8 ? 2 : 1); }
+constexpr int sb_of(int T) { return 128 * ips_of(T); }    // stage bytes
+constexpr int nx_of(int T) { return T * ips_of(T) / 2; }  // 16-byte code slots per thread
+// Weights requested this many stages ahead: 16 KB per wave in flight at
+// T <= 8, 14 KB at T = 16.
+constexpr int depth_of(int T) { return T <= 4 ? kDepth : (T <= 8 ? 4 : 7); }
+// Chunk swizzle of a token's LDS row: rows of 32 or 16 chunks take the
+// token's low four bits; rows of 8 chunks (128 bytes, two rows per 256-byte
+// bank line) take bits 1-3, so that the 16 tokens of a block read the same
+// logical chunk from 16 distinct bank groups either way.
+template <int T>
+__device__ __forceinline__ int code_swz(int tok) {
+  return ips_of(T) >= 2 ? (tok & 15) : ((tok >> 1) & 7);
+}
 
 struct Item {
   const uint8_t* qx;  // codes of the item's first K byte (row stride ldx)
@@ -90,6 +106,7 @@ struct Args {
   int units;
   int m;
   int shift;  // workgroups by which each round's deal turns (0 <= shift < grid)
+  int sb;     // stage bytes (sb_of(T))
 };
 
 __device__ __forceinline__ v8i to_v8i(uint4 lo, uint4 hi) {
@@ -116,7 +133,7 @@ __device__ __forceinline__ void cursor_at(Cursor& c, const Args& a, int unit) {
   c.item = 0;
   for (int j = 1; j < a.count; ++j)
     if (unit >= a.it[j].u0) c.item = j;
-  c.stages = (a.it[c.item].k + kStageBytes - 1) / kStageBytes;
+  c.stages = (a.it[c.item].k + a.sb - 1) / a.sb;
 }
 
 // The workgroup's unit after u: round r holds units r G .. r G + G - 1, and
@@ -140,13 +157,14 @@ struct Scales {
 };
 
 // A stage's weight fragments in one wave's registers.
+template <int T>
 struct Weights {
-  uint4 w[kItemsPerStage][2];
+  uint4 w[ips_of(T)][2];
 };
 // This thread's share of a stage's codes (LDS slots j * 256 + tid).
 template <int T>
 struct Codes {
-  uint4 x[2 * T];
+  uint4 x[nx_of(T)];
 };
 
 // Requests for stage c.  When `live` is false the same instructions go out
@@ -158,33 +176,35 @@ __device__ __forceinline__ void load_codes(Codes<T>& xc, const Args& a, const Cu
                                            bool live, int M, int tid) {
   const Item& it = a.it[c.item];
   const int K = it.k;
-  const int k0 = c.stage * kStageBytes;
+  constexpr int CPR = sb_of(T) / 16;  // 16-byte chunks per token row
+  const int k0 = c.stage * sb_of(T);
   // The descriptor ends with token M - 1's last byte of the K range, so
   // tokens past M read as zero.
   const auto xr = row_rsrc(it.qx, static_cast<uint32_t>((M - 1) * it.ldx + K));
 #pragma unroll
-  for (int j = 0; j < 2 * T; ++j) {
-    // LDS slot p (16 bytes) = token p / 32, chunk (p % 32) ^ (token % 16).
+  for (int j = 0; j < nx_of(T); ++j) {
+    // LDS slot p (16 bytes) = token p / CPR, chunk (p % CPR) ^ swizzle.
     const int p = j * 256 + tid;
-    const int tok = p >> 5;
-    const int ch = (p & 31) ^ (tok & 15);
+    const int tok = p / CPR;
+    const int ch = (p % CPR) ^ code_swz<T>(tok);
     const bool ok = live && k0 + (ch >> 3) * 128 < K && tok < M;
     xc.x[j] = buf_load16(xr, ok ? static_cast<uint32_t>(tok * it.ldx + k0 + ch * 16)
                                 : kPastEnd);
   }
 }
 
-__device__ __forceinline__ void load_weights(Weights& s, const Args& a, const Cursor& c,
+template <int T>
+__device__ __forceinline__ void load_weights(Weights<T>& s, const Args& a, const Cursor& c,
                                              bool live, int wave, int lane) {
   const Item& it = a.it[c.item];
   const int K = it.k;
-  const int k0 = c.stage * kStageBytes;
+  const int k0 = c.stage * sb_of(T);
   // The wave's row block: K / 128 consecutive 2 KB tiles.
   const int rb = (c.unit - it.u0) * 4 + wave;
   const auto wr = row_rsrc(it.qw + static_cast<int64_t>(rb) * it.wrb,
                            static_cast<uint32_t>(16 * K));
 #pragma unroll
-  for (int i = 0; i < kItemsPerStage; ++i)
+  for (int i = 0; i < ips_of(T); ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bool ok = live && k0 + i * 128 < K;
@@ -207,28 +227,53 @@ __device__ __forceinline__ void load_scales(Scales<T>& sc, const Args& a, const 
 template <int T>
 __device__ __forceinline__ void store_codes(const Codes<T>& xc, uint8_t* xs, int tid) {
 #pragma unroll
-  for (int j = 0; j < 2 * T; ++j)
+  for (int j = 0; j < nx_of(T); ++j)
     *reinterpret_cast<uint4*>(xs + (j * 256 + tid) * 16) = xc.x[j];
 }
 
 template <int T>
-__device__ __forceinline__ void compute_stage(v4f (&acc)[T], const Weights& s,
+__device__ __forceinline__ void compute_stage(v4f (&acc)[T], const Weights<T>& s,
                                               const uint8_t* xs, int lane) {
   const int r = lane & 15, g = lane >> 4;
+  // (Token 16 t + r has the swizzle of r: blocks start at multiples of 16.)
+  const int sw = code_swz<T>(r);
+  // Token fragment of MFMA j of the stage (item j / T, token block j % T).
+  auto frag = [&](int j) {
+    const int i = j / T, t = j % T;
+    const uint8_t* row = xs + (16 * t + r) * sb_of(T);
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + (((i * 8 + g) ^ sw) * 16));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((i * 8 + 4 + g) ^ sw) * 16));
+    return to_v8i(lo, hi);
+  };
+  if constexpr (T <= 4) {
 #pragma unroll
-  for (int i = 0; i < kItemsPerStage; ++i) {
-    const v8i a = to_v8i(s.w[i][0], s.w[i][1]);
+    for (int i = 0; i < ips_of(T); ++i) {
+      const v8i a = to_v8i(s.w[i][0], s.w[i][1]);
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint8_t* row = xs + (16 * t + r) * kStageBytes;
-      const uint4 lo = *reinterpret_cast<const uint4*>(row + (((i * 8 + g) ^ r) * 16));
-      const uint4 hi = *reinterpret_cast<const uint4*>(row + (((i * 8 + 4 + g) ^ r) * 16));
-      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          a, to_v8i(lo, hi), acc[t], 0, 0, 0, 0, 0, 0);
+      for (int t = 0; t < T; ++t)
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a, frag(i * T + t), acc[t], 0, 0, 0, 0, 0, 0);
+      // One item's fragments at a time (hoisting every LDS read of the
+      // stage would hold 4 x 8 T registers).
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // One item's fragments at a time (hoisting every LDS read of the stage
-    // would hold 4 x 8 T registers).
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // Many token blocks per item: the fragments are read kAhead MFMAs
+    // ahead through a small ring, the order pinned (left to itself the
+    // compiler read each fragment right before its MFMA and waited for it,
+    // one LDS round trip per MFMA).
+    constexpr int kN = ips_of(T) * T, kAhead = 4;
+    v8i ring[kAhead + 1];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) ring[j] = frag(j);
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      if (j + kAhead < kN) ring[(j + kAhead) % (kAhead + 1)] = frag(j + kAhead);
+      const int i = j / T, t = j % T;
+      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          to_v8i(s.w[i][0], s.w[i][1]), ring[j % (kAhead + 1)], acc[t], 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -303,8 +348,8 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
 // request is one the compiler tracks, so the waits it places are exact.
 // Returns false once C was the workgroup's last stage.
 template <int I, int T, int D, int DC>
-__device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T> (&X)[DC],
-                                     uint8_t (*xs)[16 * T * kStageBytes], uint8_t* ob,
+__device__ __forceinline__ bool step(v4f (&acc)[T], Weights<T> (&S)[D + 1], Codes<T> (&X)[DC],
+                                     uint8_t (*xs)[16 * T * sb_of(T)], uint8_t* ob,
                                      Cursor (&Q)[D + 1], const Args& a, int M, int wave,
                                      int tid) {
   static_assert(DC >= 1 && DC <= D, "codes at most as far ahead as the weights");
@@ -335,8 +380,8 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights (&S)[D + 1], Codes<T
 
 template <int T, int D, int DC, int... Is>
 __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&acc)[T],
-                                      Weights (&S)[D + 1], Codes<T> (&X)[DC],
-                                      uint8_t (*xs)[16 * T * kStageBytes], uint8_t* ob,
+                                      Weights<T> (&S)[D + 1], Codes<T> (&X)[DC],
+                                      uint8_t (*xs)[16 * T * sb_of(T)], uint8_t* ob,
                                       Cursor (&Q)[D + 1], const Args& a, int M, int wave,
                                       int tid) {
   return (step<Is, T, D, DC>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
@@ -347,8 +392,8 @@ __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&a
 // CU (a wave's registers beyond 256), for launches of at most one unit per
 // CU, where a workgroup's stage time is the codes' latency.
 template <int T, int D, int DC>
-__global__ __launch_bounds__(256, DC == 1 ? 2 : 1) void tok_group_kernel(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * kStageBytes];
+__global__ __launch_bounds__(256, DC == 1 && T <= 4 ? 2 : 1) void tok_group_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * sb_of(T)];
   __shared__ __attribute__((aligned(16))) uint8_t ob[16 * T * kOutRow];
   const int tid = static_cast<int>(threadIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -364,7 +409,7 @@ __global__ __launch_bounds__(256, DC == 1 ? 2 : 1) void tok_group_kernel(const A
     Q[j] = Q[j - 1];
     if (Q[j].unit < a.units) cursor_next(Q[j], a);
   }
-  Weights S[D + 1];
+  Weights<T> S[D + 1];
   Codes<T> X[DC];
   v4f acc[T];
 #pragma unroll
@@ -396,9 +441,10 @@ __global__ __launch_bounds__(256, DC == 1 ? 2 : 1) void tok_group_kernel(const A
 
 template <int T, int D, int DC>
 hipError_t launch_d(Args a, hipStream_t stream) {
-  // DC = 1: two workgroups per CU (LDS: 16 KB per token block; registers:
-  // two waves per SIMD); DC = 2: one.  256 CUs.
-  int64_t grid = std::min<int64_t>(a.units, (DC == 1 ? 2 : 1) * 256);
+  // T <= 4 with DC = 1: two workgroups per CU (LDS: 16 KB per token block;
+  // registers: two waves per SIMD); otherwise one.  256 CUs.
+  a.sb = sb_of(T);
+  int64_t grid = std::min<int64_t>(a.units, (DC == 1 && T <= 4 ? 2 : 1) * 256);
   if (const char* e = test_hook("FP8W8A8_TOKG_GRID")) {
     const int64_t v = std::atoll(e);
     if (v >= 1) grid = std::min<int64_t>(a.units, v);
@@ -409,12 +455,12 @@ hipError_t launch_d(Args a, hipStream_t stream) {
     int i = 0;
     for (int j = 1; j < a.count; ++j)
       if (unit >= a.it[j].u0) i = j;
-    return (a.it[i].k + kStageBytes - 1) / kStageBytes;
+    return (a.it[i].k + sb_of(T) - 1) / sb_of(T);
   };
   const int shortest = stages_of(static_cast<int>(grid) - 1);
   a.shift = 0;
   for (int i = 0; i < a.count && a.it[i].u0 < grid; ++i)
-    if ((a.it[i].k + kStageBytes - 1) / kStageBytes > shortest) {
+    if ((a.it[i].k + sb_of(T) - 1) / sb_of(T) > shortest) {
       const int end = i + 1 < a.count ? a.it[i + 1].u0 : a.units;
       a.shift += std::min<int>(end, static_cast<int>(grid)) - a.it[i].u0;
     }
@@ -427,13 +473,20 @@ hipError_t launch_d(Args a, hipStream_t stream) {
 // FP8W8A8_TOKG_CODES (1 or 2) and FP8W8A8_TOKG_DEPTH (2 or 3) override.
 template <int T>
 hipError_t launch_t(const Args& a, hipStream_t stream) {
-  const char* e = test_hook("FP8W8A8_TOKG_DEPTH");
-  const int d = e ? std::atoi(e) : kDepth;
   const char* c = test_hook("FP8W8A8_TOKG_CODES");
-  const int dc = c ? std::atoi(c) : (a.units <= 256 ? 2 : 1);
-  if (dc == 2)
-    return d == 3 ? launch_d<T, 3, 2>(a, stream) : launch_d<T, 2, 2>(a, stream);
-  return d == 3 ? launch_d<T, 3, 1>(a, stream) : launch_d<T, 2, 1>(a, stream);
+  const int dc = c ? std::atoi(c) : (T > 4 || a.units <= 256 ? 2 : 1);
+  if constexpr (T > 4) {
+    if (dc == 1) return launch_d<T, depth_of(T), 1>(a, stream);
+    if constexpr (T == 16)
+      if (dc == 4) return launch_d<T, depth_of(T), 4>(a, stream);
+    return launch_d<T, depth_of(T), 2>(a, stream);
+  } else {
+    const char* e = test_hook("FP8W8A8_TOKG_DEPTH");
+    const int d = e ? std::atoi(e) : kDepth;
+    if (dc == 2)
+      return d == 3 ? launch_d<T, 3, 2>(a, stream) : launch_d<T, 2, 2>(a, stream);
+    return d == 3 ? launch_d<T, 3, 1>(a, stream) : launch_d<T, 2, 1>(a, stream);
+  }
 }
 
 // The MFMA-tile permutation of a row-major [n, k] code matrix: one thread
@@ -494,7 +547,9 @@ hipError_t launch_items(tokgroup::Item* list, int count, int64_t m, hipStream_t 
     case 1: return launch_t<1>(a, stream);
     case 2: return launch_t<2>(a, stream);
     case 3: return launch_t<3>(a, stream);
-    default: return launch_t<4>(a, stream);
+    case 4: return launch_t<4>(a, stream);
+    case 5: case 6: case 7: case 8: return launch_t<8>(a, stream);
+    default: return launch_t<16>(a, stream);
   }
 }
 

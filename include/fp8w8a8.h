@@ -397,9 +397,9 @@ int fp8w8a8_tile_weights(const uint8_t* qw, int64_t n, int64_t k, uint8_t* tiled
  *   items[i].qw_tiled the item's [n, k] weight codes in the order of
  *                     fp8w8a8_tile_weights, w_scale float32 [n]      (input)
  *   items[i].y        bf16 [m, n] contiguous                         (output)
- *   items[i].n, .k    64 <= n <= 2^24, n % 64 == 0;
+ *   items[i].n, .k    64 <= n <= 2^24, n % 64 == 0, m * n <= 2^30;
  *                     128 <= k <= 16384, k % 128 == 0
- * Rules: 1 <= m <= 64; 1 <= count <= 16; items is a HOST array (read during
+ * Rules: 1 <= m <= 256; 1 <= count <= 16; items is a HOST array (read during
  * the call only); all pointers 16-byte aligned; every y must overlap no
  * input of any item and no other y.  No workspace.  Errors are returned
  * before anything is launched.

@@ -506,7 +506,9 @@ def test_fp8_linear_group_validation(lib):
     assert lib.fp8w8a8_fp8_linear_group(None, 1, 64, None) == ENULL
     assert run([]) == ESHAPE                                    # count 0
     assert run([item()] * 17) == ESHAPE                         # count > 16
-    assert run([item()], m=0) == ESHAPE and run([item()], m=65) == ESHAPE
+    assert run([item()], m=0) == ESHAPE and run([item()], m=257) == ESHAPE
+    assert run([item(n=(1 << 24))], m=64) != ESHAPE              # m * n = 2^30
+    assert run([item(n=(1 << 24))], m=65) == ESHAPE              # m * n > 2^30
     assert run([item(sx=None)]) == ENULL and run([item(qw=None)]) == ENULL
     assert run([item(n=96)]) == ESHAPE and run([item(n=0)]) == ESHAPE
     assert run([item(n=(1 << 24) + 64)]) == ESHAPE              # n <= 2^24
@@ -571,7 +573,7 @@ def test_fp8_linear_group_requant_validation(lib):
     assert lib.fp8w8a8_fp8_linear_group_requant(None, 1, 64, 0, 80 * A, 96 * A, 112 * A,
                                                 1 << 24, None) == ENULL
     assert run([]) == ESHAPE and run([down] * 17) == ESHAPE
-    assert run([down], m=0) == ESHAPE and run([down], m=65) == ESHAPE
+    assert run([down], m=0) == ESHAPE and run([down], m=257) == ESHAPE
     assert run([down], rq=1) == ESHAPE and run([down], rq=-1) == ESHAPE
     assert run([item(n=16384 + 64)]) == ESHAPE
     assert run([item(sx=None)]) == ENULL

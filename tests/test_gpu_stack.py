@@ -23,7 +23,7 @@ The oracle's free-running chain (its own bf16 outputs feeding its next
 layer) over the first two layers is computed too and its relative
 Frobenius drift reported, not asserted.
 
-At M = 64 the stack also runs as the grouped few-token path would serve it
+At M = 64 (and 256) the stack also runs as the grouped few-token path would serve it
 (the layer input quantized once, q, k, v, o, gate and up in one grouped
 launch on MFMA-tiled weights, up's output quantized, then down), held to
 the same teacher-forced checks on all 36 layers; and as the bench's grouped
@@ -262,10 +262,10 @@ def test_stack_teacher_forced_every_layer(stack, m):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("chain", ["grouped", "grouped_split"])
-def test_stack_grouped_teacher_forced_every_layer_m64(stack, chain):
+@pytest.mark.parametrize("chain,m", [("grouped", 64), ("grouped_split", 64),
+                                     ("grouped_split", 256)])
+def test_stack_grouped_teacher_forced_every_layer(stack, chain, m):
     qws, ref = stack
-    m = 64
     tiled = [[fq.tile_weights(qws[layer][j][0]) for j in range(7)] for layer in range(LAYERS)]
     x0 = c4_x0(m)
     run = _gpu_chain_grouped if chain == "grouped" else _gpu_chain_grouped_split

@@ -1,6 +1,7 @@
 """The grouped call on given codes at a few tokens (fp8w8a8_fp8_linear_group,
-1 <= M <= 64 tokens, up to 16 Linears in one launch) and the weight tiling
-it reads (fp8w8a8_tile_weights).
+1 <= M <= 256 tokens, up to 16 Linears in one launch; 16, 32, 48, 64, 128 or
+256 token rows per unit, in stages of 512, 256 or 128 K bytes) and the
+weight tiling it reads (fp8w8a8_tile_weights).
 
 The tiling is bit-exact against oracle.tile_weights_ref.  Every item's
 output is held to the elementwise tolerance of oracle.check against the
@@ -17,7 +18,8 @@ one shared code buffer in one launch; down on the oracle's codes of the
 GPU's up output), the decode layer's seven Linears at M = 4 and 8 in one
 launch after one grouped quantization, ragged shapes at M = 1 .. 64 (N = 64, K with a partial
 last 512-byte stage, tokens past the last full block of 16, zero and large
-rows), 16 items at the largest K, and the tiling alone on its edge shapes.
+rows; 65-256 tokens in 128- and 256-row units), 16 items at the largest K,
+and the tiling alone on its edge shapes.
 
 fp8w8a8_fp8_linear_group_requant (one item's K summed in ranges, its output
 re-quantized): that item's output within the oracle's tolerance and its
@@ -187,7 +189,9 @@ def _ragged_inputs(m, seed, shapes):
 
 
 @pytest.mark.parametrize("m,shapes", [(m, "wide") for m in (1, 5, 16, 17, 33, 63, 64)]
-                         + [(m, "narrow") for m in (3, 40, 64)])
+                         + [(m, "narrow") for m in (3, 40, 64)]
+                         + [(m, "wide") for m in (65, 128, 129, 200, 256)]
+                         + [(m, "narrow") for m in (100, 256)])
 def test_ragged_shapes(m, shapes, monkeypatch):
     acts, weights = _ragged_inputs(m, m, WIDE if shapes == "wide" else NARROW)
     base = _run_and_check(acts, weights, f"ragged {shapes} M = {m}")
@@ -306,7 +310,7 @@ def test_group_requant_stack_layer0_m64(monkeypatch):
             check_bytes(got[i], ref_kv[i - 1], f"{s} ranges item {i} against alone")
 
 
-@pytest.mark.parametrize("m", [1, 5, 17, 33, 64])
+@pytest.mark.parametrize("m", [1, 5, 17, 33, 64, 96, 256])
 @pytest.mark.parametrize("rq", [0, 2])
 def test_group_requant_ragged(m, rq, monkeypatch):
     """Ragged items (zero and large token rows, K with a partial last
