@@ -63,8 +63,8 @@ DECODE_COPIES = 4             # 4 x 193 MB of weights > 2 x the 256 MB MALL
 # as null once that code differs.
 KERNEL_TRAFFIC = {
     "gemm": {"files": ("gemm.hip", "device_common.h"),
-             "sha1": "5a420c6a366b3ed6795c745824b1c495fbb6b86f",
-             "bytes": 1493586 * 1024},
+             "sha1": "444f460f7dc9991ea3d98b3f7609807aaac9e82b",
+             "bytes": 1493419 * 1024},
     "gemv_group": {"files": ("gemv.hip", "row_ops.h", "device_common.h"),
                    "sha1": "3a03b37f980147340cfe1bf8c5ab1fecf7d3aabd",
                    "bytes": (94860 * 2 + 101) * 1024},
