@@ -367,12 +367,15 @@ int fp8w8a8_quantize_act_group(const fp8w8a8_group_quant* items, int count,
  * statically); a pure byte permutation, its codes and scales unchanged.
  *   qw      E4M3 [n, k], contiguous (row-major, as quantized)     (input)
  *   tiled   n * k bytes                                          (output)
- * Layout: for row block rb (16 rows), K block i (128 bytes), h in {0, 1},
+ * Layout: K in panels of four 128-byte K blocks (the last panel holds the
+ * ipp(p) = min(4, k / 128 - 4 p) blocks left); for panel p, row block rb
+ * (16 rows), block j of the panel (K block i = 4 p + j), h in {0, 1},
  * l in [0, 64), e in [0, 16):
- *   tiled[(rb * (k / 128) + i) * 2048 + h * 1024 + 16 * l + e]
+ *   tiled[p * n * 512 + (rb * ipp(p) + j) * 2048 + h * 1024 + 16 * l + e]
  *     = qw[16 * rb + (l % 16), 128 * i + 64 * h + 16 * (l / 16) + e]
- * i.e. each 16 x 128-byte block is one contiguous 2 KB tile, and the tiles
- * of a row block follow each other in K order.
+ * i.e. each 16 x 128-byte block is one contiguous 2 KB tile, a panel holds
+ * the tiles of every row block for its 512 bytes of K (row block by row
+ * block), and the panels follow each other in K order.
  * Rules: n >= 0, n % 16 == 0; 128 <= k <= 16384, k % 128 == 0; both pointers
  * 16-byte aligned; the two ranges must not overlap.
  */

@@ -239,8 +239,8 @@ def test_outputs_into_given_buffers():
     assert torch.all(big[0] == 7.0) and torch.all(big[m + 1] == 7.0)
 
 
-@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (4096, 4096), (1024, 12288),
-                                 (80, 16384)])
+@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (32, 640), (64, 1408), (4096, 4096),
+                                 (1024, 12288), (80, 16384)])
 def test_tile_weights_bit_exact(n, k):
     qw = torch.from_numpy(np.random.default_rng(n + k).integers(
         0, 256, size=(n, k), dtype=np.uint8)).to("cuda")
