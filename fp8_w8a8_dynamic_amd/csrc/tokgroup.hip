@@ -399,12 +399,20 @@ __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&a
   return (step<Is, T, D, DC>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
 }
 
+// Vector-memory requests complete in order, so a step's closing wait for
+// the codes of stage C + 1 also completes every weight request issued
+// before them: at that point only DC stages of weights stay in flight.
 // DC = 1: two workgroups per CU (two waves per SIMD, 256 registers each).
-// DC = 2: the codes two stages ahead as well, which takes one workgroup per
-// CU (a wave's registers beyond 256), for launches of at most one unit per
-// CU, where a workgroup's stage time is the codes' latency.
+// DC = 2: the codes two stages ahead as well; at T <= 2 that still fits
+// two workgroups per CU, at T = 3 or 4 it takes one (a wave's registers
+// beyond 256) and is chosen for launches of at most one unit per CU.
 template <int T, int D, int DC>
-__global__ __launch_bounds__(256, DC == 1 && T <= 4 ? 2 : 1) void tok_group_kernel(const Args a) {
+constexpr int tok_group_wg_per_cu() {
+  return T <= 2 || (DC == 1 && T <= 4) ? 2 : 1;
+}
+template <int T, int D, int DC>
+__global__ __launch_bounds__(256, (tok_group_wg_per_cu<T, D, DC>())) void tok_group_kernel(
+    const Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * sb_of(T)];
   __shared__ __attribute__((aligned(16))) uint8_t ob[16 * T * kOutRow];
   const int tid = static_cast<int>(threadIdx.x);
@@ -453,10 +461,10 @@ __global__ __launch_bounds__(256, DC == 1 && T <= 4 ? 2 : 1) void tok_group_kern
 
 template <int T, int D, int DC>
 hipError_t launch_d(Args a, hipStream_t stream) {
-  // T <= 4 with DC = 1: two workgroups per CU (LDS: 16 KB per token block;
-  // registers: two waves per SIMD); otherwise one.  256 CUs.
+  // Two workgroups per CU where tok_group_wg_per_cu says so (LDS: 16 KB per
+  // token block; registers: two waves per SIMD); otherwise one.  256 CUs.
   a.sb = sb_of(T);
-  int64_t grid = std::min<int64_t>(a.units, (DC == 1 && T <= 4 ? 2 : 1) * 256);
+  int64_t grid = std::min<int64_t>(a.units, tok_group_wg_per_cu<T, D, DC>() * 256);
   if (const char* e = test_hook("FP8W8A8_TOKG_GRID")) {
     const int64_t v = std::atoll(e);
     if (v >= 1) grid = std::min<int64_t>(a.units, v);
@@ -480,13 +488,15 @@ hipError_t launch_d(Args a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Codes two stages ahead (one workgroup per CU) when the launch has at most
-// one unit per CU, else one stage ahead (two workgroups per CU); test hooks
-// FP8W8A8_TOKG_CODES (1 or 2) and FP8W8A8_TOKG_DEPTH (2 or 3) override.
+// Codes two stages ahead at up to 32 tokens (two workgroups per CU either
+// way) and, at 33-64 tokens, when the launch has at most one unit per CU
+// (then one workgroup per CU); else one stage ahead (two workgroups per
+// CU); test hooks FP8W8A8_TOKG_CODES (1 or 2) and FP8W8A8_TOKG_DEPTH (2 or
+// 3) override.
 template <int T>
 hipError_t launch_t(const Args& a, hipStream_t stream) {
   const char* c = test_hook("FP8W8A8_TOKG_CODES");
-  const int dc = c ? std::atoi(c) : (T > 4 || a.units <= 256 ? 2 : 1);
+  const int dc = c ? std::atoi(c) : (T > 4 || T <= 2 || a.units <= 256 ? 2 : 1);
   if constexpr (T > 4) {
     if (dc == 1) return launch_d<T, depth_of(T), 1>(a, stream);
     if constexpr (T == 16)
