@@ -341,6 +341,16 @@ def test_group_requant_ragged(m, rq, monkeypatch):
         monkeypatch.delenv(key)
         for i in range(3):
             check_bytes(got[i], base[i], f"ragged requant M = {m} {key}={val} item {i}")
+    # K ranges that start inside a 512-byte K panel of the tiled weights
+    # (the split item has K = 1536, twelve K blocks: 2 ranges start at
+    # blocks 0 and 6, 6 ranges at blocks 0, 2, ..., 10): the split item
+    # within the tolerance, the others the same bits.
+    for s in ("2", "6"):
+        monkeypatch.setenv("FP8W8A8_TOKG_SPLITS", s)
+        got = _requant_check(*run(), acts, weights, rq, f"ragged requant M = {m}, {s} ranges")
+        monkeypatch.delenv("FP8W8A8_TOKG_SPLITS")
+        for i in others:
+            check_bytes(got[i], base[i], f"ragged requant M = {m}, {s} ranges, item {i}")
     # Without re-quantization: the same y (the ranges added in the same
     # order by the plain reduction), no codes.
     ys, qy, sy = fq.fp8_linear_group_requant(
