@@ -963,30 +963,37 @@ def host_info(threads):
             "blas_threads": int(threads)}
 
 
-def cpu_baseline(target_s=8.0, decode_frac=4):
+def cpu_baseline(target_s=8.0, decode_frac=4, long_m=1024, long_frac=8):
     """The oracle as it stands, timed on samples of the same workloads, with
     the quantization and the matmul + epilogue timed separately:
     * prefill: all 7 Linears of the M=4096 layer, a subset of tokens and of
       output channels (weights quantized by the oracle beforehand, untimed,
       as the offline step), grown until the timed part reaches ~target_s;
     * decode: the M=1 layer's 7 Linears on 1/decode_frac of their output
-      channels, GB/s of the same algorithmic bytes as the GPU figure."""
+      channels, GB/s of the same algorithmic bytes as the GPU figure;
+    * long prefill: the 7 Linears once on the long-prefill distribution
+      (Student-t, nu = 3, with its all-zero, x1e4 and saturating rows) at
+      long_m tokens and 1/long_frac of the output channels."""
     import oracle
     from workloads import LAYER_SHAPES
-    from workloads.generators import c3_x, outlier_act_bf16, rng_for, weight_bf16
+    from workloads.generators import c3_x, c5_x, outlier_act_bf16, rng_for, weight_bf16
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         threads = os.cpu_count() or 1
 
-    def run(m_s, n_frac, decode=False):
+    def run(m_s, n_frac, decode=False, long=False):
         r = dict(flops=0, quant_s=0.0, mm_s=0.0, quant_bytes=0, mm_bytes=0)
         for j, (_, n, k) in enumerate(LAYER_SHAPES):
             n_s = max(16, n // n_frac)
-            x = (outlier_act_bf16(rng_for(2, m_s, j, 0), (m_s, k)) if decode
-                 else c3_x(PREFILL_M, k, j, rows=m_s))
-            w = weight_bf16(2 if decode else 3, 0, j, n, k, rows=n_s)
+            if long:
+                x = c5_x(m_s, k, j)
+            elif decode:
+                x = outlier_act_bf16(rng_for(2, m_s, j, 0), (m_s, k))
+            else:
+                x = c3_x(PREFILL_M, k, j, rows=m_s)
+            w = weight_bf16(5 if long else 2 if decode else 3, 0, j, n, k, rows=n_s)
             qw, sw = oracle.quant_weight_ref(w)
             t0 = time.perf_counter()
             qx, sx = oracle.quant_act_ref(x)
@@ -1010,6 +1017,8 @@ def cpu_baseline(target_s=8.0, decode_frac=4):
     secs = r["quant_s"] + r["mm_s"]
     d = run(1, decode_frac, decode=True)
     dsecs = d["quant_s"] + d["mm_s"]
+    lp = run(long_m, long_frac, long=True)
+    lsecs = lp["quant_s"] + lp["mm_s"]
     # Algorithmic bytes of the fused decode call, as on the GPU.
     dbytes = sum(max(16, n // decode_frac) * k + 4 * max(16, n // decode_frac) + 2 * k
                  + 2 * max(16, n // decode_frac) for _, n, k in LAYER_SHAPES)
@@ -1027,6 +1036,16 @@ def cpu_baseline(target_s=8.0, decode_frac=4):
                                  f"channels of each of the 7 Linears; quantize + fp64 "
                                  f"matmul + epilogue; {dsecs:.2f} s",
                        "quant_s": round(d["quant_s"], 4), "matmul_s": round(d["mm_s"], 3)},
+            "long_prefill": {"value": round(lp["flops"] / lsecs / 1e12, 6), "unit": "TFLOP/s",
+                             "sample": f"long-prefill distribution (Student-t nu=3 with "
+                                       f"all-zero, x1e4 and saturating rows) at {long_m} "
+                                       f"tokens x 1/{long_frac} of the output channels of "
+                                       f"each of the 7 Linears, once; quantize + fp64 matmul "
+                                       f"+ epilogue; {lsecs:.2f} s",
+                             "quant_gbs": round(lp["quant_bytes"] / lp["quant_s"] / 1e9, 3),
+                             "matmul_gflops": round(lp["flops"] / lp["mm_s"] / 1e9, 2),
+                             "quant_s": round(lp["quant_s"], 3),
+                             "matmul_s": round(lp["mm_s"], 3)},
             "host": host_info(threads)}
 
 
