@@ -98,7 +98,7 @@ __device__ __forceinline__ int code_swz(int tok) {
 struct Item {
   const uint8_t* qx;  // codes of the item's first K byte (row stride ldx)
   const float* sx;
-  const uint8_t* qw;  // tiled (panel order) codes of the whole Linear, n x (16 kbt) tiles
+  const uint8_t* qw;  // tiled (panel order) codes of the whole Linear: n / 16 x kbt tiles
   const float* sw;
   uint16_t* y;
   float* part;  // non-null: raw float32 sums [M, n] here instead of y
@@ -207,7 +207,7 @@ __device__ __forceinline__ void load_weights(Weights<T>& s, const Args& a, const
   const Item& it = a.it[c.item];
   const int K = it.k;
   const int k0 = c.stage * sb_of(T);
-  // The wave's row block: K / 128 consecutive 2 KB tiles.
+  // The wave's row block; its 2 KB tiles lie one per K block, in the K panels.
   const int rb = (c.unit - it.u0) * 4 + wave;
 #pragma unroll
   for (int i = 0; i < ips_of(T); ++i) {
