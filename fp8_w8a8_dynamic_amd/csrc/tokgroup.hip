@@ -30,10 +30,11 @@
 // blocks) of one item over the item's whole K; each of the four waves of a
 // workgroup owns one row block.  K is walked in stages of 512 bytes (four
 // MFMA items).  A stage's weights are requested into registers D stages
-// ahead (a ring of D + 1 slots); its codes (16 T token rows x 512 bytes,
-// T = ceil(M / 16), each thread a 16-byte share) one stage ahead, into
-// registers, and written to LDS one step before their use, where the four
-// waves read them.  A weight fragment feeds T MFMAs, one per block of 16
+// ahead (a ring of D + 1 slots, or of D slots refilled item by item as
+// the MFMAs take them); its codes (16 T token rows x 512 bytes,
+// T = ceil(M / 16), each thread a 16-byte share) one or two stages ahead,
+// into registers, and written to LDS one step before their use, where the
+// four waves read them.  A weight fragment feeds T MFMAs, one per block of 16
 // tokens, so the codes cross L2 once per 64 weight rows.  A workgroup walks
 // its units as one stream of stages: the next unit's first stages are in
 // flight while the current unit finishes.  Units are numbered longest K
@@ -201,18 +202,39 @@ __device__ __forceinline__ void load_codes(Codes<T>& xc, const Args& a, const Cu
   }
 }
 
+// Item i of stage c's weights for this wave: its 2 KB tile in the panel
+// order (panel p = ib / 4 holds ipp tiles of every row block, row block by
+// row block; all wave-uniform).
+template <int T>
+__device__ __forceinline__ void load_weight_item(uint4 (&w)[2], const Args& a, const Cursor& c,
+                                                 bool live, int i, int wave, int lane) {
+  const Item& it = a.it[c.item];
+  const int k0 = c.stage * sb_of(T);
+  // The wave's row block; its 2 KB tiles lie one per K block, in the K panels.
+  const int rb = (c.unit - it.u0) * 4 + wave;
+  const bool ok = live && k0 + i * 128 < it.k;
+  const int ib = it.kb0 + (ok ? k0 / 128 + i : 0);
+  const int p = ib >> 2, ipp = min(4, it.kbt - 4 * p);
+  const auto wr = row_rsrc(it.qw + static_cast<int64_t>(p) * it.n * 512 +
+                               (static_cast<int64_t>(rb) * ipp + (ib & 3)) * 2048,
+                           2048u);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    w[h] = buf_load16_stream(wr, ok ? static_cast<uint32_t>(h * 1024 + lane * 16) : kPastEnd);
+}
+
+// A whole stage (the same addresses as load_weight_item for each item;
+// written out here, as routing it through the per-item helper made the
+// compiler keep the T = 8 ring in scratch).
 template <int T>
 __device__ __forceinline__ void load_weights(Weights<T>& s, const Args& a, const Cursor& c,
                                              bool live, int wave, int lane) {
   const Item& it = a.it[c.item];
   const int K = it.k;
   const int k0 = c.stage * sb_of(T);
-  // The wave's row block; its 2 KB tiles lie one per K block, in the K panels.
   const int rb = (c.unit - it.u0) * 4 + wave;
 #pragma unroll
   for (int i = 0; i < ips_of(T); ++i) {
-    // Tile (rb, ib) of the panel order: panel p = ib / 4 holds ipp tiles of
-    // every row block, row block by row block (all wave-uniform).
     const bool ok = live && k0 + i * 128 < K;
     const int ib = it.kb0 + (ok ? k0 / 128 + i : 0);
     const int p = ib >> 2, ipp = min(4, it.kbt - 4 * p);
@@ -289,6 +311,38 @@ __device__ __forceinline__ void compute_stage(v4f (&acc)[T], const Weights<T>& s
   }
 }
 
+// compute_stage with a rolling refill (T <= 4): right after item i's MFMAs
+// have taken its weight fragment, item i of stage c (the stage D slots
+// later) is requested into the same registers, so D stage slots keep D
+// stages of weights in flight where the requests at the top of a step
+// need D + 1 (same MFMAs in the same order: the same bits).
+template <int T>
+__device__ __forceinline__ void compute_stage_refill(v4f (&acc)[T], Weights<T>& s,
+                                                     const uint8_t* xs, int lane,
+                                                     const Args& a, const Cursor& c,
+                                                     bool live, int wave) {
+  static_assert(T <= 4, "one item's fragments at a time");
+  const int r = lane & 15, g = lane >> 4;
+  const int sw = code_swz<T>(r);
+  auto frag = [&](int j) {
+    const int i = j / T, t = j % T;
+    const uint8_t* row = xs + (16 * t + r) * sb_of(T);
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + (((i * 8 + g) ^ sw) * 16));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((i * 8 + 4 + g) ^ sw) * 16));
+    return to_v8i(lo, hi);
+  };
+#pragma unroll
+  for (int i = 0; i < ips_of(T); ++i) {
+    const v8i wa = to_v8i(s.w[i][0], s.w[i][1]);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          wa, frag(i * T + t), acc[t], 0, 0, 0, 0, 0, 0);
+    load_weight_item<T>(s.w[i], a, c, live, i, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One token's 64 outputs of a unit in LDS (bf16), padded so that the 16
 // tokens of a write land in 16 distinct bank groups.
 constexpr int kOutRow = 64 * 2 + 16;
@@ -359,12 +413,17 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[T], const Scales<T>& sc,
 // requested before them and leaves the later requests in flight.  Every
 // request is one the compiler tracks, so the waits it places are exact.
 // Returns false once C was the workgroup's last stage.
-template <int I, int T, int D, int DC>
-__device__ __forceinline__ bool step(v4f (&acc)[T], Weights<T> (&S)[D + 1], Codes<T> (&X)[DC],
-                                     uint8_t (*xs)[16 * T * sb_of(T)], uint8_t* ob,
-                                     Cursor (&Q)[D + 1], const Args& a, int M, int wave,
-                                     int tid) {
+// Weight stage slots: D + 1 when a step requests its stage at the top, D
+// with the rolling refill (RR).
+constexpr int slots_of(int D, bool RR) { return RR ? D : D + 1; }
+
+template <int I, int T, int D, int DC, bool RR>
+__device__ __forceinline__ bool step(v4f (&acc)[T], Weights<T> (&S)[slots_of(D, RR)],
+                                     Codes<T> (&X)[DC], uint8_t (*xs)[16 * T * sb_of(T)],
+                                     uint8_t* ob, Cursor (&Q)[D + 1], const Args& a, int M,
+                                     int wave, int tid) {
   static_assert(DC >= 1 && DC <= D, "codes at most as far ahead as the weights");
+  constexpr int NS = slots_of(D, RR);
   // Q[0] = C, Q[j] = C + j (a unit past the end once the units run out).
   const int lane = tid & 63;
   const bool more1 = Q[1].unit < a.units, moreC = Q[DC].unit < a.units,
@@ -375,11 +434,16 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights<T> (&S)[D + 1], Code
   Scales<T> sc;
   if (last) load_scales(sc, a, Q[0], M, wave, lane);
   load_codes(X[I % DC], a, moreC ? Q[DC] : Q[0], moreC, M, tid);
-  load_weights(S[(I + D) % (D + 1)], a, moreD ? Q[D] : Q[0], moreD, wave, lane);
+  if constexpr (!RR)
+    load_weights(S[(I + D) % NS], a, moreD ? Q[D] : Q[0], moreD, wave, lane);
   // Keep the requests ahead of the MFMAs (the scheduler would otherwise
   // sink them below).
   __builtin_amdgcn_sched_barrier(0);
-  compute_stage(acc, S[I % (D + 1)], xs[I % 2], lane);
+  if constexpr (RR)
+    compute_stage_refill(acc, S[I % NS], xs[I % 2], lane, a, moreD ? Q[D] : Q[0], moreD,
+                         wave);
+  else
+    compute_stage(acc, S[I % NS], xs[I % 2], lane);
   if (last) epilogue(acc, sc, a, Q[0], M, wave, tid, ob);
   if (!more1) return false;
   store_codes(X[(I + 1) % DC], xs[(I + 1) % 2], tid);
@@ -390,13 +454,13 @@ __device__ __forceinline__ bool step(v4f (&acc)[T], Weights<T> (&S)[D + 1], Code
   return true;
 }
 
-template <int T, int D, int DC, int... Is>
+template <int T, int D, int DC, bool RR, int... Is>
 __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&acc)[T],
-                                      Weights<T> (&S)[D + 1], Codes<T> (&X)[DC],
+                                      Weights<T> (&S)[slots_of(D, RR)], Codes<T> (&X)[DC],
                                       uint8_t (*xs)[16 * T * sb_of(T)], uint8_t* ob,
                                       Cursor (&Q)[D + 1], const Args& a, int M, int wave,
                                       int tid) {
-  return (step<Is, T, D, DC>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
+  return (step<Is, T, D, DC, RR>(acc, S, X, xs, ob, Q, a, M, wave, tid) && ...);
 }
 
 // Vector-memory requests complete in order, so a step's closing wait for
@@ -406,13 +470,18 @@ __device__ __forceinline__ bool steps(std::integer_sequence<int, Is...>, v4f (&a
 // DC = 2: the codes two stages ahead as well; at T <= 2 that still fits
 // two workgroups per CU, at T = 3 or 4 it takes one (a wave's registers
 // beyond 256) and is chosen for launches of at most one unit per CU.
-template <int T, int D, int DC>
+// RR (T <= 4): the weights refilled item by item as each stage's MFMAs
+// take them (compute_stage_refill), so D slots hold what D + 1 held; the
+// registers freed take the second stage of codes, and DC = 2 fits two
+// workgroups per CU at T = 3 and 4 too.
+template <int T, int D, int DC, bool RR>
 constexpr int tok_group_wg_per_cu() {
-  return T <= 2 || (DC == 1 && T <= 4) ? 2 : 1;
+  return T <= 2 || ((DC == 1 || RR) && T <= 4) ? 2 : 1;
 }
-template <int T, int D, int DC>
-__global__ __launch_bounds__(256, (tok_group_wg_per_cu<T, D, DC>())) void tok_group_kernel(
+template <int T, int D, int DC, bool RR>
+__global__ __launch_bounds__(256, (tok_group_wg_per_cu<T, D, DC, RR>())) void tok_group_kernel(
     const Args a) {
+  static_assert(!RR || T <= 4, "the rolling refill reads one item's fragments at a time");
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * T * sb_of(T)];
   __shared__ __attribute__((aligned(16))) uint8_t ob[16 * T * kOutRow];
   const int tid = static_cast<int>(threadIdx.x);
@@ -429,7 +498,7 @@ __global__ __launch_bounds__(256, (tok_group_wg_per_cu<T, D, DC>())) void tok_gr
     Q[j] = Q[j - 1];
     if (Q[j].unit < a.units) cursor_next(Q[j], a);
   }
-  Weights<T> S[D + 1];
+  Weights<T> S[slots_of(D, RR)];
   Codes<T> X[DC];
   v4f acc[T];
 #pragma unroll
@@ -449,22 +518,23 @@ __global__ __launch_bounds__(256, (tok_group_wg_per_cu<T, D, DC>())) void tok_gr
   }
   store_codes(X[0], xs[0], tid);
   lds_barrier();
-  constexpr int kPeriod = (D + 1) % 2 == 0 ? D + 1 : 2 * (D + 1);
+  constexpr int NS = slots_of(D, RR);
+  constexpr int kPeriod = NS % 2 == 0 ? NS : 2 * NS;
   static_assert(kPeriod % DC == 0, "code ring period");
-  while (steps<T, D, DC>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, ob, Q,
-                         a, M, wave, tid)) {
+  while (steps<T, D, DC, RR>(std::make_integer_sequence<int, kPeriod>{}, acc, S, X, xs, ob,
+                             Q, a, M, wave, tid)) {
   }
   // Nothing in flight when the workgroup leaves (the last requests read
   // nothing, but their registers go with the workgroup).
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-template <int T, int D, int DC>
+template <int T, int D, int DC, bool RR = false>
 hipError_t launch_d(Args a, hipStream_t stream) {
   // Two workgroups per CU where tok_group_wg_per_cu says so (LDS: 16 KB per
   // token block; registers: two waves per SIMD); otherwise one.  256 CUs.
   a.sb = sb_of(T);
-  int64_t grid = std::min<int64_t>(a.units, tok_group_wg_per_cu<T, D, DC>() * 256);
+  int64_t grid = std::min<int64_t>(a.units, tok_group_wg_per_cu<T, D, DC, RR>() * 256);
   if (const char* e = test_hook("FP8W8A8_TOKG_GRID")) {
     const int64_t v = std::atoll(e);
     if (v >= 1) grid = std::min<int64_t>(a.units, v);
@@ -484,17 +554,30 @@ hipError_t launch_d(Args a, hipStream_t stream) {
       const int end = i + 1 < a.count ? a.it[i + 1].u0 : a.units;
       a.shift += std::min<int>(end, static_cast<int>(grid)) - a.it[i].u0;
     }
-  tok_group_kernel<T, D, DC><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
+  tok_group_kernel<T, D, DC, RR>
+      <<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 // Codes two stages ahead at up to 32 tokens (two workgroups per CU either
-// way) and, at 33-64 tokens, when the launch has at most one unit per CU
-// (then one workgroup per CU); else one stage ahead (two workgroups per
-// CU); test hooks FP8W8A8_TOKG_CODES (1 or 2) and FP8W8A8_TOKG_DEPTH (2 or
-// 3) override.
+// way); at 33-64 tokens the rolling refill (below), or with a test hook
+// the earlier variants: codes two stages ahead when the launch has at most
+// one unit per CU (then one workgroup per CU), else one stage ahead (two
+// workgroups per CU); test hooks FP8W8A8_TOKG_CODES (1 or 2) and
+// FP8W8A8_TOKG_DEPTH (2 or 3) override.
 template <int T>
 hipError_t launch_t(const Args& a, hipStream_t stream) {
+  if constexpr (T == 3 || T == 4) {
+    // 33-64 tokens: the rolling refill with the codes two stages ahead, two
+    // workgroups per CU (the 36-layer stack at M = 64: 2.01 -> 1.93 ms per
+    // pass).  Test hooks: FP8W8A8_TOKG_ROLL=0|1; with FP8W8A8_TOKG_CODES or
+    // FP8W8A8_TOKG_DEPTH set (and no ROLL) the variants below run instead.
+    const char* r = test_hook("FP8W8A8_TOKG_ROLL");
+    const bool roll = r ? r[0] == '1'
+                        : test_hook("FP8W8A8_TOKG_CODES") == nullptr &&
+                              test_hook("FP8W8A8_TOKG_DEPTH") == nullptr;
+    if (roll) return launch_d<T, kDepth, 2, true>(a, stream);
+  }
   const char* c = test_hook("FP8W8A8_TOKG_CODES");
   const int dc = c ? std::atoi(c) : (T > 4 || T <= 2 || a.units <= 256 ? 2 : 1);
   if constexpr (T > 4) {

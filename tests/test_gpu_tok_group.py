@@ -197,11 +197,13 @@ def test_ragged_shapes(m, shapes, monkeypatch):
     base = _run_and_check(acts, weights, f"ragged {shapes} M = {m}")
     # The same bits on a persistent grid of 1, 2 and 7 workgroups (hundreds
     # of units each, the pipeline running across unit boundaries), with
-    # the weights requested three stages ahead instead of two, and with the
-    # codes one and two stages ahead.
+    # the weights requested three stages ahead instead of two, with the
+    # codes one and two stages ahead, and (33-64 tokens) without the
+    # rolling refill of the weights.
     for key, val in (("FP8W8A8_TOKG_GRID", "1"), ("FP8W8A8_TOKG_GRID", "2"),
                      ("FP8W8A8_TOKG_GRID", "7"), ("FP8W8A8_TOKG_DEPTH", "3"),
-                     ("FP8W8A8_TOKG_CODES", "1"), ("FP8W8A8_TOKG_CODES", "2")):
+                     ("FP8W8A8_TOKG_CODES", "1"), ("FP8W8A8_TOKG_CODES", "2"),
+                     ("FP8W8A8_TOKG_ROLL", "0")):
         monkeypatch.setenv(key, val)
         ys = _group(acts, weights)
         torch.cuda.synchronize()
@@ -315,8 +317,8 @@ def test_group_requant_stack_layer0_m64(monkeypatch):
 def test_group_requant_ragged(m, rq, monkeypatch):
     """Ragged items (zero and large token rows, K with a partial last
     512-byte stage, N = 64) with the re-quantized item first or last; the
-    same bits on a persistent grid of 1 and 7 workgroups and with the codes
-    one and two stages ahead."""
+    same bits on a persistent grid of 1 and 7 workgroups, with the codes
+    one and two stages ahead and without the rolling refill."""
     # (Items 0 and 1 share one code buffer, so they share K.)
     shapes = ([(320, 1536), (64, 1536), (1024, 1152)] if rq == 0
               else [(64, 640), (192, 640), (384, 1536)])
@@ -335,7 +337,8 @@ def test_group_requant_ragged(m, rq, monkeypatch):
     for i, y in zip(others, alone):
         check_bytes(base[i], host_bits(y), f"ragged requant M = {m} item {i} against alone")
     for key, val in (("FP8W8A8_TOKG_GRID", "1"), ("FP8W8A8_TOKG_GRID", "7"),
-                     ("FP8W8A8_TOKG_CODES", "1"), ("FP8W8A8_TOKG_CODES", "2")):
+                     ("FP8W8A8_TOKG_CODES", "1"), ("FP8W8A8_TOKG_CODES", "2"),
+                     ("FP8W8A8_TOKG_ROLL", "0")):
         monkeypatch.setenv(key, val)
         got = _requant_check(*run(), acts, weights, rq, f"ragged requant M = {m} {key}={val}")
         monkeypatch.delenv(key)
